@@ -1,0 +1,430 @@
+// C ABI of the fused MoE layer (declared in include/moe.h): host-side
+// argument validation, workspace layout, launch sequencing, kernel timing.
+//
+// Every check runs before the first HIP call of an entry point, so a bad
+// argument enqueues nothing.  The library owns no device memory: all buffers
+// come from the caller, and the workspace is carved into fixed regions.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------ timing
+struct Rec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_mu;
+bool g_prof = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_before(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Rec r;
+  r.name = name;
+  r.a = pooled_event();
+  r.b = pooled_event();
+  if (r.a) (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+}
+
+void prof_after(const char*, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_recs.empty() && g_recs.back().b) (void)hipEventRecord(g_recs.back().b, s);
+}
+
+LaunchCtx make_ctx(void* stream) {
+  LaunchCtx c;
+  c.stream = (hipStream_t)stream;
+  bool prof;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    prof = g_prof;
+  }
+  c.before = prof ? prof_before : nullptr;
+  c.after = prof ? prof_after : nullptr;
+  return c;
+}
+
+// ------------------------------------------------------------------ checks
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int64_t kMaxR = int64_t(1) << 27;
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->T < 1 || s->T > kMaxT) return fail(MOE_ERR_INVALID_ARGUMENT, "T=%lld outside [1, 2^24]", (long long)s->T);
+  if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "E=%lld outside [1, 1024]", (long long)s->E);
+  if (s->k < 1 || s->k > s->E) return fail(MOE_ERR_INVALID_ARGUMENT, "k=%lld outside [1, E=%lld]", (long long)s->k, (long long)s->E);
+  if (s->T * s->k > kMaxR) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k=%lld above 2^27", (long long)(s->T * s->k));
+  if (s->d < 8 || s->d > 16384 || s->d % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "d=%lld must be a multiple of 8 in [8, 16384]", (long long)s->d);
+  if (s->I < 8 || s->I > 16384 || s->I % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "I=%lld must be a multiple of 8 in [8, 16384]", (long long)s->I);
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "dtype=%d unknown", s->dtype);
+  if (s->logits_dtype != MOE_F32 && s->logits_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_dtype=%d unknown", s->logits_dtype);
+  if (s->precision != MOE_PREC_NATIVE && s->precision != MOE_PREC_FP8_BLOCK) return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
+  if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  if (s->precision == MOE_PREC_FP8_BLOCK) {
+    if (s->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs dtype bf16");
+    if (s->d % 128 || s->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs d and I multiples of 128");
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision is not built in this library");
+  }
+  return MOE_OK;
+}
+
+#define CHECK_PTR(p) \
+  if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", #p)
+
+size_t elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t hist = 0, tile_off = 0, order = 0;         // routing / schedule
+  size_t Y = 0, A = 0, H = 0;                        // forward
+  size_t dH = 0, dXp = 0, dwp = 0, G = 0;            // backward
+  size_t total = 0;
+};
+
+Layout layout(const moe_shape* s, int op) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int64_t R = s->T * s->k;
+  const size_t es = elem_size(s->dtype);
+  const int64_t nchunks = cdiv(R, kSortChunk);
+  L.tile_off = take(sizeof(int32_t) * (s->E + 1));
+  L.order = take(sizeof(int32_t) * s->E);
+  if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
+  if (op == MOE_OP_FORWARD) {
+    L.Y = take(es * R * s->d);
+    L.A = take(es * R * s->I);
+    if (s->dtype == MOE_F32) L.H = take(es * R * 2 * s->I);
+  }
+  if (op == MOE_OP_BACKWARD) {
+    L.dH = take(es * R * 2 * s->I);
+    L.dXp = take(es * R * s->d);
+    L.dwp = take(sizeof(float) * R * cdiv(s->I, 32));
+    if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
+  }
+  L.total = off;
+  return L;
+}
+
+moe_status check_routing(const moe_routing* r, bool need_all) {
+  CHECK_PTR(r);
+  CHECK_PTR(r->topk_ids);
+  CHECK_PTR(r->topk_w);
+  CHECK_PTR(r->counts);
+  CHECK_PTR(r->offsets);
+  CHECK_PTR(r->row_of);
+  CHECK_PTR(r->src_of);
+  (void)need_all;
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape* s, int op, void* ws, size_t bytes) {
+  const size_t need = layout(s, op).total;
+  if (bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", bytes, need);
+  if (need && !ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (((uintptr_t)ws) & 255) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+moe_status check_aligned16(const void* p, const char* name) {
+  if (((uintptr_t)p) & 15) return fail(MOE_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define TRY(x)                          \
+  do {                                  \
+    moe_status _s = (x);                \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+#define HIP_TRY(x, where)                      \
+  do {                                         \
+    hipError_t _e = (x);                       \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+char* at(void* base, size_t off) { return (char*)base + off; }
+
+// routing launches shared by moe_route and moe_forward
+moe_status run_route(const moe_shape* s, moe_routing* r, void* ws, const Layout& L,
+                     const LaunchCtx& c) {
+  const int T = (int)s->T, E = (int)s->E, k = (int)s->k;
+  if (r->logits) HIP_TRY(launch_topk(c, r->logits, s->logits_dtype, T, E, k, r->topk_ids, r->topk_w), "route_topk");
+  HIP_TRY(launch_sort(c, r->topk_ids, T, E, k, (int32_t*)at(ws, L.hist), r->counts, r->offsets,
+                      r->row_of, r->src_of), "route_sort");
+  return MOE_OK;
+}
+
+LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, const void* wgu,
+                     const void* wd, void* ws, const Layout& L) {
+  LayerArgs a;
+  a.T = (int)s->T;
+  a.d = (int)s->d;
+  a.E = (int)s->E;
+  a.k = (int)s->k;
+  a.I = (int)s->I;
+  a.R = (int)(s->T * s->k);
+  a.dtype = s->dtype;
+  a.x = x;
+  a.w_gate_up = wgu;
+  a.w_down = wd;
+  a.topk_w = r->topk_w;
+  a.offsets = r->offsets;
+  a.src_of = r->src_of;
+  a.row_of = r->row_of;
+  a.tile_off = (const int32_t*)at(ws, L.tile_off);
+  a.order = (const int32_t*)at(ws, L.order);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
+  TRY(check_shape(shape));
+  CHECK_PTR(bytes);
+  if (op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) return fail(MOE_ERR_INVALID_ARGUMENT, "op=%d unknown", op);
+  *bytes = layout(shape, op).total;
+  return MOE_OK;
+}
+
+moe_status moe_saved_size(const moe_shape* shape, size_t* bytes) {
+  TRY(check_shape(shape));
+  CHECK_PTR(bytes);
+  *bytes = elem_size(shape->dtype) * (size_t)(shape->T * shape->k) * 3 * (size_t)shape->I;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, moe_routing* routing, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  TRY(check_shape(shape));
+  TRY(check_routing(routing, true));
+  TRY(check_ws(shape, MOE_OP_ROUTE, workspace, workspace_bytes));
+  const Layout L = layout(shape, MOE_OP_ROUTE);
+  (void)hipGetLastError();
+  return run_route(shape, routing, workspace, L, make_ctx(stream));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routing,
+                       const void* w_gate_up, const void* w_down, void* out, void* saved,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_shape(shape));
+  CHECK_PTR(x);
+  CHECK_PTR(w_gate_up);
+  CHECK_PTR(w_down);
+  CHECK_PTR(out);
+  TRY(check_routing(routing, true));
+  TRY(check_ws(shape, MOE_OP_FORWARD, workspace, workspace_bytes));
+  TRY(check_aligned16(x, "x"));
+  TRY(check_aligned16(w_gate_up, "w_gate_up"));
+  TRY(check_aligned16(w_down, "w_down"));
+  TRY(check_aligned16(out, "out"));
+  if (saved) TRY(check_aligned16(saved, "saved"));
+  const Layout L = layout(shape, MOE_OP_FORWARD);
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  TRY(run_route(shape, routing, workspace, L, c));
+  HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
+                          (int32_t*)at(workspace, L.order)), "route_schedule");
+  const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
+  const size_t es = elem_size(shape->dtype);
+  const int64_t R = shape->T * shape->k;
+  void* H = saved ? saved : (shape->dtype == MOE_F32 ? at(workspace, L.H) : nullptr);
+  void* A = saved ? at(saved, es * R * 2 * shape->I) : at(workspace, L.A);
+  void* Y = at(workspace, L.Y);
+  if (shape->dtype == MOE_F32)
+    HIP_TRY(f32_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
+  else
+    HIP_TRY(bf16_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
+  HIP_TRY(launch_combine(c, shape->dtype, Y, routing->row_of, routing->topk_w, (int)shape->T,
+                         (int)shape->k, (int)shape->d, out), "combine");
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
+                        const moe_routing* routing, const void* w_gate_up, const void* w_down,
+                        const void* saved, void* dx, void* dw_gate_up, void* dw_down,
+                        float* d_topk_w, void* dlogits, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  TRY(check_shape(shape));
+  CHECK_PTR(dout);
+  CHECK_PTR(x);
+  CHECK_PTR(w_gate_up);
+  CHECK_PTR(w_down);
+  CHECK_PTR(saved);
+  CHECK_PTR(dx);
+  CHECK_PTR(dw_gate_up);
+  CHECK_PTR(dw_down);
+  CHECK_PTR(d_topk_w);
+  TRY(check_routing(routing, true));
+  if (dlogits && !routing->logits)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "dlogits needs the logits form of routing");
+  TRY(check_ws(shape, MOE_OP_BACKWARD, workspace, workspace_bytes));
+  TRY(check_aligned16(dout, "dout"));
+  TRY(check_aligned16(x, "x"));
+  TRY(check_aligned16(w_gate_up, "w_gate_up"));
+  TRY(check_aligned16(w_down, "w_down"));
+  TRY(check_aligned16(saved, "saved"));
+  TRY(check_aligned16(dx, "dx"));
+  TRY(check_aligned16(dw_gate_up, "dw_gate_up"));
+  TRY(check_aligned16(dw_down, "dw_down"));
+  const Layout L = layout(shape, MOE_OP_BACKWARD);
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
+                          (int32_t*)at(workspace, L.order)), "route_schedule");
+  const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
+  const size_t es = elem_size(shape->dtype);
+  const int64_t R = shape->T * shape->k;
+  const void* H = saved;
+  const void* A = (const char*)saved + es * R * 2 * shape->I;
+  void* dH = at(workspace, L.dH);
+  void* dXp = at(workspace, L.dXp);
+  float* dwp = (float*)at(workspace, L.dwp);
+  if (shape->dtype == MOE_F32)
+    HIP_TRY(f32_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down,
+                          (float*)at(workspace, L.G)), "backward GEMMs");
+  else
+    HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down),
+            "backward GEMMs");
+  HIP_TRY(launch_topk_grad(c, dwp, (int)cdiv(shape->I, 32), routing->row_of, routing->topk_ids,
+                           routing->topk_w, (int)shape->T, (int)shape->k, (int)shape->E, d_topk_w,
+                           dlogits, shape->logits_dtype), "topk_grad");
+  HIP_TRY(launch_combine(c, shape->dtype, dXp, routing->row_of, nullptr, (int)shape->T,
+                         (int)shape->k, (int)shape->d, dx), "reduce_dx");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_shape* shape, const void* x, const moe_routing* routing,
+                       void* xp, void* stream) {
+  TRY(check_shape(shape));
+  CHECK_PTR(x);
+  CHECK_PTR(xp);
+  CHECK_PTR(routing);
+  CHECK_PTR(routing->src_of);
+  TRY(check_aligned16(x, "x"));
+  TRY(check_aligned16(xp, "xp"));
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  HIP_TRY(launch_permute(c, shape->dtype, x, routing->src_of, (int)(shape->T * shape->k),
+                         (int)shape->k, (int)shape->d, xp), "permute");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* rows, const moe_routing* routing,
+                       void* out, void* stream) {
+  TRY(check_shape(shape));
+  CHECK_PTR(rows);
+  CHECK_PTR(out);
+  CHECK_PTR(routing);
+  CHECK_PTR(routing->row_of);
+  CHECK_PTR(routing->topk_w);
+  TRY(check_aligned16(rows, "rows"));
+  TRY(check_aligned16(out, "out"));
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  HIP_TRY(launch_combine(c, shape->dtype, rows, routing->row_of, routing->topk_w, (int)shape->T,
+                         (int)shape->k, (int)shape->d, out), "combine");
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_prof = true;
+  for (auto& r : g_recs) {
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return MOE_OK;
+}
+
+moe_status moe_profile_end(moe_kernel_stat* stats, int capacity, int* count) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_prof = false;
+  std::vector<moe_kernel_stat> agg;
+  for (auto& r : g_recs) {
+    float ms = 0.0f;
+    if (r.a && r.b) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+      if (e != hipSuccess) return hip_fail(e, "profile events");
+    }
+    size_t i = 0;
+    for (; i < agg.size(); ++i)
+      if (r.name == agg[i].name) break;
+    if (i == agg.size()) {
+      moe_kernel_stat s;
+      std::memset(&s, 0, sizeof(s));
+      std::strncpy(s.name, r.name.c_str(), sizeof(s.name) - 1);
+      agg.push_back(s);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+    if (r.a) g_pool.push_back(r.a);
+    if (r.b) g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  for (int i = 0; i < (int)agg.size() && i < capacity; ++i) stats[i] = agg[i];
+  if (count) *count = (int)agg.size();
+  return MOE_OK;
+}
+
+}  // extern "C"

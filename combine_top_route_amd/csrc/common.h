@@ -1,0 +1,117 @@
+// Shared definitions of the HIP kernels (gfx950) and the host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+enum DType { F32 = 0, BF16 = 1 };
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ----------------------------------------------------------------------------
+// Host side: every launcher reports its kernel through `launched` so the API
+// layer can time it (profiling) and check the launch status.
+// ----------------------------------------------------------------------------
+struct LaunchCtx {
+  hipStream_t stream;
+  // called before and after each kernel enqueue with the kernel's name
+  void (*before)(const char* name, hipStream_t s);
+  void (*after)(const char* name, hipStream_t s);
+};
+
+#define MOE_LAUNCH(ctx, name, kernel, grid, block, shmem, ...)                     \
+  do {                                                                             \
+    if ((ctx).before) (ctx).before(name, (ctx).stream);                            \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, (ctx).stream, __VA_ARGS__);     \
+    hipError_t _e = hipGetLastError();                                             \
+    if ((ctx).after) (ctx).after(name, (ctx).stream);                              \
+    if (_e != hipSuccess) return _e;                                               \
+  } while (0)
+
+// ---------------------------------------------------------------- routing
+// Tile table sizes: row tiles of the grouped GEMMs (expert-aligned).
+constexpr int kRowTile = 128;
+// Flat entries handled by one wave in the counting sort.
+constexpr int kSortChunk = 1024;
+
+hipError_t launch_topk(const LaunchCtx& c, const void* logits, int logits_dtype, int T, int E,
+                       int k, int32_t* ids, float* w);
+// counts / offsets / permutation from ids. hist: [ceil(R/kSortChunk), E] int32 scratch.
+hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int k,
+                       int32_t* hist, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                       int32_t* src_of);
+// GEMM schedule from offsets: tile_off [E+1] (row tiles of kRowTile per expert,
+// prefix-summed) and order [E] (experts by descending row count, ties by id).
+hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
+                           int32_t* order);
+
+// ---------------------------------------------------------------- row passes
+hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
+                          int R, int k, int d, void* xp);
+// out[t] = sum_j (w ? w[t*k+j] : 1) * rows[row_of[t*k+j]]
+hipError_t launch_combine(const LaunchCtx& c, int dtype, const void* rows, const int32_t* row_of,
+                          const float* w, int T, int k, int d, void* out);
+// d_topk_w[t,j] = sum_b dwp[row_of[t*k+j]*nblk + b]; dlogits (optional).
+hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, const int32_t* row_of,
+                            const int32_t* ids, const float* w, int T, int k, int E,
+                            float* d_topk_w, void* dlogits, int logits_dtype);
+
+// ---------------------------------------------------------------- GEMMs
+struct LayerArgs {
+  int T, d, E, k, I, R;
+  int dtype;
+  const void* x;
+  const void* w_gate_up;
+  const void* w_down;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* src_of;
+  const int32_t* row_of;
+  const int32_t* tile_off;  // [E+1], kRowTile tiles
+  const int32_t* order;     // [E]
+};
+
+// bf16 MFMA path.  forward: H [R,2I] (may be null), A [R,I], Y [R,d].
+hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* A, void* Y);
+// backward: dH [R,2I], dXp [R,d], dwp [R,ceil(I/32)] fp32, dW_gu, dW_d.
+hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
+                          const void* H, const void* A, void* dH, void* dXp, float* dwp,
+                          void* dW_gu, void* dW_d);
+
+// float32 path (plain FMA kernels, unfused epilogues).  forward needs H.
+hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* A, void* Y);
+// backward needs G [R,I] fp32 scratch.
+hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
+                         const void* H, const void* A, void* dH, void* dXp, float* dwp,
+                         void* dW_gu, void* dW_d, float* G);
+
+}  // namespace moe

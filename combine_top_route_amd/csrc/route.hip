@@ -1,0 +1,316 @@
+// Routing kernels: top-k selection with renormalised softmax weights,
+// per-expert counts and offsets, and the stable token sort into expert order.
+//
+// The router sends each token to a small subset of experts and the dispatch
+// sorts tokens into expert order ("Prime Intellect's Prime Mega MoE Trains
+// Giant AI Models 55% Faster", section "Where MoE training loses time"); the
+// routing tensors are top scores, selected expert indices and per-expert
+// token counts ("Mario/overlap moe kernel integration", commit on
+// GroupedExperts.forward).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// Monotone map float -> uint32 (larger float -> larger key). -0.0 is folded
+// onto +0.0 first so that the two tie.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unordered_bits(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+constexpr int kMaxKeysPerLane = 1024 / kWave;  // E <= 1024
+
+// One wavefront per token.  Key = ordered(logit) << 32 | ~expert, so the
+// wave-wide maximum is the largest logit and, among equal logits, the lowest
+// expert index.  k rounds of a wave arg-max; the winner's key is cleared.
+template <typename LT>
+__global__ __launch_bounds__(256) void topk_kernel(const LT* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const LT* row = logits + (int64_t)t * E;
+  uint64_t key[kMaxKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    int e = lane + kWave * i;
+    key[i] = 0;
+    if (e < E) {
+      float v = to_f32<LT>(row[e]);
+      key[i] = ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e);
+    }
+  }
+  float my_logit = 0.0f;
+  int my_id = 0;
+  float top = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) m = key[i] > m ? key[i] : m;
+    m = wave_max_u64(m);
+    int e = (int)(~(uint32_t)(m & 0xffffffffu));
+    float l = unordered_bits((uint32_t)(m >> 32));
+    if (j == 0) top = l;
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i)
+        if (i == (e >> 6)) key[i] = 0;
+    }
+    if (lane == j) {
+      my_logit = l;
+      my_id = e;
+    }
+  }
+  // softmax over the k selected logits (float32), summed in slot order
+  float ex = lane < k ? expf(my_logit - top) : 0.0f;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += __shfl(ex, j, kWave);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    w[(int64_t)t * k + lane] = ex / s;
+  }
+}
+
+// Same selection for k > 64 (one lane per slot no longer fits a wave): the
+// winners' logits and ids go through shared memory.
+template <typename LT>
+__global__ __launch_bounds__(64) void topk_kernel_bigk(const LT* __restrict__ logits, int T,
+                                                       int E, int k, int32_t* __restrict__ ids,
+                                                       float* __restrict__ w) {
+  __shared__ float sl[1024];
+  __shared__ int si[1024];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const LT* row = logits + (int64_t)t * E;
+  uint64_t key[kMaxKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxKeysPerLane; ++i) {
+    int e = lane + kWave * i;
+    key[i] = 0;
+    if (e < E) key[i] = ((uint64_t)ordered_bits(to_f32<LT>(row[e])) << 32) | (uint32_t)(~(uint32_t)e);
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) m = key[i] > m ? key[i] : m;
+    m = wave_max_u64(m);
+    int e = (int)(~(uint32_t)(m & 0xffffffffu));
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < kMaxKeysPerLane; ++i)
+        if (i == (e >> 6)) key[i] = 0;
+      sl[j] = unordered_bits((uint32_t)(m >> 32));
+      si[j] = e;
+    }
+  }
+  __syncthreads();
+  const float top = sl[0];
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += expf(sl[j] - top);
+  for (int j = lane; j < k; j += kWave) {
+    ids[(int64_t)t * k + j] = si[j];
+    w[(int64_t)t * k + j] = expf(sl[j] - top) / s;
+  }
+}
+
+__device__ __forceinline__ int clamp_id(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Histogram of one chunk of kSortChunk flat entries per block (one wave).
+__global__ __launch_bounds__(64) void count_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                   int32_t* __restrict__ hist) {
+  __shared__ int32_t h[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += kWave) h[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kSortChunk;
+  for (int i = lane; i < kSortChunk; i += kWave) {
+    int64_t f = base + i;
+    if (f < R) atomicAdd(&h[clamp_id(ids[f], E)], 1);
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Block-wide exclusive scan of one value per thread (blockDim.x <= 1024).
+__device__ int block_exclusive_scan(int v, int* sh_waves, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) sh_waves[wid] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    for (int i = 0; i < nw; ++i) {
+      int tmp = sh_waves[i];
+      sh_waves[i] = run;
+      run += tmp;
+    }
+    *total = run;
+  }
+  __syncthreads();
+  int r = sh_waves[wid] + incl - v;
+  __syncthreads();
+  return r;
+}
+
+// Per expert: prefix over chunks (hist becomes each chunk's start inside the
+// expert's segment), counts, and offsets = exclusive scan of counts.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ hist, int nchunks, int E,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int sh_waves[16];
+  __shared__ int total;
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    // loads of a batch are independent; only the running sum is serial
+    for (int c0 = 0; c0 < nchunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < nchunks) hist[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    counts[e] = run;
+  }
+  int off = block_exclusive_scan(e < E ? run : 0, sh_waves, &total);
+  if (e < E) offsets[e] = off;
+  if (e == 0) offsets[E] = total;
+}
+
+// Stable scatter: each wave walks its chunk in order, 64 entries at a time.
+// Lanes routed to the same expert are found with one ballot per id bit; a
+// lane's rank among them is the count of lower lanes in its match mask.
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                     const int32_t* __restrict__ hist,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ row_of,
+                                                     int32_t* __restrict__ src_of) {
+  __shared__ int32_t base[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += kWave) base[e] = offsets[e] + hist[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t chunk0 = (int64_t)blockIdx.x * kSortChunk;
+  for (int s = 0; s < kSortChunk; s += kWave) {
+    const int64_t f = chunk0 + s + lane;
+    const bool valid = f < R;
+    const int e = valid ? clamp_id(ids[f], E) : 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t mb = __ballot(bit);
+      m &= bit ? mb : ~mb;
+    }
+    const int rank = __popcll(m & lt_mask);
+    const int cnt = __popcll(m);
+    int dest = 0;
+    if (valid) dest = base[e] + rank;
+    __syncthreads();
+    if (valid) {
+      row_of[f] = dest;
+      src_of[dest] = (int32_t)f;
+      if (rank == cnt - 1) base[e] = dest + 1;
+    }
+    __syncthreads();
+  }
+}
+
+// Tile table of the grouped GEMMs and the expert order of the weight-gradient
+// GEMMs (largest expert first, so the longest tiles start first).
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
+                                                        int32_t* __restrict__ tile_off,
+                                                        int32_t* __restrict__ order) {
+  __shared__ int sh_waves[16];
+  __shared__ int total;
+  __shared__ int cnt[1024];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) c = offsets[e + 1] - offsets[e];
+  if (e < E) cnt[e] = c;
+  int tiles = (c + kRowTile - 1) / kRowTile;
+  int off = block_exclusive_scan(e < E ? tiles : 0, sh_waves, &total);
+  if (e < E) tile_off[e] = off;
+  if (e == 0) tile_off[E] = total;
+  __syncthreads();
+  if (e < E) {
+    int rank = 0;
+    for (int o = 0; o < E; ++o) {
+      int co = cnt[o];
+      rank += (co > c) || (co == c && o < e);
+    }
+    order[rank] = e;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const LaunchCtx& c, const void* logits, int logits_dtype, int T, int E,
+                       int k, int32_t* ids, float* w) {
+  if (k <= kWave) {
+    dim3 grid((T + 3) / 4);
+    if (logits_dtype == F32)
+      MOE_LAUNCH(c, "route_topk", topk_kernel<float>, grid, dim3(256), 0, (const float*)logits, T,
+                 E, k, ids, w);
+    else
+      MOE_LAUNCH(c, "route_topk", topk_kernel<bf16_t>, grid, dim3(256), 0, (const bf16_t*)logits,
+                 T, E, k, ids, w);
+  } else {
+    if (logits_dtype == F32)
+      MOE_LAUNCH(c, "route_topk", topk_kernel_bigk<float>, dim3(T), dim3(64), 0,
+                 (const float*)logits, T, E, k, ids, w);
+    else
+      MOE_LAUNCH(c, "route_topk", topk_kernel_bigk<bf16_t>, dim3(T), dim3(64), 0,
+                 (const bf16_t*)logits, T, E, k, ids, w);
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int k, int32_t* hist,
+                       int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of) {
+  const int R = T * k;
+  const int nchunks = (int)cdiv(R, kSortChunk);
+  MOE_LAUNCH(c, "route_count", count_kernel, dim3(nchunks), dim3(64), 0, ids, R, E, hist);
+  MOE_LAUNCH(c, "route_scan", scan_kernel, dim3(1), dim3(1024), 0, hist, nchunks, E, counts,
+             offsets);
+  MOE_LAUNCH(c, "route_scatter", scatter_kernel, dim3(nchunks), dim3(64), 0, ids, R, E, hist,
+             offsets, row_of, src_of);
+  return hipSuccess;
+}
+
+hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
+                           int32_t* order) {
+  MOE_LAUNCH(c, "route_schedule", schedule_kernel, dim3(1), dim3(1024), 0, offsets, E, tile_off,
+             order);
+  return hipSuccess;
+}
+
+}  // namespace moe

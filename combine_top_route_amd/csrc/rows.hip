@@ -1,0 +1,189 @@
+// Row passes of the layer: dispatch gather, combine (weighted sum of each
+// token's k expert rows, returned to the token's original position), the
+// input-gradient reduction, and the top-k-weight / router-logit gradients.
+//
+// Dispatch and combine are the steps that move tokens to their experts and
+// bring the results back to their original positions ("Prime Intellect's
+// Prime Mega MoE Trains Giant AI Models 55% Faster", section "Where MoE
+// training loses time"; "Prime Intellect Fused MoE Kernel: 3.11x MoE
+// Training Speed", section "What a mixture-of-experts layer actually does").
+// All are HBM-bound copies/reductions: 16-byte vector accesses, one wave per
+// row, float32 accumulation in a fixed (slot) order, no atomics.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct Vec;  // 16-byte vector of T
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+};
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4& v, float* f) {
+  if constexpr (sizeof(T) == 4) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack(const float* f) {
+  uint4 v;
+  if constexpr (sizeof(T) == 4) {
+    v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+    v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+  } else {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+    v.x = u[0]; v.y = u[1]; v.z = u[2]; v.w = u[3];
+  }
+  return v;
+}
+
+// xp[r] = x[src_of[r] / k]; one wave per row, 4 rows per block.
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ src_of, int R,
+                                                      int k, int row_vecs, uint4* __restrict__ xp) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = src_of[r] / k;
+  const uint4* src = x + t * row_vecs;
+  uint4* dst = xp + (int64_t)r * row_vecs;
+  for (int c = lane; c < row_vecs; c += kWave) dst[c] = src[c];
+}
+
+// out[t] = sum_j w[t,j] * rows[row_of[t*k+j]] (w == null: weight 1), float32
+// sum in slot order, one rounding at the end.  One wave per token.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ rows,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ w, int Tn, int k,
+                                                      int row_vecs, uint4* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* ro = row_of + (int64_t)t * k;
+  for (int c = lane; c < row_vecs; c += kWave) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {  // four rows in flight, summed in slot order
+      uint4 v[4];
+      float s[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = rows[(int64_t)ro[j + q] * row_vecs + c];
+        s[q] = w ? w[(int64_t)t * k + j + q] : 1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[N];
+        unpack<T>(v[q], f);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] += s[q] * f[i];
+      }
+    }
+    for (; j < k; ++j) {
+      float f[N];
+      unpack<T>(rows[(int64_t)ro[j] * row_vecs + c], f);
+      const float s = w ? w[(int64_t)t * k + j] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += s * f[i];
+    }
+    out[(int64_t)t * row_vecs + c] = pack<T>(acc);
+  }
+}
+
+// d_topk_w[t,j] = sum over the partial dot products of row row_of[t*k+j]
+// (fixed order); dlogits[t,e] = w_e (dw_e - sum_j w_j dw_j) on the selected
+// experts, 0 elsewhere.  One wave per token.
+template <typename LT>
+__global__ __launch_bounds__(256) void topk_grad_kernel(const float* __restrict__ dwp, int nblk,
+                                                        const int32_t* __restrict__ row_of,
+                                                        const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ w, int Tn, int k,
+                                                        int E, float* __restrict__ d_topk_w,
+                                                        LT* __restrict__ dlogits) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int lane = threadIdx.x & 63;
+  float inner = 0.0f;
+  for (int j0 = 0; j0 < k; j0 += kWave) {
+    const int j = j0 + lane;
+    float dw = 0.0f, wj = 0.0f;
+    if (j < k) {
+      const float* p = dwp + (int64_t)row_of[(int64_t)t * k + j] * nblk;
+      for (int b = 0; b < nblk; ++b) dw += p[b];
+      d_topk_w[(int64_t)t * k + j] = dw;
+      wj = w[(int64_t)t * k + j];
+    }
+    const int lim = min(kWave, k - j0);
+    for (int q = 0; q < lim; ++q) inner += __shfl(wj * dw, q, kWave);
+  }
+  if (!dlogits) return;
+  for (int e = lane; e < E; e += kWave) {
+    float g = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      if (ids[(int64_t)t * k + j] == e) {
+        const float wj = w[(int64_t)t * k + j];
+        const int64_t r = row_of[(int64_t)t * k + j];
+        float dw = 0.0f;
+        for (int b = 0; b < nblk; ++b) dw += dwp[r * nblk + b];
+        g = wj * (dw - inner);
+      }
+    }
+    dlogits[(int64_t)t * E + e] = from_f32<LT>(g);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
+                          int R, int k, int d, void* xp) {
+  const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
+  MOE_LAUNCH(c, "permute", permute_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)x,
+             src_of, R, k, row_vecs, (uint4*)xp);
+  return hipSuccess;
+}
+
+hipError_t launch_combine(const LaunchCtx& c, int dtype, const void* rows, const int32_t* row_of,
+                          const float* w, int T, int k, int d, void* out) {
+  const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
+  const char* name = w ? "combine" : "reduce_dx";
+  if (dtype == F32)
+    MOE_LAUNCH(c, name, combine_kernel<float>, dim3((T + 3) / 4), dim3(256), 0,
+               (const uint4*)rows, row_of, w, T, k, row_vecs, (uint4*)out);
+  else
+    MOE_LAUNCH(c, name, combine_kernel<bf16_t>, dim3((T + 3) / 4), dim3(256), 0,
+               (const uint4*)rows, row_of, w, T, k, row_vecs, (uint4*)out);
+  return hipSuccess;
+}
+
+hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, const int32_t* row_of,
+                            const int32_t* ids, const float* w, int T, int k, int E,
+                            float* d_topk_w, void* dlogits, int logits_dtype) {
+  if (logits_dtype == F32)
+    MOE_LAUNCH(c, "topk_grad", topk_grad_kernel<float>, dim3((T + 3) / 4), dim3(256), 0, dwp,
+               nblk, row_of, ids, w, T, k, E, d_topk_w, (float*)dlogits);
+  else
+    MOE_LAUNCH(c, "topk_grad", topk_grad_kernel<bf16_t>, dim3((T + 3) / 4), dim3(256), 0, dwp,
+               nblk, row_of, ids, w, T, k, E, d_topk_w, (bf16_t*)dlogits);
+  return hipSuccess;
+}
+
+}  // namespace moe

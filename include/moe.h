@@ -1,0 +1,171 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused mixture-of-experts layer:
+ * top-k routing, token sort into expert order (dispatch), grouped gate/up
+ * GEMM with SwiGLU, grouped down GEMM, weighted combine, and the full
+ * backward of that layer, for one GPU's share of the work.
+ *
+ * The operation is the one described on the pages
+ *   "Prime Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster"
+ *     (section "Where MoE training loses time": dispatch tokens to their
+ *     experts, run the expert MLPs, return outputs to their original
+ *     positions; the backward repeats the exchange for gradients) and
+ *   "Prime Intellect Fused MoE Kernel: 3.11x MoE Training Speed"
+ *     (section "What a mixture-of-experts layer actually does": dispatch,
+ *     both expert linear layers, SwiGLU and the combine), with the routing
+ *     inputs of "Mario/overlap moe kernel integration" (prime-rl PR 3651,
+ *     commit on GroupedExperts.forward: either per-expert token counts or
+ *     top scores plus selected expert indices).
+ *
+ * Notation: T tokens, d hidden size, E experts, k experts per token, I expert
+ * intermediate size, R = T*k routed rows.  All matrices are row-major and
+ * densely packed (leading dimension = last extent).
+ *
+ * Math (per token t, slot j, expert e = topk_ids[t][j]):
+ *   topk_ids[t]  = the k largest logits of row t, largest first, ties to the
+ *                  lower expert index (-0.0 equals +0.0);
+ *   topk_w[t][j] = exp(l_tj) / sum_{i<k} exp(l_ti)   (softmax over the k
+ *                  selected logits = full softmax renormalised over top k);
+ *   h = W_gate_up[e] x_t  (rows [0,I) gate g, rows [I,2I) up u),
+ *   a = silu(g) * u,  y_tj = W_down[e] a,  out_t = sum_j topk_w[t][j] y_tj.
+ *   The backward is the exact gradient of L = sum(dout * out).
+ *
+ * Ownership: the caller allocates every buffer (device memory unless noted)
+ * and keeps it alive until the stream has finished the call.  The library
+ * never allocates, frees or keeps device memory between calls, performs no
+ * device-to-host copy and no stream synchronisation: every call only
+ * enqueues kernels on `stream` (a hipStream_t; NULL = the default stream),
+ * so calls may be captured into a HIP graph.  Calls on different streams
+ * need separate workspaces and outputs.
+ *
+ * Errors: every argument check runs on the host before any HIP call; a
+ * failing check returns a status and enqueues nothing.  moe_last_error()
+ * gives a message for the last failure on the calling thread.  Device-side
+ * contract violations in the ids-in form (an id outside [0, E), repeated ids
+ * in a row, non-finite values) are not detected; ids are clamped into
+ * [0, E) so that no access leaves its buffer, and results are then
+ * unspecified.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad extent, k > E, ...     */
+  MOE_ERR_UNSUPPORTED = 2,      /* valid but not built (dtype, alignment)   */
+  MOE_ERR_WORKSPACE = 3,        /* workspace smaller than moe_workspace_size */
+  MOE_ERR_HIP = 4               /* a kernel launch failed                   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Precision of the GEMM operands.  MOE_PREC_FP8_BLOCK: blockwise FP8
+ * ("Prime Mega MoE Trains Giant AI Models 55% Faster", section "Precision and
+ * hardware support": one scale shared by a block of values) as OCP e4m3 with
+ * fp32 scales over 1x128 activation blocks and 128x128 weight blocks
+ * (weight-gradient operands: 128-row blocks along the token dimension), fp32
+ * accumulation; requires dtype MOE_BF16 and d, I multiples of 128. */
+typedef enum { MOE_PREC_NATIVE = 0, MOE_PREC_FP8_BLOCK = 1 } moe_precision;
+
+typedef enum { MOE_OP_ROUTE = 0, MOE_OP_FORWARD = 1, MOE_OP_BACKWARD = 2 } moe_op;
+
+typedef struct {
+  int64_t T, d, E, k, I;
+  int32_t dtype;        /* moe_dtype of x, weights, out, saved, dout, grads */
+  int32_t logits_dtype; /* moe_dtype of logits and dlogits                  */
+  int32_t precision;    /* moe_precision                                    */
+  int32_t reserved;     /* must be 0                                        */
+} moe_shape;
+
+/* Limits checked by every call: 1 <= T <= 2^24, 1 <= k <= E <= 1024,
+ * T*k <= 2^27, d and I multiples of 8 in [8, 16384]. */
+
+/* Routing tensors (device pointers).  logits [T,E] in logits_dtype, or NULL
+ * for the ids-in form, where topk_ids/topk_w are inputs used as given (no
+ * renormalisation).  Otherwise topk_ids/topk_w are outputs.
+ *   topk_ids [T,k] int32, topk_w [T,k] float32
+ *   counts  [E]   int32  rows per expert
+ *   offsets [E+1] int32  exclusive prefix sum of counts, offsets[E] = T*k
+ *   row_of  [T*k] int32  flat entry t*k+j -> its row in expert order
+ *   src_of  [T*k] int32  row -> flat entry; rows are ordered by expert, then
+ *                        by flat entry (token order inside each expert) */
+typedef struct {
+  const void* logits;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_of;
+  int32_t* src_of;
+} moe_routing;
+
+/* Bytes of device workspace a call with this shape needs (op: moe_op). */
+moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
+
+/* Bytes of the `saved` buffer written by moe_forward and read by
+ * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
+ * A [T*k, I] (SwiGLU output), both in dtype, in expert-sorted row order. */
+moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
+
+/* Routing only: top-k (when logits != NULL), per-expert counts and offsets,
+ * and the stable expert-order permutation. */
+moe_status moe_route(const moe_shape* shape, moe_routing* routing,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Layer forward: routing as moe_route, then out [T,d] (dtype).
+ * x [T,d], w_gate_up [E,2I,d], w_down [E,d,I] in dtype.  saved: NULL, or a
+ * buffer of moe_saved_size bytes that moe_backward will read. */
+moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routing,
+                       const void* w_gate_up, const void* w_down, void* out,
+                       void* saved, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Layer backward from the routing and `saved` of a moe_forward call with
+ * the same inputs.  dout [T,d] (dtype).  Outputs: dx [T,d],
+ * dw_gate_up [E,2I,d], dw_down [E,d,I] (dtype; experts with no rows get
+ * exact zeros), d_topk_w [T,k] float32, and dlogits [T,E] (logits_dtype;
+ * zero outside the selected experts) or NULL.  dlogits requires the logits
+ * form of routing (routing->logits != NULL). */
+moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
+                        const moe_routing* routing, const void* w_gate_up,
+                        const void* w_down, const void* saved, void* dx,
+                        void* dw_gate_up, void* dw_down, float* d_topk_w,
+                        void* dlogits, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Dispatch alone: xp[r] = x[src_of[r] / k], xp [T*k, d] (dtype). */
+moe_status moe_permute(const moe_shape* shape, const void* x,
+                       const moe_routing* routing, void* xp, void* stream);
+
+/* Combine alone: out[t] = sum_j topk_w[t][j] * rows[row_of[t*k+j]],
+ * summed in float32 in slot order; rows [T*k, d], out [T,d] (dtype). */
+moe_status moe_combine(const moe_shape* shape, const void* rows,
+                       const moe_routing* routing, void* out, void* stream);
+
+const char* moe_status_string(moe_status status);
+const char* moe_last_error(void);
+
+/* Kernel timing for measurement: between moe_profile_begin and
+ * moe_profile_end every kernel the library enqueues is bracketed by HIP
+ * events on its stream.  moe_profile_end waits for those events and returns,
+ * per kernel name, the number of launches and their summed duration. */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} moe_kernel_stat;
+
+moe_status moe_profile_begin(void);
+moe_status moe_profile_end(moe_kernel_stat* stats, int capacity, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,83 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C
+ABI and the oracle on the same seeded inputs, and compare."""
+import numpy as np
+import torch
+
+from combine_top_route_amd import binding as B
+from combine_top_route_amd import synthetic as S
+from oracle import moe_oracle as O
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def to_np(t):
+    return t.detach().cpu().double().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def run_gpu(wl, inp, ids=None, w=None, backward=True):
+    """Runs forward (+ backward) of the layer on cuda:0; returns CPU numpy
+    results and the routing artefacts."""
+    dev = torch.device("cuda", 0)
+    dt = S.torch_dtype(wl.dtype)
+    layer = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt, logits_dtype=S.torch_dtype(wl.logits_dtype),
+                       precision=wl.precision, device=dev)
+    x = inp["x"].to(dev)
+    wgu = inp["w_gate_up"].to(dev)
+    wd = inp["w_down"].to(dev)
+    if ids is None:
+        layer.forward(x, wgu, wd, logits=inp["logits"].to(dev))
+    else:
+        layer.forward(x, wgu, wd, topk_ids=ids.to(dev), topk_w=w.to(dev))
+    res = {"out": to_np(layer.out)}
+    r = layer.routing
+    for n in ("topk_ids", "topk_w", "counts", "offsets", "row_of", "src_of"):
+        res[n] = to_np(getattr(r, n))
+    if backward:
+        g = layer.backward(inp["dout"].to(dev), x, wgu, wd)
+        for n, v in g.items():
+            res[n] = to_np(v)
+    torch.cuda.synchronize()
+    return res
+
+
+def run_oracle(wl, inp, ids=None, w=None, backward=True):
+    f = lambda t: t.double().numpy()
+    logits = f(inp["logits"]) if ids is None else None
+    if ids is None:
+        rt = O.route(logits, wl.k, wl.E)
+    else:
+        rt = O.route(None, wl.k, wl.E, ids=ids.numpy(), w=w.double().numpy())
+    Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
+    fw = O.forward(f(inp["x"]), rt, Wgu, Wd)
+    res = {"rt": rt, "out": fw["out"]}
+    if backward:
+        bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
+        res.update(bw)
+    return res
+
+
+def check_routing(gpu, ref):
+    rt = ref["rt"]
+    assert np.array_equal(gpu["topk_ids"], rt["ids"]), "topk_ids"
+    assert np.array_equal(gpu["counts"], rt["counts"]), "counts"
+    assert np.array_equal(gpu["offsets"], rt["offsets"]), "offsets"
+    assert np.array_equal(gpu["src_of"], rt["src_of"]), "src_of"
+    assert np.array_equal(gpu["row_of"], rt["row_of"]), "row_of"
+    assert rel_err(gpu["topk_w"], rt["w"]) < 1e-5, "topk_w"
+
+
+def check_floats(gpu, ref, tol, names=("out", "dx", "dW_gate_up", "dW_down", "d_topk_w", "dlogits")):
+    errs = {}
+    for n in names:
+        if n in gpu and n in ref:
+            errs[n] = rel_err(gpu[n], ref[n])
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"tolerance {tol} exceeded: {bad} (all: {errs})"
+    return errs

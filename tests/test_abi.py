@@ -1,0 +1,138 @@
+"""The C-ABI library: it loads, exports every entry point include/moe.h
+declares, and rejects bad arguments on the host before any HIP call (so
+these run without a GPU: fake non-null device pointers are never touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from combine_top_route_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
+              "moe_workspace_size", "moe_saved_size", "moe_status_string", "moe_last_error",
+              "moe_profile_begin", "moe_profile_end"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = B.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def _shape(**kw):
+    base = dict(T=64, d=64, E=8, k=2, I=128, dtype=torch.float32)
+    base.update(kw)
+    return B.make_shape(**base)
+
+
+def _status(shape, op=B.OP_FORWARD):
+    n = ctypes.c_size_t()
+    return B.lib().moe_workspace_size(ctypes.byref(shape), op, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw", [dict(T=0), dict(E=0), dict(E=1025), dict(k=0), dict(k=9),
+                                dict(d=12), dict(I=4), dict(d=16392), dict(T=(1 << 24) + 1)])
+def test_bad_shapes_rejected(kw):
+    st, _ = _status(_shape(**kw))
+    assert st == 1  # MOE_ERR_INVALID_ARGUMENT
+    assert B.lib().moe_last_error().decode()
+
+
+def test_bad_enums_rejected():
+    s = _shape()
+    s.dtype = 7
+    assert _status(s)[0] == 1
+    s = _shape()
+    s.reserved = 1
+    assert _status(s)[0] == 1
+
+
+def test_fp8_requirements():
+    s = _shape(precision="fp8_block")                     # f32 storage
+    assert _status(s)[0] == 2                            # MOE_ERR_UNSUPPORTED
+    s = _shape(precision="fp8_block", dtype=torch.bfloat16, d=192, I=128)
+    assert _status(s)[0] == 2
+
+
+def test_workspace_sizes_grow_with_problem():
+    _, a = _status(_shape(T=64))
+    _, b = _status(_shape(T=640))
+    assert 0 < a < b
+    st, r = _status(_shape(), op=B.OP_ROUTE)
+    assert st == 0 and 0 < r < a
+    st, bw = _status(_shape(), op=B.OP_BACKWARD)
+    assert st == 0 and bw > 0
+    n = ctypes.c_size_t()
+    s = _shape(T=10, k=2, I=16, dtype=torch.bfloat16)
+    assert B.lib().moe_saved_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == 2 * 20 * 3 * 16
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation
+
+
+def _routing(**null):
+    r = B.MoeRouting(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k in null:
+        setattr(r, k, None)
+    return r
+
+
+def test_forward_rejects_null_and_short_workspace_without_touching_the_gpu():
+    lib = B.lib()
+    s = _shape()
+    r = _routing()
+    args = lambda **o: [ctypes.byref(s), o.get("x", FAKE), ctypes.byref(o.get("r", r)), FAKE, FAKE,
+                        o.get("out", FAKE), None, FAKE, o.get("ws", 1 << 40), None]
+    assert lib.moe_forward(*args(x=None)) == 1
+    assert lib.moe_forward(*args(out=None)) == 1
+    assert lib.moe_forward(*args(r=_routing(row_of=1))) == 1
+    assert lib.moe_forward(*args(ws=16)) == 3           # MOE_ERR_WORKSPACE
+    assert "workspace" in lib.moe_last_error().decode()
+
+
+def test_backward_rejects_dlogits_without_logits():
+    lib = B.lib()
+    s = _shape()
+    r = _routing(logits=1)
+    st = lib.moe_backward(ctypes.byref(s), FAKE, FAKE, ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == 1
+    assert "dlogits" in lib.moe_last_error().decode()
+
+
+def test_misaligned_pointer_rejected():
+    lib = B.lib()
+    s = _shape()
+    r = _routing()
+    st = lib.moe_permute(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 2), ctypes.byref(r), FAKE, None)
+    assert st == 1
+
+
+def test_status_strings():
+    lib = B.lib()
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"

@@ -1,0 +1,132 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Integer routing artefacts must match bit for bit; floating outputs and
+gradients within max|err|/max|ref| <= 1e-4 (float32 storage), 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_top_route_amd import binding as B
+from combine_top_route_amd import synthetic as S
+from oracle import moe_oracle as O
+
+from gpu_util import TOL, check_floats, check_routing, rel_err, run_gpu, run_oracle, to_np
+
+pytestmark = pytest.mark.gpu
+
+TINY = S.WORKLOADS["tiny"]
+BF = dict(dtype="bf16", logits_dtype="bf16")
+
+SMALL_CASES = {
+    # float32 storage (plain FMA path)
+    "tiny": TINY,
+    "f32_ragged": TINY.scaled(T=100, d=48, E=5, k=3, I=40),
+    # bf16 MFMA path: several tiles, ragged row tails, N and K tails
+    "bf16_tiles": TINY.scaled(T=777, d=384, E=16, k=4, I=320, **BF),
+    "bf16_ktail": TINY.scaled(T=1000, d=200, E=16, k=4, I=72, **BF),
+    "bf16_bigrows": TINY.scaled(T=2048, d=256, E=4, k=2, I=192, **BF),
+    "bf16_one_token": TINY.scaled(T=1, d=128, E=8, k=2, I=64, **BF),
+    "bf16_k_equals_E": TINY.scaled(T=64, d=128, E=4, k=4, I=64, **BF),
+    "bf16_single_expert": TINY.scaled(T=200, d=128, E=1, k=1, I=128, **BF),
+    "bf16_k80": TINY.scaled(T=16, d=64, E=128, k=80, I=64, **BF),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_layer_parity_small(name):
+    wl = SMALL_CASES[name]
+    print(f"case {name}: {wl}", flush=True)
+    inp = S.make_inputs(wl, seed=1)
+    gpu = run_gpu(wl, inp)
+    ref = run_oracle(wl, inp)
+    check_routing(gpu, ref)
+    errs = check_floats(gpu, ref, TOL[wl.dtype])
+    print(name, errs)
+
+
+def test_layer_parity_ids_in_with_empty_and_hot_experts():
+    wl = TINY.scaled(T=1500, d=256, E=16, k=4, I=128, **BF)
+    ids, w = S.random_topk(wl.T, wl.E - 3, wl.k, seed=5)
+    ids = ids + (ids >= 2).int() + (ids >= 5).int() + (ids >= 11).int()   # experts 2, 6, 13 ... get none
+    ids = ids.numpy()
+    ids[:1000, 0] = np.where((ids[:1000, 1:] == 0).any(1), ids[:1000, 0], 0)  # expert 0 is hot
+    ids = torch.from_numpy(np.ascontiguousarray(ids.astype(np.int32)))
+    inp = S.make_inputs(wl, seed=2)
+    gpu = run_gpu(wl, inp, ids=ids, w=w)
+    ref = run_oracle(wl, inp, ids=ids, w=w)
+    assert (ref["rt"]["counts"] == 0).sum() >= 3 and ref["rt"]["counts"].max() > 900
+    check_routing(gpu, ref)
+    errs = check_floats(gpu, ref, TOL["bf16"], names=("out", "dx", "dW_gate_up", "dW_down", "d_topk_w"))
+    for e in np.nonzero(ref["rt"]["counts"] == 0)[0]:
+        assert np.all(gpu["dW_gate_up"][e] == 0) and np.all(gpu["dW_down"][e] == 0)
+    print(errs)
+
+
+def test_layer_parity_q30b_t4096():
+    """Qwen3-30B-A3B layer shape at 4096 tokens, every element."""
+    wl = S.WORKLOADS["q30b_t4096"]
+    inp = S.make_inputs(wl, seed=0)
+    gpu = run_gpu(wl, inp)
+    ref = run_oracle(wl, inp)
+    check_routing(gpu, ref)
+    errs = check_floats(gpu, ref, TOL["bf16"])
+    print(errs)
+
+
+def test_layer_parity_q30b_full_size_sampled():
+    """Qwen3-30B-A3B layer shape at 16,384 tokens in the benchmark's launch
+    configuration: all routing artefacts bit-exact; out, dx, top-k-weight and
+    logit gradients on sampled tokens; weight gradients of sampled experts."""
+    wl = S.WORKLOADS["q30b"]
+    inp = S.make_inputs(wl, seed=0)
+    gpu = run_gpu(wl, inp)
+    lg = inp["logits"].double().numpy()
+    rt = O.route(lg, wl.k, wl.E)
+    check_routing(gpu, {"rt": rt})
+    Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
+    x, dout = inp["x"].double().numpy(), inp["dout"].double().numpy()
+    toks = np.random.default_rng(0).choice(wl.T, 24, replace=False)
+    toks[:2] = [0, wl.T - 1]
+    s = O.forward_backward_tokens(x, lg, dout, Wgu, Wd, wl.k, toks)
+    for n in ("out", "dx", "d_topk_w", "dlogits"):
+        e = rel_err(gpu[n][toks], s[n])
+        assert e <= TOL["bf16"], (n, e)
+    hot = int(np.argmax(rt["counts"]))
+    for e in (0, hot):
+        dgu, dd = O.expert_weight_grads(x, dout, rt, Wgu, Wd, e)
+        assert rel_err(gpu["dW_gate_up"][e], dgu) <= TOL["bf16"]
+        assert rel_err(gpu["dW_down"][e], dd) <= TOL["bf16"]
+
+
+def test_deterministic_bitwise():
+    wl = TINY.scaled(T=1024, d=256, E=16, k=4, I=192, **BF)
+    inp = S.make_inputs(wl, seed=3)
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_permute_combine_identity(dtype):
+    """Identity experts: dispatch then combine returns the input (k=1, w=1:
+    bit for bit; renormalised top-k weights: to within one rounding)."""
+    dev = torch.device("cuda", 0)
+    wl = TINY.scaled(T=515, d=136, E=8, k=1, dtype=dtype, logits_dtype=dtype)
+    inp = S.make_inputs(wl, seed=4)
+    x = inp["x"].to(dev)
+    ids, _ = S.random_topk(wl.T, wl.E, 1, seed=4)
+    r = B.route_ids(ids.to(dev), torch.ones((wl.T, 1), dtype=torch.float32, device=dev), wl.E)
+    xp = B.permute(x, r, 1)
+    out = B.combine(xp, r, wl.T, 1)
+    assert torch.equal(out, x)
+    rt = O.route(None, 1, wl.E, ids=ids.numpy(), w=np.ones((wl.T, 1)))
+    assert np.array_equal(to_np(xp), O.dispatch(inp["x"].double().numpy(), rt))
+    wl4 = wl.scaled(k=4)
+    r4 = B.route(inp["logits"].to(dev)[:, :8].contiguous(), 4)
+    xp4 = B.permute(x, r4, 4)
+    out4 = B.combine(xp4, r4, wl.T, 4)
+    ref = inp["x"].double().numpy()
+    ulp = 2.0 ** -23 if dtype == "f32" else 2.0 ** -8
+    assert np.max(np.abs(to_np(out4) - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2 * ulp

@@ -100,18 +100,22 @@ struct LayerArgs {
   const int32_t* order;     // [E]
 };
 
-// bf16 MFMA path.  forward: H [R,2I] (may be null), A [R,I], Y [R,d].
-hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* A, void* Y);
-// backward: dH [R,2I], dXp [R,d], dwp [R,ceil(I/32)] fp32, dW_gu, dW_d.
+// Forward GEMMs write H [R,2I] (gate|up, may be null), Aw [R,I] = w_row *
+// silu(gate) * up (each row already carries its top-k weight) and Yw [R,d] =
+// Aw W_down^T, so the combine is a plain sum of each token's k rows.
+// bf16 MFMA path.
+hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
+// backward: Xp [R,d] and doutp [R,d] are x and dout gathered into row order;
+// outputs dH [R,2I], dXp [R,d], dwp [R,ceil(I/32)] fp32, dW_gu, dW_d.
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
-                          const void* H, const void* A, void* dH, void* dXp, float* dwp,
-                          void* dW_gu, void* dW_d);
+                          const void* H, const void* Aw, const void* Xp, const void* doutp,
+                          void* dH, void* dXp, float* dwp, void* dW_gu, void* dW_d);
 
 // float32 path (plain FMA kernels, unfused epilogues).  forward needs H.
-hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* A, void* Y);
+hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
 // backward needs G [R,I] fp32 scratch.
 hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
-                         const void* H, const void* A, void* dH, void* dXp, float* dwp,
+                         const void* H, const void* Aw, void* dH, void* dXp, float* dwp,
                          void* dW_gu, void* dW_d, float* G);
 
 }  // namespace moe

@@ -135,15 +135,17 @@ __global__ __launch_bounds__(256) void f32_wgrad(const float* __restrict__ A, in
   }
 }
 
-// A[r, i] = silu(H[r, i]) * H[r, I + i]
-__global__ __launch_bounds__(256) void f32_swiglu_fwd(const float* __restrict__ H, int64_t R, int I,
-                                                      float* __restrict__ Aout) {
+// Aw[r, i] = w_r * silu(H[r, i]) * H[r, I + i], w_r = topk_w[src_of[r]]
+__global__ __launch_bounds__(256) void f32_swiglu_fwd(const float* __restrict__ H,
+                                                      const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ src_of, int64_t R,
+                                                      int I, float* __restrict__ Aout) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= R * I) return;
   const int64_t r = q / I;
   const int i = (int)(q % I);
   const float g = H[r * 2 * I + i], u = H[r * 2 * I + I + i];
-  Aout[q] = g / (1.0f + expf(-g)) * u;
+  Aout[q] = topk_w[src_of[r]] * (g / (1.0f + expf(-g)) * u);
 }
 
 // From G = dout_t W_down[e] (per row): dwp[r, b] = sum over the 32 columns of
@@ -201,7 +203,7 @@ hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* 
                              (int)(2 * I), a.d);
   if (err != hipSuccess) return err;
   MOE_LAUNCH(c, "swiglu_fwd", f32_swiglu_fwd, dim3((unsigned)cdiv(R * I, 256)), dim3(256), 0,
-             (const float*)H, R, a.I, (float*)Aact);
+             (const float*)H, a.topk_w, a.src_of, R, a.I, (float*)Aact);
   return rows_gemm(c, "gemm_down_fwd", a, (const float*)Aact, I, nullptr, 1,
                    (const float*)a.w_down, d * I, I, 1, (float*)Y, d, a.d, a.I);
 }
@@ -217,7 +219,8 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
   if (err != hipSuccess) return err;
   MOE_LAUNCH(c, "swiglu_bwd", f32_swiglu_bwd, dim3((unsigned)cdiv(R * nblk, 256)), dim3(256), 0,
              (const float*)G, (const float*)H, a.topk_w, a.src_of, R, a.I, nblk, (float*)dH, dwp);
-  err = wgrad(c, "gemm_down_wgrad", a, (const float*)dout, d, 1, a.topk_w, (const float*)Aact, I,
+  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]  (Aw carries w_r)
+  err = wgrad(c, "gemm_down_wgrad", a, (const float*)dout, d, 1, nullptr, (const float*)Aact, I,
               0, a.d, a.I, (float*)dW_d);
   if (err != hipSuccess) return err;
   // gate/up dgrad: dXp[r, c] = sum_j dH[r, j] W_gate_up[e][j, c]

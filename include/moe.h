@@ -110,7 +110,8 @@ moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 
 /* Bytes of the `saved` buffer written by moe_forward and read by
  * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
- * A [T*k, I] (SwiGLU output), both in dtype, in expert-sorted row order. */
+ * Aw [T*k, I] (SwiGLU output times the row's top-k weight), both in dtype,
+ * in expert-sorted row order. */
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
 
 /* Routing only: top-k (when logits != NULL), per-expert counts and offsets,

@@ -143,7 +143,7 @@ Layout layout(const moe_shape* s, int op) {
   if (op == MOE_OP_BACKWARD) {
     L.dH = take(es * R * 2 * s->I);
     L.dXp = take(es * R * s->d);
-    L.dwp = take(sizeof(float) * R * cdiv(s->I, 32));
+    L.dwp = take(sizeof(float) * R * cdiv(s->I, 128));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
     if (s->dtype == MOE_BF16) {
       L.Xp = take(es * R * s->d);
@@ -344,7 +344,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
     HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, Xp, doutp, dH, dXp, dwp, dw_gate_up, dw_down),
             "backward GEMMs");
   }
-  HIP_TRY(launch_topk_grad(c, dwp, (int)cdiv(shape->I, 32), routing->row_of, routing->topk_ids,
+  HIP_TRY(launch_topk_grad(c, dwp, (int)cdiv(shape->I, 128), routing->row_of, routing->topk_ids,
                            routing->topk_w, (int)shape->T, (int)shape->k, (int)shape->E, d_topk_w,
                            dlogits, shape->logits_dtype), "topk_grad");
   HIP_TRY(launch_combine(c, shape->dtype, dXp, routing->row_of, nullptr, (int)shape->T,

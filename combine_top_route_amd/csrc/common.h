@@ -106,7 +106,7 @@ struct LayerArgs {
 // bf16 MFMA path.
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
 // backward: Xp [R,d] and doutp [R,d] are x and dout gathered into row order;
-// outputs dH [R,2I], dXp [R,d], dwp [R,ceil(I/32)] fp32, dW_gu, dW_d.
+// outputs dH [R,2I], dXp [R,d], dwp [R,ceil(I/128)] fp32, dW_gu, dW_d.
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
                           const void* H, const void* Aw, const void* Xp, const void* doutp,
                           void* dH, void* dXp, float* dwp, void* dW_gu, void* dW_d);

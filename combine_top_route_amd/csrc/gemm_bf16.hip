@@ -37,6 +37,7 @@ constexpr int NSTAGE = 3;
 constexpr int NTHR = 256;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_t;  // byte pointer into LDS (32-bit)
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
@@ -44,9 +45,12 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // past N, rows past an expert's segment in the weight gradients).
 __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64] = {0};
 
-__device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
+__device__ __forceinline__ void dma16(const void* g, lds_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
+
+// Index of this thread's wave, as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -76,14 +80,16 @@ __device__ __forceinline__ int km_swz(int krow) { return ((krow & 3) << 1) ^ ((k
 // ---------------------------------------------------------------------------
 // Operand with K-contiguous rows (row r at rowp(r), element k at rowp(r)[k]).
 // ROWS x 64 tile; instruction q covers rows 8q..8q+7 (1 KB of LDS); wave w
-// issues q = w, w+4, ...
+// issues q = w, w+4, ...  Each lane keeps one global pointer per instruction,
+// advanced by 64 elements per K step; only a partial last K step checks
+// bounds.
 // ---------------------------------------------------------------------------
 template <int ROWS>
 struct OpMK {
   static constexpr int NI = ROWS / 32;
   static constexpr int BYTES = ROWS * BK * 2;
-  const bf16_t* rowp[NI];
-  int koff[NI];  // element offset of this lane's logical 16-byte chunk
+  const bf16_t* ptr[NI];  // address of this lane's chunk at the current K step
+  int koff[NI];           // element offset of that chunk inside the K step
   int K;
 
   template <class F>
@@ -94,29 +100,38 @@ struct OpMK {
     for (int i = 0; i < NI; ++i) {
       const int q = w + 4 * i;
       const int row = 8 * q + (lane >> 3);
-      rowp[i] = rowp_of(row);
       koff[i] = (((lane & 7) ^ mk_swz(row)) << 3);
+      ptr[i] = rowp_of(row) + koff[i];
     }
   }
-  __device__ void issue(int kt, char* s) const {
-    const int w = threadIdx.x >> 6;
+  // true when K step kt lies entirely inside K (no per-lane checks needed)
+  __device__ bool full(int kt) const { return (kt + 1) * BK <= K; }
+  // issues instructions [i0, i1) of K step kt into stage base s
+  template <int I0, int I1>
+  __device__ void issue(int kt, lds_t* s, bool full_step) const {
+    const int w = wave_id();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int k = kt * BK + koff[i];
-      const void* g = (k < K) ? (const void*)(rowp[i] + k) : (const void*)g_zero_page;
+    for (int i = I0; i < I1; ++i) {
+      const void* g = ptr[i];
+      if (!full_step && kt * BK + koff[i] >= K) g = g_zero_page;
       dma16(g, s + (w + 4 * i) * 1024);
     }
   }
-  __device__ static bf16x8_t frag(const char* s, int rb, int kk) {
+  __device__ void advance() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ptr[i] += BK;
+  }
+  __device__ static bf16x8_t frag(const lds_t* s, int rb, int kk) {
     const int lane = threadIdx.x & 63;
     const int row = rb + (lane & 31);
-    return *(const bf16x8_t*)(s + mk_off(row, kk * 2 + (lane >> 5)));
+    return *(const __attribute__((address_space(3))) bf16x8_t*)(s + mk_off(row, kk * 2 + (lane >> 5)));
   }
 };
 
 // ---------------------------------------------------------------------------
-// Operand with column-contiguous k-rows: element (col, k) = krow_ptr(k)[col].
-// COLS x 64 tile stored [k][COLS]; instruction q covers k-rows q*RPI..
+// Operand with column-contiguous k-rows: element (col, k) = base[k * ld + col]
+// for k < KR (rows past KR read as zero).  COLS x 64 tile stored [k][COLS];
+// instruction q covers k-rows q*RPI..  Columns at or past N read as zero.
 // ---------------------------------------------------------------------------
 template <int COLS>
 struct OpKM {
@@ -125,45 +140,54 @@ struct OpKM {
   static constexpr int RPI = 1024 / RB;     // k-rows per instruction
   static constexpr int NI = BK / RPI / 4;   // instructions per wave per stage
   static constexpr int BYTES = COLS * BK * 2;
-  int krow[NI];   // k-row (0..63) of this lane in instruction i
-  int coff[NI];   // column offset of this lane's logical 16-byte unit
-  int c0, N;
+  const bf16_t* ptr[NI];  // address at the current K step (not dereferenced when outside)
+  int krow[NI];           // k-row (0..63) of this lane in instruction i
+  int col[NI];            // column of this lane's 16-byte unit in instruction i
+  int64_t step;           // elements per K step (64 * ld)
+  int KR, N;
+  bool cfull;             // the tile's columns all lie inside N
 
-  __device__ void init(int c0_, int N_) {
-    c0 = c0_;
+  __device__ void init(const bf16_t* base, int64_t ld, int c0, int N_, int KR_) {
+    KR = KR_;
     N = N_;
+    cfull = c0 + COLS <= N_;
+    step = (int64_t)BK * ld;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int p = lane % UPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = w + 4 * i;
       const int kr = q * RPI + lane / UPR;
-      const int p = lane % UPR;
       const int u = (((p >> 1) ^ km_swz(kr)) << 1) | (p & 1);
       krow[i] = kr;
-      coff[i] = u * 8;
+      col[i] = c0 + u * 8;
+      ptr[i] = base + (int64_t)kr * ld + col[i];
     }
   }
-  // kptr(k) returns the k-row's base pointer or nullptr (row outside the operand).
-  template <class F>
-  __device__ void issue(int kt, char* s, F kptr) const {
-    const int w = threadIdx.x >> 6;
+  __device__ bool full(int kt) const { return cfull && (kt + 1) * BK <= KR; }
+  template <int I0, int I1>
+  __device__ void issue(int kt, lds_t* s, bool full_step) const {
+    const int w = wave_id();
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bf16_t* p = kptr(kt * BK + krow[i]);
-      const int c = c0 + coff[i];
-      const void* g = (p && c < N) ? (const void*)(p + c) : (const void*)g_zero_page;
+    for (int i = I0; i < I1; ++i) {
+      const void* g = ptr[i];
+      if (!full_step && (kt * BK + krow[i] >= KR || col[i] >= N)) g = g_zero_page;
       dma16(g, s + (w + 4 * i) * 1024);
     }
   }
-  __device__ static bf16x8_t frag(const char* s, int cb, int kk) {
+  __device__ void advance() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ptr[i] += step;
+  }
+  __device__ static bf16x8_t frag(const lds_t* s, int cb, int kk) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, sl = lane & 15;
     const int col = cb + (g & 1) * 16 + 4 * (sl & 3);
     const int kr0 = kk * 16 + (g >> 1) * 8 + (sl >> 2);
     const int kr1 = kr0 + 4;
     const int ch = col >> 4;
-    const char* p0 = s + kr0 * RB + ((ch ^ km_swz(kr0)) << 5) + ((col & 15) << 1);
-    const char* p1 = s + kr1 * RB + ((ch ^ km_swz(kr1)) << 5) + ((col & 15) << 1);
+    const lds_t* p0 = s + kr0 * RB + ((ch ^ km_swz(kr0)) << 5) + ((col & 15) << 1);
+    const lds_t* p1 = s + kr1 * RB + ((ch ^ km_swz(kr1)) << 5) + ((col & 15) << 1);
     s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p0);
     s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p1);
     s16x8_t c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -171,12 +195,25 @@ struct OpKM {
   }
 };
 
+// Issues part P (of 4) of a stage's direct loads of operand O.
+template <int P, class O>
+__device__ __forceinline__ void issue_part(const O& o, int kt, lds_t* s, bool full_step) {
+  constexpr int per = (O::NI + 3) / 4;
+  constexpr int i0 = P * per < O::NI ? P * per : O::NI;
+  constexpr int i1 = (P + 1) * per < O::NI ? (P + 1) * per : O::NI;
+  if constexpr (i1 > i0) o.template issue<i0, i1>(kt, s, full_step);
+}
+
 // ---------------------------------------------------------------------------
 // Main loop.  2 x 2 waves; wave tile (BM/2) x (BN/2) as TM x TN MFMA 32x32.
+// Per K step: wait for this wave's loads of the step, barrier (all waves'
+// loads landed, everybody done with the slot about to be refilled), then the
+// four 16-k sub-steps, each issuing a quarter of the loads of step k+2 and
+// reading the fragments of the next sub-step while its MFMAs run.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, class OA, class OB, class IA, class IB>
-__device__ __forceinline__ void mainloop(const OA& oa, const OB& ob, IA issue_a, IB issue_b, int nk,
-                                         char* smem, f32x16_t (&acc)[BM / 64][BN / 64]) {
+template <int BM, int BN, class OA, class OB>
+__device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem,
+                                         f32x16_t (&acc)[BM / 64][BN / 64]) {
   constexpr int TM = BM / 64, TN = BN / 64;
   constexpr int ST = OA::BYTES + OB::BYTES;
   constexpr int L = OA::NI + OB::NI;
@@ -189,36 +226,58 @@ __device__ __forceinline__ void mainloop(const OA& oa, const OB& ob, IA issue_a,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (nk <= 0) return;
-  issue_a(0, smem);
-  issue_b(0, smem + OA::BYTES);
-  if (nk > 1) {
-    issue_a(1, smem + ST);
-    issue_b(1, smem + ST + OA::BYTES);
-  }
+  lds_t* const base = (lds_t*)smem;
+  auto issue_stage = [&](int kt, lds_t* s) {
+    const bool f = oa.full(kt) && ob.full(kt);
+    issue_part<0>(oa, kt, s, f); issue_part<1>(oa, kt, s, f);
+    issue_part<2>(oa, kt, s, f); issue_part<3>(oa, kt, s, f);
+    issue_part<0>(ob, kt, s + OA::BYTES, f); issue_part<1>(ob, kt, s + OA::BYTES, f);
+    issue_part<2>(ob, kt, s + OA::BYTES, f); issue_part<3>(ob, kt, s + OA::BYTES, f);
+    oa.advance();
+    ob.advance();
+  };
+  issue_stage(0, base);
+  if (nk > 1) issue_stage(1, base + ST);
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) wait_vmcnt<L>();
     else wait_vmcnt<0>();
     barrier_lds();
-    if (kt + 2 < nk) {
-      const int s2 = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3
-      issue_a(kt + 2, smem + s2 * ST);
-      issue_b(kt + 2, smem + s2 * ST + OA::BYTES);
-    }
-    const char* As = smem + slot * ST;
-    const char* Bs = As + OA::BYTES;
+    const bool pre = kt + 2 < nk;
+    const int s2 = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3
+    lds_t* const dst = base + s2 * ST;
+    const bool f = pre && oa.full(kt + 2) && ob.full(kt + 2);
+    const lds_t* As = base + slot * ST;
+    const lds_t* Bs = As + OA::BYTES;
+    bf16x8_t a[2][TM], b[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (BM / 2) + i * 32, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (BN / 2) + j * 32, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t a[TM], b[TN];
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = OA::frag(As, wm * (BM / 2) + i * 32, kk);
+        for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (BM / 2) + i * 32, kk + 1);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = OB::frag(Bs, wn * (BN / 2) + j * 32, kk);
+        for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (BN / 2) + j * 32, kk + 1);
+      }
+      if (pre) {
+        if (kk == 0) { issue_part<0>(oa, kt + 2, dst, f); issue_part<0>(ob, kt + 2, dst + OA::BYTES, f); }
+        if (kk == 1) { issue_part<1>(oa, kt + 2, dst, f); issue_part<1>(ob, kt + 2, dst + OA::BYTES, f); }
+        if (kk == 2) { issue_part<2>(oa, kt + 2, dst, f); issue_part<2>(ob, kt + 2, dst + OA::BYTES, f); }
+        if (kk == 3) { issue_part<3>(oa, kt + 2, dst, f); issue_part<3>(ob, kt + 2, dst + OA::BYTES, f); }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+    }
+    if (pre) {
+      oa.advance();
+      ob.advance();
     }
     slot = slot == 2 ? 0 : slot + 1;
   }
@@ -253,6 +312,80 @@ __device__ __forceinline__ int xcd_tile(int bid, int real) {
   if (idx >= per) return -1;
   const int L = (bid & 7) * per + idx;
   return L < real ? L : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue staging: accumulators -> bf16 tile in LDS (row stride S bytes) ->
+// 16-byte coalesced rows in global memory.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+
+template <int COLS>
+constexpr int ep_stride() { return COLS * 2 + 16; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Swaps a value with the neighbouring lane (lane ^ 1) through DPP.
+__device__ __forceinline__ float swap_adjacent(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Writes the wave's TM x TN MFMA tiles, value v(i, j, r), at tile rows
+// row0.. and columns col0.. .  Adjacent lanes hold adjacent columns of the
+// same rows, and registers r, r+1 (r even) adjacent rows: one lane swap lets
+// the even lane store the column pair of row r and the odd lane that of
+// row r+1, as 32-bit writes.
+template <int TM, int TN, int S, class V>
+__device__ __forceinline__ void stage_pairs(lds_t* t, int row0, int col0, V v) {
+  const int lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float a0 = v(i, j, r), a1 = v(i, j, r + 1);
+        const float recv = swap_adjacent(odd ? a0 : a1);
+        const uint32_t packed = odd ? pack_bf16x2(recv, a1) : pack_bf16x2(a0, recv);
+        const int row = row0 + acc_row(i, r, lane) + (odd ? 1 : 0);
+        const int col = col0 + j * 32 + ((lane & 31) & ~1);
+        *(__attribute__((address_space(3))) uint32_t*)(t + row * S + col * 2) = packed;
+      }
+}
+
+// Copies the staged ROWS x COLS tile to C (leading dimension ldc elements):
+// rows >= row_lim and columns >= col_lim are skipped.
+template <int ROWS, int COLS, int S>
+__device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t ldc, int row_lim,
+                                              int col_lim) {
+  constexpr int CPR = COLS / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
+    const int row = q / CPR, c8 = q % CPR;
+    if (row < row_lim && c8 * 8 < col_lim)
+      *(u32x4_t*)(C + (int64_t)row * ldc + c8 * 8) =
+          *(const __attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16);
+  }
+}
+
+// Loads a ROWS x COLS bf16 block of G (leading dimension ld) into LDS;
+// rows >= row_lim and columns >= col_lim are left unwritten.
+template <int ROWS, int COLS, int S>
+__device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t ld, int row_lim,
+                                              int col_lim) {
+  constexpr int CPR = COLS / 8;
+#pragma unroll 4
+  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
+    const int row = q / CPR, c8 = q % CPR;
+    if (row < row_lim && c8 * 8 < col_lim)
+      *(__attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16) =
+          *(const u32x4_t*)(G + (int64_t)row * ld + c8 * 8);
+  }
 }
 
 // ===========================================================================
@@ -290,7 +423,7 @@ struct RowsArgs {
   int I;
   const float* topk_w;
   const int32_t* src_of;
-  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk] partial <G, silu(g) u>;
+  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk] partial <G, silu(g) u> per 128 columns;
   // dH [R,2I]; weight of row = topk_w[src_of[row]]
   const bf16_t* Hin;
   float* dwp;
@@ -319,19 +452,13 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
     return p.A + ar * p.lda;
   }, p.K);
   const bf16_t* Be = p.B + (int64_t)e * p.b_estride;
-  auto issue_a = [&](int kt, char* s) { oa.issue(kt, s); };
 
   f32x16_t acc[RBM / 64][RBN / 64];
   const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
     OpKM<RBN> ob;
-    ob.init(nt * RBN, p.N);
-    const int K = p.K;
-    const int64_t ldb = p.ldb;
-    auto issue_b = [&](int kt, char* s) {
-      ob.issue(kt, s, [&](int k) { return k < K ? Be + (int64_t)k * ldb : (const bf16_t*)nullptr; });
-    };
-    mainloop<RBM, RBN>(oa, ob, issue_a, issue_b, nk, smem, acc);
+    ob.init(Be, p.ldb, nt * RBN, p.N, p.K);
+    mainloop<RBM, RBN>(oa, ob, nk, smem, acc);
   } else {
     OpMK<RBN> ob;
     ob.init([&](int n) {
@@ -347,76 +474,103 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
       }
       return Be + (int64_t)wrow * p.ldb;
     }, p.K);
-    auto issue_b = [&](int kt, char* s) { ob.issue(kt, s); };
-    mainloop<RBM, RBN>(oa, ob, issue_a, issue_b, nk, smem, acc);
+    mainloop<RBM, RBN>(oa, ob, nk, smem, acc);
   }
 
-  constexpr int TM = RBM / 64, TN = RBN / 64;
-  const int rbase = m0 + wm * (RBM / 2);
+  // ------------------------------------------------------------- epilogues
+  // The LDS ring is free once every wave has left the main loop.
+  barrier_lds();
+  lds_t* const lds = (lds_t*)smem;
+  const int rows_valid = seg1 - m0;  // rows of this tile inside the segment (may exceed 128)
+  const int r0w = wm * (RBM / 2);    // first tile row of this wave
   if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = nt * RBN + wn * (RBN / 2) + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + acc_row(i, r, lane);
-          if (row < seg1) p.C[(int64_t)row * p.ldc + col] = f2bf(acc[i][j][r]);
-        }
-    }
+    constexpr int S = ep_stride<RBN>();
+    const int c0w = wn * (RBN / 2);
+    stage_pairs<RBM / 64, RBN / 64, S>(lds, r0w, c0w,
+                                       [&](int i, int j, int r) { return acc[i][j][r]; });
+    barrier_lds();
+    lds_to_global<RBM, RBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * RBN, p.ldc, rows_valid,
+                               p.N - nt * RBN);
   } else if constexpr (EPI == EPI_GATEUP) {
-    // acc[i][2h] = gate, acc[i][2h+1] = up, gate column gc
-#pragma unroll
-    for (int h = 0; h < TN / 2; ++h) {
-      const int gc = nt * (RBN / 2) + wn * (RBN / 4) + h * 32 + (lane & 31);
-      if (gc >= p.I) continue;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + acc_row(i, r, lane);
-          if (row >= seg1) continue;
-          const float g = acc[i][2 * h][r], u = acc[i][2 * h + 1][r];
-          const float wr = p.topk_w[p.src_of[row]];
-          p.Aout[(int64_t)row * p.I + gc] = f2bf(wr * (g * sigmoidf_(g) * u));
-          if (p.H) {
-            p.H[(int64_t)row * 2 * p.I + gc] = f2bf(g);
-            p.H[(int64_t)row * 2 * p.I + p.I + gc] = f2bf(u);
-          }
-        }
+    // acc[i][2h] = gate, acc[i][2h+1] = up, for the tile's gate column
+    // wn * 64 + h * 32 + (lane & 31) (128 gate columns per tile)
+    constexpr int S = ep_stride<RBN / 2>();
+    constexpr int TB = RBM * S;  // bytes of one staged 128 x 128 tile
+    lds_f32_t* wl = (lds_f32_t*)(lds + 3 * TB);
+    const int tid = threadIdx.x;
+    if (tid < RBM) {
+      const int row = m0 + tid;
+      wl[tid] = row < seg1 ? p.topk_w[p.src_of[row]] : 0.0f;
     }
-  } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] at column col
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int cb = nt * RBN + wn * (RBN / 2) + j * 32;
-      const int col = cb + (lane & 31);
-      const bool cok = col < p.N;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + acc_row(i, r, lane);
-          const bool rok = row < seg1;
-          float part = 0.0f;
-          if (rok && cok) {
-            const float G = acc[i][j][r];
-            const int64_t hb = (int64_t)row * 2 * p.I;
-            const float g = bf2f(p.Hin[hb + col]);
-            const float u = bf2f(p.Hin[hb + p.I + col]);
-            const float wr = p.topk_w[p.src_of[row]];
-            const float s = sigmoidf_(g);
-            part = G * (g * s * u);
-            const float dA = wr * G;
-            p.dH[hb + col] = f2bf(dA * u * s * (1.0f + g * (1.0f - s)));
-            p.dH[hb + p.I + col] = f2bf(dA * g * s);
-          }
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
-          if ((lane & 31) == 0 && rok && cb < p.N) p.dwp[(int64_t)row * p.nblk + (cb >> 5)] = part;
-        }
+    barrier_lds();
+    const int c0w = wn * (RBN / 4);
+    stage_pairs<RBM / 64, RBN / 128, S>(lds, r0w, c0w, [&](int i, int h, int r) {
+      const float g = acc[i][2 * h][r], u = acc[i][2 * h + 1][r];
+      return wl[r0w + acc_row(i, r, lane)] * (g * sigmoidf_(g) * u);
+    });
+    if (p.H) {
+      stage_pairs<RBM / 64, RBN / 128, S>(lds + TB, r0w, c0w,
+                                          [&](int i, int h, int r) { return acc[i][2 * h][r]; });
+      stage_pairs<RBM / 64, RBN / 128, S>(lds + 2 * TB, r0w, c0w,
+                                          [&](int i, int h, int r) { return acc[i][2 * h + 1][r]; });
     }
+    barrier_lds();
+    const int gc0 = nt * (RBN / 2);
+    lds_to_global<RBM, RBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
+    if (p.H) {
+      bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
+      lds_to_global<RBM, RBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<RBM, RBN / 2, S>(lds + 2 * TB, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
+    }
+  } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] for the tile's column nt*256 + c
+    constexpr int S = ep_stride<RBN>();
+    constexpr int TB = RBM * S;
+    lds_t* Hg = lds;
+    lds_t* Hu = lds + TB;
+    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
+    const int col0 = nt * RBN;
+    const int64_t ldh = 2 * (int64_t)p.I;
+    // gate and up slices of H for the tile's rows and columns, coalesced
+    global_to_lds<RBM, RBN, S>(Hg, p.Hin + (int64_t)m0 * ldh + col0, ldh, rows_valid, p.N - col0);
+    global_to_lds<RBM, RBN, S>(Hu, p.Hin + (int64_t)m0 * ldh + p.I + col0, ldh, rows_valid, p.N - col0);
+    const int tid = threadIdx.x;
+    if (tid < RBM) {
+      const int row = m0 + tid;
+      wl[tid] = row < seg1 ? p.topk_w[p.src_of[row]] : 0.0f;
+    }
+    __syncthreads();
+    const int c0w = wn * (RBN / 2);
+    constexpr int TM = RBM / 64, TN = RBN / 64;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = r0w + acc_row(i, r, lane);
+        const float wr = wl[rl];
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int cl = c0w + j * 32 + (lane & 31);
+          lds_bf16_t* pg = (lds_bf16_t*)(Hg + rl * S + cl * 2);
+          lds_bf16_t* pu = (lds_bf16_t*)(Hu + rl * S + cl * 2);
+          const float G = acc[i][j][r];
+          const float g = bf2f(*pg), u = bf2f(*pu);
+          const float sg = sigmoidf_(g);
+          if (col0 + cl < p.N) part += G * (g * sg * u);  // columns past N hold stale bytes
+          const float dA = wr * G;
+          *pg = f2bf(dA * u * sg * (1.0f + g * (1.0f - sg)));
+          *pu = f2bf(dA * g * sg);
+        }
+        // partial <G, a> over this wave's 128 columns (G is zero past N)
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+        const int row = m0 + rl;
+        if ((lane & 31) == 0 && row < seg1 && col0 + c0w < p.N)
+          p.dwp[(int64_t)row * p.nblk + nt * 2 + wn] = part;
+      }
+    barrier_lds();
+    lds_to_global<RBM, RBN, S>(Hg, p.dH + (int64_t)m0 * ldh + col0, ldh, rows_valid, p.N - col0);
+    lds_to_global<RBM, RBN, S>(Hu, p.dH + (int64_t)m0 * ldh + p.I + col0, ldh, rows_valid, p.N - col0);
   }
 }
 
@@ -450,34 +604,20 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   const int len = p.offsets[e + 1] - seg0;
   OpKM<WBM> oa;
   OpKM<WBN> ob;
-  oa.init(mt * WBM, p.M);
-  ob.init(nt * WBN, p.N);
-  const bf16_t* Ab = p.A + (int64_t)seg0 * p.lda;
-  const bf16_t* Bb = p.B + (int64_t)seg0 * p.ldb;
-  const int64_t lda = p.lda, ldb = p.ldb;
-  auto issue_a = [&](int kt, char* s) {
-    oa.issue(kt, s, [&](int k) { return k < len ? Ab + (int64_t)k * lda : (const bf16_t*)nullptr; });
-  };
-  auto issue_b = [&](int kt, char* s) {
-    ob.issue(kt, s, [&](int k) { return k < len ? Bb + (int64_t)k * ldb : (const bf16_t*)nullptr; });
-  };
+  oa.init(p.A + (int64_t)seg0 * p.lda, p.lda, mt * WBM, p.M, len);
+  ob.init(p.B + (int64_t)seg0 * p.ldb, p.ldb, nt * WBN, p.N, len);
   f32x16_t acc[WBM / 64][WBN / 64];
-  mainloop<WBM, WBN>(oa, ob, issue_a, issue_b, (int)cdiv(len, BK), smem, acc);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mainloop<WBM, WBN>(oa, ob, (int)cdiv(len, BK), smem, acc);
+  const int wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  bf16_t* C = p.C + (int64_t)e * p.c_estride;
-#pragma unroll
-  for (int j = 0; j < WBN / 64; ++j) {
-    const int col = nt * WBN + wn * (WBN / 2) + j * 32 + (lane & 31);
-    if (col >= p.N) continue;
-#pragma unroll
-    for (int i = 0; i < WBM / 64; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mt * WBM + wm * (WBM / 2) + acc_row(i, r, lane);
-        if (row < p.M) C[(int64_t)row * p.N + col] = f2bf(acc[i][j][r]);
-      }
-  }
+  barrier_lds();
+  lds_t* const lds = (lds_t*)smem;
+  constexpr int S = ep_stride<WBN>();
+  stage_pairs<WBM / 64, WBN / 64, S>(lds, wm * (WBM / 2), wn * (WBN / 2),
+                                     [&](int i, int j, int r) { return acc[i][j][r]; });
+  barrier_lds();
+  lds_to_global<WBM, WBN, S>(lds, p.C + (int64_t)e * p.c_estride + (int64_t)mt * WBM * p.N + nt * WBN,
+                             p.N, p.M - mt * WBM, p.N - nt * WBN);
 }
 
 constexpr size_t kRowsSmem = (size_t)NSTAGE * (RBM + RBN) * BK * 2;
@@ -553,7 +693,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, RBN);
     p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
-    p.dwp = dwp; p.nblk = (int)cdiv(a.I, 32); p.dH = (bf16_t*)dH; p.I = a.I;
+    p.dwp = dwp; p.nblk = (int)cdiv(a.I, 128); p.dH = (bf16_t*)dH; p.I = a.I;
     err = launch_rows<EPI_DGRAD_SWIGLU, B_KM>(c, "gemm_down_dgrad", p, a.R);
     if (err != hipSuccess) return err;
   }

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void f32_swiglu_fwd(const float* __restrict__ 
   Aout[q] = topk_w[src_of[r]] * (g / (1.0f + expf(-g)) * u);
 }
 
-// From G = dout_t W_down[e] (per row): dwp[r, b] = sum over the 32 columns of
+// From G = dout_t W_down[e] (per row): dwp[r, b] = sum over the 128 columns of
 // block b of G * silu(g) * u; dA = w_r G; dH = (dA u s (1 + g (1 - s)), dA silu(g)).
 __global__ __launch_bounds__(256) void f32_swiglu_bwd(const float* __restrict__ G,
                                                       const float* __restrict__ H,
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void f32_swiglu_bwd(const float* __restrict__ 
   const int b = (int)(q % nblk);
   const float w = topk_w[src_of[r]];
   float part = 0.0f;
-  for (int i = b * 32; i < min(I, b * 32 + 32); ++i) {
+  for (int i = b * 128; i < min(I, b * 128 + 128); ++i) {
     const float Gv = G[r * I + i];
     const float g = H[r * 2 * I + i], u = H[r * 2 * I + I + i];
     const float s = 1.0f / (1.0f + expf(-g));
@@ -212,7 +212,7 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
                          const void* Aact, void* dH, void* dXp, float* dwp, void* dW_gu,
                          void* dW_d, float* G) {
   const int64_t I = a.I, d = a.d, R = a.R;
-  const int nblk = (int)cdiv(a.I, 32);
+  const int nblk = (int)cdiv(a.I, 128);
   // down dgrad: G[r, i] = sum_c dout[t_r, c] W_down[e][c, i]
   hipError_t err = rows_gemm(c, "gemm_down_dgrad", a, (const float*)dout, d, a.src_of, a.k,
                              (const float*)a.w_down, d * I, 1, I, G, I, a.I, a.d);

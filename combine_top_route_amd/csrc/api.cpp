@@ -111,6 +111,9 @@ moe_status check_shape(const moe_shape* s) {
   if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", #p)
 
 size_t elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+int dw_blocks(const moe_shape* s) {
+  return s->dtype == MOE_F32 ? f32_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
+}
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
@@ -143,7 +146,7 @@ Layout layout(const moe_shape* s, int op) {
   if (op == MOE_OP_BACKWARD) {
     L.dH = take(es * R * 2 * s->I);
     L.dXp = take(es * R * s->d);
-    L.dwp = take(sizeof(float) * R * cdiv(s->I, 128));
+    L.dwp = take(sizeof(float) * R * dw_blocks(s));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
     if (s->dtype == MOE_BF16) {
       L.Xp = take(es * R * s->d);
@@ -344,7 +347,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
     HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, Xp, doutp, dH, dXp, dwp, dw_gate_up, dw_down),
             "backward GEMMs");
   }
-  HIP_TRY(launch_topk_grad(c, dwp, (int)cdiv(shape->I, 128), routing->row_of, routing->topk_ids,
+  HIP_TRY(launch_topk_grad(c, dwp, dw_blocks(shape), routing->row_of, routing->topk_ids,
                            routing->topk_w, (int)shape->T, (int)shape->k, (int)shape->E, d_topk_w,
                            dlogits, shape->logits_dtype), "topk_grad");
   HIP_TRY(launch_combine(c, shape->dtype, dXp, routing->row_of, nullptr, (int)shape->T,

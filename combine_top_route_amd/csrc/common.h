@@ -59,7 +59,7 @@ struct LaunchCtx {
 
 // ---------------------------------------------------------------- routing
 // Tile table sizes: row tiles of the grouped GEMMs (expert-aligned).
-constexpr int kRowTile = 128;
+constexpr int kRowTile = 256;
 // Flat entries handled by one wave in the counting sort.
 constexpr int kSortChunk = 1024;
 
@@ -106,10 +106,14 @@ struct LayerArgs {
 // bf16 MFMA path.
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
 // backward: Xp [R,d] and doutp [R,d] are x and dout gathered into row order;
-// outputs dH [R,2I], dXp [R,d], dwp [R,ceil(I/128)] fp32, dW_gu, dW_d.
+// outputs dH [R,2I], dXp [R,d], dwp [R, bf16_dw_blocks(I)] fp32, dW_gu, dW_d.
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
                           const void* H, const void* Aw, const void* Xp, const void* doutp,
                           void* dH, void* dXp, float* dwp, void* dW_gu, void* dW_d);
+
+// Number of per-row partials of <G, a> that the down dgrad writes (dwp [R, n]).
+int bf16_dw_blocks(int I);
+int f32_dw_blocks(int I);
 
 // float32 path (plain FMA kernels, unfused epilogues).  forward needs H.
 hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);

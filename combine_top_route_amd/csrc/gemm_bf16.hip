@@ -11,14 +11,16 @@
 // plus the top-k-weight partial dot products are the epilogue of the down
 // dgrad GEMM.
 //
-// Tile engine (all six GEMMs): C[m,n] = sum_k A(m,k) B(n,k) on a 128x256 or
-// 256x128 output tile, K in steps of 64, four waves of 64x128 / 128x64, each
-// a grid of MFMA 32x32x16 bf16 tiles.  Operands move global -> LDS with
-// direct loads (global_load_lds_dwordx4, no register staging) into a
-// three-stage ring: while the MFMAs consume stage k, the loads of stage k+2
-// are in flight - for the gate/up GEMM those are the gathered token rows of
-// the next K slice, the one-GPU analogue of computing on one token group
-// while the next one moves.  One barrier per K step.
+// Tile engine (all six GEMMs): C[m,n] = sum_k A(m,k) B(n,k) on a 256x256
+// output tile, K in steps of 64, eight waves (two per SIMD) of 128x64, each
+// 4x2 MFMA 32x32x16 bf16 tiles.  The tile size is set by the memory side:
+// a CU sustains roughly 30 bytes/clock of global->LDS traffic with eight
+// waves, and a 256x256x64 step moves 64 KB per 2048 MFMA cycles (32 B/clk).
+// Operands move global -> LDS with direct loads (global_load_lds_dwordx4, no
+// register staging) into a two-stage ring: the loads of step k+1 are in
+// flight while the MFMAs consume step k - for the gate/up GEMM those are the
+// gathered token rows of the next K slice, the one-GPU analogue of computing
+// on one token group while the next one moves.  One barrier per K step.
 //
 // LDS layouts: an operand whose rows are K-contiguous in memory is stored
 // [row][64 k] and read with ds_read_b128; an operand whose rows are contiguous
@@ -33,13 +35,22 @@ namespace moe {
 namespace {
 
 constexpr int BK = 64;
-constexpr int NSTAGE = 3;
-constexpr int NTHR = 256;
+constexpr int NSTAGE = 2;
+constexpr int NWAVE = 8;
+constexpr int NTHR = NWAVE * 64;
+constexpr int WM = 2, WN = 4;          // wave grid
+constexpr int TBM = 256, TBN = 256;    // output tile
+constexpr int TM = TBM / WM / 32;      // MFMA tiles per wave along M (4)
+constexpr int TN = TBN / WN / 32;      // MFMA tiles per wave along N (2)
+static_assert(TBM == kRowTile, "tile table is built for 256-row tiles");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_t;  // byte pointer into LDS (32-bit)
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // Source of the direct loads that fall outside an operand (K tail, columns
 // past N, rows past an expert's segment in the weight gradients).
@@ -80,13 +91,13 @@ __device__ __forceinline__ int km_swz(int krow) { return ((krow & 3) << 1) ^ ((k
 // ---------------------------------------------------------------------------
 // Operand with K-contiguous rows (row r at rowp(r), element k at rowp(r)[k]).
 // ROWS x 64 tile; instruction q covers rows 8q..8q+7 (1 KB of LDS); wave w
-// issues q = w, w+4, ...  Each lane keeps one global pointer per instruction,
+// issues q = w, w+8, ...  Each lane keeps one global pointer per instruction,
 // advanced by 64 elements per K step; only a partial last K step checks
 // bounds.
 // ---------------------------------------------------------------------------
 template <int ROWS>
 struct OpMK {
-  static constexpr int NI = ROWS / 32;
+  static constexpr int NI = ROWS * BK * 2 / 1024 / NWAVE;
   static constexpr int BYTES = ROWS * BK * 2;
   const bf16_t* ptr[NI];  // address of this lane's chunk at the current K step
   int koff[NI];           // element offset of that chunk inside the K step
@@ -98,15 +109,13 @@ struct OpMK {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + NWAVE * i;
       const int row = 8 * q + (lane >> 3);
       koff[i] = (((lane & 7) ^ mk_swz(row)) << 3);
       ptr[i] = rowp_of(row) + koff[i];
     }
   }
-  // true when K step kt lies entirely inside K (no per-lane checks needed)
   __device__ bool full(int kt) const { return (kt + 1) * BK <= K; }
-  // issues instructions [i0, i1) of K step kt into stage base s
   template <int I0, int I1>
   __device__ void issue(int kt, lds_t* s, bool full_step) const {
     const int w = wave_id();
@@ -114,7 +123,7 @@ struct OpMK {
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
       if (!full_step && kt * BK + koff[i] >= K) g = g_zero_page;
-      dma16(g, s + (w + 4 * i) * 1024);
+      dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
   __device__ void advance() {
@@ -138,7 +147,7 @@ struct OpKM {
   static constexpr int RB = COLS * 2;       // bytes per k-row
   static constexpr int UPR = RB / 16;       // 16-byte units per k-row
   static constexpr int RPI = 1024 / RB;     // k-rows per instruction
-  static constexpr int NI = BK / RPI / 4;   // instructions per wave per stage
+  static constexpr int NI = BK / RPI / NWAVE;
   static constexpr int BYTES = COLS * BK * 2;
   const bf16_t* ptr[NI];  // address at the current K step (not dereferenced when outside)
   int krow[NI];           // k-row (0..63) of this lane in instruction i
@@ -156,7 +165,7 @@ struct OpKM {
     const int p = lane % UPR;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + NWAVE * i;
       const int kr = q * RPI + lane / UPR;
       const int u = (((p >> 1) ^ km_swz(kr)) << 1) | (p & 1);
       krow[i] = kr;
@@ -172,7 +181,7 @@ struct OpKM {
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
       if (!full_step && (kt * BK + krow[i] >= KR || col[i] >= N)) g = g_zero_page;
-      dma16(g, s + (w + 4 * i) * 1024);
+      dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
   __device__ void advance() {
@@ -204,21 +213,20 @@ __device__ __forceinline__ void issue_part(const O& o, int kt, lds_t* s, bool fu
   if constexpr (i1 > i0) o.template issue<i0, i1>(kt, s, full_step);
 }
 
+// Wave position in the 2 x 4 wave grid.
+__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
+__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
+
 // ---------------------------------------------------------------------------
-// Main loop.  2 x 2 waves; wave tile (BM/2) x (BN/2) as TM x TN MFMA 32x32.
-// Per K step: wait for this wave's loads of the step, barrier (all waves'
-// loads landed, everybody done with the slot about to be refilled), then the
-// four 16-k sub-steps, each issuing a quarter of the loads of step k+2 and
-// reading the fragments of the next sub-step while its MFMAs run.
+// Main loop.  Per K step: wait for this wave's loads of the step, barrier
+// (all waves' loads landed, everybody done with the slot to be refilled),
+// then four 16-k sub-steps, each issuing a quarter of the next step's loads
+// and reading the fragments of the next sub-step while its MFMAs run.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, class OA, class OB>
-__device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem,
-                                         f32x16_t (&acc)[BM / 64][BN / 64]) {
-  constexpr int TM = BM / 64, TN = BN / 64;
+template <class OA, class OB>
+__device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32x16_t (&acc)[TM][TN]) {
   constexpr int ST = OA::BYTES + OB::BYTES;
-  constexpr int L = OA::NI + OB::NI;
-  const int wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wave_m(), wn = wave_n();
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -227,47 +235,43 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (nk <= 0) return;
   lds_t* const base = (lds_t*)smem;
-  auto issue_stage = [&](int kt, lds_t* s) {
-    const bool f = oa.full(kt) && ob.full(kt);
-    issue_part<0>(oa, kt, s, f); issue_part<1>(oa, kt, s, f);
-    issue_part<2>(oa, kt, s, f); issue_part<3>(oa, kt, s, f);
-    issue_part<0>(ob, kt, s + OA::BYTES, f); issue_part<1>(ob, kt, s + OA::BYTES, f);
-    issue_part<2>(ob, kt, s + OA::BYTES, f); issue_part<3>(ob, kt, s + OA::BYTES, f);
+  {
+    const bool f = oa.full(0) && ob.full(0);
+    issue_part<0>(oa, 0, base, f); issue_part<1>(oa, 0, base, f);
+    issue_part<2>(oa, 0, base, f); issue_part<3>(oa, 0, base, f);
+    issue_part<0>(ob, 0, base + OA::BYTES, f); issue_part<1>(ob, 0, base + OA::BYTES, f);
+    issue_part<2>(ob, 0, base + OA::BYTES, f); issue_part<3>(ob, 0, base + OA::BYTES, f);
     oa.advance();
     ob.advance();
-  };
-  issue_stage(0, base);
-  if (nk > 1) issue_stage(1, base + ST);
+  }
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();
     barrier_lds();
-    const bool pre = kt + 2 < nk;
-    const int s2 = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3
-    lds_t* const dst = base + s2 * ST;
-    const bool f = pre && oa.full(kt + 2) && ob.full(kt + 2);
+    const bool pre = kt + 1 < nk;
+    lds_t* const dst = base + (slot ^ 1) * ST;
+    const bool f = pre && oa.full(kt + 1) && ob.full(kt + 1);
     const lds_t* As = base + slot * ST;
     const lds_t* Bs = As + OA::BYTES;
     bf16x8_t a[2][TM], b[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (BM / 2) + i * 32, 0);
+    for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (TBM / WM) + i * 32, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (BN / 2) + j * 32, 0);
+    for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int cur = kk & 1;
       if (kk + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (BM / 2) + i * 32, kk + 1);
+        for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TBM / WM) + i * 32, kk + 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (BN / 2) + j * 32, kk + 1);
+        for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
       }
       if (pre) {
-        if (kk == 0) { issue_part<0>(oa, kt + 2, dst, f); issue_part<0>(ob, kt + 2, dst + OA::BYTES, f); }
-        if (kk == 1) { issue_part<1>(oa, kt + 2, dst, f); issue_part<1>(ob, kt + 2, dst + OA::BYTES, f); }
-        if (kk == 2) { issue_part<2>(oa, kt + 2, dst, f); issue_part<2>(ob, kt + 2, dst + OA::BYTES, f); }
-        if (kk == 3) { issue_part<3>(oa, kt + 2, dst, f); issue_part<3>(ob, kt + 2, dst + OA::BYTES, f); }
+        if (kk == 0) { issue_part<0>(oa, kt + 1, dst, f); issue_part<0>(ob, kt + 1, dst + OA::BYTES, f); }
+        if (kk == 1) { issue_part<1>(oa, kt + 1, dst, f); issue_part<1>(ob, kt + 1, dst + OA::BYTES, f); }
+        if (kk == 2) { issue_part<2>(oa, kt + 1, dst, f); issue_part<2>(ob, kt + 1, dst + OA::BYTES, f); }
+        if (kk == 3) { issue_part<3>(oa, kt + 1, dst, f); issue_part<3>(ob, kt + 1, dst + OA::BYTES, f); }
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -279,7 +283,7 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem,
       oa.advance();
       ob.advance();
     }
-    slot = slot == 2 ? 0 : slot + 1;
+    slot ^= 1;
   }
 }
 
@@ -318,10 +322,6 @@ __device__ __forceinline__ int xcd_tile(int bid, int real) {
 // Epilogue staging: accumulators -> bf16 tile in LDS (row stride S bytes) ->
 // 16-byte coalesced rows in global memory.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) float lds_f32_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
-
 template <int COLS>
 constexpr int ep_stride() { return COLS * 2 + 16; }
 
@@ -334,19 +334,19 @@ __device__ __forceinline__ float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
-// Writes the wave's TM x TN MFMA tiles, value v(i, j, r), at tile rows
-// row0.. and columns col0.. .  Adjacent lanes hold adjacent columns of the
-// same rows, and registers r, r+1 (r even) adjacent rows: one lane swap lets
-// the even lane store the column pair of row r and the odd lane that of
-// row r+1, as 32-bit writes.
-template <int TM, int TN, int S, class V>
+// Writes the wave's MFMA tiles i in [0, NI), j in [0, NJ), value v(i, j, r),
+// at tile rows row0.. and columns col0.. .  Adjacent lanes hold adjacent
+// columns of the same rows, and registers r, r+1 (r even) adjacent rows: one
+// lane swap lets the even lane store the column pair of row r and the odd
+// lane that of row r+1, as 32-bit writes.
+template <int NI, int NJ, int S, class V>
 __device__ __forceinline__ void stage_pairs(lds_t* t, int row0, int col0, V v) {
   const int lane = threadIdx.x & 63;
   const bool odd = lane & 1;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float a0 = v(i, j, r), a1 = v(i, j, r + 1);
@@ -388,13 +388,18 @@ __device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t
   }
 }
 
+// Weights of the tile's rows (topk_w of each row's flat entry; 0 past seg1).
+__device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
+                                                 const int32_t* src_of, int m0, int seg1) {
+  for (int t = threadIdx.x; t < TBM; t += NTHR) {
+    const int row = m0 + t;
+    wl[t] = row < seg1 ? topk_w[src_of[row]] : 0.0f;
+  }
+}
+
 // ===========================================================================
 // Ragged-M GEMMs: rows are an expert's segment of the expert-sorted rows.
-// Tile 128 rows x 256 columns.
 // ===========================================================================
-constexpr int RBM = 128, RBN = 256;
-static_assert(RBM == kRowTile, "tile table is built for 128-row tiles");
-
 enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_DGRAD_SWIGLU = 2 };
 enum BLay { B_MK = 0, B_MK_GATEUP = 1, B_KM = 2 };
 
@@ -423,8 +428,8 @@ struct RowsArgs {
   int I;
   const float* topk_w;
   const int32_t* src_of;
-  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk] partial <G, silu(g) u> per 128 columns;
-  // dH [R,2I]; weight of row = topk_w[src_of[row]]
+  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk] partial <G, silu(g) u> per
+  // 64 columns; dH [R,2I]; weight of row = topk_w[src_of[row]]
   const bf16_t* Hin;
   float* dwp;
   int nblk;
@@ -440,11 +445,11 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   const int mt = L / p.n_tiles;
   const int e = find_expert(p.tile_off, p.E, mt);
   const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-  const int m0 = seg0 + (mt - p.tile_off[e]) * RBM;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = seg0 + (mt - p.tile_off[e]) * TBM;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave_m(), wn = wave_n();
 
-  OpMK<RBM> oa;
+  OpMK<TBM> oa;
   oa.init([&](int row) {
     int r = m0 + row;
     if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
@@ -453,134 +458,129 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   }, p.K);
   const bf16_t* Be = p.B + (int64_t)e * p.b_estride;
 
-  f32x16_t acc[RBM / 64][RBN / 64];
+  f32x16_t acc[TM][TN];
   const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
-    OpKM<RBN> ob;
-    ob.init(Be, p.ldb, nt * RBN, p.N, p.K);
-    mainloop<RBM, RBN>(oa, ob, nk, smem, acc);
+    OpKM<TBN> ob;
+    ob.init(Be, p.ldb, nt * TBN, p.N, p.K);
+    mainloop(oa, ob, nk, smem, acc);
   } else {
-    OpMK<RBN> ob;
+    OpMK<TBN> ob;
     ob.init([&](int n) {
       int wrow;
       if constexpr (BL == B_MK_GATEUP) {
         const int blk = n >> 5;
-        int gc = nt * (RBN / 2) + (blk >> 1) * 32 + (n & 31);
+        int gc = nt * (TBN / 2) + (blk >> 1) * 32 + (n & 31);
         if (gc >= p.I) gc = 0;
         wrow = (blk & 1) ? p.I + gc : gc;
       } else {
-        wrow = nt * RBN + n;
+        wrow = nt * TBN + n;
         if (wrow >= p.N) wrow = 0;
       }
       return Be + (int64_t)wrow * p.ldb;
     }, p.K);
-    mainloop<RBM, RBN>(oa, ob, nk, smem, acc);
+    mainloop(oa, ob, nk, smem, acc);
   }
 
   // ------------------------------------------------------------- epilogues
   // The LDS ring is free once every wave has left the main loop.
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
-  const int rows_valid = seg1 - m0;  // rows of this tile inside the segment (may exceed 128)
-  const int r0w = wm * (RBM / 2);    // first tile row of this wave
+  const int rows_valid = seg1 - m0;  // rows of this tile inside the segment (may exceed 256)
+  const int r0w = wm * (TBM / WM);   // first tile row of this wave
   if constexpr (EPI == EPI_STORE) {
-    constexpr int S = ep_stride<RBN>();
-    const int c0w = wn * (RBN / 2);
-    stage_pairs<RBM / 64, RBN / 64, S>(lds, r0w, c0w,
-                                       [&](int i, int j, int r) { return acc[i][j][r]; });
+    constexpr int S = ep_stride<TBN>();
+    stage_pairs<TM, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
     barrier_lds();
-    lds_to_global<RBM, RBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * RBN, p.ldc, rows_valid,
-                               p.N - nt * RBN);
+    lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
+                               p.N - nt * TBN);
   } else if constexpr (EPI == EPI_GATEUP) {
-    // acc[i][2h] = gate, acc[i][2h+1] = up, for the tile's gate column
-    // wn * 64 + h * 32 + (lane & 31) (128 gate columns per tile)
-    constexpr int S = ep_stride<RBN / 2>();
-    constexpr int TB = RBM * S;  // bytes of one staged 128 x 128 tile
-    lds_f32_t* wl = (lds_f32_t*)(lds + 3 * TB);
-    const int tid = threadIdx.x;
-    if (tid < RBM) {
-      const int row = m0 + tid;
-      wl[tid] = row < seg1 ? p.topk_w[p.src_of[row]] : 0.0f;
-    }
+    // acc[i][0] = gate, acc[i][1] = up, for the tile's gate column
+    // wn * 32 + (lane & 31) (128 gate columns per tile)
+    constexpr int S = ep_stride<TBN / 2>();
+    constexpr int TB = TBM * S;  // bytes of one staged 256 x 128 tile
+    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
+    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
     barrier_lds();
-    const int c0w = wn * (RBN / 4);
-    stage_pairs<RBM / 64, RBN / 128, S>(lds, r0w, c0w, [&](int i, int h, int r) {
-      const float g = acc[i][2 * h][r], u = acc[i][2 * h + 1][r];
+    const int c0w = wn * 32;
+    stage_pairs<TM, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
+      const float g = acc[i][0][r], u = acc[i][1][r];
       return wl[r0w + acc_row(i, r, lane)] * (g * sigmoidf_(g) * u);
     });
-    if (p.H) {
-      stage_pairs<RBM / 64, RBN / 128, S>(lds + TB, r0w, c0w,
-                                          [&](int i, int h, int r) { return acc[i][2 * h][r]; });
-      stage_pairs<RBM / 64, RBN / 128, S>(lds + 2 * TB, r0w, c0w,
-                                          [&](int i, int h, int r) { return acc[i][2 * h + 1][r]; });
-    }
+    if (p.H) stage_pairs<TM, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
     barrier_lds();
-    const int gc0 = nt * (RBN / 2);
-    lds_to_global<RBM, RBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
+    const int gc0 = nt * (TBN / 2);
+    lds_to_global<TBM, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
     if (p.H) {
       bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
-      lds_to_global<RBM, RBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
-      lds_to_global<RBM, RBN / 2, S>(lds + 2 * TB, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<TBM, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
+      barrier_lds();
+      stage_pairs<TM, 1, S>(lds, r0w, c0w, [&](int i, int, int r) { return acc[i][1][r]; });
+      barrier_lds();
+      lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
   } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] for the tile's column nt*256 + c
-    constexpr int S = ep_stride<RBN>();
-    constexpr int TB = RBM * S;
+    // Two rounds of 128 rows (one wave row each): H's gate and up slices of
+    // those rows come into LDS with coalesced loads, turn into dH in place,
+    // and leave with coalesced stores.
+    constexpr int HR = TBM / WM;  // rows per round
+    constexpr int S = ep_stride<TBN>();
+    constexpr int TB = HR * S;
     lds_t* Hg = lds;
     lds_t* Hu = lds + TB;
     lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    const int col0 = nt * RBN;
+    const int col0 = nt * TBN;
     const int64_t ldh = 2 * (int64_t)p.I;
-    // gate and up slices of H for the tile's rows and columns, coalesced
-    global_to_lds<RBM, RBN, S>(Hg, p.Hin + (int64_t)m0 * ldh + col0, ldh, rows_valid, p.N - col0);
-    global_to_lds<RBM, RBN, S>(Hu, p.Hin + (int64_t)m0 * ldh + p.I + col0, ldh, rows_valid, p.N - col0);
-    const int tid = threadIdx.x;
-    if (tid < RBM) {
-      const int row = m0 + tid;
-      wl[tid] = row < seg1 ? p.topk_w[p.src_of[row]] : 0.0f;
-    }
-    __syncthreads();
-    const int c0w = wn * (RBN / 2);
-    constexpr int TM = RBM / 64, TN = RBN / 64;
+    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
+    const int c0w = wn * (TBN / WN);
+#pragma unroll 1
+    for (int h = 0; h < WM; ++h) {
+      const int mh = m0 + h * HR;
+      global_to_lds<HR, TBN, S>(Hg, p.Hin + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
+      global_to_lds<HR, TBN, S>(Hu, p.Hin + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
+      __syncthreads();
+      if (wm == h) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = r0w + acc_row(i, r, lane);
-        const float wr = wl[rl];
-        float part = 0.0f;
+          for (int r = 0; r < 16; ++r) {
+            const int rl = acc_row(i, r, lane);  // row inside this round
+            const float wr = wl[h * HR + rl];
+            float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int cl = c0w + j * 32 + (lane & 31);
-          lds_bf16_t* pg = (lds_bf16_t*)(Hg + rl * S + cl * 2);
-          lds_bf16_t* pu = (lds_bf16_t*)(Hu + rl * S + cl * 2);
-          const float G = acc[i][j][r];
-          const float g = bf2f(*pg), u = bf2f(*pu);
-          const float sg = sigmoidf_(g);
-          if (col0 + cl < p.N) part += G * (g * sg * u);  // columns past N hold stale bytes
-          const float dA = wr * G;
-          *pg = f2bf(dA * u * sg * (1.0f + g * (1.0f - sg)));
-          *pu = f2bf(dA * g * sg);
-        }
-        // partial <G, a> over this wave's 128 columns (G is zero past N)
+            for (int j = 0; j < TN; ++j) {
+              const int cl = c0w + j * 32 + (lane & 31);
+              lds_bf16_t* pg = (lds_bf16_t*)(Hg + rl * S + cl * 2);
+              lds_bf16_t* pu = (lds_bf16_t*)(Hu + rl * S + cl * 2);
+              const float G = acc[i][j][r];
+              const float g = bf2f(*pg), u = bf2f(*pu);
+              const float sg = sigmoidf_(g);
+              if (col0 + cl < p.N) part += G * (g * sg * u);  // columns past N hold stale bytes
+              const float dA = wr * G;
+              *pg = f2bf(dA * u * sg * (1.0f + g * (1.0f - sg)));
+              *pu = f2bf(dA * g * sg);
+            }
+            // partial <G, a> over this wave's 64 columns
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
-        const int row = m0 + rl;
-        if ((lane & 31) == 0 && row < seg1 && col0 + c0w < p.N)
-          p.dwp[(int64_t)row * p.nblk + nt * 2 + wn] = part;
+            for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+            const int row = mh + rl;
+            if ((lane & 31) == 0 && row < seg1)  // 0 when all 64 columns lie past N
+              p.dwp[(int64_t)row * p.nblk + nt * WN + wn] = part;
+          }
       }
-    barrier_lds();
-    lds_to_global<RBM, RBN, S>(Hg, p.dH + (int64_t)m0 * ldh + col0, ldh, rows_valid, p.N - col0);
-    lds_to_global<RBM, RBN, S>(Hu, p.dH + (int64_t)m0 * ldh + p.I + col0, ldh, rows_valid, p.N - col0);
+      barrier_lds();
+      lds_to_global<HR, TBN, S>(Hg, p.dH + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
+      lds_to_global<HR, TBN, S>(Hu, p.dH + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
+      barrier_lds();
+    }
   }
 }
 
 // ===========================================================================
 // Weight gradients: dW[e][m, n] = sum over the expert's rows r of
 // A[seg0 + r][m] * B[seg0 + r][n]; both operands are row-major [R, *] with
-// rows in expert order (contiguous per expert).  Tile 256 x 128.
+// rows in expert order (contiguous per expert).
 // ===========================================================================
-constexpr int WBM = 256, WBN = 128;
-
 struct WgradArgs {
   const bf16_t* A;
   int64_t lda;
@@ -602,61 +602,66 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   const int e = p.order[oi];
   const int seg0 = p.offsets[e];
   const int len = p.offsets[e + 1] - seg0;
-  OpKM<WBM> oa;
-  OpKM<WBN> ob;
-  oa.init(p.A + (int64_t)seg0 * p.lda, p.lda, mt * WBM, p.M, len);
-  ob.init(p.B + (int64_t)seg0 * p.ldb, p.ldb, nt * WBN, p.N, len);
-  f32x16_t acc[WBM / 64][WBN / 64];
-  mainloop<WBM, WBN>(oa, ob, (int)cdiv(len, BK), smem, acc);
-  const int wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  OpKM<TBM> oa;
+  OpKM<TBN> ob;
+  oa.init(p.A + (int64_t)seg0 * p.lda, p.lda, mt * TBM, p.M, len);
+  ob.init(p.B + (int64_t)seg0 * p.ldb, p.ldb, nt * TBN, p.N, len);
+  f32x16_t acc[TM][TN];
+  mainloop(oa, ob, (int)cdiv(len, BK), smem, acc);
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
-  constexpr int S = ep_stride<WBN>();
-  stage_pairs<WBM / 64, WBN / 64, S>(lds, wm * (WBM / 2), wn * (WBN / 2),
-                                     [&](int i, int j, int r) { return acc[i][j][r]; });
+  constexpr int S = ep_stride<TBN>();
+  stage_pairs<TM, TN, S>(lds, wave_m() * (TBM / WM), wave_n() * (TBN / WN),
+                         [&](int i, int j, int r) { return acc[i][j][r]; });
   barrier_lds();
-  lds_to_global<WBM, WBN, S>(lds, p.C + (int64_t)e * p.c_estride + (int64_t)mt * WBM * p.N + nt * WBN,
-                             p.N, p.M - mt * WBM, p.N - nt * WBN);
+  lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)e * p.c_estride + (int64_t)mt * TBM * p.N + nt * TBN,
+                             p.N, p.M - mt * TBM, p.N - nt * TBN);
 }
 
-constexpr size_t kRowsSmem = (size_t)NSTAGE * (RBM + RBN) * BK * 2;
-constexpr size_t kWgradSmem = (size_t)NSTAGE * (WBM + WBN) * BK * 2;
+// Dynamic LDS: the operand ring, or the largest epilogue staging area.
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+constexpr size_t kRingBytes = (size_t)NSTAGE * (TBM + TBN) * BK * 2;
+constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
+constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
+constexpr size_t kDgradEpi = (size_t)2 * (TBM / WM) * ep_stride<TBN>() + TBM * 4;
+constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreEpi), cmax(kGateupEpi, kDgradEpi));
+static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <class K>
-hipError_t allow_smem(K kernel, size_t bytes) {
+hipError_t allow_smem(K kernel) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+                             (int)kSmem);
 }
 
 template <int EPI, int BL>
 hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(rows_gemm_kernel<EPI, BL>, kRowsSmem);
+    hipError_t e = allow_smem(rows_gemm_kernel<EPI, BL>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   // upper bound of the tile count (the kernel reads the exact one)
-  const int64_t tiles = (int64_t)(R / RBM + p.E) * p.n_tiles;
+  const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
-  MOE_LAUNCH(c, name, (rows_gemm_kernel<EPI, BL>), dim3(nblocks), dim3(NTHR), kRowsSmem, p);
+  MOE_LAUNCH(c, name, (rows_gemm_kernel<EPI, BL>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
 hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p, int E) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(wgrad_kernel, kWgradSmem);
+    hipError_t e = allow_smem(wgrad_kernel);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(c, name, wgrad_kernel, dim3((unsigned)(E * p.m_tiles * p.n_tiles)), dim3(NTHR),
-             kWgradSmem, p);
+  MOE_LAUNCH(c, name, wgrad_kernel, dim3((unsigned)(E * p.m_tiles * p.n_tiles)), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
 }  // namespace
+
+int bf16_dw_blocks(int I) { return (int)cdiv(I, TBN) * WN; }
 
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw) {
   const int64_t I = a.I, d = a.d;
@@ -665,7 +670,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = (const bf16_t*)a.x; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
-    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, RBN / 2);
+    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R);
@@ -676,7 +681,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
   q.offsets = a.offsets; q.tile_off = a.tile_off; q.E = a.E;
   q.A = (const bf16_t*)Aw; q.lda = I; q.a_src = nullptr; q.a_div = 1;
   q.B = (const bf16_t*)a.w_down; q.b_estride = d * I; q.ldb = I;
-  q.N = a.d; q.K = a.I; q.n_tiles = (int)cdiv(a.d, RBN);
+  q.N = a.d; q.K = a.I; q.n_tiles = (int)cdiv(a.d, TBN);
   q.C = (bf16_t*)Yw; q.ldc = d;
   return launch_rows<EPI_STORE, B_MK>(c, "gemm_down_fwd", q, a.R);
 }
@@ -691,9 +696,9 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
-    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, RBN);
+    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
-    p.dwp = dwp; p.nblk = (int)cdiv(a.I, 128); p.dH = (bf16_t*)dH; p.I = a.I;
+    p.dwp = dwp; p.nblk = bf16_dw_blocks(a.I); p.dH = (bf16_t*)dH; p.I = a.I;
     err = launch_rows<EPI_DGRAD_SWIGLU, B_KM>(c, "gemm_down_dgrad", p, a.R);
     if (err != hipSuccess) return err;
   }
@@ -701,7 +706,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     WgradArgs p = {};
     p.A = (const bf16_t*)doutp; p.lda = d;
     p.B = (const bf16_t*)Aw; p.ldb = I;
-    p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, WBM); p.n_tiles = (int)cdiv(a.I, WBN);
+    p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
     err = launch_wgrad(c, "gemm_down_wgrad", p, a.E);
@@ -712,7 +717,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = (const bf16_t*)dH; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
-    p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, RBN);
+    p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
     err = launch_rows<EPI_STORE, B_KM>(c, "gemm_gateup_dgrad", p, a.R);
     if (err != hipSuccess) return err;
@@ -721,7 +726,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     WgradArgs p = {};
     p.A = (const bf16_t*)dH; p.lda = 2 * I;
     p.B = (const bf16_t*)Xp; p.ldb = d;
-    p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, WBM); p.n_tiles = (int)cdiv(a.d, WBN);
+    p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
     err = launch_wgrad(c, "gemm_gateup_wgrad", p, a.E);

@@ -7,7 +7,7 @@ namespace moe {
 namespace {
 
 constexpr int FBM = 128, FBN = 64, FBK = 16;
-static_assert(FBM == kRowTile, "tile table is built for 128-row tiles");
+static_assert(kRowTile % FBM == 0, "a row tile of the tile table is whole FBM-row blocks");
 
 __device__ __forceinline__ int find_expert_f(const int32_t* tile_off, int E, int mt) {
   int lo = 0, hi = E;
@@ -35,10 +35,11 @@ __global__ __launch_bounds__(256) void f32_rows_gemm(const float* __restrict__ A
   if (mt >= tile_off[E]) return;
   const int e = find_expert_f(tile_off, E, mt);
   const int seg0 = offsets[e], seg1 = offsets[e + 1];
-  const int m0 = seg0 + (mt - tile_off[e]) * FBM;
   const int n0 = nt * FBN;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const float* Be = B + (int64_t)e * bes;
+  for (int m0 = seg0 + (mt - tile_off[e]) * kRowTile;
+       m0 < seg1 && m0 < seg0 + (mt - tile_off[e] + 1) * kRowTile; m0 += FBM) {
   float acc[8][4] = {};
   for (int k0 = 0; k0 < K; k0 += FBK) {
     for (int i = 0; i < 8; ++i) {
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(256) void f32_rows_gemm(const float* __restrict__ A
       const int col = n0 + tx * 4 + j;
       if (col < N) C[(int64_t)row * ldc + col] = acc[i][j];
     }
+  }
   }
 }
 
@@ -178,7 +180,7 @@ hipError_t rows_gemm(const LaunchCtx& c, const char* name, const LayerArgs& a, c
                      int64_t lda, const int32_t* a_src, int a_div, const float* B, int64_t bes,
                      int64_t bsn, int64_t bsk, float* C, int64_t ldc, int N, int K) {
   const int n_tiles = (int)cdiv(N, FBN);
-  const int64_t blocks = (int64_t)(a.R / FBM + a.E) * n_tiles;
+  const int64_t blocks = (int64_t)(a.R / kRowTile + a.E) * n_tiles;
   MOE_LAUNCH(c, name, f32_rows_gemm, dim3((unsigned)blocks), dim3(256), 0, A, lda, a_src, a_div,
              B, bes, bsn, bsk, C, ldc, N, K, a.offsets, a.tile_off, a.E, n_tiles);
   return hipSuccess;
@@ -196,6 +198,8 @@ hipError_t wgrad(const LaunchCtx& c, const char* name, const LayerArgs& a, const
 
 }  // namespace
 
+int f32_dw_blocks(int I) { return (int)cdiv(I, 128); }
+
 hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aact, void* Y) {
   const int64_t I = a.I, d = a.d, R = a.R;
   hipError_t err = rows_gemm(c, "gemm_gateup_fwd", a, (const float*)a.x, d, a.src_of, a.k,
@@ -212,7 +216,7 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
                          const void* Aact, void* dH, void* dXp, float* dwp, void* dW_gu,
                          void* dW_d, float* G) {
   const int64_t I = a.I, d = a.d, R = a.R;
-  const int nblk = (int)cdiv(a.I, 128);
+  const int nblk = f32_dw_blocks(a.I);
   // down dgrad: G[r, i] = sum_c dout[t_r, c] W_down[e][c, i]
   hipError_t err = rows_gemm(c, "gemm_down_dgrad", a, (const float*)dout, d, a.src_of, a.k,
                              (const float*)a.w_down, d * I, 1, I, G, I, a.I, a.d);

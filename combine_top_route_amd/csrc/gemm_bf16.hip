@@ -100,19 +100,22 @@ struct OpMK {
   static constexpr int NI = ROWS * BK * 2 / 1024 / NWAVE;
   static constexpr int BYTES = ROWS * BK * 2;
   const bf16_t* ptr[NI];  // address of this lane's chunk at the current K step
-  int koff[NI];           // element offset of that chunk inside the K step
   int K;
 
+  // element offset inside a K step of this lane's chunk in instruction i
+  __device__ static int koff(int i) {
+    const int lane = threadIdx.x & 63;
+    const int row = 8 * ((threadIdx.x >> 6) + NWAVE * i) + (lane >> 3);
+    return ((lane & 7) ^ mk_swz(row)) << 3;
+  }
   template <class F>
   __device__ void init(F rowp_of, int K_) {
     K = K_;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + NWAVE * i;
-      const int row = 8 * q + (lane >> 3);
-      koff[i] = (((lane & 7) ^ mk_swz(row)) << 3);
-      ptr[i] = rowp_of(row) + koff[i];
+      const int row = 8 * (w + NWAVE * i) + (lane >> 3);
+      ptr[i] = rowp_of(row) + koff(i);
     }
   }
   __device__ bool full(int kt) const { return (kt + 1) * BK <= K; }
@@ -122,7 +125,7 @@ struct OpMK {
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
-      if (!full_step && kt * BK + koff[i] >= K) g = g_zero_page;
+      if (!full_step && kt * BK + koff(i) >= K) g = g_zero_page;
       dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
@@ -150,28 +153,26 @@ struct OpKM {
   static constexpr int NI = BK / RPI / NWAVE;
   static constexpr int BYTES = COLS * BK * 2;
   const bf16_t* ptr[NI];  // address at the current K step (not dereferenced when outside)
-  int krow[NI];           // k-row (0..63) of this lane in instruction i
-  int col[NI];            // column of this lane's 16-byte unit in instruction i
   int64_t step;           // elements per K step (64 * ld)
-  int KR, N;
+  int c0, KR, N;
   bool cfull;             // the tile's columns all lie inside N
 
-  __device__ void init(const bf16_t* base, int64_t ld, int c0, int N_, int KR_) {
+  // k-row (0..63) and tile column of this lane's 16-byte unit in instruction i
+  __device__ static int krow(int i) {
+    return ((threadIdx.x >> 6) + NWAVE * i) * RPI + (threadIdx.x & 63) / UPR;
+  }
+  __device__ static int ucol(int i) {
+    const int p = (threadIdx.x & 63) % UPR;
+    return ((((p >> 1) ^ km_swz(krow(i))) << 1) | (p & 1)) * 8;
+  }
+  __device__ void init(const bf16_t* base, int64_t ld, int c0_, int N_, int KR_) {
+    c0 = c0_;
     KR = KR_;
     N = N_;
-    cfull = c0 + COLS <= N_;
+    cfull = c0_ + COLS <= N_;
     step = (int64_t)BK * ld;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int p = lane % UPR;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int q = w + NWAVE * i;
-      const int kr = q * RPI + lane / UPR;
-      const int u = (((p >> 1) ^ km_swz(kr)) << 1) | (p & 1);
-      krow[i] = kr;
-      col[i] = c0 + u * 8;
-      ptr[i] = base + (int64_t)kr * ld + col[i];
-    }
+    for (int i = 0; i < NI; ++i) ptr[i] = base + (int64_t)krow(i) * ld + c0_ + ucol(i);
   }
   __device__ bool full(int kt) const { return cfull && (kt + 1) * BK <= KR; }
   template <int I0, int I1>
@@ -180,7 +181,7 @@ struct OpKM {
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
-      if (!full_step && (kt * BK + krow[i] >= KR || col[i] >= N)) g = g_zero_page;
+      if (!full_step && (kt * BK + krow(i) >= KR || c0 + ucol(i) >= N)) g = g_zero_page;
       dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
@@ -325,10 +326,6 @@ __device__ __forceinline__ int xcd_tile(int bid, int real) {
 template <int COLS>
 constexpr int ep_stride() { return COLS * 2 + 16; }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-}
-
 // Swaps a value with the neighbouring lane (lane ^ 1) through DPP.
 __device__ __forceinline__ float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -351,8 +348,8 @@ __device__ __forceinline__ void stage_pairs(lds_t* t, int row0, int col0, V v) {
       for (int r = 0; r < 16; r += 2) {
         const float a0 = v(i, j, r), a1 = v(i, j, r + 1);
         const float recv = swap_adjacent(odd ? a0 : a1);
-        const uint32_t packed = odd ? pack_bf16x2(recv, a1) : pack_bf16x2(a0, recv);
-        const int row = row0 + acc_row(i, r, lane) + (odd ? 1 : 0);
+        const uint32_t packed = pack_bf16x2(odd ? recv : a0, odd ? a1 : recv);
+        const int row = row0 + acc_row(i, r, lane) + (lane & 1);
         const int col = col0 + j * 32 + ((lane & 31) & ~1);
         *(__attribute__((address_space(3))) uint32_t*)(t + row * S + col * 2) = packed;
       }

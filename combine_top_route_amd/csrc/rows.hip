@@ -46,7 +46,7 @@ __device__ __forceinline__ uint4 pack(const float* f) {
   } else {
     uint32_t u[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = (uint32_t)f2bf(f[2 * i]) | ((uint32_t)f2bf(f[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     v.x = u[0]; v.y = u[1]; v.z = u[2]; v.w = u[3];
   }
   return v;

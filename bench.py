@@ -45,8 +45,8 @@ def kernel_work(wl):
         "gemm_down_wgrad": ("flop", 2.0 * R * d * I),
         "gemm_gateup_dgrad": ("flop", 4.0 * R * d * I),
         "gemm_gateup_wgrad": ("flop", 4.0 * R * d * I),
-        # read R rows + write T rows + row_of (+ weights)
-        "combine": ("byte", float(R * d * es + T * d * es + 8 * R)),
+        # read R rows + write T rows + row_of (the rows already carry their weight)
+        "combine": ("byte", float(R * d * es + T * d * es + 4 * R)),
         "reduce_dx": ("byte", float(R * d * es + T * d * es + 4 * R)),
         "permute": ("byte", float(T * d * es + R * d * es + 4 * R)),
         "route_topk": ("byte", float(T * E * es + 8 * R)),

@@ -120,7 +120,6 @@ struct Layout {
   size_t hist = 0, tile_off = 0, order = 0;         // routing / schedule
   size_t Y = 0, A = 0, H = 0;                        // forward
   size_t dH = 0, dXp = 0, dwp = 0, G = 0;            // backward
-  size_t Xp = 0, doutp = 0;                          // backward, bf16 path
   size_t total = 0;
 };
 
@@ -148,10 +147,6 @@ Layout layout(const moe_shape* s, int op) {
     L.dXp = take(es * R * s->d);
     L.dwp = take(sizeof(float) * R * dw_blocks(s));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
-    if (s->dtype == MOE_BF16) {
-      L.Xp = take(es * R * s->d);
-      L.doutp = take(es * R * s->d);
-    }
   }
   L.total = off;
   return L;
@@ -289,7 +284,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   else
     HIP_TRY(bf16_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
   // rows already carry their top-k weight: the combine is a plain sum
-  HIP_TRY(launch_combine(c, shape->dtype, Y, routing->row_of, nullptr, (int)shape->T,
+  HIP_TRY(launch_combine(c, "combine", shape->dtype, Y, routing->row_of, nullptr, (int)shape->T,
                          (int)shape->k, (int)shape->d, out), "combine");
   return MOE_OK;
 }
@@ -337,20 +332,12 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   if (shape->dtype == MOE_F32)
     HIP_TRY(f32_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down,
                           (float*)at(workspace, L.G)), "backward GEMMs");
-  else {
-    const int R32 = (int)R, k32 = (int)shape->k, d32 = (int)shape->d;
-    void* Xp = at(workspace, L.Xp);
-    void* doutp = at(workspace, L.doutp);
-    HIP_TRY(launch_permute(c, shape->dtype, x, routing->src_of, R32, k32, d32, Xp), "permute x");
-    HIP_TRY(launch_permute(c, shape->dtype, dout, routing->src_of, R32, k32, d32, doutp),
-            "permute dout");
-    HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, Xp, doutp, dH, dXp, dwp, dw_gate_up, dw_down),
-            "backward GEMMs");
-  }
+  else
+    HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
   HIP_TRY(launch_topk_grad(c, dwp, dw_blocks(shape), routing->row_of, routing->topk_ids,
                            routing->topk_w, (int)shape->T, (int)shape->k, (int)shape->E, d_topk_w,
                            dlogits, shape->logits_dtype), "topk_grad");
-  HIP_TRY(launch_combine(c, shape->dtype, dXp, routing->row_of, nullptr, (int)shape->T,
+  HIP_TRY(launch_combine(c, "reduce_dx", shape->dtype, dXp, routing->row_of, nullptr, (int)shape->T,
                          (int)shape->k, (int)shape->d, dx), "reduce_dx");
   return MOE_OK;
 }
@@ -383,7 +370,7 @@ moe_status moe_combine(const moe_shape* shape, const void* rows, const moe_routi
   TRY(check_aligned16(out, "out"));
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
-  HIP_TRY(launch_combine(c, shape->dtype, rows, routing->row_of, routing->topk_w, (int)shape->T,
+  HIP_TRY(launch_combine(c, "combine_weighted", shape->dtype, rows, routing->row_of, routing->topk_w, (int)shape->T,
                          (int)shape->k, (int)shape->d, out), "combine");
   return MOE_OK;
 }

@@ -83,8 +83,8 @@ hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, in
 hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
                           int R, int k, int d, void* xp);
 // out[t] = sum_j (w ? w[t*k+j] : 1) * rows[row_of[t*k+j]]
-hipError_t launch_combine(const LaunchCtx& c, int dtype, const void* rows, const int32_t* row_of,
-                          const float* w, int T, int k, int d, void* out);
+hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const void* rows,
+                          const int32_t* row_of, const float* w, int T, int k, int d, void* out);
 // d_topk_w[t,j] = sum_b dwp[row_of[t*k+j]*nblk + b]; dlogits (optional).
 hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, const int32_t* row_of,
                             const int32_t* ids, const float* w, int T, int k, int E,
@@ -110,11 +110,10 @@ struct LayerArgs {
 // Aw W_down^T, so the combine is a plain sum of each token's k rows.
 // bf16 MFMA path.
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
-// backward: Xp [R,d] and doutp [R,d] are x and dout gathered into row order;
-// outputs dH [R,2I], dXp [R,d], dwp [R, bf16_dw_blocks(I)] fp32, dW_gu, dW_d.
+// backward outputs dH [R,2I], dXp [R,d], dwp [R, bf16_dw_blocks(I)] fp32, dW_gu, dW_d.
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
-                          const void* H, const void* Aw, const void* Xp, const void* doutp,
-                          void* dH, void* dXp, float* dwp, void* dW_gu, void* dW_d);
+                          const void* H, const void* Aw, void* dH, void* dXp, float* dwp,
+                          void* dW_gu, void* dW_d);
 
 // Number of per-row partials of <G, a> that the down dgrad writes (dwp [R, n]).
 int bf16_dw_blocks(int I);

@@ -205,6 +205,66 @@ struct OpKM {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Column-contiguous operand whose k-rows are rows of an expert's segment:
+// element (col, k) = base[row(seg0 + k) * ld + col] for k < KR, with
+// row(r) = src_of[r] / kdiv (a token of x or dout) or r itself (src_of null).
+// The row indices of the next stage to issue are loaded one K step ahead.
+// ---------------------------------------------------------------------------
+template <int COLS>
+struct OpKMg {
+  static constexpr int RB = COLS * 2;
+  static constexpr int UPR = RB / 16;
+  static constexpr int RPI = 1024 / RB;
+  static constexpr int NI = BK / RPI / NWAVE;
+  static constexpr int BYTES = COLS * BK * 2;
+  const bf16_t* base;
+  int64_t ld;
+  const int32_t* src_of;
+  int kdiv, seg0, c0, KR, N;
+  int nkt;       // stage whose rows are in nrow[]
+  int nrow[NI];  // row of this lane's k-row in instruction i for stage nkt (-1: outside)
+  bool cfull;
+
+  __device__ static int krow(int i) {
+    return ((threadIdx.x >> 6) + NWAVE * i) * RPI + (threadIdx.x & 63) / UPR;
+  }
+  __device__ static int ucol(int i) {
+    const int p = (threadIdx.x & 63) % UPR;
+    return ((((p >> 1) ^ km_swz(krow(i))) << 1) | (p & 1)) * 8;
+  }
+  __device__ void fetch_rows(int kt) {
+    nkt = kt;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = kt * BK + krow(i);
+      nrow[i] = k < KR ? (src_of ? src_of[seg0 + k] / kdiv : seg0 + k) : -1;
+    }
+  }
+  __device__ void init(const bf16_t* base_, int64_t ld_, const int32_t* src_of_, int kdiv_, int seg0_,
+                       int c0_, int N_, int KR_) {
+    base = base_; ld = ld_; src_of = src_of_; kdiv = kdiv_; seg0 = seg0_;
+    c0 = c0_; N = N_; KR = KR_;
+    cfull = c0_ + COLS <= N_;
+    fetch_rows(0);
+  }
+  __device__ bool full(int kt) const { return cfull && (kt + 1) * BK <= KR; }
+  template <int I0, int I1>
+  __device__ void issue(int, lds_t* s, bool full_step) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+      const int c = c0 + ucol(i);
+      const bool ok = nrow[i] >= 0 && (full_step || c < N);
+      const void* g = ok ? (const void*)(base + (int64_t)nrow[i] * ld + c) : (const void*)g_zero_page;
+      dma16(g, s + (w + NWAVE * i) * 1024);
+    }
+  }
+  // the stage just issued is done with nrow[]: fetch the rows of the next one
+  __device__ void advance() { fetch_rows(nkt + 1); }
+  __device__ static bf16x8_t frag(const lds_t* s, int cb, int kk) { return OpKM<COLS>::frag(s, cb, kk); }
+};
+
 // Issues part P (of 4) of a stage's direct loads of operand O.
 template <int P, class O>
 __device__ __forceinline__ void issue_part(const O& o, int kt, lds_t* s, bool full_step) {
@@ -579,30 +639,40 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
 // rows in expert order (contiguous per expert).
 // ===========================================================================
 struct WgradArgs {
+  // A(m, r) = A[arow(r) * lda + m], arow(r) = a_src ? a_src[r] / kdiv : r
   const bf16_t* A;
   int64_t lda;
+  const int32_t* a_src;
+  // B(n, r) = B[brow(r) * ldb + n], brow(r) = b_src ? b_src[r] / kdiv : r
   const bf16_t* B;
   int64_t ldb;
-  int M, N, m_tiles, n_tiles;
+  const int32_t* b_src;
+  int kdiv;
+  int M, N, m_tiles, n_tiles, E;
   const int32_t* offsets;
   const int32_t* order;
   bf16_t* C;  // dW[e] = C + e * c_estride, row-major [M, N]
   int64_t c_estride;
 };
 
+// Experts, largest first, are dealt round-robin to the 8 XCDs (work-groups
+// go to XCD bid % 8); all tiles of an expert run on one XCD, so its rows are
+// fetched into one L2.
 __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
-  const int oi = blockIdx.x / per;
-  const int rem = blockIdx.x % per;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int oi = (idx / per) * 8 + xcd;
+  if (oi >= p.E) return;
+  const int rem = idx % per;
   const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
   const int e = p.order[oi];
   const int seg0 = p.offsets[e];
   const int len = p.offsets[e + 1] - seg0;
-  OpKM<TBM> oa;
-  OpKM<TBN> ob;
-  oa.init(p.A + (int64_t)seg0 * p.lda, p.lda, mt * TBM, p.M, len);
-  ob.init(p.B + (int64_t)seg0 * p.ldb, p.ldb, nt * TBN, p.N, len);
+  OpKMg<TBM> oa;
+  OpKMg<TBN> ob;
+  oa.init(p.A, p.lda, p.a_src, p.kdiv, seg0, mt * TBM, p.M, len);
+  ob.init(p.B, p.ldb, p.b_src, p.kdiv, seg0, nt * TBN, p.N, len);
   f32x16_t acc[TM][TN];
   mainloop(oa, ob, (int)cdiv(len, BK), smem, acc);
   barrier_lds();
@@ -652,7 +722,8 @@ hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(c, name, wgrad_kernel, dim3((unsigned)(E * p.m_tiles * p.n_tiles)), dim3(NTHR), kSmem, p);
+  const unsigned nblocks = (unsigned)(cdiv(E, 8) * 8 * p.m_tiles * p.n_tiles);
+  MOE_LAUNCH(c, name, wgrad_kernel, dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
@@ -684,8 +755,8 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
 }
 
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
-                          const void* H, const void* Aw, const void* Xp, const void* doutp,
-                          void* dH, void* dXp, float* dwp, void* dW_gu, void* dW_d) {
+                          const void* H, const void* Aw, void* dH, void* dXp, float* dwp,
+                          void* dW_gu, void* dW_d) {
   const int64_t I = a.I, d = a.d;
   hipError_t err;
   {  // down dgrad: G = dout_t W_down[e]; epilogue: dw partials, SwiGLU backward -> dH
@@ -701,8 +772,8 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
   }
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
     WgradArgs p = {};
-    p.A = (const bf16_t*)doutp; p.lda = d;
-    p.B = (const bf16_t*)Aw; p.ldb = I;
+    p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.kdiv = a.k;
+    p.B = (const bf16_t*)Aw; p.ldb = I; p.b_src = nullptr; p.E = a.E;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
@@ -721,8 +792,8 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
     WgradArgs p = {};
-    p.A = (const bf16_t*)dH; p.lda = 2 * I;
-    p.B = (const bf16_t*)Xp; p.ldb = d;
+    p.A = (const bf16_t*)dH; p.lda = 2 * I; p.a_src = nullptr; p.kdiv = a.k;
+    p.B = (const bf16_t*)a.x; p.ldb = d; p.b_src = a.src_of; p.E = a.E;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;

@@ -88,6 +88,65 @@ __global__ __launch_bounds__(256) void topk_kernel(const LT* __restrict__ logits
   }
 }
 
+// One lane per token: the lane walks its token's logits once and keeps the
+// KMAX largest keys in a register list sorted descending (branch-free
+// bubble insert), so no cross-lane reduction is needed.  Used for k <= KMAX.
+template <typename LT, int KMAX>
+__global__ __launch_bounds__(256) void topk_lane_kernel(const LT* __restrict__ logits, int T, int E,
+                                                        int k, int32_t* __restrict__ ids,
+                                                        float* __restrict__ w) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  uint64_t top[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) top[j] = 0;
+  auto push = [&](float v, int e) {
+    uint64_t x = ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const uint64_t hi = top[j] > x ? top[j] : x;
+      x = top[j] > x ? x : top[j];
+      top[j] = hi;
+    }
+  };
+  const LT* row = logits + (int64_t)t * E;
+  constexpr int VEC = 16 / sizeof(LT);
+  if (E % VEC == 0 && ((uintptr_t)logits & 15) == 0) {
+    for (int e0 = 0; e0 < E; e0 += VEC) {
+      const uint4 v = *(const uint4*)(row + e0);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (sizeof(LT) == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) push(__uint_as_float(u[q]), e0 + q);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          push(__uint_as_float(u[q] << 16), e0 + 2 * q);
+          push(__uint_as_float(u[q] & 0xffff0000u), e0 + 2 * q + 1);
+        }
+      }
+    }
+  } else {
+    for (int e = 0; e < E; ++e) push(to_f32<LT>(row[e]), e);
+  }
+  // softmax over the k selected logits (float32), summed in slot order
+  const float top0 = unordered_bits((uint32_t)(top[0] >> 32));
+  float ex[KMAX];
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ex[j] = j < k ? expf(unordered_bits((uint32_t)(top[j] >> 32)) - top0) : 0.0f;
+    s += ex[j];
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      ids[(int64_t)t * k + j] = (int32_t)(~(uint32_t)(top[j] & 0xffffffffu));
+      w[(int64_t)t * k + j] = ex[j] / s;
+    }
+  }
+}
+
 // Same selection for k > 64 (one lane per slot no longer fits a wave): the
 // winners' logits and ids go through shared memory.
 template <typename LT>
@@ -275,7 +334,24 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 
 hipError_t launch_topk(const LaunchCtx& c, const void* logits, int logits_dtype, int T, int E,
                        int k, int32_t* ids, float* w) {
-  if (k <= kWave) {
+  if (k <= 16) {
+    dim3 grid((T + 255) / 256);
+    if (k <= 8) {
+      if (logits_dtype == F32)
+        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<float, 8>), grid, dim3(256), 0,
+                   (const float*)logits, T, E, k, ids, w);
+      else
+        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<bf16_t, 8>), grid, dim3(256), 0,
+                   (const bf16_t*)logits, T, E, k, ids, w);
+    } else {
+      if (logits_dtype == F32)
+        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<float, 16>), grid, dim3(256), 0,
+                   (const float*)logits, T, E, k, ids, w);
+      else
+        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<bf16_t, 16>), grid, dim3(256), 0,
+                   (const bf16_t*)logits, T, E, k, ids, w);
+    }
+  } else if (k <= kWave) {
     dim3 grid((T + 3) / 4);
     if (logits_dtype == F32)
       MOE_LAUNCH(c, "route_topk", topk_kernel<float>, grid, dim3(256), 0, (const float*)logits, T,

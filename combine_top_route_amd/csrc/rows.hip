@@ -109,6 +109,61 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   }
 }
 
+// Same sum with CPL 16-byte chunks per lane known at compile time (row width
+// 64 * CPL chunks): every lane issues the loads of four rows x CPL chunks
+// before accumulating, so more of each token's rows are in flight.
+template <typename T, int CPL>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const uint4* __restrict__ rows,
+                                                           const int32_t* __restrict__ row_of,
+                                                           const float* __restrict__ w, int Tn, int k,
+                                                           uint4* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  constexpr int RV = 64 * CPL;  // 16-byte chunks per row
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* ro = row_of + (int64_t)t * k;
+  float acc[CPL][N];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[c][i] = 0.0f;
+  int j = 0;
+  for (; j + 4 <= k; j += 4) {
+    uint4 v[4][CPL];
+    float s[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4* src = rows + (int64_t)ro[j + q] * RV + lane;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[q][c] = src[c * 64];
+      s[q] = w ? w[(int64_t)t * k + j + q] : 1.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float f[N];
+        unpack<T>(v[q][c], f);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[c][i] += s[q] * f[i];
+      }
+  }
+  for (; j < k; ++j) {
+    const uint4* src = rows + (int64_t)ro[j] * RV + lane;
+    const float sj = w ? w[(int64_t)t * k + j] : 1.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float f[N];
+      unpack<T>(src[c * 64], f);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[c][i] += sj * f[i];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) out[(int64_t)t * RV + c * 64 + lane] = pack<T>(acc[c]);
+}
+
 // d_topk_w[t,j] = sum over the partial dot products of row row_of[t*k+j]
 // (fixed order); dlogits[t,e] = w_e (dw_e - sum_j w_j dw_j) on the selected
 // experts, 0 elsewhere.  One wave per token.
@@ -161,10 +216,20 @@ hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const in
   return hipSuccess;
 }
 
-hipError_t launch_combine(const LaunchCtx& c, int dtype, const void* rows, const int32_t* row_of,
-                          const float* w, int T, int k, int d, void* out) {
+hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const void* rows,
+                          const int32_t* row_of, const float* w, int T, int k, int d, void* out) {
   const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
-  const char* name = w ? "combine" : "reduce_dx";
+  const dim3 grid((T + 3) / 4);
+  if (dtype == BF16 && row_vecs == 256) {
+    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 4>), grid, dim3(256), 0, (const uint4*)rows,
+               row_of, w, T, k, (uint4*)out);
+    return hipSuccess;
+  }
+  if (dtype == BF16 && row_vecs == 512) {
+    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 8>), grid, dim3(256), 0, (const uint4*)rows,
+               row_of, w, T, k, (uint4*)out);
+    return hipSuccess;
+  }
   if (dtype == F32)
     MOE_LAUNCH(c, name, combine_kernel<float>, dim3((T + 3) / 4), dim3(256), 0,
                (const uint4*)rows, row_of, w, T, k, row_vecs, (uint4*)out);

@@ -45,9 +45,11 @@ What the pages fix, and the readings taken where they leave a step open:
     and 128x128 weight blocks.  Readings: scale = amax/448 in fp32 (1 where a
     block is all zero), round-to-nearest-even with saturation at +-448,
     weight-gradient GEMMs quantise both operands in 128-row blocks along the
-    token dimension aligned to each expert's first row, the down dgrad
-    quantises the unweighted upstream gradient, and the stored intermediates
-    H, A and dH are bf16.
+    token dimension aligned to each expert's first row, the top-k weight is
+    folded into the SwiGLU output before the down GEMM (Aw = w * a, which the
+    down GEMM and the down wgrad quantise), the down dgrad quantises the
+    unweighted upstream gradient, the top-k-weight gradient uses that
+    dgrad's output, and the stored intermediates H, Aw and dH are bf16.
 """
 from __future__ import annotations
 
@@ -431,29 +433,39 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
 
 
 def forward_fp8(x, rt: dict, w_gate_up, w_down) -> dict:
-    """Forward with both GEMMs on block-quantised e4m3 operands."""
+    """Forward with both GEMMs on block-quantised e4m3 operands.  The top-k
+    weight of each row is folded into the SwiGLU output before the down GEMM
+    (Aw = w * silu(g) * up, stored bf16), so the combine is a plain sum."""
     off, E = rt["offsets"], rt["E"]
     Xp = dispatch(x, rt)
     R = Xp.shape[0]
     I = w_gate_up.shape[1] // 2
     d = w_down.shape[1]
+    w_row = rt["w"].ravel()[rt["src_of"]]
     H = np.zeros((R, 2 * I))
-    A = np.zeros((R, I))
-    Y = np.zeros((R, d))
+    Aw = np.zeros((R, I))
+    Yw = np.zeros((R, d))
     for e in range(E):
         s = slice(off[e], off[e + 1])
         if off[e + 1] == off[e]:
             continue
         Hs = quant_rows_1x128(Xp[s]) @ quant_weight_128x128(w_gate_up[e]).T
-        A[s] = bf16_round(swiglu(Hs, I))
+        Aw[s] = bf16_round(w_row[s, None] * swiglu(Hs, I))
         H[s] = bf16_round(Hs)
-        Y[s] = quant_rows_1x128(A[s]) @ quant_weight_128x128(w_down[e]).T
-    return dict(out=combine(Y, rt), H=H, A=A, Y=Y, Xp=Xp)
+        Yw[s] = quant_rows_1x128(Aw[s]) @ quant_weight_128x128(w_down[e]).T
+    T, k = rt["ids"].shape
+    out = np.zeros((T, d))
+    for j in range(k):
+        out += Yw[rt["row_of"][np.arange(T) * k + j]]
+    return dict(out=out, H=H, Aw=Aw, Yw=Yw, Xp=Xp)
 
 
 def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
                  logits=None) -> dict:
-    """Backward with all four GEMMs on block-quantised e4m3 operands."""
+    """Backward with all four GEMMs on block-quantised e4m3 operands.  The
+    top-k-weight gradient is <G_r, a_r> with G_r the quantised down dgrad
+    (the backward's estimate of W_down^T dout_t) and a_r = silu(g) * up from
+    the stored H; the down wgrad quantises dout and Aw in token blocks."""
     dout = np.asarray(dout, F64)
     T, k, E = rt["ids"].shape[0], rt["k"], rt["E"]
     off, src_of, row_of = rt["offsets"], rt["src_of"], rt["row_of"]
@@ -462,8 +474,8 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
     R = src_of.size
     tok = src_of // k
     w_row = rt["w"].ravel()[src_of]
-    H, A, Xp, Y = fwd["H"], fwd["A"], fwd["Xp"], fwd["Y"]
-    d_topk_w = np.einsum("td,tjd->tj", dout, Y[row_of.reshape(T, k)])
+    H, Aw, Xp = fwd["H"], fwd["Aw"], fwd["Xp"]
+    dw_row = np.zeros(R)
     dW_down = np.zeros((E, d, I))
     dW_gate_up = np.zeros((E, 2 * I, d))
     dXp = np.zeros((R, d))
@@ -473,13 +485,14 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
             continue
         Wd_q = quant_weight_128x128(w_down[e])
         Wgu_q = quant_weight_128x128(w_gate_up[e])
-        G = quant_rows_1x128(dout[tok[s]]) @ Wd_q             # down dgrad
+        G = quant_rows_1x128(dout[tok[s]]) @ Wd_q               # down dgrad
+        dw_row[s] = np.sum(G * swiglu(H[s], I), axis=1)
         dA = w_row[s, None] * G
-        dYs = w_row[s, None] * dout[tok[s]]
-        dW_down[e] = quant_tokens_128(dYs).T @ quant_tokens_128(A[s])
+        dW_down[e] = quant_tokens_128(dout[tok[s]]).T @ quant_tokens_128(Aw[s])
         dH = bf16_round(swiglu_backward(H[s], dA, I))
-        dXp[s] = quant_rows_1x128(dH) @ Wgu_q                  # gate/up dgrad
+        dXp[s] = quant_rows_1x128(dH) @ Wgu_q                    # gate/up dgrad
         dW_gate_up[e] = quant_tokens_128(dH).T @ quant_tokens_128(Xp[s])
+    d_topk_w = dw_row[row_of].reshape(T, k)
     dx = np.zeros((T, d))
     for j in range(k):
         dx += dXp[row_of[np.arange(T) * k + j]]

@@ -381,6 +381,25 @@ def test_fp8_layer_close_to_unquantised_layer():
     f8 = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"])
     b8 = O.backward_fp8(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], f8)
     for ref, got in ((fw["out"], f8["out"]), (bw["dx"], b8["dx"]),
-                     (bw["dW_gate_up"], b8["dW_gate_up"]), (bw["dW_down"], b8["dW_down"])):
+                     (bw["dW_gate_up"], b8["dW_gate_up"]), (bw["dW_down"], b8["dW_down"]),
+                     (bw["d_topk_w"], b8["d_topk_w"])):
         err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
         assert 1e-3 < err < 0.1
+
+
+def test_fp8_gate_up_exact_on_representable_operands():
+    """x and W_gate_up already on the e4m3 grid of their blocks (each block's
+    largest magnitude 448 * 2^-s): quantisation is the identity, so the fp8
+    pre-activations equal the bf16-rounded exact product."""
+    wl = S.WORKLOADS["tiny"].scaled(d=256, I=128, T=40, E=4, k=2, dtype="bf16")
+    rng = np.random.default_rng(16)
+    x = O.e4m3_round(rng.standard_normal((wl.T, wl.d)) * 60) * 2.0 ** -4
+    x[:, 0], x[:, 128] = 448 * 2.0 ** -4, -448 * 2.0 ** -4
+    W = O.e4m3_round(rng.standard_normal((wl.E, 2 * wl.I, wl.d)) * 60) * 2.0 ** -9
+    W[:, 0::128, 0::128] = 448 * 2.0 ** -9
+    Wd = rng.standard_normal((wl.E, wl.d, wl.I)) * 0.05
+    rt = O.route(rng.standard_normal((wl.T, wl.E)), wl.k, wl.E)
+    f8 = O.forward_fp8(x, rt, W, Wd)
+    H = np.concatenate([O.dispatch(x, rt)[s0:s1] @ W[e].T for e, (s0, s1) in
+                        enumerate(zip(rt["offsets"][:-1], rt["offsets"][1:]))])
+    assert np.array_equal(f8["H"], O.bf16_round(H))

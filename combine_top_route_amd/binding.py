@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 MOE_F32, MOE_BF16 = 0, 1
 PREC_NATIVE, PREC_FP8_BLOCK = 0, 1
 OP_ROUTE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+QUANT_ROWS, QUANT_WEIGHT, QUANT_WEIGHT_T = 0, 1, 2
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
@@ -56,6 +57,10 @@ _SIGS = [
                                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("moe_permute", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.POINTER(MoeRouting), _P, _P]),
     ("moe_combine", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.POINTER(MoeRouting), _P, _P]),
+    ("moe_quantize_fp8", ctypes.c_int, [ctypes.c_int, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                        _P]),
+    ("moe_quantize_tokens_fp8", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.POINTER(MoeRouting), _P, _P, _P, ctypes.c_size_t, _P]),
     ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("moe_last_error", ctypes.c_char_p, []),
     ("moe_profile_begin", ctypes.c_int, []),
@@ -288,3 +293,44 @@ def profile_end() -> dict:
     n = ctypes.c_int()
     _check("moe_profile_end", lib().moe_profile_end(arr, cap, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n.value, cap))}
+
+
+def quantize_fp8(src, kind=QUANT_ROWS):
+    """e4m3 codes (uint8) and float32 scales of a bf16 tensor: kind
+    QUANT_ROWS for [n0, n1] (1x128 blocks), QUANT_WEIGHT / QUANT_WEIGHT_T for
+    [n0, n1, n2] (128x128 blocks, written as is or transposed)."""
+    dev = src.device
+    if src.dtype != torch.bfloat16 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 tensor")
+    if kind == QUANT_ROWS:
+        n0, n1 = src.shape
+        n2 = 0
+        q = torch.empty((n0, n1), dtype=torch.uint8, device=dev)
+        s = torch.empty((n0, n1 // 128), dtype=torch.float32, device=dev)
+    else:
+        n0, n1, n2 = src.shape
+        qs = (n0, n1, n2) if kind == QUANT_WEIGHT else (n0, n2, n1)
+        q = torch.empty(qs, dtype=torch.uint8, device=dev)
+        s = torch.empty((qs[0], qs[1] // 128, qs[2] // 128), dtype=torch.float32, device=dev)
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(kind, _ptr(src), n0, n1, n2, _ptr(q), _ptr(s),
+                                                      _stream(dev)))
+    return q, s
+
+
+def quantize_tokens_fp8(src, routing: Routing, T, k, gather):
+    """Token-block codes q [C, 128 nblk] and scales s [C, nblk] of a
+    weight-gradient operand (see moe_quantize_tokens_fp8); nblk =
+    ceil(T*k/128) + E."""
+    dev = src.device
+    C = src.shape[1]
+    E = routing.counts.numel()
+    shape = make_shape(T, C, E, k, 128, torch.bfloat16)
+    nblk = -(-T * k // 128) + E
+    q = torch.zeros((C, 128 * nblk), dtype=torch.uint8, device=dev)
+    s = torch.zeros((C, nblk), dtype=torch.float32, device=dev)
+    ws = torch.empty(workspace_size(shape, OP_ROUTE), dtype=torch.uint8, device=dev)
+    cr = routing.c()
+    _check("moe_quantize_tokens_fp8", lib().moe_quantize_tokens_fp8(
+        ctypes.byref(shape), _ptr(src), C, 1 if gather else 0, ctypes.byref(cr), _ptr(q), _ptr(s), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return q, s

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.cpp", "route.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["api.cpp", "route.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip", "gemm_fp8.hip",
+           "quant_fp8.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -102,7 +102,9 @@ moe_status check_shape(const moe_shape* s) {
   if (s->precision == MOE_PREC_FP8_BLOCK) {
     if (s->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs dtype bf16");
     if (s->d % 128 || s->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs d and I multiples of 128");
-    return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision is not built in this library");
+    const int64_t widest = s->d > 2 * s->I ? s->d : 2 * s->I;
+    if (s->T * s->k * (widest / 128) >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision: T*k*max(d,2I)/128 must stay below 2^31");
   }
   return MOE_OK;
 }
@@ -111,15 +113,23 @@ moe_status check_shape(const moe_shape* s) {
   if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", #p)
 
 size_t elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+bool is_fp8(const moe_shape* s) { return s->precision == MOE_PREC_FP8_BLOCK; }
 int dw_blocks(const moe_shape* s) {
-  return s->dtype == MOE_F32 ? f32_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
+  if (s->dtype == MOE_F32) return f32_dw_blocks((int)s->I);
+  return is_fp8(s) ? fp8_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
 }
+// upper bound of the 128-row token blocks over all experts
+int64_t nblk_max(const moe_shape* s) { return cdiv(s->T * s->k, kTokBlock) + s->E; }
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t hist = 0, tile_off = 0, order = 0;         // routing / schedule
-  size_t Y = 0, A = 0, H = 0;                        // forward
-  size_t dH = 0, dXp = 0, dwp = 0, G = 0;            // backward
+  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0;  // routing / schedule
+  size_t Y = 0, A = 0, H = 0;                             // forward
+  size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
+  // fp8: quantised operands (q) and their scales (s)
+  size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
+  size_t doutq = 0, douts = 0, wdtq = 0, wdts = 0, wgutq = 0, wguts = 0, dhq = 0, dhs = 0;
+  size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0;
   size_t total = 0;
 };
 
@@ -136,6 +146,7 @@ Layout layout(const moe_shape* s, int op) {
   const int64_t nchunks = cdiv(R, kSortChunk);
   L.tile_off = take(sizeof(int32_t) * (s->E + 1));
   L.order = take(sizeof(int32_t) * s->E);
+  L.blk_off = take(sizeof(int32_t) * (s->E + 1));
   if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
   if (op == MOE_OP_FORWARD) {
     L.Y = take(es * R * s->d);
@@ -147,6 +158,36 @@ Layout layout(const moe_shape* s, int op) {
     L.dXp = take(es * R * s->d);
     L.dwp = take(sizeof(float) * R * dw_blocks(s));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
+  }
+  if (is_fp8(s)) {
+    const int64_t T = s->T, d = s->d, I = s->I, E = s->E;
+    const size_t f = sizeof(float);
+    if (op == MOE_OP_FORWARD) {
+      L.xq = take(T * d);
+      L.xs = take(f * T * (d / 128));
+      L.wguq = take(E * 2 * I * d);
+      L.wgus = take(f * E * (2 * I / 128) * (d / 128));
+      L.wdq = take(E * d * I);
+      L.wds = take(f * E * (d / 128) * (I / 128));
+      L.awq = take(R * I);
+      L.aws = take(f * R * (I / 128));
+    }
+    if (op == MOE_OP_BACKWARD) {
+      const int64_t nb = nblk_max(s);
+      L.doutq = take(T * d);
+      L.douts = take(f * T * (d / 128));
+      L.wdtq = take(E * I * d);
+      L.wdts = take(f * E * (I / 128) * (d / 128));
+      L.wgutq = take(E * d * 2 * I);
+      L.wguts = take(f * E * (d / 128) * (2 * I / 128));
+      L.dhq = take(R * 2 * I);
+      L.dhs = take(f * R * (2 * I / 128));
+      const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;
+      L.tqa = take(ra * nb * kTokBlock);
+      L.tsa = take(f * ra * nb);
+      L.tqb = take(rb * nb * kTokBlock);
+      L.tsb = take(f * rb * nb);
+    }
   }
   L.total = off;
   return L;
@@ -272,17 +313,25 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   (void)hipGetLastError();
   TRY(run_route(shape, routing, workspace, L, c));
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order)), "route_schedule");
+                          (int32_t*)at(workspace, L.order), nullptr), "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
   const int64_t R = shape->T * shape->k;
   void* H = saved ? saved : (shape->dtype == MOE_F32 ? at(workspace, L.H) : nullptr);
   void* A = saved ? at(saved, es * R * 2 * shape->I) : at(workspace, L.A);
   void* Y = at(workspace, L.Y);
-  if (shape->dtype == MOE_F32)
+  if (shape->dtype == MOE_F32) {
     HIP_TRY(f32_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
-  else
+  } else if (is_fp8(shape)) {
+    Fp8Fwd q;
+    q.xq = (uint8_t*)at(workspace, L.xq); q.xs = (float*)at(workspace, L.xs);
+    q.wguq = (uint8_t*)at(workspace, L.wguq); q.wgus = (float*)at(workspace, L.wgus);
+    q.wdq = (uint8_t*)at(workspace, L.wdq); q.wds = (float*)at(workspace, L.wds);
+    q.awq = (uint8_t*)at(workspace, L.awq); q.aws = (float*)at(workspace, L.aws);
+    HIP_TRY(fp8_fwd_gemms(c, a, q, H, A, Y), "forward GEMMs");
+  } else {
     HIP_TRY(bf16_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
+  }
   // rows already carry their top-k weight: the combine is a plain sum
   HIP_TRY(launch_combine(c, "combine", shape->dtype, Y, routing->row_of, nullptr, (int)shape->T,
                          (int)shape->k, (int)shape->d, out), "combine");
@@ -320,7 +369,9 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order)), "route_schedule");
+                          (int32_t*)at(workspace, L.order),
+                          is_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr),
+          "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
   const int64_t R = shape->T * shape->k;
@@ -332,7 +383,18 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   if (shape->dtype == MOE_F32)
     HIP_TRY(f32_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down,
                           (float*)at(workspace, L.G)), "backward GEMMs");
-  else
+  else if (is_fp8(shape)) {
+    Fp8Bwd q;
+    q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = (float*)at(workspace, L.douts);
+    q.wdtq = (uint8_t*)at(workspace, L.wdtq); q.wdts = (float*)at(workspace, L.wdts);
+    q.wgutq = (uint8_t*)at(workspace, L.wgutq); q.wguts = (float*)at(workspace, L.wguts);
+    q.dhq = (uint8_t*)at(workspace, L.dhq); q.dhs = (float*)at(workspace, L.dhs);
+    q.tqa = (uint8_t*)at(workspace, L.tqa); q.tsa = (float*)at(workspace, L.tsa);
+    q.tqb = (uint8_t*)at(workspace, L.tqb); q.tsb = (float*)at(workspace, L.tsb);
+    q.blk_off = (const int32_t*)at(workspace, L.blk_off);
+    q.nblk_max = (int)nblk_max(shape);
+    HIP_TRY(fp8_bwd_gemms(c, a, q, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
+  } else
     HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
   HIP_TRY(launch_topk_grad(c, dwp, dw_blocks(shape), routing->row_of, routing->topk_ids,
                            routing->topk_w, (int)shape->T, (int)shape->k, (int)shape->E, d_topk_w,
@@ -372,6 +434,65 @@ moe_status moe_combine(const moe_shape* shape, const void* rows, const moe_routi
   (void)hipGetLastError();
   HIP_TRY(launch_combine(c, "combine_weighted", shape->dtype, rows, routing->row_of, routing->topk_w, (int)shape->T,
                          (int)shape->k, (int)shape->d, out), "combine");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                            uint8_t* q, float* s, void* stream) {
+  CHECK_PTR(src);
+  CHECK_PTR(q);
+  CHECK_PTR(s);
+  if (kind != MOE_QUANT_ROWS && kind != MOE_QUANT_WEIGHT && kind != MOE_QUANT_WEIGHT_T)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "kind=%d unknown", kind);
+  if (n0 < 1 || n1 < 1 || (kind != MOE_QUANT_ROWS && n2 < 1))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "extents must be positive");
+  if (kind == MOE_QUANT_ROWS) {
+    if (n1 % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "n1=%lld must be a multiple of 128", (long long)n1);
+    if (n0 > (int64_t(1) << 31) / (n1 / 128)) return fail(MOE_ERR_INVALID_ARGUMENT, "too many blocks");
+  } else {
+    if (n1 % 128 || n2 % 128)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "n1=%lld and n2=%lld must be multiples of 128", (long long)n1,
+                  (long long)n2);
+    if (n0 > 65535 || n1 > 65535 * 128 || n2 > 65535 * 128)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "weight extents too large");
+  }
+  TRY(check_aligned16(src, "src"));
+  TRY(check_aligned16(q, "q"));
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  if (kind == MOE_QUANT_ROWS)
+    HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s), "quant_rows");
+  else
+    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2,
+                                kind == MOE_QUANT_WEIGHT_T, q, s), "quant_weight");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int64_t C, int gather,
+                                   const moe_routing* routing, uint8_t* q, float* s, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  TRY(check_shape(shape));
+  CHECK_PTR(src);
+  CHECK_PTR(q);
+  CHECK_PTR(s);
+  CHECK_PTR(routing);
+  CHECK_PTR(routing->offsets);
+  if (gather) CHECK_PTR(routing->src_of);
+  if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "token-block quantisation reads bf16");
+  if (C < 128 || C > 65535 * 64 || C % 128)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "C=%lld must be a positive multiple of 128", (long long)C);
+  TRY(check_ws(shape, MOE_OP_ROUTE, workspace, workspace_bytes));
+  TRY(check_aligned16(src, "src"));
+  TRY(check_aligned16(q, "q"));
+  const Layout L = layout(shape, MOE_OP_ROUTE);
+  const LaunchCtx c = make_ctx(stream);
+  (void)hipGetLastError();
+  int32_t* blk_off = (int32_t*)at(workspace, L.blk_off);
+  HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
+                          (int32_t*)at(workspace, L.order), blk_off), "route_schedule");
+  HIP_TRY(launch_quant_tok(c, "quant_tokens", src, C, gather ? routing->src_of : nullptr,
+                           (int)shape->k, (int)C, routing->offsets, blk_off, (int)shape->E,
+                           (int)nblk_max(shape), q, s), "quant_tokens");
   return MOE_OK;
 }
 

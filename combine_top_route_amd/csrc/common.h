@@ -62,6 +62,12 @@ struct LaunchCtx {
     if (_e != hipSuccess) return _e;                                               \
   } while (0)
 
+#define HIP_RET(x)                          \
+  do {                                      \
+    hipError_t _r = (x);                    \
+    if (_r != hipSuccess) return _r;        \
+  } while (0)
+
 // ---------------------------------------------------------------- routing
 // Tile table sizes: row tiles of the grouped GEMMs (expert-aligned).
 constexpr int kRowTile = 256;
@@ -75,9 +81,12 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
                        int32_t* hist, int32_t* counts, int32_t* offsets, int32_t* row_of,
                        int32_t* src_of);
 // GEMM schedule from offsets: tile_off [E+1] (row tiles of kRowTile per expert,
-// prefix-summed) and order [E] (experts by descending row count, ties by id).
+// prefix-summed), order [E] (experts by descending row count, ties by id) and,
+// when blk_off is not null, blk_off [E+1] (runs of kTokBlock rows per expert,
+// prefix-summed: the token blocks of the fp8 weight-gradient operands).
+constexpr int kTokBlock = 128;
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order);
+                           int32_t* order, int32_t* blk_off);
 
 // ---------------------------------------------------------------- row passes
 hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
@@ -125,5 +134,47 @@ hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* 
 hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
                          const void* H, const void* Aw, void* dH, void* dXp, float* dwp,
                          void* dW_gu, void* dW_d, float* G);
+
+// ---------------------------------------------------------------- fp8 path
+// Block quantisation to e4m3 (quant_fp8.hip).  rows: 1 x 128 blocks along the
+// rows of src [rows, C]; weight: 128 x 128 blocks of W [E, N, K], written as
+// [E, N, K] or transposed [E, K, N] (scales [E, N/128, K/128] or transposed);
+// tok: 128-row runs of each expert's segment x 1 column, written transposed
+// q [C, 128 nblk_max], s [C, nblk_max].
+hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
+                             int64_t rows, int C, uint8_t* q, float* s);
+hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
+                               int K, bool transpose, uint8_t* q, float* s);
+hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
+                            const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
+                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, float* s);
+
+// Workspace of the fp8 forward: quantised x, weights and Aw with their scales.
+struct Fp8Fwd {
+  uint8_t* xq; float* xs;      // [T,d], [T,d/128]
+  uint8_t* wguq; float* wgus;  // [E,2I,d], [E,2I/128,d/128]
+  uint8_t* wdq; float* wds;    // [E,d,I], [E,d/128,I/128]
+  uint8_t* awq; float* aws;    // [R,I], [R,I/128]
+};
+// Workspace of the fp8 backward.  tqa/tsa and tqb/tsb hold the two
+// token-blocked operands of one weight gradient at a time
+// ([max(d,2I)] and [max(I,d)] rows of 128 nblk_max bytes).
+struct Fp8Bwd {
+  uint8_t* doutq; float* douts;  // [T,d], [T,d/128]
+  uint8_t* wdtq; float* wdts;    // [E,I,d], [E,I/128,d/128]
+  uint8_t* wgutq; float* wguts;  // [E,d,2I], [E,d/128,2I/128]
+  uint8_t* dhq; float* dhs;      // [R,2I], [R,2I/128]
+  uint8_t* tqa; float* tsa;
+  uint8_t* tqb; float* tsb;
+  const int32_t* blk_off;        // [E+1]
+  int nblk_max;
+};
+int fp8_dw_blocks(int I);
+// Same outputs as the bf16 path; H and Aw are stored in bf16.
+hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q, void* H, void* Aw,
+                         void* Yw);
+hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
+                         const void* H, const void* Aw, void* dH, void* dXp, float* dwp, void* dW_gu,
+                         void* dW_d);
 
 }  // namespace moe

@@ -30,9 +30,11 @@
 // layouts are XOR-swizzled so the reads of one instruction hit distinct
 // banks.
 #include "common.h"
+#include "tile.h"
 
 namespace moe {
 namespace {
+using namespace tile;
 
 constexpr int BK = 64;
 constexpr int NSTAGE = 2;
@@ -352,31 +354,6 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
 // column is (lane & 31) + 32 * j.
 __device__ __forceinline__ int acc_row(int i, int r, int lane) {
   return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
-// Largest e with tile_off[e] <= mt (empty experts share their successor's offset).
-__device__ __forceinline__ int find_expert(const int32_t* tile_off, int E, int mt) {
-  int lo = 0, hi = E;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_off[mid] <= mt) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Work-group id -> logical tile id.  Work-groups are dealt to the 8 XCDs
-// round-robin; XCD x takes the x-th contiguous eighth of the `real` tiles, so
-// each XCD walks consecutive tiles of the same expert (its row tiles share
-// weight tiles, its N tiles share token rows, all through that XCD's L2) and
-// the eight XCDs get equal tile counts whatever the routing.  Returns -1 for
-// a work-group with nothing to do.
-__device__ __forceinline__ int xcd_tile(int bid, int real) {
-  const int per = (real + 7) >> 3;
-  const int idx = bid >> 3;
-  if (idx >= per) return -1;
-  const int L = (bid & 7) * per + idx;
-  return L < real ? L : -1;
 }
 
 // ---------------------------------------------------------------------------

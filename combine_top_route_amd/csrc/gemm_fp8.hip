@@ -1,0 +1,641 @@
+// Grouped GEMMs of the expert MLPs on block-scaled fp8 operands (OCP e4m3,
+// fp32 scales; "Prime Intellect's Prime Mega MoE Trains Giant AI Models 55%
+// Faster", section "Precision and hardware support": blockwise FP8 with a
+// scale shared by each block) on gfx950 MFMA with fp32 accumulation.
+//
+// Every operand arrives quantised and contiguous along K (see
+// quant_fp8.hip), K is a multiple of 128, and one K step of 128 is exactly one
+// scale block.  Per step each 16x16 output tile is one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block exponents into a fresh
+// partial sum P, which is promoted into the fp32 accumulator with the product
+// of the two operands' scales: acc += P * (s_row * s_col).
+//
+// Tile engine: 256 (token rows) x 256 (features) per work-group, eight waves
+// of 128 x 64, 128 bytes of K per stage for both operands (the same 64 KB
+// per stage as the bf16 engine, for twice the MFMA work).  Operands and their
+// per-row scales move global -> LDS with direct loads into a two-stage ring.
+// The MFMA's A operand is the feature side and its B operand the token side,
+// so a lane's four results share one token row and one scale of each side:
+// the promotion costs one multiply-add per result.
+#include "common.h"
+#include "tile.h"
+
+namespace moe {
+namespace {
+using namespace tile;
+
+constexpr int KB = 128;                // K per stage (bytes = e4m3 elements)
+constexpr int NWAVE = 8;
+constexpr int NTHR = NWAVE * 64;
+constexpr int WM = 2, WN = 4;          // wave grid: token halves x feature quarters
+constexpr int TBM = 256, TBN = 256;    // tokens x features per work-group
+constexpr int TM = TBM / WM / 16;      // 16-row MFMA tiles per wave along tokens (8)
+constexpr int TN = TBN / WN / 16;      // along features (4)
+constexpr int OPB = TBM * KB;          // bytes of one operand per stage
+constexpr int SCB = 256 * 4;           // bytes of one side's scales per stage
+constexpr int STB = 2 * OPB + 2 * SCB; // stage: token op | feature op | token scales | feature scales
+static_assert(TBM == kRowTile, "tile table is built for 256-row tiles");
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// LDS operand layout: [row][128 bytes], 16-byte chunk c of row r stored at
+// position c ^ swz8(r).  The swizzle depends on row bits 1..3 only, so the 16
+// rows of an MFMA fragment (16-aligned) read at one chunk cover all 16 slots
+// of a 256-byte bank window, and a lane's address for any 16-aligned row base
+// is its own offset plus a constant.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// ---------------------------------------------------------------------------
+// One operand: 256 rows x 128 bytes per stage.  Instruction q covers rows
+// 8q..8q+7 (1 KB); wave w issues q = w + 8i, i < 4.
+// ---------------------------------------------------------------------------
+struct Op8 {
+  const uint8_t* ptr[4];  // this lane's 16-byte chunk at the current stage
+
+  __device__ static int koff(int i) {
+    const int lane = threadIdx.x & 63;
+    const int row = 8 * ((threadIdx.x >> 6) + NWAVE * i) + (lane >> 3);
+    return ((lane & 7) ^ swz8(row)) << 4;
+  }
+  // rowp(row) -> first byte of the row's K range
+  template <class F>
+  __device__ void init(F rowp) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ptr[i] = rowp(8 * (w + NWAVE * i) + (lane >> 3)) + koff(i);
+  }
+  template <int I0, int I1>
+  __device__ void issue(lds_t* s) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int i = I0; i < I1; ++i) dma16(ptr[i], s + (w + NWAVE * i) * 1024);
+  }
+  __device__ void advance() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ptr[i] += KB;
+  }
+};
+
+// MFMA operand of 16 rows: lane holds row lane % 16 of the fragment, bytes
+// 32 (lane / 16) .. +31 of the stage's K range (chunks 2 (lane/16) and +1).
+struct FragOff {
+  int lo, hi;  // byte offsets of this lane's two chunks from the fragment's first row
+  __device__ FragOff() {
+    const int lane = threadIdx.x & 63, r = lane & 15, c = 2 * (lane >> 4);
+    lo = r * KB + ((c ^ swz8(r)) << 4);
+    hi = r * KB + (((c + 1) ^ swz8(r)) << 4);
+  }
+};
+__device__ __forceinline__ i32x8_t frag8(const lds_t* s, const FragOff& o) {
+  const u32x4_t lo = *(const __attribute__((address_space(3))) u32x4_t*)(s + o.lo);
+  const u32x4_t hi = *(const __attribute__((address_space(3))) u32x4_t*)(s + o.hi);
+  const i32x8_t r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  return r;
+}
+
+__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
+__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
+
+// Scales: waves 0-3 load the token rows' scales (rows 64w .. 64w+63), waves
+// 4-7 the feature rows' (rows 64(w-4) ..); sp is the lane's source at the
+// current stage, advanced by one float per K step.
+
+// Issues the next stage's loads of both operands spread over the sub-steps:
+// sub-step i < 8 issues token-operand instruction i / 2 (even i) or
+// feature-operand instruction i / 2 (odd i); sub-step 0 adds the scales.
+template <int I>
+__device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const float* sp, lds_t* dst) {
+  constexpr int q = I / 2;
+  if constexpr (I % 2 == 0) ot.issue<q, q + 1>(dst);
+  else of.issue<q, q + 1>(dst + OPB);
+  if constexpr (I == 0) dma4(sp, dst + 2 * OPB + 256 * wave_id());
+}
+
+// ---------------------------------------------------------------------------
+// Main loop over nkb K steps.  ROW_SCALE_F: the feature side has a scale per
+// row (token-blocked operands) rather than per 128 rows (weights), so each of
+// a lane's four results takes its own feature scale.
+// acc[i][j][r]: token wave_m*128 + 16 i + lane % 16, feature
+// wave_n*64 + 16 j + 4 (lane / 16) + r.
+// ---------------------------------------------------------------------------
+template <bool ROW_SCALE_F, bool PRE, int I>
+__device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const float* sp, lds_t* dst,
+                                        const i32x8_t (&f)[TN], const i32x8_t& t,
+                                        const lds_f32_t* SAw, float& sa, const f32x4_t (&sb)[TN],
+                                        f32x4_t (&acc)[TM][TN]) {
+  if constexpr (PRE) issue_step<I>(ot, of, sp, dst);
+  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const f32x4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, zero, 0, 0, 0, 127, 0, 127);
+    if constexpr (ROW_SCALE_F) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r] * sb[j][r], sa, acc[I][j][r]);
+    } else {
+      const float s = sa * sb[j][0];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r], s, acc[I][j][r]);
+    }
+  }
+  if constexpr (I + 1 < TM) sa = SAw[(I + 1) * 16];  // token scale of the next sub-step
+  // keep the scheduler from hoisting later sub-steps' fragment reads and
+  // MFMAs: each would hold its own registers live
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K step on the stage in `cur`; PRE: also load the next stage into `dst`
+// (a branch-free body, so the sub-step boundaries hold).
+template <bool ROW_SCALE_F, bool PRE>
+__device__ __forceinline__ void kstep(Op8& ot, Op8& of, const float*& sp, const lds_t* cur,
+                                      lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
+  const int wm = wave_m(), wn = wave_n();
+  const int lane = threadIdx.x & 63;
+  wait_vmcnt<0>();
+  barrier_lds();
+  const lds_f32_t* SA = (const lds_f32_t*)(cur + 2 * OPB);
+  const lds_f32_t* SB = (const lds_f32_t*)(cur + 2 * OPB + SCB);
+  const lds_f32_t* SAw = SA + wm * 128 + (lane & 15);
+  float sa = SAw[0];
+  f32x4_t sb[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int fr = wn * 64 + j * 16 + 4 * (lane >> 4);
+    if constexpr (ROW_SCALE_F) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
+    else sb[j][0] = SB[fr];
+  }
+  const lds_t* tb = cur + wm * 128 * KB;       // this wave's token rows
+  const lds_t* fb = cur + OPB + wn * 64 * KB;  // this wave's feature rows
+  i32x8_t f[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
+  i32x8_t t0 = frag8(tb, fo);
+  i32x8_t t1 = frag8(tb + 16 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 0>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  t0 = frag8(tb + 32 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 1>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  t1 = frag8(tb + 48 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 2>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  t0 = frag8(tb + 64 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 3>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  t1 = frag8(tb + 80 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 4>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  t0 = frag8(tb + 96 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 5>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  t1 = frag8(tb + 112 * KB, fo);
+  substep<ROW_SCALE_F, PRE, 6>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  substep<ROW_SCALE_F, PRE, 7>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  if constexpr (PRE) {
+    ot.advance();
+    of.advance();
+    sp += 1;
+  }
+}
+
+template <bool ROW_SCALE_F>
+__device__ __forceinline__ void mainloop8(Op8& ot, Op8& of, const float* sp, int nkb, char* smem,
+                                          f32x4_t (&acc)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (nkb <= 0) return;
+  lds_t* const base = (lds_t*)smem;
+  const FragOff fo;
+  issue_step<0>(ot, of, sp, base); issue_step<1>(ot, of, sp, base); issue_step<2>(ot, of, sp, base);
+  issue_step<3>(ot, of, sp, base); issue_step<4>(ot, of, sp, base); issue_step<5>(ot, of, sp, base);
+  issue_step<6>(ot, of, sp, base); issue_step<7>(ot, of, sp, base);
+  ot.advance();
+  of.advance();
+  sp += 1;
+  int slot = 0;
+  for (int kb = 0; kb + 1 < nkb; ++kb) {
+    kstep<ROW_SCALE_F, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+    slot ^= 1;
+  }
+  kstep<ROW_SCALE_F, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue staging: a lane's four results of tile (i, j) are four
+// consecutive features of one token row: one 8-byte LDS write as bf16.
+// ---------------------------------------------------------------------------
+template <int COLS>
+constexpr int ep_stride() { return COLS * 2 + 32; }
+
+template <int NI, int NJ, int S, class V>
+__device__ __forceinline__ void stage4(lds_t* t, int row0, int col0, V v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int row = row0 + i * 16 + (lane & 15);
+      const int col = col0 + j * 16 + 4 * (lane >> 4);
+      u32x2_t w;
+      w[0] = pack_bf16x2(v(i, j, 0), v(i, j, 1));
+      w[1] = pack_bf16x2(v(i, j, 2), v(i, j, 3));
+      *(__attribute__((address_space(3))) u32x2_t*)(t + row * S + col * 2) = w;
+    }
+}
+
+template <int ROWS, int COLS, int S>
+__device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t ldc, int row_lim,
+                                              int col_lim) {
+  constexpr int CPR = COLS / 8;
+#pragma unroll 4
+  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
+    const int row = q / CPR, c8 = q % CPR;
+    if (row < row_lim && c8 * 8 < col_lim)
+      *(u32x4_t*)(C + (int64_t)row * ldc + c8 * 8) =
+          *(const __attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16);
+  }
+}
+
+template <int ROWS, int COLS, int S>
+__device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t ld, int row_lim,
+                                              int col_lim) {
+  constexpr int CPR = COLS / 8;
+#pragma unroll 4
+  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
+    const int row = q / CPR, c8 = q % CPR;
+    if (row < row_lim && c8 * 8 < col_lim)
+      *(__attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16) =
+          *(const u32x4_t*)(G + (int64_t)row * ld + c8 * 8);
+  }
+}
+
+__device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
+                                                 const int32_t* src_of, int m0, int seg1) {
+  for (int t = threadIdx.x; t < TBM; t += NTHR) {
+    const int row = m0 + t;
+    wl[t] = row < seg1 ? topk_w[src_of[row]] : 0.0f;
+  }
+}
+
+// ===========================================================================
+// Ragged-row GEMMs: token rows are an expert's segment of the sorted rows.
+// ===========================================================================
+enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_DGRAD_SWIGLU = 2 };
+
+struct Rows8Args {
+  // token side: row r reads A + arow(r) * lda, arow = a_src ? a_src[r] / a_div : r;
+  // its scale at K step kb is As[arow * a_sld + kb]
+  const uint8_t* A;
+  int64_t lda;
+  const int32_t* a_src;
+  int a_div;
+  const float* As;
+  int64_t a_sld;
+  // feature side (expert e): row n reads B + e * b_estride + wrow(n) * ldb,
+  // scale Bs[e * bs_estride + (wrow(n) / 128) * b_sld + kb].  gateup: 32-row
+  // blocks alternate gate rows (even) and up rows (odd).
+  const uint8_t* B;
+  int64_t b_estride, ldb;
+  const float* Bs;
+  int64_t bs_estride, b_sld;
+  int gateup;
+  int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
+  const int32_t* offsets;
+  const int32_t* tile_off;
+  int E;
+  // EPI_STORE: C [R, ldc] bf16
+  bf16_t* C;
+  int64_t ldc;
+  // EPI_GATEUP: H [R,2I] (optional), Aout [R,I] = w_row * silu(g) * u
+  bf16_t* H;
+  bf16_t* Aout;
+  int I;
+  const float* topk_w;
+  const int32_t* src_of;
+  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk]; dH [R,2I]
+  const bf16_t* Hin;
+  float* dwp;
+  int nblk;
+  bf16_t* dH;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
+  if (L < 0) return;
+  const int nt = L % p.n_tiles;
+  const int mt = L / p.n_tiles;
+  const int e = find_expert(p.tile_off, p.E, mt);
+  const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
+  const int m0 = seg0 + (mt - p.tile_off[e]) * TBM;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave_m(), wn = wave_n();
+
+  auto arow = [&](int row) -> int64_t {
+    int r = m0 + row;
+    if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
+    return p.a_src ? (int64_t)(p.a_src[r] / p.a_div) : (int64_t)r;
+  };
+  auto wrow = [&](int n) -> int {
+    if (p.gateup) {
+      const int blk = n >> 5;
+      int gc = nt * (TBN / 2) + (blk >> 1) * 32 + (n & 31);
+      if (gc >= p.I) gc = 0;
+      return (blk & 1) ? p.I + gc : gc;
+    }
+    const int w = nt * TBN + n;
+    return w < p.N ? w : 0;
+  };
+  const uint8_t* Be = p.B + (int64_t)e * p.b_estride;
+  const float* Bse = p.Bs + (int64_t)e * p.bs_estride;
+  Op8 ot, of;
+  ot.init([&](int row) { return p.A + arow(row) * p.lda; });
+  of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
+  const int srow = 64 * (wave_id() & 3) + lane;
+  const float* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_sld
+                                  : Bse + (int64_t)(wrow(srow) >> 7) * p.b_sld;
+  f32x4_t acc[TM][TN];
+  mainloop8<false>(ot, of, sp, p.K / KB, smem, acc);
+
+  // ------------------------------------------------------------- epilogues
+  barrier_lds();
+  lds_t* const lds = (lds_t*)smem;
+  const int rows_valid = seg1 - m0;
+  const int r0w = wm * (TBM / WM);
+  if constexpr (EPI == EPI_STORE) {
+    constexpr int S = ep_stride<TBN>();
+    stage4<TM, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
+    barrier_lds();
+    lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
+                               p.N - nt * TBN);
+  } else if constexpr (EPI == EPI_GATEUP) {
+    // features j = 0, 1 are gate columns wn*32 + 16 j + ..., j = 2, 3 the up
+    // columns of the same gate columns
+    constexpr int S = ep_stride<TBN / 2>();
+    constexpr int TB = TBM * S;
+    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
+    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
+    barrier_lds();
+    const int c0w = wn * 32;
+    stage4<TM, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) {
+      const float g = acc[i][j][r], u = acc[i][j + 2][r];
+      return wl[r0w + i * 16 + (lane & 15)] * (g * sigmoidf_(g) * u);
+    });
+    if (p.H) stage4<TM, 2, S>(lds + TB, r0w, c0w, [&](int i, int j, int r) { return acc[i][j][r]; });
+    barrier_lds();
+    const int gc0 = nt * (TBN / 2);
+    lds_to_global<TBM, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
+    if (p.H) {
+      bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
+      lds_to_global<TBM, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
+      barrier_lds();
+      stage4<TM, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) { return acc[i][j + 2][r]; });
+      barrier_lds();
+      lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
+    }
+  } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] at feature column nt*256 + c
+    constexpr int HR = TBM / WM;
+    constexpr int S = ep_stride<TBN>();
+    constexpr int TB = HR * S;
+    lds_t* Hg = lds;
+    lds_t* Hu = lds + TB;
+    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
+    const int col0 = nt * TBN;
+    const int64_t ldh = 2 * (int64_t)p.I;
+    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
+    const int c0w = wn * (TBN / WN);
+#pragma unroll 1
+    for (int h = 0; h < WM; ++h) {
+      const int mh = m0 + h * HR;
+      global_to_lds<HR, TBN, S>(Hg, p.Hin + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
+      global_to_lds<HR, TBN, S>(Hu, p.Hin + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
+      __syncthreads();
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int rl = i * 16 + (lane & 15);
+          const float wr = wl[h * HR + rl];
+          float part = 0.0f;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int cl = c0w + j * 16 + 4 * (lane >> 4);
+            auto* pg = (__attribute__((address_space(3))) u32x2_t*)(Hg + rl * S + cl * 2);
+            auto* pu = (__attribute__((address_space(3))) u32x2_t*)(Hu + rl * S + cl * 2);
+            const u32x2_t gw = *pg, uw = *pu;
+            const bool in = col0 + cl < p.N;  // columns past N hold stale bytes
+            float dg[4], du[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t gb = gw[r >> 1], ub = uw[r >> 1];
+              const float g = __uint_as_float((r & 1) ? (gb & 0xFFFF0000u) : (gb << 16));
+              const float u = __uint_as_float((r & 1) ? (ub & 0xFFFF0000u) : (ub << 16));
+              const float G = acc[i][j][r];
+              const float sg = sigmoidf_(g);
+              if (in) part += G * (g * sg * u);
+              const float dA = wr * G;
+              dg[r] = dA * u * sg * (1.0f + g * (1.0f - sg));
+              du[r] = dA * g * sg;
+            }
+            u32x2_t og, ou;
+            og[0] = pack_bf16x2(dg[0], dg[1]);
+            og[1] = pack_bf16x2(dg[2], dg[3]);
+            ou[0] = pack_bf16x2(du[0], du[1]);
+            ou[1] = pack_bf16x2(du[2], du[3]);
+            *pg = og;
+            *pu = ou;
+          }
+          // partial <G, a> of the row over this wave's 64 columns
+          part += __shfl_xor(part, 16, kWave);
+          part += __shfl_xor(part, 32, kWave);
+          const int row = mh + rl;
+          if ((lane >> 4) == 0 && row < seg1) p.dwp[(int64_t)row * p.nblk + nt * WN + wn] = part;
+        }
+      }
+      barrier_lds();
+      lds_to_global<HR, TBN, S>(Hg, p.dH + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
+      lds_to_global<HR, TBN, S>(Hu, p.dH + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
+      barrier_lds();
+    }
+  }
+}
+
+// ===========================================================================
+// Weight gradients: dW[e][m, n] = sum over expert e's token blocks of
+// A(m, k) B(n, k) s_A(m, blk) s_B(n, blk).  Both operands are transposed
+// token-blocked ([features][padded rows], see quant_fp8.hip): expert e owns
+// K bytes [128 blk_off[e], 128 blk_off[e+1]) of every row.
+// ===========================================================================
+struct Wgrad8Args {
+  const uint8_t* A;  // output-row side, [M][ldk]
+  const float* As;   // [M][nblk]
+  const uint8_t* B;  // output-column side, [N][ldk]
+  const float* Bs;   // [N][nblk]
+  int64_t ldk, nblk;
+  int M, N, m_tiles, n_tiles, E;
+  const int32_t* blk_off;
+  const int32_t* order;
+  bf16_t* C;  // dW[e] = C + e * c_estride, row-major [M, N]
+  int64_t c_estride;
+};
+
+__global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int per = p.m_tiles * p.n_tiles;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int oi = (idx / per) * 8 + xcd;
+  if (oi >= p.E) return;
+  const int rem = idx % per;
+  const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
+  const int e = p.order[oi];
+  const int b0 = p.blk_off[e];
+  const int nkb = p.blk_off[e + 1] - b0;
+  auto mrow = [&](int row) { const int m = mt * TBM + row; return m < p.M ? m : 0; };
+  auto nrow = [&](int row) { const int n = nt * TBN + row; return n < p.N ? n : 0; };
+  Op8 ot, of;
+  ot.init([&](int row) { return p.A + (int64_t)mrow(row) * p.ldk + (int64_t)b0 * KB; });
+  of.init([&](int row) { return p.B + (int64_t)nrow(row) * p.ldk + (int64_t)b0 * KB; });
+  const int srow = 64 * (wave_id() & 3) + (threadIdx.x & 63);
+  const float* sp = wave_id() < 4 ? p.As + (int64_t)mrow(srow) * p.nblk + b0
+                                  : p.Bs + (int64_t)nrow(srow) * p.nblk + b0;
+  f32x4_t acc[TM][TN];
+  mainloop8<true>(ot, of, sp, nkb, smem, acc);
+  barrier_lds();
+  lds_t* const lds = (lds_t*)smem;
+  constexpr int S = ep_stride<TBN>();
+  stage4<TM, TN, S>(lds, wave_m() * (TBM / WM), wave_n() * (TBN / WN),
+                    [&](int i, int j, int r) { return acc[i][j][r]; });
+  barrier_lds();
+  lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)e * p.c_estride + (int64_t)mt * TBM * p.N + nt * TBN,
+                             p.N, p.M - mt * TBM, p.N - nt * TBN);
+}
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+constexpr size_t kRingBytes = (size_t)2 * STB;
+constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
+constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
+constexpr size_t kDgradEpi = (size_t)2 * (TBM / WM) * ep_stride<TBN>() + TBM * 4;
+constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreEpi), cmax(kGateupEpi, kDgradEpi));
+static_assert(kSmem <= 160 * 1024, "LDS");
+
+template <class K>
+hipError_t allow_smem(K kernel) {
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)kSmem);
+}
+
+template <int EPI>
+hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = allow_smem(rows8_kernel<EPI>);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
+  const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
+  MOE_LAUNCH(c, name, rows8_kernel<EPI>, dim3(nblocks), dim3(NTHR), kSmem, p);
+  return hipSuccess;
+}
+
+hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args& p) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = allow_smem(wgrad8_kernel);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned nblocks = (unsigned)(cdiv(p.E, 8) * 8 * p.m_tiles * p.n_tiles);
+  MOE_LAUNCH(c, name, wgrad8_kernel, dim3(nblocks), dim3(NTHR), kSmem, p);
+  return hipSuccess;
+}
+
+}  // namespace
+
+int fp8_dw_blocks(int I) { return (int)cdiv(I, TBN) * WN; }
+
+hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q, void* H, void* Aw,
+                         void* Yw) {
+  const int64_t I = a.I, d = a.d;
+  hipError_t err;
+  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs));
+  HIP_RET(launch_quant_weight(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, false, q.wguq, q.wgus));
+  HIP_RET(launch_quant_weight(c, "quant_w_down", a.w_down, a.E, a.d, a.I, false, q.wdq, q.wds));
+  {  // gate/up GEMM on token rows gathered from xq; SwiGLU and top-k weight in the epilogue
+    Rows8Args p = {};
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.xs; p.a_sld = d / 128;
+    p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
+    p.Bs = q.wgus; p.bs_estride = (2 * I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 1;
+    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
+    p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
+    p.topk_w = a.topk_w; p.src_of = a.src_of;
+    HIP_RET(launch_rows8<EPI_GATEUP>(c, "gemm_gateup_fwd", p, a.R));
+  }
+  HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws));
+  Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
+  p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+  p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1; p.As = q.aws; p.a_sld = I / 128;
+  p.B = q.wdq; p.b_estride = d * I; p.ldb = I;
+  p.Bs = q.wds; p.bs_estride = (d / 128) * (I / 128); p.b_sld = I / 128; p.gateup = 0;
+  p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+  p.C = (bf16_t*)Yw; p.ldc = d;
+  (void)err;
+  return launch_rows8<EPI_STORE>(c, "gemm_down_fwd", p, a.R);
+}
+
+hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
+                         const void* H, const void* Aw, void* dH, void* dXp, float* dwp, void* dW_gu,
+                         void* dW_d) {
+  const int64_t I = a.I, d = a.d;
+  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts));
+  HIP_RET(launch_quant_weight(c, "quant_w_down_t", a.w_down, a.E, a.d, a.I, true, q.wdtq, q.wdts));
+  HIP_RET(launch_quant_weight(c, "quant_w_gate_up_t", a.w_gate_up, a.E, 2 * a.I, a.d, true, q.wgutq,
+                              q.wguts));
+  {  // down dgrad: G = dout_t W_down[e]; epilogue: dw partials, SwiGLU backward -> dH
+    Rows8Args p = {};
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.douts; p.a_sld = d / 128;
+    p.B = q.wdtq; p.b_estride = I * d; p.ldb = d;
+    p.Bs = q.wdts; p.bs_estride = (I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 0;
+    p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
+    p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
+    p.dwp = dwp; p.nblk = fp8_dw_blocks(a.I); p.dH = (bf16_t*)dH; p.I = a.I;
+    HIP_RET(launch_rows8<EPI_DGRAD_SWIGLU>(c, "gemm_down_dgrad", p, a.R));
+  }
+  HIP_RET(launch_quant_rows(c, "quant_dh", dH, 2 * I, a.R, 2 * a.I, q.dhq, q.dhs));
+  {  // gate/up dgrad: dXp = dH W_gate_up[e]
+    Rows8Args p = {};
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1; p.As = q.dhs; p.a_sld = 2 * I / 128;
+    p.B = q.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
+    p.Bs = q.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;
+    p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+    p.C = (bf16_t*)dXp; p.ldc = d;
+    HIP_RET(launch_rows8<EPI_STORE>(c, "gemm_gateup_dgrad", p, a.R));
+  }
+  const int nb = q.nblk_max;
+  {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
+    HIP_RET(launch_quant_tok(c, "quant_dout_tok", dout, d, a.src_of, a.k, a.d, a.offsets, q.blk_off,
+                             a.E, nb, q.tqa, q.tsa));
+    HIP_RET(launch_quant_tok(c, "quant_aw_tok", Aw, I, nullptr, 1, a.I, a.offsets, q.blk_off, a.E, nb,
+                             q.tqb, q.tsb));
+    Wgrad8Args p = {};
+    p.A = q.tqa; p.As = q.tsa; p.B = q.tqb; p.Bs = q.tsb; p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN); p.E = a.E;
+    p.blk_off = q.blk_off; p.order = a.order;
+    p.C = (bf16_t*)dW_d; p.c_estride = d * I;
+    HIP_RET(launch_wgrad8(c, "gemm_down_wgrad", p));
+  }
+  {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
+    HIP_RET(launch_quant_tok(c, "quant_dh_tok", dH, 2 * I, nullptr, 1, 2 * a.I, a.offsets, q.blk_off,
+                             a.E, nb, q.tqa, q.tsa));
+    HIP_RET(launch_quant_tok(c, "quant_x_tok", a.x, d, a.src_of, a.k, a.d, a.offsets, q.blk_off, a.E,
+                             nb, q.tqb, q.tsb));
+    Wgrad8Args p = {};
+    p.A = q.tqa; p.As = q.tsa; p.B = q.tqb; p.Bs = q.tsb; p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
+    p.E = a.E; p.blk_off = q.blk_off; p.order = a.order;
+    p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
+    HIP_RET(launch_wgrad8(c, "gemm_gateup_wgrad", p));
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

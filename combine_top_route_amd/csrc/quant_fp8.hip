@@ -1,0 +1,254 @@
+// Block quantisation of GEMM operands to OCP e4m3 with fp32 scales.
+//
+// Blockwise FP8 shares one scale among a block of values ("Prime
+// Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster", section
+// "Precision and hardware support").  Three block shapes are used:
+//   rows:    1 x 128 along a row (activations and gradients in the forward
+//            and data-gradient GEMMs, blocks along their K dimension);
+//   weights: 128 x 128 tiles of one expert's matrix;
+//   tokens:  128 consecutive rows of one expert's segment x 1 column (both
+//            operands of the weight-gradient GEMMs, whose K is the token
+//            dimension), the count starting at the expert's first row.
+// For a block with largest magnitude amax the scale is s = amax / 448 in
+// fp32 (s = 1 for an all-zero block) and each value x becomes the e4m3
+// number nearest to the fp32 quotient x / s, ties to even; the GEMMs use
+// q * s.  The token-blocked operands are written transposed ([column][row],
+// each expert's rows padded with zeros to a multiple of 128) so that every
+// GEMM operand is contiguous along its K dimension.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+
+// Scale of a block with largest magnitude amax (correctly rounded division).
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+}
+
+// e4m3 codes of four quotients packed little-endian.  v_cvt_pk_fp8_f32
+// rounds to nearest even; the operand is clamped to +-448 first, so values a
+// rounding of s pushed just past 448 saturate instead of overflowing.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lo = -kE4M3Max, hi = kE4M3Max;
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                          __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
+                                      __builtin_amdgcn_fmed3f(d, lo, hi), v, true);
+  return (uint32_t)v;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4_t v, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+// Eight values divided by s, as eight e4m3 codes.
+__device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
+  u32x2_t q;
+  q[0] = e4m3x4(__fdiv_rn(f[0], s), __fdiv_rn(f[1], s), __fdiv_rn(f[2], s), __fdiv_rn(f[3], s));
+  q[1] = e4m3x4(__fdiv_rn(f[4], s), __fdiv_rn(f[5], s), __fdiv_rn(f[6], s), __fdiv_rn(f[7], s));
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// 1 x 128 blocks along rows: src [rows, C] (leading dimension ld) -> q [rows,
+// C], s [rows, C/128].  A 16-lane group handles one block, 8 values a lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restrict__ src, int64_t ld,
+                                                        int64_t rows, int C, uint8_t* __restrict__ q,
+                                                        float* __restrict__ s) {
+  const int nbc = C / 128;
+  const int64_t nb = rows * nbc;
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sl = threadIdx.x & 15;
+  const bool ok = g < nb;
+  const int64_t r = ok ? g / nbc : 0;
+  const int cb = ok ? (int)(g % nbc) : 0;
+  u32x4_t v = {0, 0, 0, 0};
+  if (ok) v = *(const u32x4_t*)(src + r * ld + cb * 128 + sl * 8);
+  float f[8];
+  unpack8(v, f);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  const float sc = block_scale(amax);
+  if (!ok) return;
+  *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8(f, sc);
+  if (sl == 0) s[r * nbc + cb] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// 128 x 128 weight blocks: W [E, N, K] -> q [E, N, K], s [E, N/128, K/128], or
+// (transpose) q [E, K, N], s [E, K/128, N/128].  One work-group per block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restrict__ W, int N, int K,
+                                                          int transpose, uint8_t* __restrict__ q,
+                                                          float* __restrict__ s) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[128 * 144];  // [k][n] codes, 144-byte rows
+  const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
+  const int t = threadIdx.x;
+  const int ch = t & 15;  // 8-element chunk along K
+  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128 + ch * 8;
+  u32x4_t v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) v[p] = *(const u32x4_t*)(Wb + (int64_t)((t >> 4) + 16 * p) * K);
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float f[8];
+    unpack8(v[p], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  const float sc = block_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  const int nbn = N / 128, nbk = K / 128;
+  if (!transpose) {
+    uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128 + ch * 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      float f[8];
+      unpack8(v[p], f);
+      *(u32x2_t*)(qb + (int64_t)((t >> 4) + 16 * p) * K) = quant8(f, sc);
+    }
+    if (t == 0) s[((int64_t)e * nbn + nb) * nbk + kb] = sc;
+    return;
+  }
+  // transposed: codes go through LDS as [k][n], then out as 64-byte row pieces
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    float f[8];
+    unpack8(v[p], f);
+    const u32x2_t c = quant8(f, sc);
+    const int n = (t >> 4) + 16 * p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tr[(ch * 8 + i) * 144 + n] = (uint8_t)(c[i >> 2] >> (8 * (i & 3)));
+  }
+  __syncthreads();
+  const int k = t >> 1, half = t & 1;
+  uint8_t* qt = q + (int64_t)e * K * N + (int64_t)(kb * 128 + k) * N + nb * 128 + half * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(u32x4_t*)(qt + i * 16) = *(const u32x4_t*)(tr + k * 144 + half * 64 + i * 16);
+  if (t == 0) s[((int64_t)e * nbk + kb) * nbn + nb] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Token blocks, transposed.  Block b (of blk_off[E] in all) is the
+// (b - blk_off[e])-th run of 128 rows of expert e's segment; row i of the run
+// is src row srow(offsets[e] + 128 * (b - blk_off[e]) + i), with srow(r) =
+// src_of[r] / kdiv (token rows of x or dout) or r.  A work-group handles 64
+// columns: q[c][128 b + i] = code (0 past the segment), s[c][b] = scale.
+// ---------------------------------------------------------------------------
+constexpr int kTokCols = 64;
+
+__global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict__ src, int64_t ld,
+                                                       const int32_t* __restrict__ src_of, int kdiv,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ blk_off, int E,
+                                                       uint8_t* __restrict__ q, int64_t ldq,
+                                                       float* __restrict__ s, int64_t lds) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 136];  // [row][64 bf16], 136-byte rows
+  const int b = blockIdx.x;
+  if (b >= blk_off[E]) return;
+  int lo = 0, hi = E;  // largest e with blk_off[e] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (blk_off[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (b - blk_off[e]) * 128;
+  const int n = min(128, offsets[e + 1] - r0);
+  const int c0 = blockIdx.y * kTokCols;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = (t >> 3) + 32 * p, ch = t & 7;
+    u32x4_t v = {0, 0, 0, 0};
+    if (i < n) {
+      const int64_t sr = src_of ? (int64_t)(src_of[r0 + i] / kdiv) : (int64_t)(r0 + i);
+      v = *(const u32x4_t*)(src + sr * ld + c0 + ch * 8);
+    }
+    u32x2_t* dst = (u32x2_t*)(tile + i * 136 + ch * 16);
+    dst[0] = u32x2_t{v[0], v[1]};
+    dst[1] = u32x2_t{v[2], v[3]};
+  }
+  __syncthreads();
+  // thread: column pair cp (columns c0 + 2cp, +1), rows 16 rg .. 16 rg + 15
+  const int cp = t >> 3, rg = t & 7;
+  float f0[16], f1[16];
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w = *(const uint32_t*)(tile + (16 * rg + i) * 136 + cp * 4);
+    f0[i] = __uint_as_float(w << 16);
+    f1[i] = __uint_as_float(w & 0xFFFF0000u);
+    a0 = fmaxf(a0, fabsf(f0[i]));
+    a1 = fmaxf(a1, fabsf(f1[i]));
+  }
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) {
+    a0 = fmaxf(a0, __shfl_xor(a0, off, kWave));
+    a1 = fmaxf(a1, __shfl_xor(a1, off, kWave));
+  }
+  const float s0 = block_scale(a0), s1 = block_scale(a1);
+  const int c = c0 + 2 * cp;
+  u32x4_t q0, q1;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    q0[w] = e4m3x4(__fdiv_rn(f0[4 * w], s0), __fdiv_rn(f0[4 * w + 1], s0), __fdiv_rn(f0[4 * w + 2], s0),
+                   __fdiv_rn(f0[4 * w + 3], s0));
+    q1[w] = e4m3x4(__fdiv_rn(f1[4 * w], s1), __fdiv_rn(f1[4 * w + 1], s1), __fdiv_rn(f1[4 * w + 2], s1),
+                   __fdiv_rn(f1[4 * w + 3], s1));
+  }
+  *(u32x4_t*)(q + (int64_t)c * ldq + (int64_t)b * 128 + rg * 16) = q0;
+  *(u32x4_t*)(q + (int64_t)(c + 1) * ldq + (int64_t)b * 128 + rg * 16) = q1;
+  if (rg == 0) {
+    s[(int64_t)c * lds + b] = s0;
+    s[(int64_t)(c + 1) * lds + b] = s1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
+                             int64_t rows, int C, uint8_t* q, float* s) {
+  const int64_t nb = rows * (C / 128);
+  if (nb == 0) return hipSuccess;
+  MOE_LAUNCH(c, name, quant_rows_kernel, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
+             (const bf16_t*)src, ld, rows, C, q, s);
+  return hipSuccess;
+}
+
+hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
+                               int K, bool transpose, uint8_t* q, float* s) {
+  MOE_LAUNCH(c, name, quant_weight_kernel, dim3(K / 128, N / 128, E), dim3(256), 0,
+             (const bf16_t*)W, N, K, transpose ? 1 : 0, q, s);
+  return hipSuccess;
+}
+
+hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
+                            const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
+                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, float* s) {
+  MOE_LAUNCH(c, name, quant_tok_kernel, dim3(nblk_max, C / kTokCols), dim3(256), 0,
+             (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
+             s, (int64_t)nblk_max);
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -307,7 +307,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 // GEMMs (largest expert first, so the longest tiles start first).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         int32_t* __restrict__ tile_off,
-                                                        int32_t* __restrict__ order) {
+                                                        int32_t* __restrict__ order,
+                                                        int32_t* __restrict__ blk_off) {
   __shared__ int sh_waves[16];
   __shared__ int total;
   __shared__ int cnt[1024];
@@ -320,6 +321,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   if (e < E) tile_off[e] = off;
   if (e == 0) tile_off[E] = total;
   __syncthreads();
+  if (blk_off) {
+    const int blks = (c + kTokBlock - 1) / kTokBlock;
+    const int boff = block_exclusive_scan(e < E ? blks : 0, sh_waves, &total);
+    if (e < E) blk_off[e] = boff;
+    if (e == 0) blk_off[E] = total;
+    __syncthreads();
+  }
   if (e < E) {
     int rank = 0;
     for (int o = 0; o < E; ++o) {
@@ -383,9 +391,9 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
 }
 
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order) {
+                           int32_t* order, int32_t* blk_off) {
   MOE_LAUNCH(c, "route_schedule", schedule_kernel, dim3(1), dim3(1024), 0, offsets, E, tile_off,
-             order);
+             order, blk_off);
   return hipSuccess;
 }
 

@@ -149,6 +149,42 @@ moe_status moe_permute(const moe_shape* shape, const void* x,
 moe_status moe_combine(const moe_shape* shape, const void* rows,
                        const moe_routing* routing, void* out, void* stream);
 
+/* Block quantisation to OCP e4m3 with fp32 scales, the operand encoding of
+ * MOE_PREC_FP8_BLOCK ("Prime Mega MoE Trains Giant AI Models 55% Faster",
+ * section "Precision and hardware support": one scale per block of values).
+ * For a block with largest magnitude amax the scale is s = amax / 448 (1 for
+ * an all-zero block) and each value x becomes the code of the e4m3 number
+ * nearest to the float32 quotient x / s (ties to even, saturating at 448);
+ * x is then represented as decode(code) * s.  src is bf16, q holds the
+ * 8-bit codes, s the float32 scales (device pointers; src and q 16-byte
+ * aligned).  Kinds:
+ *   MOE_QUANT_ROWS:     src [n0, n1], 1 x 128 blocks along rows
+ *                       -> q [n0, n1], s [n0, n1/128]; n1 % 128 == 0;
+ *   MOE_QUANT_WEIGHT:   src [n0, n1, n2], 128 x 128 blocks of each [n1, n2]
+ *                       matrix -> q [n0, n1, n2], s [n0, n1/128, n2/128];
+ *   MOE_QUANT_WEIGHT_T: the same blocks written transposed
+ *                       -> q [n0, n2, n1], s [n0, n2/128, n1/128].
+ * n2 is ignored for MOE_QUANT_ROWS. */
+typedef enum { MOE_QUANT_ROWS = 0, MOE_QUANT_WEIGHT = 1, MOE_QUANT_WEIGHT_T = 2 } moe_quant_kind;
+moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                            uint8_t* q, float* s, void* stream);
+
+/* Token-block quantisation of a weight-gradient operand (same encoding):
+ * blocks are runs of 128 consecutive expert-sorted rows of one expert's
+ * segment (counted from the expert's first row, the last run short) by one
+ * column.  Row r of the operand is src[src_of[r] / k] when gather != 0 (src
+ * [T, C], token rows) and src[r] otherwise (src [T*k, C], expert order).
+ * Output transposed and padded: with nblk = ceil(T*k / 128) + E and
+ * blk_off[e] = sum over e' < e of ceil(counts[e'] / 128), run i of expert e
+ * is block b = blk_off[e] + i, q [C, 128 nblk] holds its codes at
+ * q[c][128 b + j] (zero past the segment) and s [C, nblk] its scales at
+ * s[c][b]; blocks b >= blk_off[E] are not written.  shape->dtype must be
+ * MOE_BF16, C a multiple of 128; routing->offsets (and src_of when
+ * gathering) are read; workspace as for moe_route. */
+moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int64_t C, int gather,
+                                   const moe_routing* routing, uint8_t* q, float* s,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
 

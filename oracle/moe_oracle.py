@@ -500,3 +500,70 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
     if logits is not None:
         res["dlogits"] = router_logit_grad(rt, d_topk_w, logits.shape[1])
     return res
+
+
+def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
+                                tokens: np.ndarray, ids=None, w=None) -> dict:
+    """forward_fp8 / backward_fp8 results (out, dx, d_topk_w, dlogits) for a
+    subset of tokens.  Activation blocks are 1 x 128 within one row and weight
+    blocks depend only on the weights, so each token's results follow from
+    its own rows; the same steps as the full functions, row by row."""
+    tokens = np.asarray(tokens)
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    if logits is not None:
+        lg = np.asarray(logits)[tokens]
+        ids_t = topk_select(lg, k)
+        w_t = topk_weights(lg, ids_t)
+    else:
+        ids_t = np.asarray(ids)[tokens].astype(np.int64)
+        w_t = np.asarray(w, F64)[tokens]
+    qw = {}
+
+    def weights(e):
+        if e not in qw:
+            qw[e] = (quant_weight_128x128(w_gate_up[e]), quant_weight_128x128(w_down[e]))
+        return qw[e]
+
+    n, d = tokens.size, w_down.shape[1]
+    out, dx = np.zeros((n, d)), np.zeros((n, d))
+    dtw = np.zeros((n, k))
+    for i, t in enumerate(tokens):
+        xq = quant_rows_1x128(np.asarray(x, F64)[t][None, :])
+        gq = quant_rows_1x128(np.asarray(dout, F64)[t][None, :])
+        for j in range(k):
+            Wgu_q, Wd_q = weights(ids_t[i, j])
+            Hs = xq @ Wgu_q.T
+            H = bf16_round(Hs)
+            Aw = bf16_round(w_t[i, j] * swiglu(Hs, I))
+            out[i] += (quant_rows_1x128(Aw) @ Wd_q.T)[0]
+            G = gq @ Wd_q
+            dtw[i, j] = np.sum(G * swiglu(H, I))
+            dH = bf16_round(swiglu_backward(H, w_t[i, j] * G, I))
+            dx[i] += (quant_rows_1x128(dH) @ Wgu_q)[0]
+    res = dict(out=out, dx=dx, d_topk_w=dtw, ids=ids_t, w=w_t)
+    if logits is not None:
+        res["dlogits"] = router_logit_grad(dict(ids=ids_t, w=w_t), dtw, E)
+    return res
+
+
+def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int):
+    """backward_fp8's dW_gate_up[e], dW_down[e] from the rows of expert e
+    alone (token blocks are counted from the expert's first row)."""
+    k = rt["k"]
+    s = slice(rt["offsets"][e], rt["offsets"][e + 1])
+    src = rt["src_of"][s]
+    I = w_gate_up.shape[1] // 2
+    Wgu_q = quant_weight_128x128(w_gate_up[e])
+    Wd_q = quant_weight_128x128(w_down[e])
+    Xp = np.asarray(x, F64)[src // k]
+    g = np.asarray(dout, F64)[src // k]
+    wr = rt["w"].ravel()[src]
+    Hs = quant_rows_1x128(Xp) @ Wgu_q.T
+    H = bf16_round(Hs)
+    Aw = bf16_round(wr[:, None] * swiglu(Hs, I))
+    G = quant_rows_1x128(g) @ Wd_q
+    dH = bf16_round(swiglu_backward(H, wr[:, None] * G, I))
+    dW_down = quant_tokens_128(g).T @ quant_tokens_128(Aw)
+    dW_gate_up = quant_tokens_128(dH).T @ quant_tokens_128(Xp)
+    return dW_gate_up, dW_down

@@ -55,10 +55,11 @@ def run_oracle(wl, inp, ids=None, w=None, backward=True):
     else:
         rt = O.route(None, wl.k, wl.E, ids=ids.numpy(), w=w.double().numpy())
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
-    fw = O.forward(f(inp["x"]), rt, Wgu, Wd)
+    fp8 = wl.precision == "fp8_block"
+    fw = (O.forward_fp8 if fp8 else O.forward)(f(inp["x"]), rt, Wgu, Wd)
     res = {"rt": rt, "out": fw["out"]}
     if backward:
-        bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
+        bw = (O.backward_fp8 if fp8 else O.backward)(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
         res.update(bw)
     return res
 

@@ -75,6 +75,30 @@ def test_fp8_requirements():
     assert _status(s)[0] == 2                            # MOE_ERR_UNSUPPORTED
     s = _shape(precision="fp8_block", dtype=torch.bfloat16, d=192, I=128)
     assert _status(s)[0] == 2
+    # a valid fp8 shape: its workspaces hold the quantised operands besides the bf16 ones
+    for op in (B.OP_FORWARD, B.OP_BACKWARD):
+        st8, w8 = _status(_shape(precision="fp8_block", dtype=torch.bfloat16, d=256, I=128), op=op)
+        st16, w16 = _status(_shape(dtype=torch.bfloat16, d=256, I=128), op=op)
+        assert st8 == 0 and st16 == 0 and w8 > w16
+
+
+def test_quantize_entry_points_validate():
+    L = B.lib()
+    q, sc = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert L.moe_quantize_fp8(B.QUANT_ROWS, None, 4, 128, 0, q, sc, None) == 1       # NULL src
+    assert L.moe_quantize_fp8(9, FAKE, 4, 128, 0, q, sc, None) == 1                  # unknown kind
+    assert L.moe_quantize_fp8(B.QUANT_ROWS, FAKE, 4, 100, 0, q, sc, None) == 1       # 100 % 128
+    assert L.moe_quantize_fp8(B.QUANT_WEIGHT, FAKE, 2, 128, 96, q, sc, None) == 1    # 96 % 128
+    assert L.moe_quantize_fp8(B.QUANT_ROWS, ctypes.c_void_p((1 << 20) + 8), 4, 128, 0, q, sc, None) == 1
+    s = _shape(dtype=torch.bfloat16)
+    r = B.MoeRouting(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_quantize_tokens_fp8(ctypes.byref(s), FAKE, 100, 1, ctypes.byref(r), q, sc, FAKE,
+                                     1 << 30, None) == 1                            # C % 128
+    assert L.moe_quantize_tokens_fp8(ctypes.byref(s), FAKE, 128, 1, ctypes.byref(r), q, sc, FAKE,
+                                     0, None) == 3                                  # workspace
+    s32 = _shape()
+    assert L.moe_quantize_tokens_fp8(ctypes.byref(s32), FAKE, 128, 1, ctypes.byref(r), q, sc, FAKE,
+                                     1 << 30, None) == 2                            # f32 storage
 
 
 def test_workspace_sizes_grow_with_problem():

@@ -1,0 +1,152 @@
+"""Blockwise fp8 (OCP e4m3, fp32 block scales) path against the oracle.
+
+Quantisation is byte work and must match bit for bit: every e4m3 code and
+every scale.  Layer outputs and gradients match the oracle's emulation of the
+same quantisation within max|err|/max|ref| <= 6e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_top_route_amd import binding as B
+from combine_top_route_amd import synthetic as S
+from oracle import moe_oracle as O
+
+from gpu_util import TOL, check_floats, check_routing, rel_err, run_gpu, run_oracle, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+FP8 = dict(dtype="bf16", logits_dtype="bf16", precision="fp8_block")
+BASE = S.WORKLOADS["tiny"].scaled(**FP8)
+
+
+def _bf16_matrix(shape, seed):
+    """bf16 values spanning e4m3's normal and subnormal ranges after
+    scaling: per-row magnitudes from 1e-6 to 1e3, a zero block, exact ties."""
+    g = np.random.default_rng(seed)
+    a = g.standard_normal(shape) * np.exp(g.uniform(np.log(1e-6), np.log(1e3), shape[:-1] + (1,)))
+    a = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    flat = a.view(-1, a.shape[-1])
+    flat[0, :128] = 0.0                         # an all-zero block
+    flat[1, :4] = torch.tensor([448.0, 224.0, 0.5, -0.5])
+    return a.contiguous()
+
+
+def _decode(q, s_expanded):
+    return q.view(torch.float8_e4m3fn).double().cpu().numpy() * s_expanded
+
+
+def test_quantize_rows_bit_exact():
+    x = _bf16_matrix((300, 512), 1)
+    q, s = B.quantize_fp8(x.to(DEV), B.QUANT_ROWS)
+    s_np = s.cpu().numpy().astype(np.float64)
+    ref = O.quant_rows_1x128(x.float().numpy())
+    got = _decode(q, np.repeat(s_np, 128, axis=1))
+    assert np.array_equal(got, ref)
+    # codes: the oracle's values over the (equal) scales, cast to e4m3
+    codes = torch.from_numpy(ref / np.repeat(s_np, 128, axis=1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(q.cpu(), codes)
+
+
+@pytest.mark.parametrize("kind", [B.QUANT_WEIGHT, B.QUANT_WEIGHT_T])
+def test_quantize_weight_bit_exact(kind):
+    W = _bf16_matrix((3, 256, 384), 2)
+    q, s = B.quantize_fp8(W.to(DEV), kind)
+    q, s = q.cpu(), s.cpu().numpy().astype(np.float64)
+    for e in range(3):
+        ref = O.quant_weight_128x128(W[e].float().numpy())
+        if kind == B.QUANT_WEIGHT_T:
+            ref = ref.T
+        got = _decode(q[e], np.kron(s[e], np.ones((128, 128))))
+        assert np.array_equal(got, ref), e
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_quantize_tokens_bit_exact(gather):
+    """Runs of 128 expert-sorted rows per column, counted from each expert's
+    first row, with experts that are empty, shorter than a run, or ragged."""
+    T, E, k, C = 700, 8, 2, 256
+    g = np.random.default_rng(3)
+    pool = np.array([0, 1, 2, 4])                           # experts 3 and 5 stay empty
+    ids = np.stack([g.permutation(pool)[:k] for _ in range(T)])
+    ids[:40] = [7, 6]                                       # experts 6, 7: 40 rows each
+    ids = torch.from_numpy(ids.astype(np.int32))
+    w = torch.from_numpy(g.uniform(0.1, 1.0, (T, k)).astype(np.float32))
+    r = B.route_ids(ids.to(DEV), w.to(DEV), E)
+    R = T * k
+    src = _bf16_matrix((T if gather else R, C), 4)
+    q, s = B.quantize_tokens_fp8(src.to(DEV), r, T, k, gather)
+    q, s = q.cpu(), s.cpu().numpy().astype(np.float64)
+    rt = O.route(None, k, E, ids=ids.numpy(), w=w.double().numpy())
+    counts, off = rt["counts"], rt["offsets"]
+    assert counts[3] == 0 and counts[5] == 0 and counts[6] == 40
+    rows = src.float().numpy()[rt["src_of"] // k] if gather else src.float().numpy()
+    blk = 0
+    for e in range(E):
+        n = counts[e]
+        nb = -(-n // 128)
+        if n:
+            ref = O.quant_tokens_128(rows[off[e]:off[e + 1]])          # [n, C]
+            cols = slice(128 * blk, 128 * (blk + nb))
+            got = _decode(q[:, cols], np.repeat(s[:, blk:blk + nb], 128, axis=1))   # [C, 128 nb]
+            assert np.array_equal(got[:, :n], ref.T), e
+            assert np.all(q[:, cols][:, n:].numpy() == 0), e
+        blk += nb
+
+
+SMALL = {
+    # several tiles, ragged rows, a 128-wide feature tail (d = I = 384)
+    "fp8_tiles": BASE.scaled(T=777, d=384, E=16, k=4, I=384),
+    "fp8_wide": BASE.scaled(T=600, d=512, E=8, k=2, I=256),
+    "fp8_one_token": BASE.scaled(T=1, d=128, E=8, k=2, I=128),
+    "fp8_single_expert": BASE.scaled(T=300, d=256, E=1, k=1, I=128),
+    # the skewed router (Zipf bias, empty experts) at a small hidden size
+    "fp8_skew_small": S.WORKLOADS["fp8_skew"].scaled(T=1024, d=256, I=256),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp8_layer_parity_small(name):
+    wl = SMALL[name]
+    print(f"case {name}: {wl}", flush=True)
+    inp = S.make_inputs(wl, seed=1)
+    gpu = run_gpu(wl, inp)
+    ref = run_oracle(wl, inp)
+    check_routing(gpu, ref)
+    errs = check_floats(gpu, ref, TOL["fp8"])
+    print(name, errs)
+
+
+def test_fp8_layer_parity_full_size_sampled():
+    """Skewed-routing fp8 layer at 16,384 tokens, d=4096, I=1536 in the
+    benchmark's launch configuration: routing bit-exact (hot and empty
+    experts), out/dx/top-k-weight/logit gradients on sampled tokens, weight
+    gradients of the smallest non-empty expert and of a mid-sized one."""
+    wl = S.WORKLOADS["fp8_skew"]
+    inp = S.make_inputs(wl, seed=0)
+    gpu = run_gpu(wl, inp)
+    lg = inp["logits"].double().numpy()
+    rt = O.route(lg, wl.k, wl.E)
+    check_routing(gpu, {"rt": rt})
+    counts = rt["counts"]
+    assert (counts == 0).sum() >= 4 and counts.max() >= 8 * counts.mean()
+    Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
+    x, dout = inp["x"].double().numpy(), inp["dout"].double().numpy()
+    toks = np.random.default_rng(0).choice(wl.T, 12, replace=False)
+    toks[:2] = [0, wl.T - 1]
+    s = O.forward_backward_tokens_fp8(x, lg, dout, Wgu, Wd, wl.k, toks)
+    for n in ("out", "dx", "d_topk_w", "dlogits"):
+        e = rel_err(gpu[n][toks], s[n])
+        print(n, e)
+        assert e <= TOL["fp8"], (n, e)
+    nz = np.nonzero(counts)[0]
+    order = nz[np.argsort(counts[nz])]
+    for e in (order[0], order[len(order) // 2]):
+        dgu, dd = O.expert_weight_grads_fp8(x, dout, rt, Wgu, Wd, e)
+        for n, got, ref in (("dW_gate_up", gpu["dW_gate_up"][e], dgu), ("dW_down", gpu["dW_down"][e], dd)):
+            err = rel_err(got, ref)
+            print(n, e, counts[e], err)
+            assert err <= TOL["fp8"], (n, e, err)
+    for e in np.nonzero(counts == 0)[0]:
+        assert np.all(gpu["dW_gate_up"][e] == 0) and np.all(gpu["dW_down"][e] == 0)

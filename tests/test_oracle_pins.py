@@ -403,3 +403,23 @@ def test_fp8_gate_up_exact_on_representable_operands():
     H = np.concatenate([O.dispatch(x, rt)[s0:s1] @ W[e].T for e, (s0, s1) in
                         enumerate(zip(rt["offsets"][:-1], rt["offsets"][1:]))])
     assert np.array_equal(f8["H"], O.bf16_round(H))
+
+
+def test_fp8_sampled_evaluators_match_full_layer():
+    """The per-token and per-expert fp8 evaluators reproduce forward_fp8 /
+    backward_fp8 (same arithmetic, different grouping)."""
+    wl = S.WORKLOADS["tiny"].scaled(d=256, I=128, T=96, E=6, k=2, dtype="bf16")
+    inp = {k: _np(v) for k, v in S.make_inputs(wl, seed=17).items()}
+    rt = O.route(inp["logits"], wl.k, wl.E)
+    f8 = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"])
+    b8 = O.backward_fp8(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], f8, logits=inp["logits"])
+    toks = np.array([0, 5, 50, 95])
+    s = O.forward_backward_tokens_fp8(inp["x"], inp["logits"], inp["dout"], inp["w_gate_up"],
+                                      inp["w_down"], wl.k, toks)
+    for n, ref in (("out", f8["out"]), ("dx", b8["dx"]), ("d_topk_w", b8["d_topk_w"]),
+                   ("dlogits", b8["dlogits"])):
+        np.testing.assert_allclose(s[n], ref[toks], rtol=1e-12, atol=1e-12 * np.max(np.abs(ref)))
+    for e in range(wl.E):
+        dgu, dd = O.expert_weight_grads_fp8(inp["x"], inp["dout"], rt, inp["w_gate_up"], inp["w_down"], e)
+        np.testing.assert_allclose(dgu, b8["dW_gate_up"][e], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dd, b8["dW_down"][e], rtol=1e-12, atol=1e-12)

@@ -30,15 +30,52 @@ from combine_top_route_amd import binding as B
 from combine_top_route_amd import synthetic as S
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (the float32 path runs on FMA units)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE layer fwd+bwd ms and TFLOP/s (MFMA util %), Qwen3-30B-A3B shape T=16384"
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "combine_top_route_amd", "csrc")
+
+# rocprofv3 kernel name (template instance) -> the library's launch name
+KERNEL_SITES = [
+    ("rows_gemm_kernel<1, 1>(", "gemm_gateup_fwd"), ("rows_gemm_kernel<0, 0>(", "gemm_down_fwd"),
+    ("rows_gemm_kernel<2, 2>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2>(", "gemm_gateup_dgrad"),
+    ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
+    ("rows8_kernel<1, 0>(", "gemm_gateup_fwd"), ("rows8_kernel<0, 0>(", "gemm_down_fwd"),
+    ("rows8_kernel<2, 0>(", "gemm_down_dgrad"), ("rows8_kernel<0, 1>(", "gemm_gateup_dgrad"),
+    ("wgrad8_kernel<0>(", "gemm_down_wgrad"), ("wgrad8_kernel<1>(", "gemm_gateup_wgrad"),
+    ("combine_wide_kernel<", "combine + reduce_dx"), ("combine_kernel<", "combine + reduce_dx"),
+    ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
+    ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
+    ("topk_grad_kernel", "topk_grad"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
+    ("quant_weight_kernel", "quant_w_*"), ("quant_tok_kernel", "quant_*_tok"),
+]
+# source files whose text defines each GEMM kernel (a change voids measured traffic)
+KERNEL_SOURCES = {
+    "native": ["gemm_bf16.hip", "tile.h", "common.h"],
+    "fp8_block": ["gemm_fp8.hip", "tile.h", "common.h"],
+}
+
+
+def site_of(kernel_name: str) -> str | None:
+    for key, site in KERNEL_SITES:
+        if key in kernel_name:
+            return site
+    return None
+
+
+def mfma_peak(wl) -> float:
+    if wl.precision == "fp8_block":
+        return PEAK_FP8_TFLOPS
+    return PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
 
 
 def kernel_work(wl):
     """Algorithmic work per launch of each kernel: ('flop'|'byte', amount)."""
     R, d, I, T, k, E = wl.R, wl.d, wl.I, wl.T, wl.k, wl.E
     es = 2 if wl.dtype == "bf16" else 4
-    return {
+    work = {
         "gemm_gateup_fwd": ("flop", 4.0 * R * d * I),
         "gemm_down_fwd": ("flop", 2.0 * R * d * I),
         "gemm_down_dgrad": ("flop", 2.0 * R * d * I),
@@ -51,6 +88,52 @@ def kernel_work(wl):
         "permute": ("byte", float(T * d * es + R * d * es + 4 * R)),
         "route_topk": ("byte", float(T * E * es + 8 * R)),
     }
+    if wl.precision == "fp8_block":
+        # bf16 in, one code byte out per element, one float scale per block
+        q = lambda n, blk: float(n * 2 + n + 4 * n // blk)
+        work.update({
+            "quant_x": ("byte", q(T * d, 128)), "quant_dout": ("byte", q(T * d, 128)),
+            "quant_aw": ("byte", q(R * I, 128)), "quant_dh": ("byte", q(R * 2 * I, 128)),
+            "quant_w_gate_up": ("byte", q(E * 2 * I * d, 128 * 128)),
+            "quant_w_down": ("byte", q(E * d * I, 128 * 128)),
+            "quant_w_gate_up_t": ("byte", q(E * 2 * I * d, 128 * 128)),
+            "quant_w_down_t": ("byte", q(E * d * I, 128 * 128)),
+            "quant_dout_tok": ("byte", q(R * d, 128) + 4 * R), "quant_x_tok": ("byte", q(R * d, 128) + 4 * R),
+            "quant_aw_tok": ("byte", q(R * I, 128)), "quant_dh_tok": ("byte", q(R * 2 * I, 128)),
+        })
+    return work
+
+
+def source_digest(wl) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[wl.precision]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wl, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the kernel's
+    source changed since the counters were taken."""
+    path = os.path.join(HERE, "profiles", f"hbm_traffic_{wl.name}.md")
+    if not os.path.exists(path):
+        return None
+    digest = None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source digest:"):
+                digest = line.split(":", 1)[1].strip()
+            if line.startswith("traffic:"):
+                parts = dict(p.split("=") for p in line.split()[2:])
+                vals[line.split()[1]] = parts
+    if digest != source_digest(wl) or kernel not in vals:
+        return None
+    v = vals[kernel]
+    return {"fetch_bytes": float(v["fetch"]), "write_bytes": float(v["write"]),
+            "bytes": float(v["fetch"]) + float(v["write"])}
 
 
 def cpu_baseline(wl, inp: dict, tokens: int):
@@ -66,15 +149,112 @@ def cpu_baseline(wl, inp: dict, tokens: int):
     f = lambda t: t[:tokens].double().numpy()
     x, lg, dout = f(inp["x"]), f(inp["logits"]), f(inp["dout"])
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
+    fp8 = wl.precision == "fp8_block"
     t0 = time.perf_counter()
     rt = O.route(lg, wl.k, wl.E)
-    fw = O.forward(x, rt, Wgu, Wd)
-    O.backward(dout, rt, Wgu, Wd, fw, logits=lg)
+    fw = (O.forward_fp8 if fp8 else O.forward)(x, rt, Wgu, Wd)
+    (O.backward_fp8 if fp8 else O.backward)(dout, rt, Wgu, Wd, fw, logits=lg)
     dt = time.perf_counter() - t0
     flops = sub.flops_fwd() + sub.flops_bwd()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {tokens} of {wl.T} tokens of the {wl.name} workload, all {wl.E} experts, "
-                      f"fwd+bwd in float64 numpy, {dt:.1f} s"}
+                      f"fwd+bwd in float64 numpy{' emulating the fp8 quantisation' if fp8 else ''}, "
+                      f"{dt:.1f} s"}
+
+
+COPY_BYTES = 1 << 30
+
+
+def gemm_operand_bytes(wl):
+    """Bytes each GEMM must move at least once: both operands and the result
+    (weights once, activation rows once), in the storage types it reads."""
+    R, d, I, T, E = wl.R, wl.d, wl.I, wl.T, wl.E
+    a = 1 if wl.precision == "fp8_block" else (2 if wl.dtype == "bf16" else 4)
+    o = 2 if wl.dtype == "bf16" else 4
+    return {
+        "gemm_gateup_fwd": T * d * a + E * 2 * I * d * a + R * 3 * I * o,
+        "gemm_down_fwd": R * I * a + E * d * I * a + R * d * o,
+        "gemm_down_dgrad": T * d * a + E * d * I * a + 2 * R * 2 * I * o,
+        "gemm_down_wgrad": R * d * a + R * I * a + E * d * I * o,
+        "gemm_gateup_dgrad": R * 2 * I * a + E * 2 * I * d * a + R * d * o,
+        "gemm_gateup_wgrad": R * 2 * I * a + R * d * a + E * 2 * I * d * o,
+    }
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, write_dir: str | None = None):
+    """Markdown summary of rocprofv3 output: per-kernel durations from
+    --kernel-trace --stats and, given two --pmc runs (FETCH_SIZE, WRITE_SIZE),
+    HBM bytes per launch scaled by the same counters on the 1 GiB copy."""
+    n = wl.name
+    lines = [f"# rocprofv3 summary, {n} workload (T={wl.T}, d={wl.d}, E={wl.E}, k={wl.k}, "
+             f"I={wl.I}, {wl.dtype}, {wl.precision})", "",
+             "Commands (repository root, TMPDIR=/tmp):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o {n} -- "
+             f"python3 bench.py --workload {n} --steps 5 --warmup 2 --no-cpu"]
+    if fetch_dir and write_dir:
+        for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            lines.append(f"    rocprofv3 --pmc {key} --output-format csv -d {d} -o {n} -- python3 bench.py "
+                         f"--workload {n} --steps 2 --warmup 1 --no-cpu --copy-calibration")
+    lines += [f"    python3 bench.py --workload {n} --rocprof-summary {out} {stats_dir}"
+              + (f" {fetch_dir} {write_dir}" if fetch_dir and write_dir else ""), ""]
+    stats = _csv_rows(stats_dir, "kernel_stats.csv")
+    lines += ["Kernel durations (rocprofv3 --kernel-trace --stats):", "",
+              "| launch | kernel | calls | avg us | % GPU time |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["Percentage"])):
+        name = r["Name"]
+        short = name.replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {site_of(name) or '-'} | `{short}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    if fetch_dir and write_dir:
+        per = {}
+        for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            for r in _csv_rows(d, "counter_collection.csv"):
+                if r["Counter_Name"] != key:
+                    continue
+                site = site_of(r["Kernel_Name"])
+                if site is None and "moe::" not in r["Kernel_Name"]:
+                    site = "calibration copy"
+                if site is None:
+                    continue
+                per.setdefault(site, {}).setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        cal = per.get("calibration copy")
+        if not cal:
+            raise SystemExit("no calibration copy kernel in the counter runs (bench.py --copy-calibration)")
+        f_fetch = COPY_BYTES / float(np.mean(cal["FETCH_SIZE"]))
+        f_write = COPY_BYTES / float(np.mean(cal["WRITE_SIZE"]))
+        lines += ["", "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, KiB per "
+                      "dispatch), scaled by the counters of a plain 1 GiB copy kernel in the same runs:",
+                  f"fetch factor {f_fetch:.4f} (copy read {np.mean(cal['FETCH_SIZE']) / 2**20:.1f} MiB by "
+                  f"the counter), write factor {f_write:.4f} (copy wrote "
+                  f"{np.mean(cal['WRITE_SIZE']) / 2**20:.1f} MiB).", "",
+                  f"source digest: {source_digest(wl)}", "",
+                  "| launch | dispatches | fetch MB | write MB | operand MB (minimum) |", "|---|---|---|---|---|"]
+        ops = gemm_operand_bytes(wl)
+        tr = []
+        for site, v in sorted(per.items()):
+            if site == "calibration copy" or "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
+                continue
+            fb = float(np.mean(v["FETCH_SIZE"])) * f_fetch
+            wb = float(np.mean(v["WRITE_SIZE"])) * f_write
+            om = ops.get(site)
+            lines.append(f"| {site} | {len(v['FETCH_SIZE'])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                         f"{'' if om is None else f'{om / 1e6:.1f}'} |")
+            if site.startswith("gemm_"):
+                tr.append(f"traffic: {site} fetch={fb:.0f} write={wb:.0f}")
+        lines += ["", "Machine-readable (bytes per launch, read by bench.py while the source digest matches):",
+                  ""] + tr
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def main():
@@ -86,7 +266,16 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurement, copy 1 GiB once (a plain copy kernel of known size "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="ARG",
+                    help="OUT.md STATS_DIR [FETCH_DIR WRITE_DIR]: write the summary of rocprofv3 "
+                         "--kernel-trace --stats output (and of two --pmc runs) for --workload")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(S.WORKLOADS[args.workload], *args.rocprof_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the layer: this build runs on exactly one GPU "
               "(expert-parallel exchange across GPUs is not built); use --gpus 1", file=sys.stderr)
@@ -127,6 +316,14 @@ def main():
     kstats = B.profile_end()
     ms_per_step = elapsed * 1e3 / args.steps
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # forward alone and backward alone (events around each call)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     fwd_ms, bwd_ms = [], []
@@ -152,7 +349,7 @@ def main():
             kind, amt = work[name]
             if kind == "flop":
                 entry["tflops"] = amt / (avg * 1e-3) / 1e12
-                entry["mfma_frac"] = entry["tflops"] / PEAK_BF16_TFLOPS
+                entry["mfma_frac"] = entry["tflops"] / mfma_peak(wl)
             else:
                 entry["gbs"] = amt / (avg * 1e-3) / 1e9
                 entry["hbm_frac"] = entry["gbs"] / PEAK_HBM_GBS
@@ -161,13 +358,18 @@ def main():
     kind, amt = work[dom]
     avg = kernels[dom]["avg_ms"]
     if kind == "flop":
-        roof = {"kernel": dom, "bound": "mfma", "achieved": amt / (avg * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        bound = "mfma" if (wl.dtype == "bf16") else "alu"
+        roof = {"kernel": dom, "bound": bound, "achieved": amt / (avg * 1e-3) / 1e12,
+                "peak": mfma_peak(wl), "unit": "TFLOP/s"}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": amt / (avg * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    tr = measured_traffic(wl, dom)
+    roof["traffic"] = None if tr is None else tr["bytes"]
+    if tr is not None:
+        roof["traffic_detail"] = {**tr, "source": f"profiles/hbm_traffic_{wl.name}.md",
+                                  "algorithmic_operand_bytes": gemm_operand_bytes(wl).get(dom)}
     gemm_ms = sum(kernels[k]["avg_ms"] * kernels[k]["launches_per_step"] for k in kernels if k.startswith("gemm"))
 
     res = {
@@ -181,19 +383,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": ("fp8_e4m3 (fp32 block scales, fp32 accumulate)" if wl.precision == "fp8_block"
+                  else ("bf16" if wl.dtype == "bf16" else "f32")),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: MoE layer fwd+bwd, T={wl.T} tokens, d={wl.d}, E={wl.E}, "
                                f"top-{wl.k}, I={wl.I}, {wl.dtype}, {wl.precision}",
                    "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "I": wl.I, "precision": wl.precision},
-        "mfma_util": tflops / PEAK_BF16_TFLOPS,
+        "mfma_util": tflops / mfma_peak(wl),
         "fwd_ms": float(np.median(fwd_ms)),
         "bwd_ms": float(np.median(bwd_ms)),
         "fwd_ms_mean": float(np.mean(fwd_ms)),
         "bwd_ms_mean": float(np.mean(bwd_ms)),
         "two_fwd_plus_bwd_ms": float(2 * np.median(fwd_ms) + np.median(bwd_ms)),
         "gemm_ms_per_step": gemm_ms,
-        "gemm_mfma_util": (wl.flops_fwd() + wl.flops_bwd()) / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gemm_mfma_util": (wl.flops_fwd() + wl.flops_bwd()) / (gemm_ms * 1e-3) / 1e12 / mfma_peak(wl),
         "roofline": roof,
         "kernels": kernels,
     }

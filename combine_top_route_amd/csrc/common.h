@@ -62,9 +62,9 @@ struct LaunchCtx {
     if (_e != hipSuccess) return _e;                                               \
   } while (0)
 
-#define HIP_RET(x)                          \
+#define HIP_RET(...)                        \
   do {                                      \
-    hipError_t _r = (x);                    \
+    hipError_t _r = (__VA_ARGS__);          \
     if (_r != hipSuccess) return _r;        \
   } while (0)
 

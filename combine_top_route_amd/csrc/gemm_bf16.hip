@@ -330,11 +330,11 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
 #pragma unroll
         for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
       }
-      if (pre) {
-        if (kk == 0) { issue_part<0>(oa, kt + 1, dst, f); issue_part<0>(ob, kt + 1, dst + OA::BYTES, f); }
-        if (kk == 1) { issue_part<1>(oa, kt + 1, dst, f); issue_part<1>(ob, kt + 1, dst + OA::BYTES, f); }
-        if (kk == 2) { issue_part<2>(oa, kt + 1, dst, f); issue_part<2>(ob, kt + 1, dst + OA::BYTES, f); }
-        if (kk == 3) { issue_part<3>(oa, kt + 1, dst, f); issue_part<3>(ob, kt + 1, dst + OA::BYTES, f); }
+      if (pre && kk == 0) {
+        issue_part<0>(oa, kt + 1, dst, f); issue_part<0>(ob, kt + 1, dst + OA::BYTES, f);
+        issue_part<1>(oa, kt + 1, dst, f); issue_part<1>(ob, kt + 1, dst + OA::BYTES, f);
+        issue_part<2>(oa, kt + 1, dst, f); issue_part<2>(ob, kt + 1, dst + OA::BYTES, f);
+        issue_part<3>(oa, kt + 1, dst, f); issue_part<3>(ob, kt + 1, dst + OA::BYTES, f);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -635,6 +635,8 @@ struct WgradArgs {
 // Experts, largest first, are dealt round-robin to the 8 XCDs (work-groups
 // go to XCD bid % 8); all tiles of an expert run on one XCD, so its rows are
 // fetched into one L2.
+// TAG only tells the launch sites apart in profiles (0: down, 1: gate/up).
+template <int TAG>
 __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
@@ -692,15 +694,16 @@ hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) 
   return hipSuccess;
 }
 
+template <int TAG>
 hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p, int E) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(wgrad_kernel);
+    hipError_t e = allow_smem(wgrad_kernel<TAG>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned nblocks = (unsigned)(cdiv(E, 8) * 8 * p.m_tiles * p.n_tiles);
-  MOE_LAUNCH(c, name, wgrad_kernel, dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, wgrad_kernel<TAG>, dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
@@ -754,7 +757,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
-    err = launch_wgrad(c, "gemm_down_wgrad", p, a.E);
+    err = launch_wgrad<0>(c, "gemm_down_wgrad", p, a.E);
     if (err != hipSuccess) return err;
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
@@ -774,7 +777,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
-    err = launch_wgrad(c, "gemm_gateup_wgrad", p, a.E);
+    err = launch_wgrad<1>(c, "gemm_gateup_wgrad", p, a.E);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -415,7 +415,7 @@ moe_status moe_permute(const moe_shape* shape, const void* x, const moe_routing*
   TRY(check_aligned16(xp, "xp"));
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
-  HIP_TRY(launch_permute(c, shape->dtype, x, routing->src_of, (int)(shape->T * shape->k),
+  HIP_TRY(launch_permute(c, "permute", shape->dtype, x, routing->src_of, (int)(shape->T * shape->k),
                          (int)shape->k, (int)shape->d, xp), "permute");
   return MOE_OK;
 }

@@ -89,11 +89,16 @@ hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, in
                            int32_t* order, int32_t* blk_off);
 
 // ---------------------------------------------------------------- row passes
-hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
+hipError_t launch_permute(const LaunchCtx& c, const char* name, int dtype, const void* x,
+                          const int32_t* src_of,
                           int R, int k, int d, void* xp);
 // out[t] = sum_j (w ? w[t*k+j] : 1) * rows[row_of[t*k+j]]
 hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const void* rows,
                           const int32_t* row_of, const float* w, int T, int k, int d, void* out);
+// bf16 SwiGLU backward per row from G [R,I] and H [R,2I]: dH [R,2I] and the
+// row's top-k-weight gradient dw [R] = <G, silu(g) u>.
+hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, const float* topk_w,
+                             const int32_t* src_of, int R, int I, void* dH, float* dw);
 // d_topk_w[t,j] = sum_b dwp[row_of[t*k+j]*nblk + b]; dlogits (optional).
 hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, const int32_t* row_of,
                             const int32_t* ids, const float* w, int T, int k, int E,

@@ -434,7 +434,7 @@ __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* top
 // ===========================================================================
 // Ragged-M GEMMs: rows are an expert's segment of the expert-sorted rows.
 // ===========================================================================
-enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_DGRAD_SWIGLU = 2 };
+enum Epi { EPI_STORE = 0, EPI_GATEUP = 1 };
 enum BLay { B_MK = 0, B_MK_GATEUP = 1, B_KM = 2 };
 
 struct RowsArgs {
@@ -462,12 +462,6 @@ struct RowsArgs {
   int I;
   const float* topk_w;
   const int32_t* src_of;
-  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk] partial <G, silu(g) u> per
-  // 64 columns; dH [R,2I]; weight of row = topk_w[src_of[row]]
-  const bf16_t* Hin;
-  float* dwp;
-  int nblk;
-  bf16_t* dH;
 };
 
 template <int EPI, int BL>
@@ -553,60 +547,6 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
       barrier_lds();
       lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
-  } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] for the tile's column nt*256 + c
-    // Two rounds of 128 rows (one wave row each): H's gate and up slices of
-    // those rows come into LDS with coalesced loads, turn into dH in place,
-    // and leave with coalesced stores.
-    constexpr int HR = TBM / WM;  // rows per round
-    constexpr int S = ep_stride<TBN>();
-    constexpr int TB = HR * S;
-    lds_t* Hg = lds;
-    lds_t* Hu = lds + TB;
-    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    const int col0 = nt * TBN;
-    const int64_t ldh = 2 * (int64_t)p.I;
-    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
-    const int c0w = wn * (TBN / WN);
-#pragma unroll 1
-    for (int h = 0; h < WM; ++h) {
-      const int mh = m0 + h * HR;
-      global_to_lds<HR, TBN, S>(Hg, p.Hin + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
-      global_to_lds<HR, TBN, S>(Hu, p.Hin + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
-      __syncthreads();
-      if (wm == h) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = acc_row(i, r, lane);  // row inside this round
-            const float wr = wl[h * HR + rl];
-            float part = 0.0f;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int cl = c0w + j * 32 + (lane & 31);
-              lds_bf16_t* pg = (lds_bf16_t*)(Hg + rl * S + cl * 2);
-              lds_bf16_t* pu = (lds_bf16_t*)(Hu + rl * S + cl * 2);
-              const float G = acc[i][j][r];
-              const float g = bf2f(*pg), u = bf2f(*pu);
-              const float sg = sigmoidf_(g);
-              if (col0 + cl < p.N) part += G * (g * sg * u);  // columns past N hold stale bytes
-              const float dA = wr * G;
-              *pg = f2bf(dA * u * sg * (1.0f + g * (1.0f - sg)));
-              *pu = f2bf(dA * g * sg);
-            }
-            // partial <G, a> over this wave's 64 columns
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
-            const int row = mh + rl;
-            if ((lane & 31) == 0 && row < seg1)  // 0 when all 64 columns lie past N
-              p.dwp[(int64_t)row * p.nblk + nt * WN + wn] = part;
-          }
-      }
-      barrier_lds();
-      lds_to_global<HR, TBN, S>(Hg, p.dH + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
-      lds_to_global<HR, TBN, S>(Hu, p.dH + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
-      barrier_lds();
-    }
   }
 }
 
@@ -669,8 +609,7 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kRingBytes = (size_t)NSTAGE * (TBM + TBN) * BK * 2;
 constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
 constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
-constexpr size_t kDgradEpi = (size_t)2 * (TBM / WM) * ep_stride<TBN>() + TBM * 4;
-constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreEpi), cmax(kGateupEpi, kDgradEpi));
+constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <class K>
@@ -709,7 +648,7 @@ hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p
 
 }  // namespace
 
-int bf16_dw_blocks(int I) { return (int)cdiv(I, TBN) * WN; }
+int bf16_dw_blocks(int) { return 1; }
 
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw) {
   const int64_t I = a.I, d = a.d;
@@ -739,15 +678,18 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
                           void* dW_gu, void* dW_d) {
   const int64_t I = a.I, d = a.d;
   hipError_t err;
-  {  // down dgrad: G = dout_t W_down[e]; epilogue: dw partials, SwiGLU backward -> dH
+  {  // down dgrad: G = dout_t W_down[e] (into the dXp buffer, free until the
+     // gate/up dgrad), then the SwiGLU backward and <G, a> as a row pass
+    bf16_t* G = (bf16_t*)dXp;
     RowsArgs p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
-    p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
-    p.dwp = dwp; p.nblk = bf16_dw_blocks(a.I); p.dH = (bf16_t*)dH; p.I = a.I;
-    err = launch_rows<EPI_DGRAD_SWIGLU, B_KM>(c, "gemm_down_dgrad", p, a.R);
+    p.C = G; p.ldc = I;
+    err = launch_rows<EPI_STORE, B_KM>(c, "gemm_down_dgrad", p, a.R);
+    if (err != hipSuccess) return err;
+    err = launch_swiglu_bwd(c, G, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp);
     if (err != hipSuccess) return err;
   }
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]

@@ -315,7 +315,8 @@ struct Rows8Args {
   bf16_t* dH;
 };
 
-template <int EPI>
+// TAG only tells launch sites with the same epilogue apart in profiles.
+template <int EPI, int TAG>
 __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
@@ -475,6 +476,7 @@ struct Wgrad8Args {
   int64_t c_estride;
 };
 
+template <int TAG>
 __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
@@ -520,29 +522,30 @@ hipError_t allow_smem(K kernel) {
                              (int)kSmem);
 }
 
-template <int EPI>
+template <int EPI, int TAG>
 hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(rows8_kernel<EPI>);
+    hipError_t e = allow_smem(rows8_kernel<EPI, TAG>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
-  MOE_LAUNCH(c, name, rows8_kernel<EPI>, dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, (rows8_kernel<EPI, TAG>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
+template <int TAG>
 hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args& p) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(wgrad8_kernel);
+    hipError_t e = allow_smem(wgrad8_kernel<TAG>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned nblocks = (unsigned)(cdiv(p.E, 8) * 8 * p.m_tiles * p.n_tiles);
-  MOE_LAUNCH(c, name, wgrad8_kernel, dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, wgrad8_kernel<TAG>, dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
@@ -566,7 +569,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
-    HIP_RET(launch_rows8<EPI_GATEUP>(c, "gemm_gateup_fwd", p, a.R));
+    HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R));
   }
   HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws));
   Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
@@ -577,7 +580,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
   p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
   p.C = (bf16_t*)Yw; p.ldc = d;
   (void)err;
-  return launch_rows8<EPI_STORE>(c, "gemm_down_fwd", p, a.R);
+  return launch_rows8<EPI_STORE, 0>(c, "gemm_down_fwd", p, a.R);
 }
 
 hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
@@ -597,7 +600,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
     p.dwp = dwp; p.nblk = fp8_dw_blocks(a.I); p.dH = (bf16_t*)dH; p.I = a.I;
-    HIP_RET(launch_rows8<EPI_DGRAD_SWIGLU>(c, "gemm_down_dgrad", p, a.R));
+    HIP_RET(launch_rows8<EPI_DGRAD_SWIGLU, 0>(c, "gemm_down_dgrad", p, a.R));
   }
   HIP_RET(launch_quant_rows(c, "quant_dh", dH, 2 * I, a.R, 2 * a.I, q.dhq, q.dhs));
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
@@ -608,7 +611,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.Bs = q.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
-    HIP_RET(launch_rows8<EPI_STORE>(c, "gemm_gateup_dgrad", p, a.R));
+    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R));
   }
   const int nb = q.nblk_max;
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
@@ -621,7 +624,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN); p.E = a.E;
     p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
-    HIP_RET(launch_wgrad8(c, "gemm_down_wgrad", p));
+    HIP_RET(launch_wgrad8<0>(c, "gemm_down_wgrad", p));
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
     HIP_RET(launch_quant_tok(c, "quant_dh_tok", dH, 2 * I, nullptr, 1, 2 * a.I, a.offsets, q.blk_off,
@@ -633,7 +636,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.E = a.E; p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
-    HIP_RET(launch_wgrad8(c, "gemm_gateup_wgrad", p));
+    HIP_RET(launch_wgrad8<1>(c, "gemm_gateup_wgrad", p));
   }
   return hipSuccess;
 }

@@ -206,12 +206,63 @@ __global__ __launch_bounds__(256) void topk_grad_kernel(const float* __restrict_
   }
 }
 
+// SwiGLU backward of one row per wave, from G = dout_t W_down[e] (bf16):
+// a = silu(g) u, dw_r = <G, a> (the row's top-k-weight gradient), dA = w_r G,
+// dH = (dA u s (1 + g (1 - s)), dA silu(g)) with s = sigmoid(g).  Lane l
+// handles the 8-column chunks l, l + 64, ...; the float32 dot product is
+// reduced across the wave in a fixed order.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict__ G,
+                                                         const uint4* __restrict__ H,
+                                                         const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ src_of, int R,
+                                                         int chunks, uint4* __restrict__ dH,
+                                                         float* __restrict__ dw) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int lane = threadIdx.x & 63;
+  const float wr = topk_w[src_of[r]];
+  const uint4* Gr = G + (int64_t)r * chunks;
+  const uint4* Hg = H + (int64_t)r * 2 * chunks;
+  const uint4* Hu = Hg + chunks;
+  uint4* dg_out = dH + (int64_t)r * 2 * chunks;
+  uint4* du_out = dg_out + chunks;
+  float part = 0.0f;
+  for (int c = lane; c < chunks; c += kWave) {
+    float gv[8], g[8], u[8], dg[8], du[8];
+    unpack<bf16_t>(Gr[c], gv);
+    unpack<bf16_t>(Hg[c], g);
+    unpack<bf16_t>(Hu[c], u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = sigmoidf_(g[i]);
+      const float a = g[i] * sg * u[i];
+      part += gv[i] * a;
+      const float dA = wr * gv[i];
+      dg[i] = dA * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
+      du[i] = dA * g[i] * sg;
+    }
+    dg_out[c] = pack<bf16_t>(dg);
+    du_out[c] = pack<bf16_t>(du);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+  if (lane == 0) dw[r] = part;
+}
+
 }  // namespace
 
-hipError_t launch_permute(const LaunchCtx& c, int dtype, const void* x, const int32_t* src_of,
+hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, const float* topk_w,
+                             const int32_t* src_of, int R, int I, void* dH, float* dw) {
+  MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)G,
+             (const uint4*)H, topk_w, src_of, R, I / 8, (uint4*)dH, dw);
+  return hipSuccess;
+}
+
+hipError_t launch_permute(const LaunchCtx& c, const char* name, int dtype, const void* x,
+                          const int32_t* src_of,
                           int R, int k, int d, void* xp) {
   const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
-  MOE_LAUNCH(c, "permute", permute_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)x,
+  MOE_LAUNCH(c, name, permute_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)x,
              src_of, R, k, row_vecs, (uint4*)xp);
   return hipSuccess;
 }

@@ -43,12 +43,12 @@ KERNEL_SITES = [
     ("rows_gemm_kernel<2, 2>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2>(", "gemm_gateup_dgrad"),
     ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
     ("rows8_kernel<1, 0>(", "gemm_gateup_fwd"), ("rows8_kernel<0, 0>(", "gemm_down_fwd"),
-    ("rows8_kernel<2, 0>(", "gemm_down_dgrad"), ("rows8_kernel<0, 1>(", "gemm_gateup_dgrad"),
+    ("rows8_kernel<0, 2>(", "gemm_down_dgrad"), ("rows8_kernel<0, 1>(", "gemm_gateup_dgrad"),
     ("wgrad8_kernel<0>(", "gemm_down_wgrad"), ("wgrad8_kernel<1>(", "gemm_gateup_wgrad"),
     ("combine_wide_kernel<", "combine + reduce_dx"), ("combine_kernel<", "combine + reduce_dx"),
     ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
-    ("topk_grad_kernel", "topk_grad"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
+    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
     ("quant_weight_kernel", "quant_w_*"), ("quant_tok_kernel", "quant_*_tok"),
 ]
 # source files whose text defines each GEMM kernel (a change voids measured traffic)
@@ -93,11 +93,10 @@ def kernel_work(wl):
         q = lambda n, blk: float(n * 2 + n + 4 * n // blk)
         work.update({
             "quant_x": ("byte", q(T * d, 128)), "quant_dout": ("byte", q(T * d, 128)),
-            "quant_aw": ("byte", q(R * I, 128)), "quant_dh": ("byte", q(R * 2 * I, 128)),
-            "quant_w_gate_up": ("byte", q(E * 2 * I * d, 128 * 128)),
-            "quant_w_down": ("byte", q(E * d * I, 128 * 128)),
-            "quant_w_gate_up_t": ("byte", q(E * 2 * I * d, 128 * 128)),
-            "quant_w_down_t": ("byte", q(E * d * I, 128 * 128)),
+            "quant_aw": ("byte", q(R * I, 128)),
+            # both layouts (the transposed one is kept for the backward)
+            "quant_w_gate_up": ("byte", q(E * 2 * I * d, 128 * 128) + E * 2 * I * d + 4 * E * 2 * I * d // 16384),
+            "quant_w_down": ("byte", q(E * d * I, 128 * 128) + E * d * I + 4 * E * d * I // 16384),
             "quant_dout_tok": ("byte", q(R * d, 128) + 4 * R), "quant_x_tok": ("byte", q(R * d, 128) + 4 * R),
             "quant_aw_tok": ("byte", q(R * I, 128)), "quant_dh_tok": ("byte", q(R * 2 * I, 128)),
         })

@@ -128,7 +128,7 @@ struct Layout {
   size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
   // fp8: quantised operands (q) and their scales (s)
   size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
-  size_t doutq = 0, douts = 0, wdtq = 0, wdts = 0, wgutq = 0, wguts = 0, dhq = 0, dhs = 0;
+  size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
   size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0;
   size_t total = 0;
 };
@@ -176,10 +176,6 @@ Layout layout(const moe_shape* s, int op) {
       const int64_t nb = nblk_max(s);
       L.doutq = take(T * d);
       L.douts = take(f * T * (d / 128));
-      L.wdtq = take(E * I * d);
-      L.wdts = take(f * E * (I / 128) * (d / 128));
-      L.wgutq = take(E * d * 2 * I);
-      L.wguts = take(f * E * (d / 128) * (2 * I / 128));
       L.dhq = take(R * 2 * I);
       L.dhs = take(f * R * (2 * I / 128));
       const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;
@@ -191,6 +187,47 @@ Layout layout(const moe_shape* s, int op) {
   }
   L.total = off;
   return L;
+}
+
+// `saved`: H [R,2I] then Aw [R,I] (dtype); for fp8 also the transposed weight
+// codes and scales the backward's dgrads read.
+struct SavedLayout {
+  size_t H = 0, A = 0, wgutq = 0, wdtq = 0, wguts = 0, wdts = 0, total = 0;
+};
+
+SavedLayout saved_layout(const moe_shape* s) {
+  SavedLayout L;
+  const int64_t R = s->T * s->k, d = s->d, I = s->I, E = s->E;
+  const size_t es = elem_size(s->dtype);
+  L.H = 0;
+  L.A = es * R * 2 * I;
+  size_t off = L.A + es * R * I;
+  if (is_fp8(s)) {
+    auto take = [&](size_t bytes) {
+      off = align256(off);
+      const size_t o = off;
+      off += bytes;
+      return o;
+    };
+    L.wgutq = take(E * d * 2 * I);
+    L.wdtq = take(E * I * d);
+    L.wguts = take(sizeof(float) * E * (d / 128) * (2 * I / 128));
+    L.wdts = take(sizeof(float) * E * (I / 128) * (d / 128));
+  }
+  L.total = off;
+  return L;
+}
+
+Fp8Saved fp8_saved(const moe_shape* s, const void* saved) {
+  Fp8Saved v = {};
+  if (!saved) return v;
+  const SavedLayout L = saved_layout(s);
+  char* b = (char*)saved;
+  v.wgutq = (uint8_t*)(b + L.wgutq);
+  v.wdtq = (uint8_t*)(b + L.wdtq);
+  v.wguts = (float*)(b + L.wguts);
+  v.wdts = (float*)(b + L.wdts);
+  return v;
 }
 
 moe_status check_routing(const moe_routing* r, bool need_all) {
@@ -279,7 +316,7 @@ moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes) {
   TRY(check_shape(shape));
   CHECK_PTR(bytes);
-  *bytes = elem_size(shape->dtype) * (size_t)(shape->T * shape->k) * 3 * (size_t)shape->I;
+  *bytes = saved_layout(shape).total;
   return MOE_OK;
 }
 
@@ -328,6 +365,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
     q.wguq = (uint8_t*)at(workspace, L.wguq); q.wgus = (float*)at(workspace, L.wgus);
     q.wdq = (uint8_t*)at(workspace, L.wdq); q.wds = (float*)at(workspace, L.wds);
     q.awq = (uint8_t*)at(workspace, L.awq); q.aws = (float*)at(workspace, L.aws);
+    q.sv = fp8_saved(shape, saved);
     HIP_TRY(fp8_fwd_gemms(c, a, q, H, A, Y), "forward GEMMs");
   } else {
     HIP_TRY(bf16_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
@@ -386,8 +424,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   else if (is_fp8(shape)) {
     Fp8Bwd q;
     q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = (float*)at(workspace, L.douts);
-    q.wdtq = (uint8_t*)at(workspace, L.wdtq); q.wdts = (float*)at(workspace, L.wdts);
-    q.wgutq = (uint8_t*)at(workspace, L.wgutq); q.wguts = (float*)at(workspace, L.wguts);
+    q.sv = fp8_saved(shape, saved);
     q.dhq = (uint8_t*)at(workspace, L.dhq); q.dhs = (float*)at(workspace, L.dhs);
     q.tqa = (uint8_t*)at(workspace, L.tqa); q.tsa = (float*)at(workspace, L.tsa);
     q.tqb = (uint8_t*)at(workspace, L.tqb); q.tsb = (float*)at(workspace, L.tsb);
@@ -462,9 +499,12 @@ moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, i
   (void)hipGetLastError();
   if (kind == MOE_QUANT_ROWS)
     HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s), "quant_rows");
+  else if (kind == MOE_QUANT_WEIGHT)
+    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, q, s, nullptr,
+                                nullptr), "quant_weight");
   else
-    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2,
-                                kind == MOE_QUANT_WEIGHT_T, q, s), "quant_weight");
+    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, nullptr, nullptr,
+                                q, s), "quant_weight");
   return MOE_OK;
 }
 

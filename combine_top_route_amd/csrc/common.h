@@ -149,25 +149,36 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                              int64_t rows, int C, uint8_t* q, float* s);
 hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
-                               int K, bool transpose, uint8_t* q, float* s);
+                               int K, uint8_t* q, float* s, uint8_t* qt, float* st);
 hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                             const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
                             const int32_t* blk_off, int E, int nblk_max, uint8_t* q, float* s);
 
+// fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd, plus dH's 1x128
+// e4m3 codes dhq [R,2I] and scales dhs [R,2I/128] (I % 128 == 0).
+hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const void* G, const void* H,
+                                 const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
+                                 float* dw, uint8_t* dhq, float* dhs);
+
+// Transposed weight codes the fp8 forward leaves in `saved` for the backward.
+struct Fp8Saved {
+  uint8_t* wdtq; float* wdts;    // [E,I,d], [E,I/128,d/128]
+  uint8_t* wgutq; float* wguts;  // [E,d,2I], [E,d/128,2I/128]
+};
 // Workspace of the fp8 forward: quantised x, weights and Aw with their scales.
 struct Fp8Fwd {
   uint8_t* xq; float* xs;      // [T,d], [T,d/128]
   uint8_t* wguq; float* wgus;  // [E,2I,d], [E,2I/128,d/128]
   uint8_t* wdq; float* wds;    // [E,d,I], [E,d/128,I/128]
   uint8_t* awq; float* aws;    // [R,I], [R,I/128]
+  Fp8Saved sv;                 // written when saving for the backward (else null)
 };
 // Workspace of the fp8 backward.  tqa/tsa and tqb/tsb hold the two
 // token-blocked operands of one weight gradient at a time
 // ([max(d,2I)] and [max(I,d)] rows of 128 nblk_max bytes).
 struct Fp8Bwd {
   uint8_t* doutq; float* douts;  // [T,d], [T,d/128]
-  uint8_t* wdtq; float* wdts;    // [E,I,d], [E,I/128,d/128]
-  uint8_t* wgutq; float* wguts;  // [E,d,2I], [E,d/128,2I/128]
+  Fp8Saved sv;                   // from the forward's saved buffer
   uint8_t* dhq; float* dhs;      // [R,2I], [R,2I/128]
   uint8_t* tqa; float* tsa;
   uint8_t* tqb; float* tsb;

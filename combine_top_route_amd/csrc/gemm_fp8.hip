@@ -101,9 +101,8 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 // 4-7 the feature rows' (rows 64(w-4) ..); sp is the lane's source at the
 // current stage, advanced by one float per K step.
 
-// Issues the next stage's loads of both operands spread over the sub-steps:
-// sub-step i < 8 issues token-operand instruction i / 2 (even i) or
-// feature-operand instruction i / 2 (odd i); sub-step 0 adds the scales.
+// Part I of a stage's loads: token-operand instruction I / 2 (even I) or
+// feature-operand instruction I / 2 (odd I); part 0 adds the scales.
 template <int I>
 __device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const float* sp, lds_t* dst) {
   constexpr int q = I / 2;
@@ -124,7 +123,11 @@ __device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const floa
                                         const i32x8_t (&f)[TN], const i32x8_t& t,
                                         const lds_f32_t* SAw, float& sa, const f32x4_t (&sb)[TN],
                                         f32x4_t (&acc)[TM][TN]) {
-  if constexpr (PRE) issue_step<I>(ot, of, sp, dst);
+  if constexpr (PRE && I == 0) {  // the whole next stage leaves at the start of the step
+    issue_step<0>(ot, of, sp, dst); issue_step<1>(ot, of, sp, dst); issue_step<2>(ot, of, sp, dst);
+    issue_step<3>(ot, of, sp, dst); issue_step<4>(ot, of, sp, dst); issue_step<5>(ot, of, sp, dst);
+    issue_step<6>(ot, of, sp, dst); issue_step<7>(ot, of, sp, dst);
+  }
   const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -276,7 +279,7 @@ __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* top
 // ===========================================================================
 // Ragged-row GEMMs: token rows are an expert's segment of the sorted rows.
 // ===========================================================================
-enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_DGRAD_SWIGLU = 2 };
+enum Epi { EPI_STORE = 0, EPI_GATEUP = 1 };
 
 struct Rows8Args {
   // token side: row r reads A + arow(r) * lda, arow = a_src ? a_src[r] / a_div : r;
@@ -308,11 +311,6 @@ struct Rows8Args {
   int I;
   const float* topk_w;
   const int32_t* src_of;
-  // EPI_DGRAD_SWIGLU: Hin [R,2I]; dwp [R, nblk]; dH [R,2I]
-  const bf16_t* Hin;
-  float* dwp;
-  int nblk;
-  bf16_t* dH;
 };
 
 // TAG only tells launch sites with the same epilogue apart in profiles.
@@ -391,69 +389,6 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
       barrier_lds();
       lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
-  } else {  // EPI_DGRAD_SWIGLU: acc = G = dout_t W_down[e] at feature column nt*256 + c
-    constexpr int HR = TBM / WM;
-    constexpr int S = ep_stride<TBN>();
-    constexpr int TB = HR * S;
-    lds_t* Hg = lds;
-    lds_t* Hu = lds + TB;
-    lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    const int col0 = nt * TBN;
-    const int64_t ldh = 2 * (int64_t)p.I;
-    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
-    const int c0w = wn * (TBN / WN);
-#pragma unroll 1
-    for (int h = 0; h < WM; ++h) {
-      const int mh = m0 + h * HR;
-      global_to_lds<HR, TBN, S>(Hg, p.Hin + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
-      global_to_lds<HR, TBN, S>(Hu, p.Hin + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
-      __syncthreads();
-      if (wm == h) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int rl = i * 16 + (lane & 15);
-          const float wr = wl[h * HR + rl];
-          float part = 0.0f;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int cl = c0w + j * 16 + 4 * (lane >> 4);
-            auto* pg = (__attribute__((address_space(3))) u32x2_t*)(Hg + rl * S + cl * 2);
-            auto* pu = (__attribute__((address_space(3))) u32x2_t*)(Hu + rl * S + cl * 2);
-            const u32x2_t gw = *pg, uw = *pu;
-            const bool in = col0 + cl < p.N;  // columns past N hold stale bytes
-            float dg[4], du[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t gb = gw[r >> 1], ub = uw[r >> 1];
-              const float g = __uint_as_float((r & 1) ? (gb & 0xFFFF0000u) : (gb << 16));
-              const float u = __uint_as_float((r & 1) ? (ub & 0xFFFF0000u) : (ub << 16));
-              const float G = acc[i][j][r];
-              const float sg = sigmoidf_(g);
-              if (in) part += G * (g * sg * u);
-              const float dA = wr * G;
-              dg[r] = dA * u * sg * (1.0f + g * (1.0f - sg));
-              du[r] = dA * g * sg;
-            }
-            u32x2_t og, ou;
-            og[0] = pack_bf16x2(dg[0], dg[1]);
-            og[1] = pack_bf16x2(dg[2], dg[3]);
-            ou[0] = pack_bf16x2(du[0], du[1]);
-            ou[1] = pack_bf16x2(du[2], du[3]);
-            *pg = og;
-            *pu = ou;
-          }
-          // partial <G, a> of the row over this wave's 64 columns
-          part += __shfl_xor(part, 16, kWave);
-          part += __shfl_xor(part, 32, kWave);
-          const int row = mh + rl;
-          if ((lane >> 4) == 0 && row < seg1) p.dwp[(int64_t)row * p.nblk + nt * WN + wn] = part;
-        }
-      }
-      barrier_lds();
-      lds_to_global<HR, TBN, S>(Hg, p.dH + (int64_t)mh * ldh + col0, ldh, seg1 - mh, p.N - col0);
-      lds_to_global<HR, TBN, S>(Hu, p.dH + (int64_t)mh * ldh + p.I + col0, ldh, seg1 - mh, p.N - col0);
-      barrier_lds();
-    }
   }
 }
 
@@ -512,8 +447,7 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kRingBytes = (size_t)2 * STB;
 constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
 constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
-constexpr size_t kDgradEpi = (size_t)2 * (TBM / WM) * ep_stride<TBN>() + TBM * 4;
-constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreEpi), cmax(kGateupEpi, kDgradEpi));
+constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <class K>
@@ -551,15 +485,18 @@ hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args&
 
 }  // namespace
 
-int fp8_dw_blocks(int I) { return (int)cdiv(I, TBN) * WN; }
+int fp8_dw_blocks(int) { return 1; }
 
 hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q, void* H, void* Aw,
                          void* Yw) {
   const int64_t I = a.I, d = a.d;
   hipError_t err;
   HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs));
-  HIP_RET(launch_quant_weight(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, false, q.wguq, q.wgus));
-  HIP_RET(launch_quant_weight(c, "quant_w_down", a.w_down, a.E, a.d, a.I, false, q.wdq, q.wds));
+  // both layouts in one pass: the transposed codes serve the backward's dgrads
+  HIP_RET(launch_quant_weight(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, q.wguq, q.wgus,
+                              q.sv.wgutq, q.sv.wguts));
+  HIP_RET(launch_quant_weight(c, "quant_w_down", a.w_down, a.E, a.d, a.I, q.wdq, q.wds, q.sv.wdtq,
+                              q.sv.wdts));
   {  // gate/up GEMM on token rows gathered from xq; SwiGLU and top-k weight in the epilogue
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
@@ -588,27 +525,24 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
                          void* dW_d) {
   const int64_t I = a.I, d = a.d;
   HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts));
-  HIP_RET(launch_quant_weight(c, "quant_w_down_t", a.w_down, a.E, a.d, a.I, true, q.wdtq, q.wdts));
-  HIP_RET(launch_quant_weight(c, "quant_w_gate_up_t", a.w_gate_up, a.E, 2 * a.I, a.d, true, q.wgutq,
-                              q.wguts));
-  {  // down dgrad: G = dout_t W_down[e]; epilogue: dw partials, SwiGLU backward -> dH
+  {  // down dgrad: G = dout_t W_down[e] into the dXp buffer (free until the
+     // gate/up dgrad); one row pass then forms dH, <G, a> and dH's 1x128 codes
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.douts; p.a_sld = d / 128;
-    p.B = q.wdtq; p.b_estride = I * d; p.ldb = d;
-    p.Bs = q.wdts; p.bs_estride = (I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 0;
+    p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
+    p.Bs = q.sv.wdts; p.bs_estride = (I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 0;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
-    p.Hin = (const bf16_t*)H; p.topk_w = a.topk_w; p.src_of = a.src_of;
-    p.dwp = dwp; p.nblk = fp8_dw_blocks(a.I); p.dH = (bf16_t*)dH; p.I = a.I;
-    HIP_RET(launch_rows8<EPI_DGRAD_SWIGLU, 0>(c, "gemm_down_dgrad", p, a.R));
+    p.C = (bf16_t*)dXp; p.ldc = I;
+    HIP_RET(launch_rows8<EPI_STORE, 2>(c, "gemm_down_dgrad", p, a.R));
+    HIP_RET(launch_swiglu_bwd_fp8(c, dXp, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp, q.dhq, q.dhs));
   }
-  HIP_RET(launch_quant_rows(c, "quant_dh", dH, 2 * I, a.R, 2 * a.I, q.dhq, q.dhs));
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
     p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1; p.As = q.dhs; p.a_sld = 2 * I / 128;
-    p.B = q.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
-    p.Bs = q.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;
+    p.B = q.sv.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
+    p.Bs = q.sv.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
     HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R));

@@ -88,63 +88,72 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// 128 x 128 weight blocks: W [E, N, K] -> q [E, N, K], s [E, N/128, K/128], or
-// (transpose) q [E, K, N], s [E, K/128, N/128].  One work-group per block.
+// 128 x 128 weight blocks of W [E, N, K], written as q [E, N, K] with s [E,
+// N/128, K/128] and/or transposed as qt [E, K, N] with st [E, K/128, N/128]
+// (either pair may be null).  One work-group per block; thread t holds rows
+// 4 (t % 32) .. +3 and columns 16 (t / 32) .. +15 of it.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restrict__ W, int N, int K,
-                                                          int transpose, uint8_t* __restrict__ q,
-                                                          float* __restrict__ s) {
+                                                          uint8_t* __restrict__ q, float* __restrict__ s,
+                                                          uint8_t* __restrict__ qt,
+                                                          float* __restrict__ st) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t tr[128 * 144];  // [k][n] codes, 144-byte rows
+  __shared__ __attribute__((aligned(16))) uint32_t codes[128 * 33];  // [n][32 words], padded
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
-  const int ch = t & 15;  // 8-element chunk along K
-  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128 + ch * 8;
-  u32x4_t v[8];
+  const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
+  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128 + n0) * K + kb * 128 + k0;
+  float f[4][16];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) v[p] = *(const u32x4_t*)(Wb + (int64_t)((t >> 4) + 16 * p) * K);
+  for (int j = 0; j < 4; ++j) {
+    float lo[8], hi[8];
+    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K), lo);
+    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K + 8), hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[j][i] = lo[i];
+      f[j][8 + i] = hi[i];
+    }
+  }
   float amax = 0.0f;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    float f[8];
-    unpack8(v[p], f);
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  }
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   const float sc = block_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
   const int nbn = N / 128, nbk = K / 128;
-  if (!transpose) {
-    uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128 + ch * 8;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      float f[8];
-      unpack8(v[p], f);
-      *(u32x2_t*)(qb + (int64_t)((t >> 4) + 16 * p) * K) = quant8(f, sc);
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[j][i] = __fdiv_rn(f[j][i], sc);
+  if (qt) {  // a transposed row gets four consecutive codes from each of 32 lanes
+    uint8_t* qb = qt + (int64_t)e * K * N + (int64_t)(kb * 128 + k0) * N + nb * 128 + n0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *(uint32_t*)(qb + (int64_t)i * N) = e4m3x4(f[0][i], f[1][i], f[2][i], f[3][i]);
+    if (t == 0) st[((int64_t)e * nbk + kb) * nbn + nb] = sc;
+  }
+  if (q) {  // rows go through LDS so that each row leaves as 128 contiguous bytes
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        codes[(n0 + j) * 33 + (k0 >> 2) + w] =
+            e4m3x4(f[j][4 * w], f[j][4 * w + 1], f[j][4 * w + 2], f[j][4 * w + 3]);
+    __syncthreads();
+    uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int idx = p * 256 + t;  // word idx % 32 of row idx / 32
+      const int n = idx >> 5, w = idx & 31;
+      *(uint32_t*)(qb + (int64_t)n * K + 4 * w) = codes[n * 33 + w];
     }
     if (t == 0) s[((int64_t)e * nbn + nb) * nbk + kb] = sc;
-    return;
   }
-  // transposed: codes go through LDS as [k][n], then out as 64-byte row pieces
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    float f[8];
-    unpack8(v[p], f);
-    const u32x2_t c = quant8(f, sc);
-    const int n = (t >> 4) + 16 * p;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tr[(ch * 8 + i) * 144 + n] = (uint8_t)(c[i >> 2] >> (8 * (i & 3)));
-  }
-  __syncthreads();
-  const int k = t >> 1, half = t & 1;
-  uint8_t* qt = q + (int64_t)e * K * N + (int64_t)(kb * 128 + k) * N + nb * 128 + half * 64;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(u32x4_t*)(qt + i * 16) = *(const u32x4_t*)(tr + k * 144 + half * 64 + i * 16);
-  if (t == 0) s[((int64_t)e * nbk + kb) * nbn + nb] = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -224,7 +233,88 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
   }
 }
 
+// SwiGLU backward of one row per wave from G = dout_t W_down[e] (bf16), as
+// in the bf16 path, that also encodes the bf16-rounded dH in 1 x 128 blocks
+// (the A operand of the gate/up dgrad).  Lane l handles the 8-column chunks
+// l, l + 64, ... of the gate and of the up half; a 16-lane group covers one
+// 128-column block.  Requires I % 128 == 0.
+__global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
+    const u32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ src_of, int R, int chunks, u32x4_t* __restrict__ dH,
+    float* __restrict__ dw, uint8_t* __restrict__ dhq, float* __restrict__ dhs) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int lane = threadIdx.x & 63;
+  const float wr = topk_w[src_of[r]];
+  const u32x4_t* Gr = G + (int64_t)r * chunks;
+  const u32x4_t* Hg = H + (int64_t)r * 2 * chunks;
+  u32x4_t* Dr = dH + (int64_t)r * 2 * chunks;
+  uint8_t* Qr = dhq + (int64_t)r * 2 * chunks * 8;
+  float* Sr = dhs + (int64_t)r * (2 * chunks / 16);
+  float part = 0.0f;
+  for (int c0 = 0; c0 < chunks; c0 += kWave) {  // uniform trip count
+    const int c = c0 + lane;
+    const bool ok = c < chunks;  // whole 16-lane groups share ok (chunks % 16 == 0)
+    float gv[8], g[8], u[8], dg[8], du[8];
+    u32x4_t zero = {0, 0, 0, 0};
+    unpack8(ok ? Gr[c] : zero, gv);
+    unpack8(ok ? Hg[c] : zero, g);
+    unpack8(ok ? Hg[chunks + c] : zero, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = sigmoidf_(g[i]);
+      part += gv[i] * (g[i] * sg * u[i]);
+      const float dA = wr * gv[i];
+      dg[i] = dA * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
+      du[i] = dA * g[i] * sg;
+    }
+    // bf16 rounding first: the codes encode the stored dH
+    u32x4_t pg, pu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pg[i] = pack_bf16x2(dg[2 * i], dg[2 * i + 1]);
+      pu[i] = pack_bf16x2(du[2 * i], du[2 * i + 1]);
+    }
+    unpack8(pg, dg);
+    unpack8(pu, du);
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ag = fmaxf(ag, fabsf(dg[i]));
+      au = fmaxf(au, fabsf(du[i]));
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
+      au = fmaxf(au, __shfl_xor(au, off, kWave));
+    }
+    const float sgate = block_scale(ag), sup = block_scale(au);
+    if (ok) {
+      Dr[c] = pg;
+      Dr[chunks + c] = pu;
+      *(u32x2_t*)(Qr + c * 8) = quant8(dg, sgate);
+      *(u32x2_t*)(Qr + (chunks + c) * 8) = quant8(du, sup);
+      if ((lane & 15) == 0) {
+        Sr[c / 16] = sgate;
+        Sr[(chunks + c) / 16] = sup;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+  if (lane == 0) dw[r] = part;
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const void* G, const void* H,
+                                 const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
+                                 float* dw, uint8_t* dhq, float* dhs) {
+  MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel, dim3((R + 3) / 4), dim3(256), 0,
+             (const u32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
+             dhs);
+  return hipSuccess;
+}
 
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                              int64_t rows, int C, uint8_t* q, float* s) {
@@ -236,9 +326,9 @@ hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* s
 }
 
 hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
-                               int K, bool transpose, uint8_t* q, float* s) {
+                               int K, uint8_t* q, float* s, uint8_t* qt, float* st) {
   MOE_LAUNCH(c, name, quant_weight_kernel, dim3(K / 128, N / 128, E), dim3(256), 0,
-             (const bf16_t*)W, N, K, transpose ? 1 : 0, q, s);
+             (const bf16_t*)W, N, K, q, s, qt, st);
   return hipSuccess;
 }
 

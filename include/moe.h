@@ -111,7 +111,9 @@ moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 /* Bytes of the `saved` buffer written by moe_forward and read by
  * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
  * Aw [T*k, I] (SwiGLU output times the row's top-k weight), both in dtype,
- * in expert-sorted row order. */
+ * in expert-sorted row order.  With MOE_PREC_FP8_BLOCK the buffer also holds
+ * the transposed e4m3 weight codes and scales that the backward's data
+ * gradients use (both weights are quantised once, in the forward). */
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
 
 /* Routing only: top-k (when logits != NULL), per-expert counts and offsets,

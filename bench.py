@@ -39,8 +39,8 @@ CSRC = os.path.join(HERE, "combine_top_route_amd", "csrc")
 
 # rocprofv3 kernel name (template instance) -> the library's launch name
 KERNEL_SITES = [
-    ("rows_gemm_kernel<1, 1>(", "gemm_gateup_fwd"), ("rows_gemm_kernel<0, 0>(", "gemm_down_fwd"),
-    ("rows_gemm_kernel<2, 2>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2>(", "gemm_gateup_dgrad"),
+    ("rows_gemm_kernel<1, 1, 0>(", "gemm_gateup_fwd"), ("rows_gemm_kernel<0, 0, 0>(", "gemm_down_fwd"),
+    ("rows_gemm_kernel<0, 2, 1>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2, 0>(", "gemm_gateup_dgrad"),
     ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
     ("rows8_kernel<1, 0>(", "gemm_gateup_fwd"), ("rows8_kernel<0, 0>(", "gemm_down_fwd"),
     ("rows8_kernel<0, 2>(", "gemm_down_dgrad"), ("rows8_kernel<0, 1>(", "gemm_gateup_dgrad"),
@@ -162,6 +162,8 @@ def cpu_baseline(wl, inp: dict, tokens: int):
 
 
 COPY_BYTES = 1 << 30
+# oracle sample per workload: about 10-30 s of float64 numpy on 16 host cores
+CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q235b": 8192, "fp8_skew": 2048}
 
 
 def gemm_operand_bytes(wl):
@@ -263,7 +265,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="q30b", choices=sorted(S.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the oracle's CPU sample (default: sized for roughly 10-30 s)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 1 GiB once (a plain copy kernel of known size "
@@ -400,7 +403,8 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, wl.T))
+        n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(wl.name, wl.T)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, min(n, wl.T))
     print(json.dumps(res), flush=True)
 
 

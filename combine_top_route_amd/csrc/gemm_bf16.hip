@@ -7,9 +7,9 @@
 // intermediates out of separate passes ("Prime Intellect's Prime Mega MoE
 // Trains Giant AI Models 55% Faster", section "One kernel overlaps the
 // pipeline"): the token gather is the A-operand load of the gate/up GEMM,
-// SwiGLU and the top-k weighting are its epilogue, and the SwiGLU backward
-// plus the top-k-weight partial dot products are the epilogue of the down
-// dgrad GEMM.
+// and SwiGLU and the top-k weighting are its epilogue.  (The SwiGLU backward
+// is a separate row pass after the down dgrad: fused into that epilogue it
+// cost more than the HBM traffic it saved.)
 //
 // Tile engine (all six GEMMs): C[m,n] = sum_k A(m,k) B(n,k) on a 256x256
 // output tile, K in steps of 64, eight waves (two per SIMD) of 128x64, each
@@ -17,10 +17,11 @@
 // a CU sustains roughly 30 bytes/clock of global->LDS traffic with eight
 // waves, and a 256x256x64 step moves 64 KB per 2048 MFMA cycles (32 B/clk).
 // Operands move global -> LDS with direct loads (global_load_lds_dwordx4, no
-// register staging) into a two-stage ring: the loads of step k+1 are in
-// flight while the MFMAs consume step k - for the gate/up GEMM those are the
-// gathered token rows of the next K slice, the one-GPU analogue of computing
-// on one token group while the next one moves.  One barrier per K step.
+// register staging) into a two-stage ring: all loads of step k+1 leave at
+// the start of step k and are in flight while the MFMAs consume step k - for
+// the gate/up GEMM those are the gathered token rows of the next K slice, the
+// one-GPU analogue of computing on one token group while the next one moves.
+// One barrier per K step.
 //
 // LDS layouts: an operand whose rows are K-contiguous in memory is stored
 // [row][64 k] and read with ds_read_b128; an operand whose rows are contiguous
@@ -464,7 +465,9 @@ struct RowsArgs {
   const int32_t* src_of;
 };
 
-template <int EPI, int BL>
+// TAG only tells launch sites with the same epilogue and B layout apart in
+// profiles.
+template <int EPI, int BL, int TAG>
 __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
@@ -618,18 +621,18 @@ hipError_t allow_smem(K kernel) {
                              (int)kSmem);
 }
 
-template <int EPI, int BL>
+template <int EPI, int BL, int TAG = 0>
 hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(rows_gemm_kernel<EPI, BL>);
+    hipError_t e = allow_smem(rows_gemm_kernel<EPI, BL, TAG>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   // upper bound of the tile count (the kernel reads the exact one)
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
-  MOE_LAUNCH(c, name, (rows_gemm_kernel<EPI, BL>), dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, (rows_gemm_kernel<EPI, BL, TAG>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
@@ -687,7 +690,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.C = G; p.ldc = I;
-    err = launch_rows<EPI_STORE, B_KM>(c, "gemm_down_dgrad", p, a.R);
+    err = launch_rows<EPI_STORE, B_KM, 1>(c, "gemm_down_dgrad", p, a.R);
     if (err != hipSuccess) return err;
     err = launch_swiglu_bwd(c, G, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp);
     if (err != hipSuccess) return err;

@@ -78,11 +78,15 @@ def test_layer_parity_q30b_t4096():
     print(errs)
 
 
-def test_layer_parity_q30b_full_size_sampled():
-    """Qwen3-30B-A3B layer shape at 16,384 tokens in the benchmark's launch
-    configuration: all routing artefacts bit-exact; out, dx, top-k-weight and
-    logit gradients on sampled tokens; weight gradients of sampled experts."""
-    wl = S.WORKLOADS["q30b"]
+@pytest.mark.parametrize("name", ["q30b", "q235b"])
+def test_layer_parity_full_size_sampled(name):
+    """Qwen3-30B-A3B and Qwen3-235B-A22B layer shapes at 16,384 tokens in the
+    benchmark's launch configuration: all routing artefacts bit-exact; out,
+    dx, top-k-weight and logit gradients on sampled tokens; weight gradients
+    of expert 0 and of the busiest expert (q30b) or a median one (q235b,
+    whose busiest expert is too large for the float64 oracle in a test)."""
+    wl = S.WORKLOADS[name]
+    print(f"case {name}: {wl}", flush=True)
     inp = S.make_inputs(wl, seed=0)
     gpu = run_gpu(wl, inp)
     lg = inp["logits"].double().numpy()
@@ -96,8 +100,9 @@ def test_layer_parity_q30b_full_size_sampled():
     for n in ("out", "dx", "d_topk_w", "dlogits"):
         e = rel_err(gpu[n][toks], s[n])
         assert e <= TOL["bf16"], (n, e)
-    hot = int(np.argmax(rt["counts"]))
-    for e in (0, hot):
+    c = rt["counts"]
+    other = int(np.argmax(c)) if name == "q30b" else int(np.argsort(c)[len(c) // 2])
+    for e in (0, other):
         dgu, dd = O.expert_weight_grads(x, dout, rt, Wgu, Wd, e)
         assert rel_err(gpu["dW_gate_up"][e], dgu) <= TOL["bf16"]
         assert rel_err(gpu["dW_down"][e], dd) <= TOL["bf16"]

@@ -123,7 +123,7 @@ int64_t nblk_max(const moe_shape* s) { return cdiv(s->T * s->k, kTokBlock) + s->
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0;  // routing / schedule
+  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0, tiles = 0;  // routing / schedule
   size_t Y = 0, A = 0, H = 0;                             // forward
   size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
   // fp8: quantised operands (q) and their scales (s)
@@ -147,6 +147,7 @@ Layout layout(const moe_shape* s, int op) {
   L.tile_off = take(sizeof(int32_t) * (s->E + 1));
   L.order = take(sizeof(int32_t) * s->E);
   L.blk_off = take(sizeof(int32_t) * (s->E + 1));
+  L.tiles = take(sizeof(int4) * max_row_tiles(R, s->E));
   if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
   if (op == MOE_OP_FORWARD) {
     L.Y = take(es * R * s->d);
@@ -297,6 +298,7 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   a.src_of = r->src_of;
   a.row_of = r->row_of;
   a.tile_off = (const int32_t*)at(ws, L.tile_off);
+  a.tiles = (const int4*)at(ws, L.tiles);
   a.order = (const int32_t*)at(ws, L.order);
   return a;
 }
@@ -350,7 +352,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   (void)hipGetLastError();
   TRY(run_route(shape, routing, workspace, L, c));
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order), nullptr), "route_schedule");
+                          (int32_t*)at(workspace, L.order), nullptr, (int4*)at(workspace, L.tiles)),
+          "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
   const int64_t R = shape->T * shape->k;
@@ -408,7 +411,8 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   (void)hipGetLastError();
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
                           (int32_t*)at(workspace, L.order),
-                          is_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr),
+                          is_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr,
+                          (int4*)at(workspace, L.tiles)),
           "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
@@ -529,7 +533,7 @@ moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int6
   (void)hipGetLastError();
   int32_t* blk_off = (int32_t*)at(workspace, L.blk_off);
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order), blk_off), "route_schedule");
+                          (int32_t*)at(workspace, L.order), blk_off, nullptr), "route_schedule");
   HIP_TRY(launch_quant_tok(c, "quant_tokens", src, C, gather ? routing->src_of : nullptr,
                            (int)shape->k, (int)C, routing->offsets, blk_off, (int)shape->E,
                            (int)nblk_max(shape), q, s), "quant_tokens");

@@ -85,8 +85,12 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
 // when blk_off is not null, blk_off [E+1] (runs of kTokBlock rows per expert,
 // prefix-summed: the token blocks of the fp8 weight-gradient operands).
 constexpr int kTokBlock = 128;
+// tiles (optional) [tile_off[E]]: per row tile {expert, first row, end of the
+// expert's segment, 0}.
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order, int32_t* blk_off);
+                           int32_t* order, int32_t* blk_off, int4* tiles);
+// Upper bound of the row-tile count.
+inline int64_t max_row_tiles(int64_t R, int64_t E) { return R / kRowTile + E; }
 
 // ---------------------------------------------------------------- row passes
 hipError_t launch_permute(const LaunchCtx& c, const char* name, int dtype, const void* x,
@@ -116,6 +120,7 @@ struct LayerArgs {
   const int32_t* src_of;
   const int32_t* row_of;
   const int32_t* tile_off;  // [E+1], kRowTile tiles
+  const int4* tiles;        // [tile_off[E]] row-tile descriptors
   const int32_t* order;     // [E]
 };
 

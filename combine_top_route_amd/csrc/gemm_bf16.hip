@@ -453,6 +453,7 @@ struct RowsArgs {
   int N, K, n_tiles;  // N: output columns (gate/up: gate columns I)
   const int32_t* offsets;
   const int32_t* tile_off;
+  const int4* tiles;  // row-tile descriptors {expert, first row, segment end, 0}
   int E;
   // EPI_STORE: C [R, ldc]
   bf16_t* C;
@@ -473,10 +474,9 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
   if (L < 0) return;
   const int nt = L % p.n_tiles;
-  const int mt = L / p.n_tiles;
-  const int e = find_expert(p.tile_off, p.E, mt);
-  const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-  const int m0 = seg0 + (mt - p.tile_off[e]) * TBM;
+  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
+  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+  const int seg0 = m0;  // rows past the segment repeat the tile's first row
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
 
@@ -657,7 +657,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
   const int64_t I = a.I, d = a.d;
   {  // gate/up GEMM: token rows gathered from x; SwiGLU and top-k weight in the epilogue
     RowsArgs p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = (const bf16_t*)a.x; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
@@ -668,7 +668,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
   }
   // down GEMM: Yw = Aw W_down[e]^T (rows already carry their top-k weight)
   RowsArgs q = {};
-  q.offsets = a.offsets; q.tile_off = a.tile_off; q.E = a.E;
+  q.offsets = a.offsets; q.tile_off = a.tile_off; q.tiles = a.tiles; q.E = a.E;
   q.A = (const bf16_t*)Aw; q.lda = I; q.a_src = nullptr; q.a_div = 1;
   q.B = (const bf16_t*)a.w_down; q.b_estride = d * I; q.ldb = I;
   q.N = a.d; q.K = a.I; q.n_tiles = (int)cdiv(a.d, TBN);
@@ -685,7 +685,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
      // gate/up dgrad), then the SwiGLU backward and <G, a> as a row pass
     bf16_t* G = (bf16_t*)dXp;
     RowsArgs p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
@@ -707,7 +707,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
     RowsArgs p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = (const bf16_t*)dH; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);

@@ -301,6 +301,7 @@ struct Rows8Args {
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
   const int32_t* offsets;
   const int32_t* tile_off;
+  const int4* tiles;  // row-tile descriptors {expert, first row, segment end, 0}
   int E;
   // EPI_STORE: C [R, ldc] bf16
   bf16_t* C;
@@ -320,10 +321,9 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
   if (L < 0) return;
   const int nt = L % p.n_tiles;
-  const int mt = L / p.n_tiles;
-  const int e = find_expert(p.tile_off, p.E, mt);
-  const int seg0 = p.offsets[e], seg1 = p.offsets[e + 1];
-  const int m0 = seg0 + (mt - p.tile_off[e]) * TBM;
+  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
+  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+  const int seg0 = m0;  // rows past the segment repeat the tile's first row
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
 
@@ -499,7 +499,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
                               q.sv.wdts));
   {  // gate/up GEMM on token rows gathered from xq; SwiGLU and top-k weight in the epilogue
     Rows8Args p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.xs; p.a_sld = d / 128;
     p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
     p.Bs = q.wgus; p.bs_estride = (2 * I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 1;
@@ -510,7 +510,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
   }
   HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws));
   Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
-  p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+  p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
   p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1; p.As = q.aws; p.a_sld = I / 128;
   p.B = q.wdq; p.b_estride = d * I; p.ldb = I;
   p.Bs = q.wds; p.bs_estride = (d / 128) * (I / 128); p.b_sld = I / 128; p.gateup = 0;
@@ -528,7 +528,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
   {  // down dgrad: G = dout_t W_down[e] into the dXp buffer (free until the
      // gate/up dgrad); one row pass then forms dH, <G, a> and dH's 1x128 codes
     Rows8Args p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.douts; p.a_sld = d / 128;
     p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
     p.Bs = q.sv.wdts; p.bs_estride = (I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 0;
@@ -539,7 +539,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
     Rows8Args p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.E = a.E;
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1; p.As = q.dhs; p.a_sld = 2 * I / 128;
     p.B = q.sv.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
     p.Bs = q.sv.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;

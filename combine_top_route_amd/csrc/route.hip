@@ -303,12 +303,15 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+__device__ __forceinline__ int tiles_e(int rows) { return (rows + kRowTile - 1) / kRowTile; }
+
 // Tile table of the grouped GEMMs and the expert order of the weight-gradient
 // GEMMs (largest expert first, so the longest tiles start first).
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         int32_t* __restrict__ tile_off,
                                                         int32_t* __restrict__ order,
-                                                        int32_t* __restrict__ blk_off) {
+                                                        int32_t* __restrict__ blk_off,
+                                                        int4* __restrict__ tiles) {
   __shared__ int sh_waves[16];
   __shared__ int total;
   __shared__ int cnt[1024];
@@ -316,10 +319,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   int c = 0;
   if (e < E) c = offsets[e + 1] - offsets[e];
   if (e < E) cnt[e] = c;
-  int tiles = (c + kRowTile - 1) / kRowTile;
-  int off = block_exclusive_scan(e < E ? tiles : 0, sh_waves, &total);
+  int off = block_exclusive_scan(e < E ? tiles_e(c) : 0, sh_waves, &total);
   if (e < E) tile_off[e] = off;
   if (e == 0) tile_off[E] = total;
+  if (tiles && e < E) {  // one descriptor per row tile: expert, first row, end of segment
+    const int seg0 = offsets[e], seg1 = offsets[e + 1];
+    for (int t = 0; t < tiles_e(c); ++t) tiles[off + t] = make_int4(e, seg0 + t * kRowTile, seg1, 0);
+  }
   __syncthreads();
   if (blk_off) {
     const int blks = (c + kTokBlock - 1) / kTokBlock;
@@ -391,9 +397,9 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
 }
 
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order, int32_t* blk_off) {
+                           int32_t* order, int32_t* blk_off, int4* tiles) {
   MOE_LAUNCH(c, "route_schedule", schedule_kernel, dim3(1), dim3(1024), 0, offsets, E, tile_off,
-             order, blk_off);
+             order, blk_off, tiles);
   return hipSuccess;
 }
 

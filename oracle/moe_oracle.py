@@ -50,6 +50,18 @@ What the pages fix, and the readings taken where they leave a step open:
     down GEMM and the down wgrad quantise), the down dgrad quantises the
     unweighted upstream gradient, the top-k-weight gradient uses that
     dgrad's output, and the stored intermediates H, Aw and dH are bf16.
+  * MXFP8 uses smaller scaling groups than blockwise FP8 [P2 "Precision and
+    hardware support"] and is one of the layer's precision options [P4
+    overview].  Reading: the OCP microscaling format MXFP8 -- blocks of 32
+    values along each GEMM operand's contraction dimension, one power-of-two
+    (E8M0) scale 2^X per block, elements rounded to nearest e4m3, ties to
+    even.  The pages do not say how X is chosen; here it is the blockwise
+    scale amax/448 rounded up to a power of two (the smallest X with amax <=
+    448 * 2^X), so no value saturates, X >= -127 and X = 0 for an all-zero
+    block.  The weights therefore take two blockings:
+    along K for the forward GEMMs and along N for the data gradients; the
+    weight-gradient operands take 32-token blocks from each expert's first
+    row.  Everything else follows the blockwise FP8 readings above.
 """
 from __future__ import annotations
 
@@ -432,8 +444,80 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(F64)
 
 
-def forward_fp8(x, rt: dict, w_gate_up, w_down) -> dict:
-    """Forward with both GEMMs on block-quantised e4m3 operands.  The top-k
+# --------------------------------------------------------------------------
+# MXFP8: OCP microscaling blocks of 32 values with a power-of-two (E8M0)
+# scale and e4m3 elements  [P2 "Precision and hardware support": MXFP8 uses
+# smaller scaling groups than blockwise FP8; P4 overview: the mxfp8 option]
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E4M3_EMAX = 8          # exponent of e4m3's largest binade: 448 = 1.75 * 2^8
+E8M0_MIN = -127        # smallest exponent an E8M0 scale encodes
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Shared exponent X of a block whose largest magnitude is amax (float32
+    values): the smallest integer with amax <= 448 * 2^X, i.e. the blockwise
+    scale amax / 448 rounded up to a power of two, so that no value of the
+    block saturates; X >= -127 (the smallest E8M0 scale) and X = 0 for an
+    all-zero block.  With amax = m * 2^e, m in [1, 2): X = e - 8, plus one
+    when m > 1.75."""
+    a = np.asarray(amax, dtype=np.float32).astype(F64)
+    f, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    m, e = 2.0 * f, ex - 1
+    X = np.maximum(e - E4M3_EMAX + (m > 1.75), E8M0_MIN)
+    return np.where(a > 0, X, 0).astype(np.int64)
+
+
+def mx_quant_last(X: np.ndarray):
+    """1 x 32 blocks along the last axis (a multiple of 32 long).  Returns
+    (element values q, exponents [.., n/32]); the block's values are
+    q * 2^X with q the e4m3 value nearest to v / 2^X (ties to even)."""
+    b = np.asarray(X, dtype=np.float32).astype(F64)
+    sh = b.shape
+    blk = b.reshape(sh[:-1] + (sh[-1] // MX_BLOCK, MX_BLOCK))
+    ex = mx_scale_exponent(np.max(np.abs(blk), axis=-1))
+    q = e4m3_round(np.ldexp(blk, -ex[..., None]))
+    return q.reshape(sh), ex
+
+
+def mx_rows(X: np.ndarray) -> np.ndarray:
+    """Dequantised 1 x 32 blocks along rows (the K dimension of an
+    activation, a gradient, or a weight in the forward GEMMs)."""
+    q, ex = mx_quant_last(X)
+    return np.ldexp(q, np.repeat(ex, MX_BLOCK, axis=-1))
+
+
+def mx_cols(X: np.ndarray) -> np.ndarray:
+    """Dequantised 32 x 1 blocks down the columns: a weight in the data-
+    gradient GEMMs, whose contraction runs over the weight's rows."""
+    return mx_rows(np.asarray(X).T).T
+
+
+def mx_tokens(X: np.ndarray) -> np.ndarray:
+    """Weight-gradient operand blocks: 32 consecutive rows (tokens) x 1
+    column, counted from the expert's first row; the last block may be short
+    (zero padding leaves its largest magnitude unchanged)."""
+    X = np.asarray(X)
+    n = X.shape[0]
+    pad = np.zeros((-(-n // MX_BLOCK) * MX_BLOCK,) + X.shape[1:], dtype=np.float32)
+    pad[:n] = X
+    return mx_cols(pad)[:n]
+
+
+# Quantisation recipes of the fp8 layers: which block shape each GEMM operand
+# takes.  act: activations and gradients, blocks along their K (last) axis;
+# w_fwd: a weight [N, K] in the forward GEMMs (contraction over K); w_bwd: the
+# same weight in a data-gradient GEMM (contraction over N); tok: both operands
+# of a weight gradient (contraction over the expert's tokens).
+FP8_BLOCK = dict(act=quant_rows_1x128, w_fwd=quant_weight_128x128,
+                 w_bwd=quant_weight_128x128, tok=quant_tokens_128)
+MXFP8 = dict(act=mx_rows, w_fwd=mx_rows, w_bwd=mx_cols, tok=mx_tokens)
+
+
+def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK) -> dict:
+    """Forward with both GEMMs on block-quantised e4m3 operands (block
+    shapes from `recipe`: FP8_BLOCK or MXFP8).  The top-k
     weight of each row is folded into the SwiGLU output before the down GEMM
     (Aw = w * silu(g) * up, stored bf16), so the combine is a plain sum."""
     off, E = rt["offsets"], rt["E"]
@@ -449,10 +533,10 @@ def forward_fp8(x, rt: dict, w_gate_up, w_down) -> dict:
         s = slice(off[e], off[e + 1])
         if off[e + 1] == off[e]:
             continue
-        Hs = quant_rows_1x128(Xp[s]) @ quant_weight_128x128(w_gate_up[e]).T
+        Hs = recipe["act"](Xp[s]) @ recipe["w_fwd"](w_gate_up[e]).T
         Aw[s] = bf16_round(w_row[s, None] * swiglu(Hs, I))
         H[s] = bf16_round(Hs)
-        Yw[s] = quant_rows_1x128(Aw[s]) @ quant_weight_128x128(w_down[e]).T
+        Yw[s] = recipe["act"](Aw[s]) @ recipe["w_fwd"](w_down[e]).T
     T, k = rt["ids"].shape
     out = np.zeros((T, d))
     for j in range(k):
@@ -461,7 +545,7 @@ def forward_fp8(x, rt: dict, w_gate_up, w_down) -> dict:
 
 
 def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
-                 logits=None) -> dict:
+                 logits=None, recipe=FP8_BLOCK) -> dict:
     """Backward with all four GEMMs on block-quantised e4m3 operands.  The
     top-k-weight gradient is <G_r, a_r> with G_r the quantised down dgrad
     (the backward's estimate of W_down^T dout_t) and a_r = silu(g) * up from
@@ -483,15 +567,15 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
         s = slice(off[e], off[e + 1])
         if off[e + 1] == off[e]:
             continue
-        Wd_q = quant_weight_128x128(w_down[e])
-        Wgu_q = quant_weight_128x128(w_gate_up[e])
-        G = quant_rows_1x128(dout[tok[s]]) @ Wd_q               # down dgrad
+        Wd_q = recipe["w_bwd"](w_down[e])
+        Wgu_q = recipe["w_bwd"](w_gate_up[e])
+        G = recipe["act"](dout[tok[s]]) @ Wd_q               # down dgrad
         dw_row[s] = np.sum(G * swiglu(H[s], I), axis=1)
         dA = w_row[s, None] * G
-        dW_down[e] = quant_tokens_128(dout[tok[s]]).T @ quant_tokens_128(Aw[s])
+        dW_down[e] = recipe["tok"](dout[tok[s]]).T @ recipe["tok"](Aw[s])
         dH = bf16_round(swiglu_backward(H[s], dA, I))
-        dXp[s] = quant_rows_1x128(dH) @ Wgu_q                    # gate/up dgrad
-        dW_gate_up[e] = quant_tokens_128(dH).T @ quant_tokens_128(Xp[s])
+        dXp[s] = recipe["act"](dH) @ Wgu_q                    # gate/up dgrad
+        dW_gate_up[e] = recipe["tok"](dH).T @ recipe["tok"](Xp[s])
     d_topk_w = dw_row[row_of].reshape(T, k)
     dx = np.zeros((T, d))
     for j in range(k):
@@ -503,9 +587,10 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
 
 
 def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
-                                tokens: np.ndarray, ids=None, w=None) -> dict:
+                                tokens: np.ndarray, ids=None, w=None,
+                                recipe=FP8_BLOCK) -> dict:
     """forward_fp8 / backward_fp8 results (out, dx, d_topk_w, dlogits) for a
-    subset of tokens.  Activation blocks are 1 x 128 within one row and weight
+    subset of tokens.  Activation blocks lie within one row and weight
     blocks depend only on the weights, so each token's results follow from
     its own rows; the same steps as the full functions, row by row."""
     tokens = np.asarray(tokens)
@@ -520,50 +605,54 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
         w_t = np.asarray(w, F64)[tokens]
     qw = {}
 
-    def weights(e):
+    def weights(e):  # (gate/up, down) forward and data-gradient forms
         if e not in qw:
-            qw[e] = (quant_weight_128x128(w_gate_up[e]), quant_weight_128x128(w_down[e]))
+            fw = (recipe["w_fwd"](w_gate_up[e]), recipe["w_fwd"](w_down[e]))
+            bw = fw if recipe["w_bwd"] is recipe["w_fwd"] else \
+                (recipe["w_bwd"](w_gate_up[e]), recipe["w_bwd"](w_down[e]))
+            qw[e] = fw + bw
         return qw[e]
 
     n, d = tokens.size, w_down.shape[1]
     out, dx = np.zeros((n, d)), np.zeros((n, d))
     dtw = np.zeros((n, k))
     for i, t in enumerate(tokens):
-        xq = quant_rows_1x128(np.asarray(x, F64)[t][None, :])
-        gq = quant_rows_1x128(np.asarray(dout, F64)[t][None, :])
+        xq = recipe["act"](np.asarray(x, F64)[t][None, :])
+        gq = recipe["act"](np.asarray(dout, F64)[t][None, :])
         for j in range(k):
-            Wgu_q, Wd_q = weights(ids_t[i, j])
-            Hs = xq @ Wgu_q.T
+            Wgu_f, Wd_f, Wgu_b, Wd_b = weights(ids_t[i, j])
+            Hs = xq @ Wgu_f.T
             H = bf16_round(Hs)
             Aw = bf16_round(w_t[i, j] * swiglu(Hs, I))
-            out[i] += (quant_rows_1x128(Aw) @ Wd_q.T)[0]
-            G = gq @ Wd_q
+            out[i] += (recipe["act"](Aw) @ Wd_f.T)[0]
+            G = gq @ Wd_b
             dtw[i, j] = np.sum(G * swiglu(H, I))
             dH = bf16_round(swiglu_backward(H, w_t[i, j] * G, I))
-            dx[i] += (quant_rows_1x128(dH) @ Wgu_q)[0]
+            dx[i] += (recipe["act"](dH) @ Wgu_b)[0]
     res = dict(out=out, dx=dx, d_topk_w=dtw, ids=ids_t, w=w_t)
     if logits is not None:
         res["dlogits"] = router_logit_grad(dict(ids=ids_t, w=w_t), dtw, E)
     return res
 
 
-def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int):
+def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int,
+                            recipe=FP8_BLOCK):
     """backward_fp8's dW_gate_up[e], dW_down[e] from the rows of expert e
     alone (token blocks are counted from the expert's first row)."""
     k = rt["k"]
     s = slice(rt["offsets"][e], rt["offsets"][e + 1])
     src = rt["src_of"][s]
     I = w_gate_up.shape[1] // 2
-    Wgu_q = quant_weight_128x128(w_gate_up[e])
-    Wd_q = quant_weight_128x128(w_down[e])
+    Wgu_f = recipe["w_fwd"](w_gate_up[e])
+    Wd_b = recipe["w_bwd"](w_down[e])
     Xp = np.asarray(x, F64)[src // k]
     g = np.asarray(dout, F64)[src // k]
     wr = rt["w"].ravel()[src]
-    Hs = quant_rows_1x128(Xp) @ Wgu_q.T
+    Hs = recipe["act"](Xp) @ Wgu_f.T
     H = bf16_round(Hs)
     Aw = bf16_round(wr[:, None] * swiglu(Hs, I))
-    G = quant_rows_1x128(g) @ Wd_q
+    G = recipe["act"](g) @ Wd_b
     dH = bf16_round(swiglu_backward(H, wr[:, None] * G, I))
-    dW_down = quant_tokens_128(g).T @ quant_tokens_128(Aw)
-    dW_gate_up = quant_tokens_128(dH).T @ quant_tokens_128(Xp)
+    dW_down = recipe["tok"](g).T @ recipe["tok"](Aw)
+    dW_gate_up = recipe["tok"](dH).T @ recipe["tok"](Xp)
     return dW_gate_up, dW_down

@@ -423,3 +423,175 @@ def test_fp8_sampled_evaluators_match_full_layer():
         dgu, dd = O.expert_weight_grads_fp8(inp["x"], inp["dout"], rt, inp["w_gate_up"], inp["w_down"], e)
         np.testing.assert_allclose(dgu, b8["dW_gate_up"][e], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dd, b8["dW_down"][e], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def _mx_block(head):
+    b = np.zeros(32)
+    b[:len(head)] = head
+    return b
+
+
+def test_mx_hand_worked_blocks():
+    """Blocks worked by hand: X is the smallest integer with amax <= 448 *
+    2^X, elements are rounded to nearest e4m3 (ties to even) after dividing
+    by 2^X."""
+    X = np.stack([
+        # amax 3 = 1.5 * 2^1 -> X = -7, so values are multiples of 2^-7 on
+        # e4m3's grid: 3*128 = 384 exact; 0.1*128 = 12.8 -> 13; 0.02*128 =
+        # 2.56 -> 2.5 (quantum 1/4 in [2, 4)); -2.9*128 = -371.2 -> -384
+        # (quantum 32 in [256, 512))
+        _mx_block([3.0, 0.1, 0.02, -2.9]),
+        # amax 1.9 > 1.75 * 2^0 -> X = -7: 1.9*128 = 243.2 -> 240 (quantum
+        # 16); 1.0625*128 = 136 ties between 128 (even) and 144 -> 128;
+        # 1.1875*128 = 152 ties between 144 and 160 (even) -> 160; 0.75*128
+        # = 96 exact
+        _mx_block([1.9, 1.0625, 1.1875, 0.75]),
+        # amax exactly 448 * 2^-8 -> X = -8, no rounding up
+        _mx_block([1.75, -0.3]),
+        np.zeros(32),                              # all zero -> X = 0
+        # amax 2^-130 (an fp32 subnormal) -> X clamps at -127: 2^-3 exact,
+        # 2^-135 -> 2^-8 exact (e4m3 subnormal), 3*2^-138 = 0.75*2^-9 -> 2^-9
+        _mx_block([2.0 ** -130, 2.0 ** -135, 3 * 2.0 ** -138]),
+    ])
+    q, ex = O.mx_quant_last(X.reshape(1, -1))
+    assert ex.ravel().tolist() == [-7, -7, -8, 0, -127]
+    got = O.mx_rows(X)
+    want = np.stack([
+        _mx_block([3.0, 13 / 128, 2.5 / 128, -3.0]),
+        _mx_block([240 / 128, 1.0, 1.25, 0.75]),
+        # -0.3*256 = -76.8 -> -80 (quantum 8 in [64, 128))
+        _mx_block([1.75, -80 / 256]),
+        np.zeros(32),
+        _mx_block([2.0 ** -130, 2.0 ** -135, 2.0 ** -136]),
+    ])
+    x32 = X.astype(np.float32).astype(np.float64)    # 0.1, 0.02, 2.9 as float32
+    assert x32[0, 1] != 0.1
+    assert np.array_equal(got, want)
+
+
+def test_mx_scale_exponent_closed_form():
+    """For every amax above the clamp, amax / 2^X lies in (224, 448]: the
+    block's largest value lands in e4m3's top binade without saturating."""
+    rng = np.random.default_rng(30)
+    amax = (np.exp(rng.uniform(-80, 80, 100000)) * rng.choice([1, 3, 7], 100000)).astype(np.float32)
+    amax = np.concatenate([amax, np.float32([1.0, 1.75, 1.7500001, 2.0, 448.0, 449.0, 2.0 ** -118])])
+    X = O.mx_scale_exponent(amax)
+    r = amax.astype(np.float64) / np.ldexp(1.0, X)
+    assert np.all((r > 224) & (r <= 448))
+    assert O.mx_scale_exponent(np.float32(0.0)) == 0
+    assert O.mx_scale_exponent(np.float32(2.0 ** -125)) == -127
+
+
+def test_mx_quantisers_per_block_and_exact_on_grid():
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((4, 128))
+    q = O.mx_rows(X)
+    X2 = X.copy()
+    X2[2, 70] = 1e9                                # only block (2, 64..95) changes
+    q2 = O.mx_rows(X2)
+    same = np.ones_like(X, bool)
+    same[2, 64:96] = False
+    assert np.array_equal(q[same], q2[same]) and not np.array_equal(q[2, 64:96], q2[2, 64:96])
+    # any e4m3 value times a power of two whose block maximum sits in one
+    # binade [1, 1.75] * 2^c is on the grid of its block, in either blocking
+    v = O.e4m3_round(rng.uniform(1, 1.75, (64, 96)) * rng.choice([-1, 1], (64, 96)))
+    G = v * np.ldexp(1.0, rng.integers(-20, 5, (64, 1)))  # one binade per row
+    assert np.array_equal(O.mx_rows(G), G)
+    assert not np.array_equal(O.mx_cols(G), G)          # columns mix binades 2^24 apart
+    assert np.array_equal(O.mx_cols(G.T.copy()), G.T)
+
+
+def test_mx_token_blocks_start_at_the_expert_first_row():
+    """32-token blocks counted from row 0 of the segment: a large value in
+    row 31 rescales rows 0..31 only; a ragged tail is its own block."""
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((70, 3))
+    q = O.mx_tokens(X)
+    X2 = X.copy()
+    X2[31, 1] = 1e9                              # pushes its block into e4m3 subnormals
+    q2 = O.mx_tokens(X2)
+    assert np.array_equal(q2[32:], q[32:]) and np.array_equal(q2[:, [0, 2]], q[:, [0, 2]])
+    assert not np.array_equal(q2[:31, 1], q[:31, 1])
+    X3 = X.copy()
+    X3[64, 0] = 1e9                              # rows 64..69: the short last block
+    q3 = O.mx_tokens(X3)
+    assert np.array_equal(q3[:64], q[:64]) and not np.array_equal(q3[65:, 0], q[65:, 0])
+
+
+def _mx_axis_case(seed):
+    """Tiny bf16-shaped layer whose x and dout rows sit on the e4m3 grid of
+    their 1 x 32 blocks, whose W_gate_up rows and W_down columns each hold
+    one binade ([1, 1.75] * 2^c with c = 0 or -20): exact in the blocking
+    each GEMM should use, not in the other."""
+    wl = S.WORKLOADS["tiny"].scaled(d=64, I=64, T=40, E=3, k=2, dtype="bf16")
+    rng = np.random.default_rng(seed)
+
+    def grid(shape):
+        return O.e4m3_round(rng.uniform(1, 1.75, shape) * rng.choice([-1, 1], shape))
+    x = grid((wl.T, wl.d))
+    dout = grid((wl.T, wl.d))
+    Wgu = grid((wl.E, 2 * wl.I, wl.d)) * np.ldexp(1.0, rng.choice([0, -20], (wl.E, 2 * wl.I, 1)))
+    Wd = grid((wl.E, wl.d, wl.I)) * np.ldexp(1.0, rng.choice([0, -20], (wl.E, 1, wl.I)))
+    rt = O.route(rng.standard_normal((wl.T, wl.E)), wl.k, wl.E)
+    return wl, x, dout, Wgu, Wd, rt
+
+
+def test_mx_gemm_blocking_axes():
+    """Forward gate/up GEMM blocks W_gate_up along d (its rows: exact here),
+    the down dgrad blocks W_down along d (its columns: exact here).  The
+    same layer with the weight blockings swapped is not exact."""
+    wl, x, dout, Wgu, Wd, rt = _mx_axis_case(33)
+    Xp = O.dispatch(x, rt)
+    segs = list(zip(rt["offsets"][:-1], rt["offsets"][1:]))
+    H = np.concatenate([Xp[s0:s1] @ Wgu[e].T for e, (s0, s1) in enumerate(segs)])
+    tok = rt["src_of"] // wl.k
+    G = np.concatenate([dout[tok[s0:s1]] @ Wd[e] for e, (s0, s1) in enumerate(segs)])
+
+    def run(recipe):
+        f = O.forward_fp8(x, rt, Wgu, Wd, recipe=recipe)
+        b = O.backward_fp8(dout, rt, Wgu, Wd, f, recipe=recipe)
+        dw_row = np.sum(G * O.swiglu(f["H"], wl.I), axis=1)
+        return f, b, dw_row[rt["row_of"]].reshape(wl.T, wl.k)
+    f, b, dtw = run(O.MXFP8)
+    assert np.array_equal(f["H"], O.bf16_round(H))
+    np.testing.assert_allclose(b["d_topk_w"], dtw, rtol=1e-13, atol=1e-13 * np.max(np.abs(dtw)))
+    f, b, dtw = run(dict(O.MXFP8, w_fwd=O.mx_cols, w_bwd=O.mx_rows))
+    assert not np.array_equal(f["H"], O.bf16_round(H))
+    assert not np.allclose(b["d_topk_w"], dtw, rtol=1e-6, atol=0)
+
+
+def test_mx_layer_close_to_unquantised_layer():
+    wl = S.WORKLOADS["tiny"].scaled(d=256, I=256, T=64, dtype="bf16")
+    inp = {k: _np(v) for k, v in S.make_inputs(wl, seed=15).items()}
+    rt = O.route(inp["logits"], wl.k, wl.E)
+    fw = O.forward(inp["x"], rt, inp["w_gate_up"], inp["w_down"])
+    bw = O.backward(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], fw)
+    fm = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"], recipe=O.MXFP8)
+    bm = O.backward_fp8(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], fm, recipe=O.MXFP8)
+    for ref, got in ((fw["out"], fm["out"]), (bw["dx"], bm["dx"]),
+                     (bw["dW_gate_up"], bm["dW_gate_up"]), (bw["dW_down"], bm["dW_down"]),
+                     (bw["d_topk_w"], bm["d_topk_w"])):
+        err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        assert 1e-3 < err < 0.1
+
+
+def test_mx_sampled_evaluators_match_full_layer():
+    wl = S.WORKLOADS["tiny"].scaled(d=256, I=128, T=96, E=6, k=2, dtype="bf16")
+    inp = {k: _np(v) for k, v in S.make_inputs(wl, seed=34).items()}
+    rt = O.route(inp["logits"], wl.k, wl.E)
+    fm = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"], recipe=O.MXFP8)
+    bm = O.backward_fp8(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], fm, logits=inp["logits"],
+                        recipe=O.MXFP8)
+    toks = np.array([0, 7, 60, 95])
+    s = O.forward_backward_tokens_fp8(inp["x"], inp["logits"], inp["dout"], inp["w_gate_up"],
+                                      inp["w_down"], wl.k, toks, recipe=O.MXFP8)
+    for n, ref in (("out", fm["out"]), ("dx", bm["dx"]), ("d_topk_w", bm["d_topk_w"]),
+                   ("dlogits", bm["dlogits"])):
+        np.testing.assert_allclose(s[n], ref[toks], rtol=1e-12, atol=1e-12 * np.max(np.abs(ref)))
+    for e in range(wl.E):
+        dgu, dd = O.expert_weight_grads_fp8(inp["x"], inp["dout"], rt, inp["w_gate_up"], inp["w_down"],
+                                            e, recipe=O.MXFP8)
+        np.testing.assert_allclose(dgu, bm["dW_gate_up"][e], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dd, bm["dW_down"][e], rtol=1e-12, atol=1e-12)

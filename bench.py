@@ -42,20 +42,23 @@ KERNEL_SITES = [
     ("rows_gemm_kernel<1, 1, 0>(", "gemm_gateup_fwd"), ("rows_gemm_kernel<0, 0, 0>(", "gemm_down_fwd"),
     ("rows_gemm_kernel<0, 2, 1>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2, 0>(", "gemm_gateup_dgrad"),
     ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
-    ("rows8_kernel<1, 0>(", "gemm_gateup_fwd"), ("rows8_kernel<0, 0>(", "gemm_down_fwd"),
-    ("rows8_kernel<0, 2>(", "gemm_down_dgrad"), ("rows8_kernel<0, 1>(", "gemm_gateup_dgrad"),
-    ("wgrad8_kernel<0>(", "gemm_down_wgrad"), ("wgrad8_kernel<1>(", "gemm_gateup_wgrad"),
+    ("rows8_kernel<1, 0, ", "gemm_gateup_fwd"), ("rows8_kernel<0, 0, ", "gemm_down_fwd"),
+    ("rows8_kernel<2, 2, ", "gemm_down_dgrad"), ("rows8_kernel<0, 1, ", "gemm_gateup_dgrad"),
+    ("wgrad8_kernel<0, ", "gemm_down_wgrad"), ("wgrad8_kernel<1, ", "gemm_gateup_wgrad"),
     ("combine_wide_kernel<", "combine + reduce_dx"), ("combine_kernel<", "combine + reduce_dx"),
     ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
     ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
-    ("quant_weight_kernel", "quant_w_*"), ("quant_tok_kernel", "quant_*_tok"),
+    ("quant_weight_kernel", "quant_w_*"), ("quant_weight_mx_kernel", "quant_w_*"),
+    ("quant_tok_kernel", "quant_*_tok"),
 ]
 # source files whose text defines each GEMM kernel (a change voids measured traffic)
 KERNEL_SOURCES = {
     "native": ["gemm_bf16.hip", "tile.h", "common.h"],
     "fp8_block": ["gemm_fp8.hip", "tile.h", "common.h"],
+    "mxfp8": ["gemm_fp8.hip", "tile.h", "common.h"],
 }
+FP8 = ("fp8_block", "mxfp8")
 
 
 def site_of(kernel_name: str) -> str | None:
@@ -66,7 +69,7 @@ def site_of(kernel_name: str) -> str | None:
 
 
 def mfma_peak(wl) -> float:
-    if wl.precision == "fp8_block":
+    if wl.precision in FP8:
         return PEAK_FP8_TFLOPS
     return PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
 
@@ -88,17 +91,22 @@ def kernel_work(wl):
         "permute": ("byte", float(T * d * es + R * d * es + 4 * R)),
         "route_topk": ("byte", float(T * E * es + 8 * R)),
     }
-    if wl.precision == "fp8_block":
-        # bf16 in, one code byte out per element, one float scale per block
-        q = lambda n, blk: float(n * 2 + n + 4 * n // blk)
+    if wl.precision in FP8:
+        # bf16 in, one code byte out per element, plus scales: an fp32 scale
+        # per 128 values of a row (blockwise) or an E8M0 byte per 32 (MX) --
+        # the same 1/32 byte per value; weights: an fp32 scale per 128 x 128
+        # block (blockwise) or a byte per 32 values (MX), in both layouts
+        q = lambda n: float(n * 2 + n + n // 32)
+        ws = (lambda n: n // 32) if wl.precision == "mxfp8" else (lambda n: 4 * n // 16384)
+        qw = lambda n: float(n * 2 + 2 * n + 2 * ws(n))
         work.update({
-            "quant_x": ("byte", q(T * d, 128)), "quant_dout": ("byte", q(T * d, 128)),
-            "quant_aw": ("byte", q(R * I, 128)),
+            "quant_x": ("byte", q(T * d)), "quant_dout": ("byte", q(T * d)),
+            "quant_aw": ("byte", q(R * I)),
             # both layouts (the transposed one is kept for the backward)
-            "quant_w_gate_up": ("byte", q(E * 2 * I * d, 128 * 128) + E * 2 * I * d + 4 * E * 2 * I * d // 16384),
-            "quant_w_down": ("byte", q(E * d * I, 128 * 128) + E * d * I + 4 * E * d * I // 16384),
-            "quant_dout_tok": ("byte", q(R * d, 128) + 4 * R), "quant_x_tok": ("byte", q(R * d, 128) + 4 * R),
-            "quant_aw_tok": ("byte", q(R * I, 128)), "quant_dh_tok": ("byte", q(R * 2 * I, 128)),
+            "quant_w_gate_up": ("byte", qw(E * 2 * I * d)),
+            "quant_w_down": ("byte", qw(E * d * I)),
+            "quant_dout_tok": ("byte", q(R * d) + 4 * R), "quant_x_tok": ("byte", q(R * d) + 4 * R),
+            "quant_aw_tok": ("byte", q(R * I)), "quant_dh_tok": ("byte", q(R * 2 * I)),
         })
     return work
 
@@ -148,11 +156,16 @@ def cpu_baseline(wl, inp: dict, tokens: int):
     f = lambda t: t[:tokens].double().numpy()
     x, lg, dout = f(inp["x"]), f(inp["logits"]), f(inp["dout"])
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
-    fp8 = wl.precision == "fp8_block"
+    fp8 = wl.precision in FP8
+    recipe = O.MXFP8 if wl.precision == "mxfp8" else O.FP8_BLOCK
     t0 = time.perf_counter()
     rt = O.route(lg, wl.k, wl.E)
-    fw = (O.forward_fp8 if fp8 else O.forward)(x, rt, Wgu, Wd)
-    (O.backward_fp8 if fp8 else O.backward)(dout, rt, Wgu, Wd, fw, logits=lg)
+    if fp8:
+        fw = O.forward_fp8(x, rt, Wgu, Wd, recipe=recipe)
+        O.backward_fp8(dout, rt, Wgu, Wd, fw, logits=lg, recipe=recipe)
+    else:
+        fw = O.forward(x, rt, Wgu, Wd)
+        O.backward(dout, rt, Wgu, Wd, fw, logits=lg)
     dt = time.perf_counter() - t0
     flops = sub.flops_fwd() + sub.flops_bwd()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
@@ -163,14 +176,15 @@ def cpu_baseline(wl, inp: dict, tokens: int):
 
 COPY_BYTES = 1 << 30
 # oracle sample per workload: about 10-30 s of float64 numpy on 16 host cores
-CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q235b": 8192, "fp8_skew": 2048}
+CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q235b": 8192, "fp8_skew": 2048,
+                     "mxfp8_skew": 2048}
 
 
 def gemm_operand_bytes(wl):
     """Bytes each GEMM must move at least once: both operands and the result
     (weights once, activation rows once), in the storage types it reads."""
     R, d, I, T, E = wl.R, wl.d, wl.I, wl.T, wl.E
-    a = 1 if wl.precision == "fp8_block" else (2 if wl.dtype == "bf16" else 4)
+    a = 1 if wl.precision in FP8 else (2 if wl.dtype == "bf16" else 4)
     o = 2 if wl.dtype == "bf16" else 4
     return {
         "gemm_gateup_fwd": T * d * a + E * 2 * I * d * a + R * 3 * I * o,
@@ -385,8 +399,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8_e4m3 (fp32 block scales, fp32 accumulate)" if wl.precision == "fp8_block"
-                  else ("bf16" if wl.dtype == "bf16" else "f32")),
+        "dtype": {"fp8_block": "fp8_e4m3 (fp32 block scales, fp32 accumulate)",
+                  "mxfp8": "fp8_e4m3 (MXFP8: E8M0 scale per 32 values, fp32 accumulate)"}.get(
+                      wl.precision, "bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: MoE layer fwd+bwd, T={wl.T} tokens, d={wl.d}, E={wl.E}, "
                                f"top-{wl.k}, I={wl.I}, {wl.dtype}, {wl.precision}",

@@ -17,13 +17,13 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-PREC_NATIVE, PREC_FP8_BLOCK = 0, 1
+PREC_NATIVE, PREC_FP8_BLOCK, PREC_MXFP8 = 0, 1, 2
 OP_ROUTE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 QUANT_ROWS, QUANT_WEIGHT, QUANT_WEIGHT_T = 0, 1, 2
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
-_PREC = {"native": PREC_NATIVE, "fp8_block": PREC_FP8_BLOCK}
+_PREC = {"native": PREC_NATIVE, "fp8_block": PREC_FP8_BLOCK, "mxfp8": PREC_MXFP8}
 
 
 class MoeShape(ctypes.Structure):
@@ -61,6 +61,10 @@ _SIGS = [
                                         _P]),
     ("moe_quantize_tokens_fp8", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int64, ctypes.c_int,
                                                ctypes.POINTER(MoeRouting), _P, _P, _P, ctypes.c_size_t, _P]),
+    ("moe_quantize_mxfp8", ctypes.c_int, [ctypes.c_int, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P,
+                                          _P, _P]),
+    ("moe_quantize_tokens_mxfp8", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int64, ctypes.c_int,
+                                                 ctypes.POINTER(MoeRouting), _P, _P, _P, ctypes.c_size_t, _P]),
     ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("moe_last_error", ctypes.c_char_p, []),
     ("moe_profile_begin", ctypes.c_int, []),
@@ -331,6 +335,47 @@ def quantize_tokens_fp8(src, routing: Routing, T, k, gather):
     ws = torch.empty(workspace_size(shape, OP_ROUTE), dtype=torch.uint8, device=dev)
     cr = routing.c()
     _check("moe_quantize_tokens_fp8", lib().moe_quantize_tokens_fp8(
+        ctypes.byref(shape), _ptr(src), C, 1 if gather else 0, ctypes.byref(cr), _ptr(q), _ptr(s), _ptr(ws),
+        ws.numel(), _stream(dev)))
+    return q, s
+
+
+def quantize_mxfp8(src, kind=QUANT_ROWS):
+    """MXFP8 e4m3 codes (uint8) and E8M0 scale bytes (uint8) of a bf16
+    tensor: kind QUANT_ROWS for [n0, n1] (blocks of 32 along rows; s [n0,
+    n1/32]), QUANT_WEIGHT for [n0, n1, n2] (blocks of 32 along rows; s [n0,
+    n1, n2/32]), QUANT_WEIGHT_T (blocks of 32 down columns, written
+    transposed; q [n0, n2, n1], s [n0, n2, n1/32])."""
+    dev = src.device
+    if src.dtype != torch.bfloat16 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 tensor")
+    if kind == QUANT_ROWS:
+        n0, n1 = src.shape
+        n2 = 0
+        qs = (n0, n1)
+    else:
+        n0, n1, n2 = src.shape
+        qs = (n0, n1, n2) if kind == QUANT_WEIGHT else (n0, n2, n1)
+    q = torch.empty(qs, dtype=torch.uint8, device=dev)
+    s = torch.empty(qs[:-1] + (qs[-1] // 32,), dtype=torch.uint8, device=dev)
+    _check("moe_quantize_mxfp8", lib().moe_quantize_mxfp8(kind, _ptr(src), n0, n1, n2, _ptr(q), _ptr(s),
+                                                          _stream(dev)))
+    return q, s
+
+
+def quantize_tokens_mxfp8(src, routing: Routing, T, k, gather):
+    """MXFP8 token-block codes q [C, 128 nblk] and scale bytes s [C, 4 nblk]
+    of a weight-gradient operand (see moe_quantize_tokens_mxfp8)."""
+    dev = src.device
+    C = src.shape[1]
+    E = routing.counts.numel()
+    shape = make_shape(T, C, E, k, 128, torch.bfloat16)
+    nblk = -(-T * k // 128) + E
+    q = torch.zeros((C, 128 * nblk), dtype=torch.uint8, device=dev)
+    s = torch.zeros((C, 4 * nblk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(workspace_size(shape, OP_ROUTE), dtype=torch.uint8, device=dev)
+    cr = routing.c()
+    _check("moe_quantize_tokens_mxfp8", lib().moe_quantize_tokens_mxfp8(
         ctypes.byref(shape), _ptr(src), C, 1 if gather else 0, ctypes.byref(cr), _ptr(q), _ptr(s), _ptr(ws),
         ws.numel(), _stream(dev)))
     return q, s

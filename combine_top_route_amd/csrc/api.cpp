@@ -97,14 +97,15 @@ moe_status check_shape(const moe_shape* s) {
   if (s->I < 8 || s->I > 16384 || s->I % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "I=%lld must be a multiple of 8 in [8, 16384]", (long long)s->I);
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "dtype=%d unknown", s->dtype);
   if (s->logits_dtype != MOE_F32 && s->logits_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_dtype=%d unknown", s->logits_dtype);
-  if (s->precision != MOE_PREC_NATIVE && s->precision != MOE_PREC_FP8_BLOCK) return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
+  if (s->precision != MOE_PREC_NATIVE && s->precision != MOE_PREC_FP8_BLOCK && s->precision != MOE_PREC_MXFP8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
   if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "reserved field must be 0");
-  if (s->precision == MOE_PREC_FP8_BLOCK) {
-    if (s->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs dtype bf16");
-    if (s->d % 128 || s->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision needs d and I multiples of 128");
+  if (s->precision != MOE_PREC_NATIVE) {
+    if (s->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 precisions need dtype bf16");
+    if (s->d % 128 || s->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 precisions need d and I multiples of 128");
     const int64_t widest = s->d > 2 * s->I ? s->d : 2 * s->I;
     if (s->T * s->k * (widest / 128) >= (int64_t(1) << 31))
-      return fail(MOE_ERR_UNSUPPORTED, "fp8 block precision: T*k*max(d,2I)/128 must stay below 2^31");
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 precisions: T*k*max(d,2I)/128 must stay below 2^31");
   }
   return MOE_OK;
 }
@@ -113,7 +114,13 @@ moe_status check_shape(const moe_shape* s) {
   if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", #p)
 
 size_t elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
-bool is_fp8(const moe_shape* s) { return s->precision == MOE_PREC_FP8_BLOCK; }
+bool is_fp8(const moe_shape* s) { return s->precision == MOE_PREC_FP8_BLOCK || s->precision == MOE_PREC_MXFP8; }
+bool is_mx(const moe_shape* s) { return s->precision == MOE_PREC_MXFP8; }
+// Scale bytes of an expert weight [N, K] encoded along K: blockwise fp32
+// per 128 x 128 block, MX one byte per row and 32 columns.
+size_t wscale_bytes(const moe_shape* s, int64_t N, int64_t K) {
+  return is_mx(s) ? (size_t)(s->E * N * (K / 32)) : sizeof(float) * s->E * (N / 128) * (K / 128);
+}
 int dw_blocks(const moe_shape* s) {
   if (s->dtype == MOE_F32) return f32_dw_blocks((int)s->I);
   return is_fp8(s) ? fp8_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
@@ -129,7 +136,7 @@ struct Layout {
   // fp8: quantised operands (q) and their scales (s)
   size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
   size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
-  size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0;
+  size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0, Gf = 0;
   size_t total = 0;
 };
 
@@ -161,29 +168,32 @@ Layout layout(const moe_shape* s, int op) {
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
   }
   if (is_fp8(s)) {
+    // row scales take one 32-bit word per 128 columns in both formats (an
+    // fp32 scale, or four E8M0 bytes)
     const int64_t T = s->T, d = s->d, I = s->I, E = s->E;
-    const size_t f = sizeof(float);
+    const size_t w = sizeof(uint32_t);
     if (op == MOE_OP_FORWARD) {
       L.xq = take(T * d);
-      L.xs = take(f * T * (d / 128));
+      L.xs = take(w * T * (d / 128));
       L.wguq = take(E * 2 * I * d);
-      L.wgus = take(f * E * (2 * I / 128) * (d / 128));
+      L.wgus = take(wscale_bytes(s, 2 * I, d));
       L.wdq = take(E * d * I);
-      L.wds = take(f * E * (d / 128) * (I / 128));
+      L.wds = take(wscale_bytes(s, d, I));
       L.awq = take(R * I);
-      L.aws = take(f * R * (I / 128));
+      L.aws = take(w * R * (I / 128));
     }
     if (op == MOE_OP_BACKWARD) {
       const int64_t nb = nblk_max(s);
       L.doutq = take(T * d);
-      L.douts = take(f * T * (d / 128));
+      L.douts = take(w * T * (d / 128));
       L.dhq = take(R * 2 * I);
-      L.dhs = take(f * R * (2 * I / 128));
+      L.dhs = take(w * R * (2 * I / 128));
       const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;
       L.tqa = take(ra * nb * kTokBlock);
-      L.tsa = take(f * ra * nb);
+      L.tsa = take(w * ra * nb);
       L.tqb = take(rb * nb * kTokBlock);
-      L.tsb = take(f * rb * nb);
+      L.tsb = take(w * rb * nb);
+      L.Gf = take(sizeof(float) * R * I);
     }
   }
   L.total = off;
@@ -212,8 +222,8 @@ SavedLayout saved_layout(const moe_shape* s) {
     };
     L.wgutq = take(E * d * 2 * I);
     L.wdtq = take(E * I * d);
-    L.wguts = take(sizeof(float) * E * (d / 128) * (2 * I / 128));
-    L.wdts = take(sizeof(float) * E * (I / 128) * (d / 128));
+    L.wguts = take(wscale_bytes(s, d, 2 * I));
+    L.wdts = take(wscale_bytes(s, I, d));
   }
   L.total = off;
   return L;
@@ -226,8 +236,8 @@ Fp8Saved fp8_saved(const moe_shape* s, const void* saved) {
   char* b = (char*)saved;
   v.wgutq = (uint8_t*)(b + L.wgutq);
   v.wdtq = (uint8_t*)(b + L.wdtq);
-  v.wguts = (float*)(b + L.wguts);
-  v.wdts = (float*)(b + L.wdts);
+  v.wguts = b + L.wguts;
+  v.wdts = b + L.wdts;
   return v;
 }
 
@@ -364,10 +374,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
     HIP_TRY(f32_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
   } else if (is_fp8(shape)) {
     Fp8Fwd q;
-    q.xq = (uint8_t*)at(workspace, L.xq); q.xs = (float*)at(workspace, L.xs);
-    q.wguq = (uint8_t*)at(workspace, L.wguq); q.wgus = (float*)at(workspace, L.wgus);
-    q.wdq = (uint8_t*)at(workspace, L.wdq); q.wds = (float*)at(workspace, L.wds);
-    q.awq = (uint8_t*)at(workspace, L.awq); q.aws = (float*)at(workspace, L.aws);
+    q.mx = is_mx(shape);
+    q.xq = (uint8_t*)at(workspace, L.xq); q.xs = at(workspace, L.xs);
+    q.wguq = (uint8_t*)at(workspace, L.wguq); q.wgus = at(workspace, L.wgus);
+    q.wdq = (uint8_t*)at(workspace, L.wdq); q.wds = at(workspace, L.wds);
+    q.awq = (uint8_t*)at(workspace, L.awq); q.aws = at(workspace, L.aws);
     q.sv = fp8_saved(shape, saved);
     HIP_TRY(fp8_fwd_gemms(c, a, q, H, A, Y), "forward GEMMs");
   } else {
@@ -427,11 +438,13 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
                           (float*)at(workspace, L.G)), "backward GEMMs");
   else if (is_fp8(shape)) {
     Fp8Bwd q;
-    q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = (float*)at(workspace, L.douts);
+    q.mx = is_mx(shape);
+    q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = at(workspace, L.douts);
     q.sv = fp8_saved(shape, saved);
-    q.dhq = (uint8_t*)at(workspace, L.dhq); q.dhs = (float*)at(workspace, L.dhs);
-    q.tqa = (uint8_t*)at(workspace, L.tqa); q.tsa = (float*)at(workspace, L.tsa);
-    q.tqb = (uint8_t*)at(workspace, L.tqb); q.tsb = (float*)at(workspace, L.tsb);
+    q.dhq = (uint8_t*)at(workspace, L.dhq); q.dhs = at(workspace, L.dhs);
+    q.tqa = (uint8_t*)at(workspace, L.tqa); q.tsa = at(workspace, L.tsa);
+    q.tqb = (uint8_t*)at(workspace, L.tqb); q.tsb = at(workspace, L.tsb);
+    q.G = (float*)at(workspace, L.Gf);
     q.blk_off = (const int32_t*)at(workspace, L.blk_off);
     q.nblk_max = (int)nblk_max(shape);
     HIP_TRY(fp8_bwd_gemms(c, a, q, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
@@ -478,8 +491,12 @@ moe_status moe_combine(const moe_shape* shape, const void* rows, const moe_routi
   return MOE_OK;
 }
 
-moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
-                            uint8_t* q, float* s, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status quantize_common(bool mx, int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                           uint8_t* q, void* s, void* stream) {
   CHECK_PTR(src);
   CHECK_PTR(q);
   CHECK_PTR(s);
@@ -499,22 +516,30 @@ moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, i
   }
   TRY(check_aligned16(src, "src"));
   TRY(check_aligned16(q, "q"));
+  if (((uintptr_t)s) & 3) return fail(MOE_ERR_INVALID_ARGUMENT, "s must be 4-byte aligned");
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
-  if (kind == MOE_QUANT_ROWS)
-    HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s), "quant_rows");
-  else if (kind == MOE_QUANT_WEIGHT)
-    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, q, s, nullptr,
-                                nullptr), "quant_weight");
+  if (kind == MOE_QUANT_ROWS) {
+    HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s, mx), "quant_rows");
+    return MOE_OK;
+  }
+  const bool tr = kind == MOE_QUANT_WEIGHT_T;
+  uint8_t* fq = tr ? nullptr : q;
+  uint8_t* tq = tr ? q : nullptr;
+  void* fs = tr ? nullptr : s;
+  void* ts = tr ? s : nullptr;
+  if (mx)
+    HIP_TRY(launch_quant_weight_mx(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, fq, (uint8_t*)fs,
+                                   tq, (uint8_t*)ts), "quant_weight");
   else
-    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, nullptr, nullptr,
-                                q, s), "quant_weight");
+    HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, fq, (float*)fs, tq,
+                                (float*)ts), "quant_weight");
   return MOE_OK;
 }
 
-moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int64_t C, int gather,
-                                   const moe_routing* routing, uint8_t* q, float* s, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+moe_status quantize_tokens_common(bool mx, const moe_shape* shape, const void* src, int64_t C,
+                                  int gather, const moe_routing* routing, uint8_t* q, void* s,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_shape(shape));
   CHECK_PTR(src);
   CHECK_PTR(q);
@@ -528,6 +553,7 @@ moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int6
   TRY(check_ws(shape, MOE_OP_ROUTE, workspace, workspace_bytes));
   TRY(check_aligned16(src, "src"));
   TRY(check_aligned16(q, "q"));
+  if (((uintptr_t)s) & 3) return fail(MOE_ERR_INVALID_ARGUMENT, "s must be 4-byte aligned");
   const Layout L = layout(shape, MOE_OP_ROUTE);
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
@@ -536,8 +562,36 @@ moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int6
                           (int32_t*)at(workspace, L.order), blk_off, nullptr), "route_schedule");
   HIP_TRY(launch_quant_tok(c, "quant_tokens", src, C, gather ? routing->src_of : nullptr,
                            (int)shape->k, (int)C, routing->offsets, blk_off, (int)shape->E,
-                           (int)nblk_max(shape), q, s), "quant_tokens");
+                           (int)nblk_max(shape), q, s, mx), "quant_tokens");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                            uint8_t* q, float* s, void* stream) {
+  return quantize_common(false, kind, src, n0, n1, n2, q, s, stream);
+}
+
+moe_status moe_quantize_mxfp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                              uint8_t* q, uint8_t* s, void* stream) {
+  return quantize_common(true, kind, src, n0, n1, n2, q, s, stream);
+}
+
+moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int64_t C, int gather,
+                                   const moe_routing* routing, uint8_t* q, float* s, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return quantize_tokens_common(false, shape, src, C, gather, routing, q, s, workspace,
+                                workspace_bytes, stream);
+}
+
+moe_status moe_quantize_tokens_mxfp8(const moe_shape* shape, const void* src, int64_t C, int gather,
+                                     const moe_routing* routing, uint8_t* q, uint8_t* s,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_tokens_common(true, shape, src, C, gather, routing, q, s, workspace,
+                                workspace_bytes, stream);
 }
 
 const char* moe_status_string(moe_status s) {

@@ -146,48 +146,61 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
                          void* dW_gu, void* dW_d, float* G);
 
 // ---------------------------------------------------------------- fp8 path
-// Block quantisation to e4m3 (quant_fp8.hip).  rows: 1 x 128 blocks along the
-// rows of src [rows, C]; weight: 128 x 128 blocks of W [E, N, K], written as
-// [E, N, K] or transposed [E, K, N] (scales [E, N/128, K/128] or transposed);
-// tok: 128-row runs of each expert's segment x 1 column, written transposed
-// q [C, 128 nblk_max], s [C, nblk_max].
+// Block quantisation to e4m3 (quant_fp8.hip).  Two formats: blockwise (fp32
+// scales; rows 1 x 128, weights 128 x 128, tokens 128-row runs) and MX
+// (E8M0 scale bytes; rows 1 x 32, weights 1 x 32 along K and, transposed,
+// along N, tokens 32-row blocks inside the 128-row runs).  Scale buffers are
+// typed void*: fp32 values or E8M0 bytes.
+//   rows:   src [rows, C] -> q [rows, C], s [rows, C/128] fp32 or [rows, C/32] bytes;
+//   weight: W [E, N, K] -> q [E, N, K] and/or qt [E, K, N]; blockwise scales
+//           s [E, N/128, K/128] / st [E, K/128, N/128]; MX s [E, N, K/32] /
+//           st [E, K, N/32];
+//   tok:    128-row runs of each expert's segment, written transposed q [C,
+//           128 nblk_max], one 32-bit scale word per run and column [C,
+//           nblk_max] (an fp32 scale, or four E8M0 codes).
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, float* s);
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx);
 hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
                                int K, uint8_t* q, float* s, uint8_t* qt, float* st);
+hipError_t launch_quant_weight_mx(const LaunchCtx& c, const char* name, const void* W, int E, int N,
+                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st);
 hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                             const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
-                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, float* s);
+                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
+                            bool mx);
 
-// fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd, plus dH's 1x128
-// e4m3 codes dhq [R,2I] and scales dhs [R,2I/128] (I % 128 == 0).
-hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const void* G, const void* H,
+// fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd from an fp32 G
+// [R,I], plus dH's e4m3 row codes dhq [R,2I] and scales dhs (I % 128 == 0).
+hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
                                  const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
-                                 float* dw, uint8_t* dhq, float* dhs);
+                                 float* dw, uint8_t* dhq, void* dhs, bool mx);
 
 // Transposed weight codes the fp8 forward leaves in `saved` for the backward.
 struct Fp8Saved {
-  uint8_t* wdtq; float* wdts;    // [E,I,d], [E,I/128,d/128]
-  uint8_t* wgutq; float* wguts;  // [E,d,2I], [E,d/128,2I/128]
+  uint8_t* wdtq; void* wdts;    // [E,I,d] codes and scales
+  uint8_t* wgutq; void* wguts;  // [E,d,2I]
 };
 // Workspace of the fp8 forward: quantised x, weights and Aw with their scales.
 struct Fp8Fwd {
-  uint8_t* xq; float* xs;      // [T,d], [T,d/128]
-  uint8_t* wguq; float* wgus;  // [E,2I,d], [E,2I/128,d/128]
-  uint8_t* wdq; float* wds;    // [E,d,I], [E,d/128,I/128]
-  uint8_t* awq; float* aws;    // [R,I], [R,I/128]
+  bool mx;                     // MXFP8 rather than blockwise
+  uint8_t* xq; void* xs;       // [T,d]
+  uint8_t* wguq; void* wgus;   // [E,2I,d]
+  uint8_t* wdq; void* wds;     // [E,d,I]
+  uint8_t* awq; void* aws;     // [R,I]
   Fp8Saved sv;                 // written when saving for the backward (else null)
 };
 // Workspace of the fp8 backward.  tqa/tsa and tqb/tsb hold the two
 // token-blocked operands of one weight gradient at a time
 // ([max(d,2I)] and [max(I,d)] rows of 128 nblk_max bytes).
 struct Fp8Bwd {
-  uint8_t* doutq; float* douts;  // [T,d], [T,d/128]
-  Fp8Saved sv;                   // from the forward's saved buffer
-  uint8_t* dhq; float* dhs;      // [R,2I], [R,2I/128]
-  uint8_t* tqa; float* tsa;
-  uint8_t* tqb; float* tsb;
-  const int32_t* blk_off;        // [E+1]
+  bool mx;
+  uint8_t* doutq; void* douts;  // [T,d]
+  Fp8Saved sv;                  // from the forward's saved buffer
+  uint8_t* dhq; void* dhs;      // [R,2I]
+  uint8_t* tqa; void* tsa;
+  uint8_t* tqb; void* tsb;
+  float* G;                     // [R,I] the down dgrad's output
+  const int32_t* blk_off;       // [E+1]
   int nblk_max;
 };
 int fp8_dw_blocks(int I);

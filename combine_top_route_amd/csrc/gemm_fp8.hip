@@ -1,22 +1,28 @@
-// Grouped GEMMs of the expert MLPs on block-scaled fp8 operands (OCP e4m3,
-// fp32 scales; "Prime Intellect's Prime Mega MoE Trains Giant AI Models 55%
-// Faster", section "Precision and hardware support": blockwise FP8 with a
-// scale shared by each block) on gfx950 MFMA with fp32 accumulation.
+// Grouped GEMMs of the expert MLPs on block-scaled fp8 operands (OCP e4m3)
+// on gfx950 MFMA with fp32 accumulation, in two scale formats ("Prime
+// Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster", section
+// "Precision and hardware support": blockwise FP8, and MXFP8 with smaller
+// scaling groups).
 //
 // Every operand arrives quantised and contiguous along K (see
-// quant_fp8.hip), K is a multiple of 128, and one K step of 128 is exactly one
-// scale block.  Per step each 16x16 output tile is one
-// v_mfma_scale_f32_16x16x128_f8f6f4 with unit block exponents into a fresh
-// partial sum P, which is promoted into the fp32 accumulator with the product
-// of the two operands' scales: acc += P * (s_row * s_col).
+// quant_fp8.hip), K is a multiple of 128, and each output tile takes one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per K step of 128.
+//   blockwise: one K step is exactly one fp32 scale block.  The MFMA runs
+//     with unit block exponents into a fresh partial sum P, which is promoted
+//     into the fp32 accumulator with the product of the two operands'
+//     scales: acc += P * (s_row * s_col).
+//   MX: every lane hands the MFMA the E8M0 codes of its row's 32-value block
+//     (lane l: row l % 16, block l / 16 of the step), so the instruction
+//     applies the scales itself and accumulates straight into acc.
 //
 // Tile engine: 256 (token rows) x 256 (features) per work-group, eight waves
 // of 128 x 64, 128 bytes of K per stage for both operands (the same 64 KB
-// per stage as the bf16 engine, for twice the MFMA work).  Operands and their
-// per-row scales move global -> LDS with direct loads into a two-stage ring.
-// The MFMA's A operand is the feature side and its B operand the token side,
-// so a lane's four results share one token row and one scale of each side:
-// the promotion costs one multiply-add per result.
+// per stage as the bf16 engine, for twice the MFMA work).  Operands and one
+// 32-bit scale word per row and K step (an fp32 scale, or four E8M0 codes)
+// move global -> LDS with direct loads into a two-stage ring.  The MFMA's A
+// operand is the feature side and its B operand the token side, so a lane's
+// four results share one token row: the blockwise promotion costs one
+// multiply-add per result.
 #include "common.h"
 #include "tile.h"
 
@@ -37,6 +43,14 @@ constexpr int STB = 2 * OPB + 2 * SCB; // stage: token op | feature op | token s
 static_assert(TBM == kRowTile, "tile table is built for 256-row tiles");
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// Where the feature side's scales come from.
+enum ScaleMode {
+  SC_WEIGHT = 0,  // blockwise, one scale per 128 feature rows (a weight)
+  SC_ROW = 1,     // blockwise, one scale per feature row (token-blocked operand)
+  SC_MX = 2,      // MX: E8M0 codes per row and 32-value block, both sides
+};
 
 // LDS operand layout: [row][128 bytes], 16-byte chunk c of row r stored at
 // position c ^ swz8(r).  The swizzle depends on row bits 1..3 only, so the 16
@@ -76,14 +90,17 @@ struct Op8 {
   }
 };
 
-// MFMA operand of 16 rows: lane holds row lane % 16 of the fragment, bytes
-// 32 (lane / 16) .. +31 of the stage's K range (chunks 2 (lane/16) and +1).
+// MFMA operand of 16 rows in the instruction's K order: lane l holds row
+// l % 16 of the fragment and, with g = l / 16, K bytes 16 g .. 16 g + 15 in
+// its first four registers and 64 + 16 g .. +15 in the last four (chunks g
+// and g + 4 of the stage).  The instruction's 32-value scale block b is then
+// K bytes 32 b .. 32 b + 31, as the MX operands are encoded.
 struct FragOff {
   int lo, hi;  // byte offsets of this lane's two chunks from the fragment's first row
   __device__ FragOff() {
-    const int lane = threadIdx.x & 63, r = lane & 15, c = 2 * (lane >> 4);
+    const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
     lo = r * KB + ((c ^ swz8(r)) << 4);
-    hi = r * KB + (((c + 1) ^ swz8(r)) << 4);
+    hi = r * KB + (((c + 4) ^ swz8(r)) << 4);
   }
 };
 __device__ __forceinline__ i32x8_t frag8(const lds_t* s, const FragOff& o) {
@@ -97,14 +114,14 @@ __device__ __forceinline__ i32x8_t frag8(const lds_t* s, const FragOff& o) {
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 
-// Scales: waves 0-3 load the token rows' scales (rows 64w .. 64w+63), waves
-// 4-7 the feature rows' (rows 64(w-4) ..); sp is the lane's source at the
-// current stage, advanced by one float per K step.
+// Scales: waves 0-3 load the token rows' scale words (rows 64w .. 64w+63),
+// waves 4-7 the feature rows' (rows 64(w-4) ..); sp is the lane's source at
+// the current stage, advanced by one word per K step.
 
 // Part I of a stage's loads: token-operand instruction I / 2 (even I) or
 // feature-operand instruction I / 2 (odd I); part 0 adds the scales.
 template <int I>
-__device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const float* sp, lds_t* dst) {
+__device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst) {
   constexpr int q = I / 2;
   if constexpr (I % 2 == 0) ot.issue<q, q + 1>(dst);
   else of.issue<q, q + 1>(dst + OPB);
@@ -112,14 +129,14 @@ __device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const f
 }
 
 // ---------------------------------------------------------------------------
-// Main loop over nkb K steps.  ROW_SCALE_F: the feature side has a scale per
-// row (token-blocked operands) rather than per 128 rows (weights), so each of
-// a lane's four results takes its own feature scale.
+// Main loop over nkb K steps.  SC_ROW: the feature side has a scale per row
+// (token-blocked operands) rather than per 128 rows (weights), so each of a
+// lane's four results takes its own feature scale.
 // acc[i][j][r]: token wave_m*128 + 16 i + lane % 16, feature
 // wave_n*64 + 16 j + 4 (lane / 16) + r.
 // ---------------------------------------------------------------------------
-template <bool ROW_SCALE_F, bool PRE, int I>
-__device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const float* sp, lds_t* dst,
+template <int SC, bool PRE, int I>
+__device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst,
                                         const i32x8_t (&f)[TN], const i32x8_t& t,
                                         const lds_f32_t* SAw, float& sa, const f32x4_t (&sb)[TN],
                                         f32x4_t (&acc)[TM][TN]) {
@@ -132,7 +149,7 @@ __device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const floa
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const f32x4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, zero, 0, 0, 0, 127, 0, 127);
-    if constexpr (ROW_SCALE_F) {
+    if constexpr (SC == SC_ROW) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r] * sb[j][r], sa, acc[I][j][r]);
     } else {
@@ -149,8 +166,8 @@ __device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const floa
 
 // One K step on the stage in `cur`; PRE: also load the next stage into `dst`
 // (a branch-free body, so the sub-step boundaries hold).
-template <bool ROW_SCALE_F, bool PRE>
-__device__ __forceinline__ void kstep(Op8& ot, Op8& of, const float*& sp, const lds_t* cur,
+template <int SC, bool PRE>
+__device__ __forceinline__ void kstep(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
                                       lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
   const int wm = wave_m(), wn = wave_n();
   const int lane = threadIdx.x & 63;
@@ -164,7 +181,7 @@ __device__ __forceinline__ void kstep(Op8& ot, Op8& of, const float*& sp, const 
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int fr = wn * 64 + j * 16 + 4 * (lane >> 4);
-    if constexpr (ROW_SCALE_F) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
+    if constexpr (SC == SC_ROW) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
     else sb[j][0] = SB[fr];
   }
   const lds_t* tb = cur + wm * 128 * KB;       // this wave's token rows
@@ -174,20 +191,20 @@ __device__ __forceinline__ void kstep(Op8& ot, Op8& of, const float*& sp, const 
   for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
   i32x8_t t0 = frag8(tb, fo);
   i32x8_t t1 = frag8(tb + 16 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 0>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  substep<SC, PRE, 0>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
   t0 = frag8(tb + 32 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 1>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  substep<SC, PRE, 1>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
   t1 = frag8(tb + 48 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 2>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  substep<SC, PRE, 2>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
   t0 = frag8(tb + 64 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 3>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  substep<SC, PRE, 3>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
   t1 = frag8(tb + 80 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 4>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  substep<SC, PRE, 4>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
   t0 = frag8(tb + 96 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 5>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  substep<SC, PRE, 5>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
   t1 = frag8(tb + 112 * KB, fo);
-  substep<ROW_SCALE_F, PRE, 6>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
-  substep<ROW_SCALE_F, PRE, 7>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  substep<SC, PRE, 6>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
+  substep<SC, PRE, 7>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
   if constexpr (PRE) {
     ot.advance();
     of.advance();
@@ -195,8 +212,78 @@ __device__ __forceinline__ void kstep(Op8& ot, Op8& of, const float*& sp, const 
   }
 }
 
-template <bool ROW_SCALE_F>
-__device__ __forceinline__ void mainloop8(Op8& ot, Op8& of, const float* sp, int nkb, char* smem,
+// MX sub-step I: the MFMA applies the E8M0 codes (byte 0 of each scale
+// operand) and accumulates in place.  st: this lane's token-row code of
+// sub-tile I; sf[j]: its feature-row code of sub-tile j.
+template <bool PRE, int I>
+__device__ __forceinline__ void substep_mx(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst,
+                                           const i32x8_t (&f)[TN], const i32x8_t& t, const lds_u8_t* SAl,
+                                           int& st, const int (&sf)[TN], f32x4_t (&acc)[TM][TN]) {
+  if constexpr (PRE && I == 0) {
+    issue_step<0>(ot, of, sp, dst); issue_step<1>(ot, of, sp, dst); issue_step<2>(ot, of, sp, dst);
+    issue_step<3>(ot, of, sp, dst); issue_step<4>(ot, of, sp, dst); issue_step<5>(ot, of, sp, dst);
+    issue_step<6>(ot, of, sp, dst); issue_step<7>(ot, of, sp, dst);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    acc[I][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, acc[I][j], 0, 0, 0, sf[j], 0, st);
+  if constexpr (I + 1 < TM) st = SAl[(I + 1) * 16 * 4];  // token code of the next sub-step
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool PRE>
+__device__ __forceinline__ void kstep_mx(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
+                                         lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
+  const int wm = wave_m(), wn = wave_n();
+  const int lane = threadIdx.x & 63;
+  wait_vmcnt<0>();
+  barrier_lds();
+  // scale words [row] of 4 codes; this lane's code: row lane % 16 of each
+  // sub-tile, block lane / 16
+  const int lo = (lane & 15) * 4 + (lane >> 4);
+  const lds_u8_t* SAl = (const lds_u8_t*)(cur + 2 * OPB) + wm * 128 * 4 + lo;
+  const lds_u8_t* SBl = (const lds_u8_t*)(cur + 2 * OPB + SCB) + wn * 64 * 4 + lo;
+  int st = SAl[0];
+  int sf[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sf[j] = SBl[j * 16 * 4];
+  const lds_t* tb = cur + wm * 128 * KB;
+  const lds_t* fb = cur + OPB + wn * 64 * KB;
+  i32x8_t f[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
+  i32x8_t t0 = frag8(tb, fo);
+  i32x8_t t1 = frag8(tb + 16 * KB, fo);
+  substep_mx<PRE, 0>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
+  t0 = frag8(tb + 32 * KB, fo);
+  substep_mx<PRE, 1>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
+  t1 = frag8(tb + 48 * KB, fo);
+  substep_mx<PRE, 2>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
+  t0 = frag8(tb + 64 * KB, fo);
+  substep_mx<PRE, 3>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
+  t1 = frag8(tb + 80 * KB, fo);
+  substep_mx<PRE, 4>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
+  t0 = frag8(tb + 96 * KB, fo);
+  substep_mx<PRE, 5>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
+  t1 = frag8(tb + 112 * KB, fo);
+  substep_mx<PRE, 6>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
+  substep_mx<PRE, 7>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
+  if constexpr (PRE) {
+    ot.advance();
+    of.advance();
+    sp += 1;
+  }
+}
+
+template <int SC, bool PRE>
+__device__ __forceinline__ void any_kstep(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
+                                          lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
+  if constexpr (SC == SC_MX) kstep_mx<PRE>(ot, of, sp, cur, dst, fo, acc);
+  else kstep<SC, PRE>(ot, of, sp, cur, dst, fo, acc);
+}
+
+template <int SC>
+__device__ __forceinline__ void mainloop8(Op8& ot, Op8& of, const uint32_t* sp, int nkb, char* smem,
                                           f32x4_t (&acc)[TM][TN]) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -213,10 +300,10 @@ __device__ __forceinline__ void mainloop8(Op8& ot, Op8& of, const float* sp, int
   sp += 1;
   int slot = 0;
   for (int kb = 0; kb + 1 < nkb; ++kb) {
-    kstep<ROW_SCALE_F, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+    any_kstep<SC, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
     slot ^= 1;
   }
-  kstep<ROW_SCALE_F, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+  any_kstep<SC, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -279,32 +366,38 @@ __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* top
 // ===========================================================================
 // Ragged-row GEMMs: token rows are an expert's segment of the sorted rows.
 // ===========================================================================
-enum Epi { EPI_STORE = 0, EPI_GATEUP = 1 };
+// EPI_STORE: bf16 result; EPI_GATEUP: SwiGLU and top-k weight; EPI_STORE_F32:
+// fp32 result (the down dgrad's G, which the SwiGLU backward re-encodes, so
+// it is not rounded to bf16 on the way).
+enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_STORE_F32 = 2 };
 
 struct Rows8Args {
   // token side: row r reads A + arow(r) * lda, arow = a_src ? a_src[r] / a_div : r;
-  // its scale at K step kb is As[arow * a_sld + kb]
+  // its scale word at K step kb is As[arow * a_sld + kb]
   const uint8_t* A;
   int64_t lda;
   const int32_t* a_src;
   int a_div;
-  const float* As;
+  const uint32_t* As;
   int64_t a_sld;
   // feature side (expert e): row n reads B + e * b_estride + wrow(n) * ldb,
-  // scale Bs[e * bs_estride + (wrow(n) / 128) * b_sld + kb].  gateup: 32-row
-  // blocks alternate gate rows (even) and up rows (odd).
+  // scale word Bs[e * bs_estride + (wrow(n) >> b_rshift) * b_sld + kb]
+  // (b_rshift 7: one blockwise scale per 128 rows; 0: MX codes per row).
+  // gateup: 32-row blocks alternate gate rows (even) and up rows (odd).
   const uint8_t* B;
   int64_t b_estride, ldb;
-  const float* Bs;
+  const uint32_t* Bs;
   int64_t bs_estride, b_sld;
+  int b_rshift;
   int gateup;
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
   const int32_t* offsets;
   const int32_t* tile_off;
   const int4* tiles;  // row-tile descriptors {expert, first row, segment end, 0}
   int E;
-  // EPI_STORE: C [R, ldc] bf16
+  // EPI_STORE: C [R, ldc] bf16; EPI_STORE_F32: Cf [R, ldc] fp32
   bf16_t* C;
+  float* Cf;
   int64_t ldc;
   // EPI_GATEUP: H [R,2I] (optional), Aout [R,I] = w_row * silu(g) * u
   bf16_t* H;
@@ -315,7 +408,8 @@ struct Rows8Args {
 };
 
 // TAG only tells launch sites with the same epilogue apart in profiles.
-template <int EPI, int TAG>
+// SC: SC_WEIGHT (blockwise) or SC_MX.
+template <int EPI, int TAG, int SC>
 __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
@@ -343,15 +437,15 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
     return w < p.N ? w : 0;
   };
   const uint8_t* Be = p.B + (int64_t)e * p.b_estride;
-  const float* Bse = p.Bs + (int64_t)e * p.bs_estride;
+  const uint32_t* Bse = p.Bs + (int64_t)e * p.bs_estride;
   Op8 ot, of;
   ot.init([&](int row) { return p.A + arow(row) * p.lda; });
   of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
   const int srow = 64 * (wave_id() & 3) + lane;
-  const float* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_sld
-                                  : Bse + (int64_t)(wrow(srow) >> 7) * p.b_sld;
+  const uint32_t* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_sld
+                                     : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_sld;
   f32x4_t acc[TM][TN];
-  mainloop8<false>(ot, of, sp, p.K / KB, smem, acc);
+  mainloop8<SC>(ot, of, sp, p.K / KB, smem, acc);
 
   // ------------------------------------------------------------- epilogues
   barrier_lds();
@@ -364,6 +458,34 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
     barrier_lds();
     lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
                                p.N - nt * TBN);
+  } else if constexpr (EPI == EPI_STORE_F32) {
+    // two passes of 128 columns (the waves with wn = 2h, 2h + 1), 528-byte
+    // LDS rows so that a lane group's 16 rows hit distinct banks
+    constexpr int SF = 128 * 4 + 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h) barrier_lds();
+      if ((wn >> 1) == h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int row = r0w + i * 16 + (lane & 15);
+            const int col = (wn & 1) * 64 + j * 16 + 4 * (lane >> 4);
+            *(__attribute__((address_space(3))) f32x4_t*)(lds + row * SF + col * 4) = acc[i][j];
+          }
+      }
+      barrier_lds();
+      float* Cb = p.Cf + (int64_t)m0 * p.ldc + nt * TBN + 128 * h;
+      const int col_lim = p.N - nt * TBN - 128 * h;
+#pragma unroll 4
+      for (int q = threadIdx.x; q < TBM * 32; q += NTHR) {
+        const int row = q >> 5, c4 = q & 31;
+        if (row < rows_valid && c4 * 4 < col_lim)
+          *(f32x4_t*)(Cb + (int64_t)row * p.ldc + c4 * 4) =
+              *(const __attribute__((address_space(3))) f32x4_t*)(lds + row * SF + c4 * 16);
+      }
+    }
   } else if constexpr (EPI == EPI_GATEUP) {
     // features j = 0, 1 are gate columns wn*32 + 16 j + ..., j = 2, 3 the up
     // columns of the same gate columns
@@ -396,13 +518,14 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
 // Weight gradients: dW[e][m, n] = sum over expert e's token blocks of
 // A(m, k) B(n, k) s_A(m, blk) s_B(n, blk).  Both operands are transposed
 // token-blocked ([features][padded rows], see quant_fp8.hip): expert e owns
-// K bytes [128 blk_off[e], 128 blk_off[e+1]) of every row.
+// K bytes [128 blk_off[e], 128 blk_off[e+1]) of every row, and one scale
+// word per row and 128-row run.
 // ===========================================================================
 struct Wgrad8Args {
-  const uint8_t* A;  // output-row side, [M][ldk]
-  const float* As;   // [M][nblk]
-  const uint8_t* B;  // output-column side, [N][ldk]
-  const float* Bs;   // [N][nblk]
+  const uint8_t* A;    // output-row side, [M][ldk]
+  const uint32_t* As;  // [M][nblk]
+  const uint8_t* B;    // output-column side, [N][ldk]
+  const uint32_t* Bs;  // [N][nblk]
   int64_t ldk, nblk;
   int M, N, m_tiles, n_tiles, E;
   const int32_t* blk_off;
@@ -411,7 +534,8 @@ struct Wgrad8Args {
   int64_t c_estride;
 };
 
-template <int TAG>
+// SC: SC_ROW (blockwise) or SC_MX.
+template <int TAG, int SC>
 __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
@@ -429,10 +553,10 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   ot.init([&](int row) { return p.A + (int64_t)mrow(row) * p.ldk + (int64_t)b0 * KB; });
   of.init([&](int row) { return p.B + (int64_t)nrow(row) * p.ldk + (int64_t)b0 * KB; });
   const int srow = 64 * (wave_id() & 3) + (threadIdx.x & 63);
-  const float* sp = wave_id() < 4 ? p.As + (int64_t)mrow(srow) * p.nblk + b0
-                                  : p.Bs + (int64_t)nrow(srow) * p.nblk + b0;
+  const uint32_t* sp = wave_id() < 4 ? p.As + (int64_t)mrow(srow) * p.nblk + b0
+                                     : p.Bs + (int64_t)nrow(srow) * p.nblk + b0;
   f32x4_t acc[TM][TN];
-  mainloop8<true>(ot, of, sp, nkb, smem, acc);
+  mainloop8<SC>(ot, of, sp, nkb, smem, acc);
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   constexpr int S = ep_stride<TBN>();
@@ -447,7 +571,8 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kRingBytes = (size_t)2 * STB;
 constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
 constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
-constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
+constexpr size_t kStoreF32Epi = (size_t)TBM * (128 * 4 + 16);
+constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreF32Epi), cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <class K>
@@ -456,121 +581,156 @@ hipError_t allow_smem(K kernel) {
                              (int)kSmem);
 }
 
-template <int EPI, int TAG>
-hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R) {
+template <int EPI, int TAG, int SC>
+hipError_t launch_rows8_sc(const LaunchCtx& c, const char* name, const Rows8Args& p, int R) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(rows8_kernel<EPI, TAG>);
+    hipError_t e = allow_smem(rows8_kernel<EPI, TAG, SC>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
-  MOE_LAUNCH(c, name, (rows8_kernel<EPI, TAG>), dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, (rows8_kernel<EPI, TAG, SC>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
-template <int TAG>
-hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args& p) {
+template <int EPI, int TAG>
+hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R, bool mx) {
+  p.b_rshift = mx ? 0 : 7;
+  return mx ? launch_rows8_sc<EPI, TAG, SC_MX>(c, name, p, R)
+            : launch_rows8_sc<EPI, TAG, SC_WEIGHT>(c, name, p, R);
+}
+
+template <int TAG, int SC>
+hipError_t launch_wgrad8_sc(const LaunchCtx& c, const char* name, const Wgrad8Args& p) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = allow_smem(wgrad8_kernel<TAG>);
+    hipError_t e = allow_smem(wgrad8_kernel<TAG, SC>);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned nblocks = (unsigned)(cdiv(p.E, 8) * 8 * p.m_tiles * p.n_tiles);
-  MOE_LAUNCH(c, name, wgrad8_kernel<TAG>, dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, (wgrad8_kernel<TAG, SC>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
+}
+
+template <int TAG>
+hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args& p, bool mx) {
+  return mx ? launch_wgrad8_sc<TAG, SC_MX>(c, name, p) : launch_wgrad8_sc<TAG, SC_ROW>(c, name, p);
 }
 
 }  // namespace
 
 int fp8_dw_blocks(int) { return 1; }
 
+namespace {
+// Scale words per expert of a weight [N, K] encoded for a GEMM with K along
+// its rows: blockwise (N/128) x (K/128) fp32 scales, MX N x K/32 codes.
+int64_t wscale_words(int64_t N, int64_t K, bool mx) { return (mx ? N : N / 128) * (K / 128); }
+
+hipError_t quant_weights(const LaunchCtx& c, const char* name, const void* W, int E, int N, int K,
+                         bool mx, uint8_t* q, void* s, uint8_t* qt, void* st) {
+  if (mx)
+    return launch_quant_weight_mx(c, name, W, E, N, K, q, (uint8_t*)s, qt, (uint8_t*)st);
+  return launch_quant_weight(c, name, W, E, N, K, q, (float*)s, qt, (float*)st);
+}
+}  // namespace
+
 hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q, void* H, void* Aw,
                          void* Yw) {
   const int64_t I = a.I, d = a.d;
-  hipError_t err;
-  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs));
+  const bool mx = q.mx;
+  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx));
   // both layouts in one pass: the transposed codes serve the backward's dgrads
-  HIP_RET(launch_quant_weight(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, q.wguq, q.wgus,
-                              q.sv.wgutq, q.sv.wguts));
-  HIP_RET(launch_quant_weight(c, "quant_w_down", a.w_down, a.E, a.d, a.I, q.wdq, q.wds, q.sv.wdtq,
-                              q.sv.wdts));
+  HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, q.wguq, q.wgus,
+                        q.sv.wgutq, q.sv.wguts));
+  HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, q.wdq, q.wds, q.sv.wdtq,
+                        q.sv.wdts));
   {  // gate/up GEMM on token rows gathered from xq; SwiGLU and top-k weight in the epilogue
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
-    p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.xs; p.a_sld = d / 128;
+    p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
+    p.As = (const uint32_t*)q.xs; p.a_sld = d / 128;
     p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
-    p.Bs = q.wgus; p.bs_estride = (2 * I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 1;
+    p.Bs = (const uint32_t*)q.wgus; p.bs_estride = wscale_words(2 * I, d, mx); p.b_sld = d / 128;
+    p.gateup = 1;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
-    HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R));
+    HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R, mx));
   }
-  HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws));
+  HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws, mx));
   Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
   p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
-  p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1; p.As = q.aws; p.a_sld = I / 128;
+  p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1;
+  p.As = (const uint32_t*)q.aws; p.a_sld = I / 128;
   p.B = q.wdq; p.b_estride = d * I; p.ldb = I;
-  p.Bs = q.wds; p.bs_estride = (d / 128) * (I / 128); p.b_sld = I / 128; p.gateup = 0;
+  p.Bs = (const uint32_t*)q.wds; p.bs_estride = wscale_words(d, I, mx); p.b_sld = I / 128;
+  p.gateup = 0;
   p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
   p.C = (bf16_t*)Yw; p.ldc = d;
-  (void)err;
-  return launch_rows8<EPI_STORE, 0>(c, "gemm_down_fwd", p, a.R);
+  return launch_rows8<EPI_STORE, 0>(c, "gemm_down_fwd", p, a.R, mx);
 }
 
 hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
                          const void* H, const void* Aw, void* dH, void* dXp, float* dwp, void* dW_gu,
                          void* dW_d) {
   const int64_t I = a.I, d = a.d;
-  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts));
-  {  // down dgrad: G = dout_t W_down[e] into the dXp buffer (free until the
-     // gate/up dgrad); one row pass then forms dH, <G, a> and dH's 1x128 codes
+  const bool mx = q.mx;
+  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx));
+  {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
+     // <G, a> and dH's row codes
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
-    p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k; p.As = q.douts; p.a_sld = d / 128;
+    p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
+    p.As = (const uint32_t*)q.douts; p.a_sld = d / 128;
     p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
-    p.Bs = q.sv.wdts; p.bs_estride = (I / 128) * (d / 128); p.b_sld = d / 128; p.gateup = 0;
+    p.Bs = (const uint32_t*)q.sv.wdts; p.bs_estride = wscale_words(I, d, mx); p.b_sld = d / 128;
+    p.gateup = 0;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
-    p.C = (bf16_t*)dXp; p.ldc = I;
-    HIP_RET(launch_rows8<EPI_STORE, 2>(c, "gemm_down_dgrad", p, a.R));
-    HIP_RET(launch_swiglu_bwd_fp8(c, dXp, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp, q.dhq, q.dhs));
+    p.Cf = q.G; p.ldc = I;
+    HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx));
+    HIP_RET(launch_swiglu_bwd_fp8(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp, q.dhq, q.dhs, mx));
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
-    p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1; p.As = q.dhs; p.a_sld = 2 * I / 128;
+    p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
+    p.As = (const uint32_t*)q.dhs; p.a_sld = 2 * I / 128;
     p.B = q.sv.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
-    p.Bs = q.sv.wguts; p.bs_estride = (d / 128) * (2 * I / 128); p.b_sld = 2 * I / 128; p.gateup = 0;
+    p.Bs = (const uint32_t*)q.sv.wguts; p.bs_estride = wscale_words(d, 2 * I, mx); p.b_sld = 2 * I / 128;
+    p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
-    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R));
+    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx));
   }
   const int nb = q.nblk_max;
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
     HIP_RET(launch_quant_tok(c, "quant_dout_tok", dout, d, a.src_of, a.k, a.d, a.offsets, q.blk_off,
-                             a.E, nb, q.tqa, q.tsa));
+                             a.E, nb, q.tqa, q.tsa, mx));
     HIP_RET(launch_quant_tok(c, "quant_aw_tok", Aw, I, nullptr, 1, a.I, a.offsets, q.blk_off, a.E, nb,
-                             q.tqb, q.tsb));
+                             q.tqb, q.tsb, mx));
     Wgrad8Args p = {};
-    p.A = q.tqa; p.As = q.tsa; p.B = q.tqb; p.Bs = q.tsb; p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
+    p.ldk = (int64_t)nb * KB; p.nblk = nb;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN); p.E = a.E;
     p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
-    HIP_RET(launch_wgrad8<0>(c, "gemm_down_wgrad", p));
+    HIP_RET(launch_wgrad8<0>(c, "gemm_down_wgrad", p, mx));
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
     HIP_RET(launch_quant_tok(c, "quant_dh_tok", dH, 2 * I, nullptr, 1, 2 * a.I, a.offsets, q.blk_off,
-                             a.E, nb, q.tqa, q.tsa));
+                             a.E, nb, q.tqa, q.tsa, mx));
     HIP_RET(launch_quant_tok(c, "quant_x_tok", a.x, d, a.src_of, a.k, a.d, a.offsets, q.blk_off, a.E,
-                             nb, q.tqb, q.tsb));
+                             nb, q.tqb, q.tsb, mx));
     Wgrad8Args p = {};
-    p.A = q.tqa; p.As = q.tsa; p.B = q.tqb; p.Bs = q.tsb; p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
+    p.ldk = (int64_t)nb * KB; p.nblk = nb;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.E = a.E; p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
-    HIP_RET(launch_wgrad8<1>(c, "gemm_gateup_wgrad", p));
+    HIP_RET(launch_wgrad8<1>(c, "gemm_gateup_wgrad", p, mx));
   }
   return hipSuccess;
 }

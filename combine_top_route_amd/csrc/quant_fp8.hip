@@ -1,4 +1,4 @@
-// Block quantisation of GEMM operands to OCP e4m3 with fp32 scales.
+// Block quantisation of GEMM operands to OCP e4m3.
 //
 // Blockwise FP8 shares one scale among a block of values ("Prime
 // Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster", section
@@ -15,6 +15,18 @@
 // q * s.  The token-blocked operands are written transposed ([column][row],
 // each expert's rows padded with zeros to a multiple of 128) so that every
 // GEMM operand is contiguous along its K dimension.
+//
+// MXFP8 (same section: smaller scaling groups) uses the OCP microscaling
+// layout instead: 32 values along each GEMM operand's K share a power-of-two
+// scale 2^X stored as an E8M0 byte (X + 127).  X is the smallest integer
+// with amax <= 448 * 2^X (the blockwise scale rounded up to a power of two,
+// so nothing saturates), at least -127, and 0 for an all-zero block; x / 2^X
+// is exact in fp32, so each code is the e4m3 rounding of the exact quotient.
+// Rows take 1 x 32 blocks; a weight is encoded twice, 1 x 32 along K for
+// the forward and 32 x 1 along N (written transposed) for the data
+// gradients; token operands take 32-row blocks inside the same 128-row
+// padded runs.  Four consecutive blocks' codes form one 32-bit word, so a
+// 128-wide K step of the GEMMs reads one word per row, as with fp32 scales.
 #include "common.h"
 
 namespace moe {
@@ -50,6 +62,39 @@ __device__ __forceinline__ void unpack8(const u32x4_t v, float (&f)[8]) {
   }
 }
 
+// MXFP8 block scale: E8M0 code X + 127 and the exact multiplier 2^-X.
+struct MxScale {
+  uint32_t code;
+  float inv;
+};
+__device__ __forceinline__ MxScale mx_scale(float amax) {
+  const uint32_t u = __float_as_uint(amax);  // amax >= 0
+  int X = 0;
+  if (u != 0) {
+    // amax = m 2^e with m in [1, 2) (subnormals give e = -127, far below the
+    // clamp): X = e - 8, plus one when m > 1.75 (448 = 1.75 * 2^8)
+    X = (int)(u >> 23) - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    X = X < -127 ? -127 : X;
+  }
+  return MxScale{(uint32_t)(X + 127), __uint_as_float((uint32_t)(127 - X) << 23)};
+}
+
+// Eight values times 2^-X (exact), as eight e4m3 codes.
+__device__ __forceinline__ u32x2_t quant8_mx(const float (&f)[8], float inv) {
+  u32x2_t q;
+  q[0] = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+  q[1] = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+  return q;
+}
+
+// Codes of lanes base, base + stride, base + 2 stride, base + 3 stride
+// packed little-endian into one word (every lane gets it).
+__device__ __forceinline__ uint32_t gather4_codes(uint32_t code, int base, int stride) {
+  return (uint32_t)__shfl((int)code, base, kWave) | ((uint32_t)__shfl((int)code, base + stride, kWave) << 8) |
+         ((uint32_t)__shfl((int)code, base + 2 * stride, kWave) << 16) |
+         ((uint32_t)__shfl((int)code, base + 3 * stride, kWave) << 24);
+}
+
 // Eight values divided by s, as eight e4m3 codes.
 __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
   u32x2_t q;
@@ -59,12 +104,14 @@ __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
 }
 
 // ---------------------------------------------------------------------------
-// 1 x 128 blocks along rows: src [rows, C] (leading dimension ld) -> q [rows,
-// C], s [rows, C/128].  A 16-lane group handles one block, 8 values a lane.
+// Blocks along rows: src [rows, C] (leading dimension ld) -> q [rows, C] and
+// s [rows, C/128] fp32 (1 x 128 blocks) or, MX, s [rows, C/32] E8M0 bytes
+// (1 x 32 blocks).  A 16-lane group handles 128 columns, 8 values a lane.
 // ---------------------------------------------------------------------------
+template <bool MX>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restrict__ src, int64_t ld,
                                                         int64_t rows, int C, uint8_t* __restrict__ q,
-                                                        float* __restrict__ s) {
+                                                        void* __restrict__ s) {
   const int nbc = C / 128;
   const int64_t nb = rows * nbc;
   const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -79,12 +126,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  if constexpr (MX) {
+    // four lanes per 32-value block
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const MxScale sc = mx_scale(amax);
+    const int lane = threadIdx.x & 63;
+    const uint32_t word = gather4_codes(sc.code, lane & ~15, 4);
+    if (!ok) return;
+    *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8_mx(f, sc.inv);
+    if (sl == 0) ((uint32_t*)s)[r * nbc + cb] = word;
+  } else {
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-  const float sc = block_scale(amax);
-  if (!ok) return;
-  *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8(f, sc);
-  if (sl == 0) s[r * nbc + cb] = sc;
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    const float sc = block_scale(amax);
+    if (!ok) return;
+    *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8(f, sc);
+    if (sl == 0) ((float*)s)[r * nbc + cb] = sc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -157,20 +216,104 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// MXFP8 weights W [E, N, K], encoded twice from one read: q [E, N, K] with
+// 1 x 32 blocks along K and scales s [E, N, K/32], and qt [E, K, N] (the
+// transpose) with 1 x 32 blocks along N and scales st [E, K, N/32]; either
+// pair may be null (not written).  One
+// work-group per 128 x 128 tile; thread t holds rows 4 (t % 32) .. +3 and
+// columns 16 (t / 32) .. +15 of it, so a row's 32-column block spans lanes
+// t and t ^ 32 and a column's 32-row block spans the 8 lanes t ^ 0..7.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __restrict__ W, int N, int K,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                             uint8_t* __restrict__ qt,
+                                                             uint8_t* __restrict__ st) {
+  __shared__ __attribute__((aligned(16))) uint32_t codes[128 * 33];  // [n][32 words], padded
+  const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
+  const int t = threadIdx.x;
+  const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
+  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128 + n0) * K + kb * 128 + k0;
+  float f[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float lo[8], hi[8];
+    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K), lo);
+    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K + 8), hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[j][i] = lo[i];
+      f[j][8 + i] = hi[i];
+    }
+  }
+  const int nbk32 = K / 32, nbn32 = N / 32;
+  // q, qt are kernel arguments: every branch on them is uniform
+  if (q) {  // forward layout: row blocks along K
+    MxScale rs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[j][i]));
+      rs[j] = mx_scale(fmaxf(a, __shfl_xor(a, 32, kWave)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        codes[(n0 + j) * 33 + (k0 >> 2) + w] =
+            e4m3x4(f[j][4 * w] * rs[j].inv, f[j][4 * w + 1] * rs[j].inv, f[j][4 * w + 2] * rs[j].inv,
+                   f[j][4 * w + 3] * rs[j].inv);
+    if (((t >> 5) & 1) == 0) {
+      uint8_t* sb = s + ((int64_t)e * N + nb * 128 + n0) * nbk32 + kb * 4 + (t >> 6);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sb[(int64_t)j * nbk32] = (uint8_t)rs[j].code;
+    }
+  }
+  if (qt) {  // transposed layout: column blocks along N, four rows' codes per word
+    uint8_t* qb = qt + (int64_t)e * K * N + (int64_t)(kb * 128 + k0) * N + nb * 128 + n0;
+    uint8_t* sb = st + ((int64_t)e * K + kb * 128 + k0) * nbn32 + nb * 4 + ((t & 31) >> 3);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = fmaxf(fmaxf(fabsf(f[0][i]), fabsf(f[1][i])), fmaxf(fabsf(f[2][i]), fabsf(f[3][i])));
+      a = fmaxf(a, __shfl_xor(a, 1, kWave));
+      a = fmaxf(a, __shfl_xor(a, 2, kWave));
+      a = fmaxf(a, __shfl_xor(a, 4, kWave));
+      const MxScale cs = mx_scale(a);
+      *(uint32_t*)(qb + (int64_t)i * N) =
+          e4m3x4(f[0][i] * cs.inv, f[1][i] * cs.inv, f[2][i] * cs.inv, f[3][i] * cs.inv);
+      if ((t & 7) == 0) sb[(int64_t)i * nbn32] = (uint8_t)cs.code;
+    }
+  }
+  if (!q) return;
+  __syncthreads();
+  // forward rows leave as 128 contiguous bytes each
+  uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int idx = p * 256 + t;  // word idx % 32 of row idx / 32
+    const int n = idx >> 5, w = idx & 31;
+    *(uint32_t*)(qb + (int64_t)n * K + 4 * w) = codes[n * 33 + w];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Token blocks, transposed.  Block b (of blk_off[E] in all) is the
 // (b - blk_off[e])-th run of 128 rows of expert e's segment; row i of the run
 // is src row srow(offsets[e] + 128 * (b - blk_off[e]) + i), with srow(r) =
 // src_of[r] / kdiv (token rows of x or dout) or r.  A work-group handles 64
-// columns: q[c][128 b + i] = code (0 past the segment), s[c][b] = scale.
+// columns: q[c][128 b + i] = code (0 past the segment) and word b of scale
+// row c (ldw words per row): the run's fp32 scale or, MX, the E8M0 codes of
+// its four 32-row blocks.
 // ---------------------------------------------------------------------------
 constexpr int kTokCols = 64;
 
+template <bool MX>
 __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict__ src, int64_t ld,
                                                        const int32_t* __restrict__ src_of, int kdiv,
                                                        const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ blk_off, int E,
                                                        uint8_t* __restrict__ q, int64_t ldq,
-                                                       float* __restrict__ s, int64_t lds) {
+                                                       uint32_t* __restrict__ s, int64_t ldw) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 136];  // [row][64 bf16], 136-byte rows
   const int b = blockIdx.x;
   if (b >= blk_off[E]) return;
@@ -210,54 +353,79 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
     a0 = fmaxf(a0, fabsf(f0[i]));
     a1 = fmaxf(a1, fabsf(f1[i]));
   }
-#pragma unroll
-  for (int off = 4; off >= 1; off >>= 1) {
-    a0 = fmaxf(a0, __shfl_xor(a0, off, kWave));
-    a1 = fmaxf(a1, __shfl_xor(a1, off, kWave));
-  }
-  const float s0 = block_scale(a0), s1 = block_scale(a1);
   const int c = c0 + 2 * cp;
   u32x4_t q0, q1;
+  uint32_t w0, w1;
+  if constexpr (MX) {  // a 32-row block spans lanes rg = 2m, 2m + 1
+    a0 = fmaxf(a0, __shfl_xor(a0, 1, kWave));
+    a1 = fmaxf(a1, __shfl_xor(a1, 1, kWave));
+    const MxScale s0 = mx_scale(a0), s1 = mx_scale(a1);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    q0[w] = e4m3x4(__fdiv_rn(f0[4 * w], s0), __fdiv_rn(f0[4 * w + 1], s0), __fdiv_rn(f0[4 * w + 2], s0),
-                   __fdiv_rn(f0[4 * w + 3], s0));
-    q1[w] = e4m3x4(__fdiv_rn(f1[4 * w], s1), __fdiv_rn(f1[4 * w + 1], s1), __fdiv_rn(f1[4 * w + 2], s1),
-                   __fdiv_rn(f1[4 * w + 3], s1));
+    for (int w = 0; w < 4; ++w) {
+      q0[w] = e4m3x4(f0[4 * w] * s0.inv, f0[4 * w + 1] * s0.inv, f0[4 * w + 2] * s0.inv, f0[4 * w + 3] * s0.inv);
+      q1[w] = e4m3x4(f1[4 * w] * s1.inv, f1[4 * w + 1] * s1.inv, f1[4 * w + 2] * s1.inv, f1[4 * w + 3] * s1.inv);
+    }
+    const int base = (t & 63) & ~7;
+    w0 = gather4_codes(s0.code, base, 2);
+    w1 = gather4_codes(s1.code, base, 2);
+  } else {
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      a0 = fmaxf(a0, __shfl_xor(a0, off, kWave));
+      a1 = fmaxf(a1, __shfl_xor(a1, off, kWave));
+    }
+    const float s0 = block_scale(a0), s1 = block_scale(a1);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      q0[w] = e4m3x4(__fdiv_rn(f0[4 * w], s0), __fdiv_rn(f0[4 * w + 1], s0), __fdiv_rn(f0[4 * w + 2], s0),
+                     __fdiv_rn(f0[4 * w + 3], s0));
+      q1[w] = e4m3x4(__fdiv_rn(f1[4 * w], s1), __fdiv_rn(f1[4 * w + 1], s1), __fdiv_rn(f1[4 * w + 2], s1),
+                     __fdiv_rn(f1[4 * w + 3], s1));
+    }
+    w0 = __float_as_uint(s0);
+    w1 = __float_as_uint(s1);
   }
   *(u32x4_t*)(q + (int64_t)c * ldq + (int64_t)b * 128 + rg * 16) = q0;
   *(u32x4_t*)(q + (int64_t)(c + 1) * ldq + (int64_t)b * 128 + rg * 16) = q1;
   if (rg == 0) {
-    s[(int64_t)c * lds + b] = s0;
-    s[(int64_t)(c + 1) * lds + b] = s1;
+    s[(int64_t)c * ldw + b] = w0;
+    s[(int64_t)(c + 1) * ldw + b] = w1;
   }
 }
 
-// SwiGLU backward of one row per wave from G = dout_t W_down[e] (bf16), as
+// SwiGLU backward of one row per wave from G = dout_t W_down[e] (fp32), as
 // in the bf16 path, that also encodes the bf16-rounded dH in 1 x 128 blocks
-// (the A operand of the gate/up dgrad).  Lane l handles the 8-column chunks
-// l, l + 64, ... of the gate and of the up half; a 16-lane group covers one
-// 128-column block.  Requires I % 128 == 0.
+// (fp32 scales) or, MX, 1 x 32 blocks (a word of four E8M0 codes per 128
+// columns): the A operand of the gate/up dgrad.  Lane l handles the 8-column
+// chunks l, l + 64, ... of the gate and of the up half; a 16-lane group
+// covers 128 columns.  Requires I % 128 == 0.
+template <bool MX>
 __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
-    const u32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
+    const f32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
     const int32_t* __restrict__ src_of, int R, int chunks, u32x4_t* __restrict__ dH,
-    float* __restrict__ dw, uint8_t* __restrict__ dhq, float* __restrict__ dhs) {
+    float* __restrict__ dw, uint8_t* __restrict__ dhq, uint32_t* __restrict__ dhs) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   const int lane = threadIdx.x & 63;
   const float wr = topk_w[src_of[r]];
-  const u32x4_t* Gr = G + (int64_t)r * chunks;
+  const f32x4_t* Gr = G + (int64_t)r * 2 * chunks;  // 8 columns = two float4
   const u32x4_t* Hg = H + (int64_t)r * 2 * chunks;
   u32x4_t* Dr = dH + (int64_t)r * 2 * chunks;
   uint8_t* Qr = dhq + (int64_t)r * 2 * chunks * 8;
-  float* Sr = dhs + (int64_t)r * (2 * chunks / 16);
+  uint32_t* Sr = dhs + (int64_t)r * (2 * chunks / 16);
   float part = 0.0f;
   for (int c0 = 0; c0 < chunks; c0 += kWave) {  // uniform trip count
     const int c = c0 + lane;
     const bool ok = c < chunks;  // whole 16-lane groups share ok (chunks % 16 == 0)
     float gv[8], g[8], u[8], dg[8], du[8];
     u32x4_t zero = {0, 0, 0, 0};
-    unpack8(ok ? Gr[c] : zero, gv);
+    const f32x4_t fz = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4_t g0 = ok ? Gr[2 * c] : fz, g1 = ok ? Gr[2 * c + 1] : fz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gv[i] = g0[i];
+      gv[4 + i] = g1[i];
+    }
     unpack8(ok ? Hg[c] : zero, g);
     unpack8(ok ? Hg[chunks + c] : zero, u);
 #pragma unroll
@@ -283,20 +451,39 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
       ag = fmaxf(ag, fabsf(dg[i]));
       au = fmaxf(au, fabsf(du[i]));
     }
+    u32x2_t qg, qu;
+    uint32_t wg, wu;
+    if constexpr (MX) {  // four lanes per 32-column block
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
-      au = fmaxf(au, __shfl_xor(au, off, kWave));
+      for (int off = 2; off >= 1; off >>= 1) {
+        ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
+        au = fmaxf(au, __shfl_xor(au, off, kWave));
+      }
+      const MxScale sgate = mx_scale(ag), sup = mx_scale(au);
+      qg = quant8_mx(dg, sgate.inv);
+      qu = quant8_mx(du, sup.inv);
+      wg = gather4_codes(sgate.code, lane & ~15, 4);
+      wu = gather4_codes(sup.code, lane & ~15, 4);
+    } else {
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
+        au = fmaxf(au, __shfl_xor(au, off, kWave));
+      }
+      const float sgate = block_scale(ag), sup = block_scale(au);
+      qg = quant8(dg, sgate);
+      qu = quant8(du, sup);
+      wg = __float_as_uint(sgate);
+      wu = __float_as_uint(sup);
     }
-    const float sgate = block_scale(ag), sup = block_scale(au);
     if (ok) {
       Dr[c] = pg;
       Dr[chunks + c] = pu;
-      *(u32x2_t*)(Qr + c * 8) = quant8(dg, sgate);
-      *(u32x2_t*)(Qr + (chunks + c) * 8) = quant8(du, sup);
+      *(u32x2_t*)(Qr + c * 8) = qg;
+      *(u32x2_t*)(Qr + (chunks + c) * 8) = qu;
       if ((lane & 15) == 0) {
-        Sr[c / 16] = sgate;
-        Sr[(chunks + c) / 16] = sup;
+        Sr[c / 16] = wg;
+        Sr[(chunks + c) / 16] = wu;
       }
     }
   }
@@ -307,21 +494,30 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
 
 }  // namespace
 
-hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const void* G, const void* H,
+hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
                                  const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
-                                 float* dw, uint8_t* dhq, float* dhs) {
-  MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel, dim3((R + 3) / 4), dim3(256), 0,
-             (const u32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
-             dhs);
+                                 float* dw, uint8_t* dhq, void* dhs, bool mx) {
+  if (mx)
+    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<true>, dim3((R + 3) / 4), dim3(256), 0,
+               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
+               (uint32_t*)dhs);
+  else
+    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<false>, dim3((R + 3) / 4), dim3(256), 0,
+               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
+               (uint32_t*)dhs);
   return hipSuccess;
 }
 
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, float* s) {
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx) {
   const int64_t nb = rows * (C / 128);
   if (nb == 0) return hipSuccess;
-  MOE_LAUNCH(c, name, quant_rows_kernel, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
-             (const bf16_t*)src, ld, rows, C, q, s);
+  if (mx)
+    MOE_LAUNCH(c, name, quant_rows_kernel<true>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
+               (const bf16_t*)src, ld, rows, C, q, s);
+  else
+    MOE_LAUNCH(c, name, quant_rows_kernel<false>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
+               (const bf16_t*)src, ld, rows, C, q, s);
   return hipSuccess;
 }
 
@@ -332,12 +528,25 @@ hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void*
   return hipSuccess;
 }
 
+hipError_t launch_quant_weight_mx(const LaunchCtx& c, const char* name, const void* W, int E, int N,
+                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st) {
+  MOE_LAUNCH(c, name, quant_weight_mx_kernel, dim3(K / 128, N / 128, E), dim3(256), 0,
+             (const bf16_t*)W, N, K, q, s, qt, st);
+  return hipSuccess;
+}
+
 hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                             const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
-                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, float* s) {
-  MOE_LAUNCH(c, name, quant_tok_kernel, dim3(nblk_max, C / kTokCols), dim3(256), 0,
-             (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
-             s, (int64_t)nblk_max);
+                            const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
+                            bool mx) {
+  if (mx)
+    MOE_LAUNCH(c, name, quant_tok_kernel<true>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
+               (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
+               (uint32_t*)s, (int64_t)nblk_max);
+  else
+    MOE_LAUNCH(c, name, quant_tok_kernel<false>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
+               (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
+               (uint32_t*)s, (int64_t)nblk_max);
   return hipSuccess;
 }
 

@@ -70,8 +70,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * hardware support": one scale shared by a block of values) as OCP e4m3 with
  * fp32 scales over 1x128 activation blocks and 128x128 weight blocks
  * (weight-gradient operands: 128-row blocks along the token dimension), fp32
- * accumulation; requires dtype MOE_BF16 and d, I multiples of 128. */
-typedef enum { MOE_PREC_NATIVE = 0, MOE_PREC_FP8_BLOCK = 1 } moe_precision;
+ * accumulation.  MOE_PREC_MXFP8: the OCP microscaling format MXFP8 (same
+ * section: smaller scaling groups than blockwise FP8; "Mario/overlap moe
+ * kernel integration" overview: an mxfp8 precision option): e4m3 values in
+ * blocks of 32 along every GEMM operand's contraction dimension, each block
+ * with a power-of-two scale stored as an E8M0 byte (see
+ * moe_quantize_mxfp8), fp32 accumulation.  Both fp8 precisions require dtype
+ * MOE_BF16, d and I multiples of 128 and T*k*max(d, 2I)/128 < 2^31; H, Aw
+ * and dH stay bf16. */
+typedef enum { MOE_PREC_NATIVE = 0, MOE_PREC_FP8_BLOCK = 1, MOE_PREC_MXFP8 = 2 } moe_precision;
 
 typedef enum { MOE_OP_ROUTE = 0, MOE_OP_FORWARD = 1, MOE_OP_BACKWARD = 2 } moe_op;
 
@@ -111,7 +118,7 @@ moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 /* Bytes of the `saved` buffer written by moe_forward and read by
  * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
  * Aw [T*k, I] (SwiGLU output times the row's top-k weight), both in dtype,
- * in expert-sorted row order.  With MOE_PREC_FP8_BLOCK the buffer also holds
+ * in expert-sorted row order.  With an fp8 precision the buffer also holds
  * the transposed e4m3 weight codes and scales that the backward's data
  * gradients use (both weights are quantised once, in the forward). */
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
@@ -186,6 +193,37 @@ moe_status moe_quantize_fp8(int kind, const void* src, int64_t n0, int64_t n1, i
 moe_status moe_quantize_tokens_fp8(const moe_shape* shape, const void* src, int64_t C, int gather,
                                    const moe_routing* routing, uint8_t* q, float* s,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* MXFP8 encoding of MOE_PREC_MXFP8 (OCP microscaling: blocks of 32 values,
+ * one E8M0 scale byte per block, e4m3 elements).  For a block with largest
+ * magnitude amax the scale is 2^X with X the smallest integer such that
+ * amax <= 448 * 2^X (the blockwise scale amax / 448 rounded up to a power of
+ * two, so no value saturates), X >= -127, and X = 0 for an all-zero block;
+ * the scale byte is X + 127 and each value x becomes the code of the e4m3
+ * number nearest to x / 2^X (exact in float32; ties to even).  src is bf16,
+ * q the 8-bit codes, s the scale bytes (device pointers; src and q 16-byte
+ * aligned, s 4-byte aligned).  Kinds (moe_quant_kind):
+ *   MOE_QUANT_ROWS:     src [n0, n1], blocks of 32 along each row
+ *                       -> q [n0, n1], s [n0, n1/32]; n1 % 128 == 0;
+ *   MOE_QUANT_WEIGHT:   src [n0, n1, n2], blocks of 32 along each row of
+ *                       every [n1, n2] matrix (the forward GEMMs' encoding)
+ *                       -> q [n0, n1, n2], s [n0, n1, n2/32];
+ *   MOE_QUANT_WEIGHT_T: blocks of 32 down each column (the data-gradient
+ *                       encoding), written transposed
+ *                       -> q [n0, n2, n1], s [n0, n2, n1/32];
+ *                       n1, n2 multiples of 128 for both weight kinds. */
+moe_status moe_quantize_mxfp8(int kind, const void* src, int64_t n0, int64_t n1, int64_t n2,
+                              uint8_t* q, uint8_t* s, void* stream);
+
+/* MXFP8 token-block quantisation of a weight-gradient operand: as
+ * moe_quantize_tokens_fp8 (same runs of 128 rows, same q layout), but each
+ * run holds four blocks of 32 rows with their own E8M0 scales (a short last
+ * run: blocks past the segment are all zero, scale byte 127), and
+ * s [C, 4 nblk] bytes holds block m of run b of column c at s[c][4 b + m]. */
+moe_status moe_quantize_tokens_mxfp8(const moe_shape* shape, const void* src, int64_t C,
+                                     int gather, const moe_routing* routing, uint8_t* q,
+                                     uint8_t* s, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);

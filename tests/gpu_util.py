@@ -8,6 +8,7 @@ from combine_top_route_amd import synthetic as S
 from oracle import moe_oracle as O
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+RECIPE = {"fp8_block": O.FP8_BLOCK, "mxfp8": O.MXFP8}
 
 
 def rel_err(got, ref):
@@ -55,13 +56,31 @@ def run_oracle(wl, inp, ids=None, w=None, backward=True):
     else:
         rt = O.route(None, wl.k, wl.E, ids=ids.numpy(), w=w.double().numpy())
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
-    fp8 = wl.precision == "fp8_block"
-    fw = (O.forward_fp8 if fp8 else O.forward)(f(inp["x"]), rt, Wgu, Wd)
+    recipe = RECIPE.get(wl.precision)
+    if recipe is None:
+        fw = O.forward(f(inp["x"]), rt, Wgu, Wd)
+    else:
+        fw = O.forward_fp8(f(inp["x"]), rt, Wgu, Wd, recipe=recipe)
     res = {"rt": rt, "out": fw["out"]}
     if backward:
-        bw = (O.backward_fp8 if fp8 else O.backward)(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
+        if recipe is None:
+            bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
+        else:
+            bw = O.backward_fp8(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, recipe=recipe)
         res.update(bw)
     return res
+
+
+def bf16_test_matrix(shape, seed):
+    """bf16 values spanning e4m3's normal and subnormal ranges after
+    scaling: per-row magnitudes from 1e-6 to 1e3, a zero block, exact ties."""
+    g = np.random.default_rng(seed)
+    a = g.standard_normal(shape) * np.exp(g.uniform(np.log(1e-6), np.log(1e3), shape[:-1] + (1,)))
+    a = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    flat = a.view(-1, a.shape[-1])
+    flat[0, :128] = 0.0                         # an all-zero block
+    flat[1, :4] = torch.tensor([448.0, 224.0, 0.5, -0.5])
+    return a.contiguous()
 
 
 def check_routing(gpu, ref):

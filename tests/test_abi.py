@@ -82,6 +82,43 @@ def test_fp8_requirements():
         assert st8 == 0 and st16 == 0 and w8 > w16
 
 
+def test_mxfp8_requirements_and_sizes():
+    assert _status(_shape(precision="mxfp8"))[0] == 2                                  # f32 storage
+    assert _status(_shape(precision="mxfp8", dtype=torch.bfloat16, d=192, I=128))[0] == 2
+    bf = dict(dtype=torch.bfloat16, d=256, I=128)
+    for op in (B.OP_FORWARD, B.OP_BACKWARD):
+        stm, wm = _status(_shape(precision="mxfp8", **bf), op=op)
+        st8, w8 = _status(_shape(precision="fp8_block", **bf), op=op)
+        assert stm == 0 and st8 == 0 and wm >= w8
+    # the saved buffer carries the transposed weights' scales: one byte per
+    # 32 values (MX) rather than one float per 128 x 128 block
+    sizes = {}
+    for p in ("native", "fp8_block", "mxfp8"):
+        n = ctypes.c_size_t()
+        assert B.lib().moe_saved_size(ctypes.byref(_shape(precision=p, **bf)), ctypes.byref(n)) == 0
+        sizes[p] = n.value
+    E, d, I = 8, 256, 128
+    assert sizes["fp8_block"] - sizes["native"] >= 3 * E * d * I            # both transposed codes
+    assert sizes["mxfp8"] - sizes["fp8_block"] >= 3 * E * d * I // 32 - 1024   # 256-byte alignment
+
+
+def test_quantize_mxfp8_entry_points_validate():
+    L = B.lib()
+    q, sc = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert L.moe_quantize_mxfp8(B.QUANT_ROWS, None, 4, 128, 0, q, sc, None) == 1     # NULL src
+    assert L.moe_quantize_mxfp8(5, FAKE, 4, 128, 0, q, sc, None) == 1                # unknown kind
+    assert L.moe_quantize_mxfp8(B.QUANT_ROWS, FAKE, 4, 96, 0, q, sc, None) == 1      # 96 % 128
+    assert L.moe_quantize_mxfp8(B.QUANT_WEIGHT_T, FAKE, 2, 128, 64, q, sc, None) == 1
+    assert L.moe_quantize_mxfp8(B.QUANT_ROWS, FAKE, 4, 128, 0, q, ctypes.c_void_p((1 << 21) + 2),
+                                None) == 1                                          # s alignment
+    s = _shape(dtype=torch.bfloat16)
+    r = B.MoeRouting(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_quantize_tokens_mxfp8(ctypes.byref(s), FAKE, 100, 1, ctypes.byref(r), q, sc, FAKE,
+                                       1 << 30, None) == 1                          # C % 128
+    assert L.moe_quantize_tokens_mxfp8(ctypes.byref(s), FAKE, 128, 1, ctypes.byref(r), q, sc, FAKE,
+                                       0, None) == 3                                # workspace
+
+
 def test_quantize_entry_points_validate():
     L = B.lib()
     q, sc = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)

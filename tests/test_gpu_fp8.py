@@ -12,7 +12,7 @@ from combine_top_route_amd import binding as B
 from combine_top_route_amd import synthetic as S
 from oracle import moe_oracle as O
 
-from gpu_util import TOL, check_floats, check_routing, rel_err, run_gpu, run_oracle, to_np
+from gpu_util import TOL, bf16_test_matrix, check_floats, check_routing, rel_err, run_gpu, run_oracle, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -21,24 +21,12 @@ FP8 = dict(dtype="bf16", logits_dtype="bf16", precision="fp8_block")
 BASE = S.WORKLOADS["tiny"].scaled(**FP8)
 
 
-def _bf16_matrix(shape, seed):
-    """bf16 values spanning e4m3's normal and subnormal ranges after
-    scaling: per-row magnitudes from 1e-6 to 1e3, a zero block, exact ties."""
-    g = np.random.default_rng(seed)
-    a = g.standard_normal(shape) * np.exp(g.uniform(np.log(1e-6), np.log(1e3), shape[:-1] + (1,)))
-    a = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
-    flat = a.view(-1, a.shape[-1])
-    flat[0, :128] = 0.0                         # an all-zero block
-    flat[1, :4] = torch.tensor([448.0, 224.0, 0.5, -0.5])
-    return a.contiguous()
-
-
 def _decode(q, s_expanded):
     return q.view(torch.float8_e4m3fn).double().cpu().numpy() * s_expanded
 
 
 def test_quantize_rows_bit_exact():
-    x = _bf16_matrix((300, 512), 1)
+    x = bf16_test_matrix((300, 512), 1)
     q, s = B.quantize_fp8(x.to(DEV), B.QUANT_ROWS)
     s_np = s.cpu().numpy().astype(np.float64)
     ref = O.quant_rows_1x128(x.float().numpy())
@@ -51,7 +39,7 @@ def test_quantize_rows_bit_exact():
 
 @pytest.mark.parametrize("kind", [B.QUANT_WEIGHT, B.QUANT_WEIGHT_T])
 def test_quantize_weight_bit_exact(kind):
-    W = _bf16_matrix((3, 256, 384), 2)
+    W = bf16_test_matrix((3, 256, 384), 2)
     q, s = B.quantize_fp8(W.to(DEV), kind)
     q, s = q.cpu(), s.cpu().numpy().astype(np.float64)
     for e in range(3):
@@ -75,7 +63,7 @@ def test_quantize_tokens_bit_exact(gather):
     w = torch.from_numpy(g.uniform(0.1, 1.0, (T, k)).astype(np.float32))
     r = B.route_ids(ids.to(DEV), w.to(DEV), E)
     R = T * k
-    src = _bf16_matrix((T if gather else R, C), 4)
+    src = bf16_test_matrix((T if gather else R, C), 4)
     q, s = B.quantize_tokens_fp8(src.to(DEV), r, T, k, gather)
     q, s = q.cpu(), s.cpu().numpy().astype(np.float64)
     rt = O.route(None, k, E, ids=ids.numpy(), w=w.double().numpy())

@@ -62,6 +62,11 @@ What the pages fix, and the readings taken where they leave a step open:
     along K for the forward GEMMs and along N for the data gradients; the
     weight-gradient operands take 32-token blocks from each expert's first
     row.  Everything else follows the blockwise FP8 readings above.
+  * fp8_bwd is another of the layer's precision options [P4 overview], not
+    described further.  Reading: FP8 in the backward only -- the forward of
+    the bf16 layer (H and Aw stored in bf16) and the blockwise FP8 backward
+    on those stored tensors: forward_fp8 with NO_QUANT, then backward_fp8
+    with FP8_BLOCK.
 """
 from __future__ import annotations
 
@@ -515,6 +520,16 @@ FP8_BLOCK = dict(act=quant_rows_1x128, w_fwd=quant_weight_128x128,
 MXFP8 = dict(act=mx_rows, w_fwd=mx_rows, w_bwd=mx_cols, tok=mx_tokens)
 
 
+def no_quant(X: np.ndarray) -> np.ndarray:
+    """The identity encoding: operands enter the GEMM unquantised."""
+    return np.asarray(X, dtype=F64)
+
+
+# Unquantised GEMM operands: forward_fp8 with this recipe is the forward of
+# the bf16 layer (H and Aw stored in bf16), the forward half of fp8_bwd.
+NO_QUANT = dict(act=no_quant, w_fwd=no_quant, w_bwd=no_quant, tok=no_quant)
+
+
 def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK) -> dict:
     """Forward with both GEMMs on block-quantised e4m3 operands (block
     shapes from `recipe`: FP8_BLOCK or MXFP8).  The top-k
@@ -588,9 +603,9 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
 
 def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
                                 tokens: np.ndarray, ids=None, w=None,
-                                recipe=FP8_BLOCK) -> dict:
-    """forward_fp8 / backward_fp8 results (out, dx, d_topk_w, dlogits) for a
-    subset of tokens.  Activation blocks lie within one row and weight
+                                recipe=FP8_BLOCK, fwd_recipe=None) -> dict:
+    """forward_fp8 (with fwd_recipe, default recipe) / backward_fp8 (with
+    recipe) results (out, dx, d_topk_w, dlogits) for a subset of tokens.  Activation blocks lie within one row and weight
     blocks depend only on the weights, so each token's results follow from
     its own rows; the same steps as the full functions, row by row."""
     tokens = np.asarray(tokens)
@@ -603,12 +618,13 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
     else:
         ids_t = np.asarray(ids)[tokens].astype(np.int64)
         w_t = np.asarray(w, F64)[tokens]
+    fr = recipe if fwd_recipe is None else fwd_recipe
     qw = {}
 
     def weights(e):  # (gate/up, down) forward and data-gradient forms
         if e not in qw:
-            fw = (recipe["w_fwd"](w_gate_up[e]), recipe["w_fwd"](w_down[e]))
-            bw = fw if recipe["w_bwd"] is recipe["w_fwd"] else \
+            fw = (fr["w_fwd"](w_gate_up[e]), fr["w_fwd"](w_down[e]))
+            bw = fw if recipe["w_bwd"] is fr["w_fwd"] else \
                 (recipe["w_bwd"](w_gate_up[e]), recipe["w_bwd"](w_down[e]))
             qw[e] = fw + bw
         return qw[e]
@@ -617,14 +633,14 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
     out, dx = np.zeros((n, d)), np.zeros((n, d))
     dtw = np.zeros((n, k))
     for i, t in enumerate(tokens):
-        xq = recipe["act"](np.asarray(x, F64)[t][None, :])
+        xq = fr["act"](np.asarray(x, F64)[t][None, :])
         gq = recipe["act"](np.asarray(dout, F64)[t][None, :])
         for j in range(k):
             Wgu_f, Wd_f, Wgu_b, Wd_b = weights(ids_t[i, j])
             Hs = xq @ Wgu_f.T
             H = bf16_round(Hs)
             Aw = bf16_round(w_t[i, j] * swiglu(Hs, I))
-            out[i] += (recipe["act"](Aw) @ Wd_f.T)[0]
+            out[i] += (fr["act"](Aw) @ Wd_f.T)[0]
             G = gq @ Wd_b
             dtw[i, j] = np.sum(G * swiglu(H, I))
             dH = bf16_round(swiglu_backward(H, w_t[i, j] * G, I))
@@ -636,19 +652,21 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
 
 
 def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int,
-                            recipe=FP8_BLOCK):
+                            recipe=FP8_BLOCK, fwd_recipe=None):
     """backward_fp8's dW_gate_up[e], dW_down[e] from the rows of expert e
-    alone (token blocks are counted from the expert's first row)."""
+    alone (token blocks are counted from the expert's first row); the
+    forward's H and Aw with fwd_recipe (default recipe)."""
+    fr = recipe if fwd_recipe is None else fwd_recipe
     k = rt["k"]
     s = slice(rt["offsets"][e], rt["offsets"][e + 1])
     src = rt["src_of"][s]
     I = w_gate_up.shape[1] // 2
-    Wgu_f = recipe["w_fwd"](w_gate_up[e])
+    Wgu_f = fr["w_fwd"](w_gate_up[e])
     Wd_b = recipe["w_bwd"](w_down[e])
     Xp = np.asarray(x, F64)[src // k]
     g = np.asarray(dout, F64)[src // k]
     wr = rt["w"].ravel()[src]
-    Hs = recipe["act"](Xp) @ Wgu_f.T
+    Hs = fr["act"](Xp) @ Wgu_f.T
     H = bf16_round(Hs)
     Aw = bf16_round(wr[:, None] * swiglu(Hs, I))
     G = recipe["act"](g) @ Wd_b

@@ -595,3 +595,38 @@ def test_mx_sampled_evaluators_match_full_layer():
                                             e, recipe=O.MXFP8)
         np.testing.assert_allclose(dgu, bm["dW_gate_up"][e], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dd, bm["dW_down"][e], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- fp8_bwd
+
+def test_unquantised_recipe_is_the_bf16_storage_forward():
+    """forward_fp8 with NO_QUANT: the exact forward with H and Aw rounded to
+    bf16 once (H bit-equal to the rounded exact H, out within bf16 error)."""
+    wl, inp = _tiny(seed=40, T=48, dtype="bf16")
+    rt = O.route(inp["logits"], wl.k, wl.E)
+    fw = O.forward(inp["x"], rt, inp["w_gate_up"], inp["w_down"])
+    f0 = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"], recipe=O.NO_QUANT)
+    assert np.array_equal(f0["H"], O.bf16_round(fw["H"]))
+    w_row = rt["w"].ravel()[rt["src_of"]]
+    assert np.array_equal(f0["Aw"], O.bf16_round(w_row[:, None] * fw["A"]))
+    err = np.max(np.abs(f0["out"] - fw["out"])) / np.max(np.abs(fw["out"]))
+    assert 0 < err < 2 ** -7
+
+
+def test_fp8_bwd_sampled_evaluators_match_full_layer():
+    wl = S.WORKLOADS["tiny"].scaled(d=256, I=128, T=96, E=6, k=2, dtype="bf16")
+    inp = {k: _np(v) for k, v in S.make_inputs(wl, seed=41).items()}
+    rt = O.route(inp["logits"], wl.k, wl.E)
+    f0 = O.forward_fp8(inp["x"], rt, inp["w_gate_up"], inp["w_down"], recipe=O.NO_QUANT)
+    b8 = O.backward_fp8(inp["dout"], rt, inp["w_gate_up"], inp["w_down"], f0, logits=inp["logits"])
+    toks = np.array([0, 3, 47, 95])
+    s = O.forward_backward_tokens_fp8(inp["x"], inp["logits"], inp["dout"], inp["w_gate_up"],
+                                      inp["w_down"], wl.k, toks, fwd_recipe=O.NO_QUANT)
+    for n, ref in (("out", f0["out"]), ("dx", b8["dx"]), ("d_topk_w", b8["d_topk_w"]),
+                   ("dlogits", b8["dlogits"])):
+        np.testing.assert_allclose(s[n], ref[toks], rtol=1e-12, atol=1e-12 * np.max(np.abs(ref)))
+    for e in range(wl.E):
+        dgu, dd = O.expert_weight_grads_fp8(inp["x"], inp["dout"], rt, inp["w_gate_up"], inp["w_down"],
+                                            e, fwd_recipe=O.NO_QUANT)
+        np.testing.assert_allclose(dgu, b8["dW_gate_up"][e], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dd, b8["dW_down"][e], rtol=1e-12, atol=1e-12)

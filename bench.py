@@ -57,8 +57,10 @@ KERNEL_SOURCES = {
     "native": ["gemm_bf16.hip", "tile.h", "common.h"],
     "fp8_block": ["gemm_fp8.hip", "tile.h", "common.h"],
     "mxfp8": ["gemm_fp8.hip", "tile.h", "common.h"],
+    "fp8_bwd": ["gemm_bf16.hip", "gemm_fp8.hip", "tile.h", "common.h"],
 }
-FP8 = ("fp8_block", "mxfp8")
+FP8 = ("fp8_block", "mxfp8", "fp8_bwd")
+FWD_GEMMS = ("gemm_gateup_fwd", "gemm_down_fwd")
 
 
 def site_of(kernel_name: str) -> str | None:
@@ -68,8 +70,10 @@ def site_of(kernel_name: str) -> str | None:
     return None
 
 
-def mfma_peak(wl) -> float:
-    if wl.precision in FP8:
+def mfma_peak(wl, kernel: str | None = None) -> float:
+    """MFMA peak of the workload's GEMMs (of one GEMM when kernel is given:
+    fp8_bwd runs its forward GEMMs in bf16)."""
+    if wl.precision in FP8 and not (wl.precision == "fp8_bwd" and kernel in FWD_GEMMS):
         return PEAK_FP8_TFLOPS
     return PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
 
@@ -98,7 +102,8 @@ def kernel_work(wl):
         # block (blockwise) or a byte per 32 values (MX), in both layouts
         q = lambda n: float(n * 2 + n + n // 32)
         ws = (lambda n: n // 32) if wl.precision == "mxfp8" else (lambda n: 4 * n // 16384)
-        qw = lambda n: float(n * 2 + 2 * n + 2 * ws(n))
+        nl = 1 if wl.precision == "fp8_bwd" else 2   # fp8_bwd encodes the transposed layout only
+        qw = lambda n: float(n * 2 + nl * (n + ws(n)))
         work.update({
             "quant_x": ("byte", q(T * d)), "quant_dout": ("byte", q(T * d)),
             "quant_aw": ("byte", q(R * I)),
@@ -158,10 +163,11 @@ def cpu_baseline(wl, inp: dict, tokens: int):
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
     fp8 = wl.precision in FP8
     recipe = O.MXFP8 if wl.precision == "mxfp8" else O.FP8_BLOCK
+    fwd_recipe = O.NO_QUANT if wl.precision == "fp8_bwd" else recipe
     t0 = time.perf_counter()
     rt = O.route(lg, wl.k, wl.E)
     if fp8:
-        fw = O.forward_fp8(x, rt, Wgu, Wd, recipe=recipe)
+        fw = O.forward_fp8(x, rt, Wgu, Wd, recipe=fwd_recipe)
         O.backward_fp8(dout, rt, Wgu, Wd, fw, logits=lg, recipe=recipe)
     else:
         fw = O.forward(x, rt, Wgu, Wd)
@@ -177,7 +183,7 @@ def cpu_baseline(wl, inp: dict, tokens: int):
 COPY_BYTES = 1 << 30
 # oracle sample per workload: about 10-30 s of float64 numpy on 16 host cores
 CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q235b": 8192, "fp8_skew": 2048,
-                     "mxfp8_skew": 2048}
+                     "mxfp8_skew": 2048, "fp8_bwd_skew": 2048}
 
 
 def gemm_operand_bytes(wl):
@@ -365,7 +371,7 @@ def main():
             kind, amt = work[name]
             if kind == "flop":
                 entry["tflops"] = amt / (avg * 1e-3) / 1e12
-                entry["mfma_frac"] = entry["tflops"] / mfma_peak(wl)
+                entry["mfma_frac"] = entry["tflops"] / mfma_peak(wl, name)
             else:
                 entry["gbs"] = amt / (avg * 1e-3) / 1e9
                 entry["hbm_frac"] = entry["gbs"] / PEAK_HBM_GBS
@@ -376,7 +382,7 @@ def main():
     if kind == "flop":
         bound = "mfma" if (wl.dtype == "bf16") else "alu"
         roof = {"kernel": dom, "bound": bound, "achieved": amt / (avg * 1e-3) / 1e12,
-                "peak": mfma_peak(wl), "unit": "TFLOP/s"}
+                "peak": mfma_peak(wl, dom), "unit": "TFLOP/s"}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": amt / (avg * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -400,7 +406,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp8_block": "fp8_e4m3 (fp32 block scales, fp32 accumulate)",
-                  "mxfp8": "fp8_e4m3 (MXFP8: E8M0 scale per 32 values, fp32 accumulate)"}.get(
+                  "mxfp8": "fp8_e4m3 (MXFP8: E8M0 scale per 32 values, fp32 accumulate)",
+                  "fp8_bwd": "bf16 forward, fp8_e4m3 backward (fp32 block scales)"}.get(
                       wl.precision, "bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: MoE layer fwd+bwd, T={wl.T} tokens, d={wl.d}, E={wl.E}, "

@@ -17,13 +17,13 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-PREC_NATIVE, PREC_FP8_BLOCK, PREC_MXFP8 = 0, 1, 2
+PREC_NATIVE, PREC_FP8_BLOCK, PREC_MXFP8, PREC_FP8_BWD = 0, 1, 2, 3
 OP_ROUTE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 QUANT_ROWS, QUANT_WEIGHT, QUANT_WEIGHT_T = 0, 1, 2
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _TORCH = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
-_PREC = {"native": PREC_NATIVE, "fp8_block": PREC_FP8_BLOCK, "mxfp8": PREC_MXFP8}
+_PREC = {"native": PREC_NATIVE, "fp8_block": PREC_FP8_BLOCK, "mxfp8": PREC_MXFP8, "fp8_bwd": PREC_FP8_BWD}
 
 
 class MoeShape(ctypes.Structure):

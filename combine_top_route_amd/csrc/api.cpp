@@ -97,7 +97,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->I < 8 || s->I > 16384 || s->I % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "I=%lld must be a multiple of 8 in [8, 16384]", (long long)s->I);
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "dtype=%d unknown", s->dtype);
   if (s->logits_dtype != MOE_F32 && s->logits_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_dtype=%d unknown", s->logits_dtype);
-  if (s->precision != MOE_PREC_NATIVE && s->precision != MOE_PREC_FP8_BLOCK && s->precision != MOE_PREC_MXFP8)
+  if (s->precision < MOE_PREC_NATIVE || s->precision > MOE_PREC_FP8_BWD)
     return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
   if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "reserved field must be 0");
   if (s->precision != MOE_PREC_NATIVE) {
@@ -114,7 +114,9 @@ moe_status check_shape(const moe_shape* s) {
   if (!(p)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", #p)
 
 size_t elem_size(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
-bool is_fp8(const moe_shape* s) { return s->precision == MOE_PREC_FP8_BLOCK || s->precision == MOE_PREC_MXFP8; }
+// fp8 GEMMs in the forward / in the backward
+bool fwd_fp8(const moe_shape* s) { return s->precision == MOE_PREC_FP8_BLOCK || s->precision == MOE_PREC_MXFP8; }
+bool bwd_fp8(const moe_shape* s) { return s->precision != MOE_PREC_NATIVE; }
 bool is_mx(const moe_shape* s) { return s->precision == MOE_PREC_MXFP8; }
 // Scale bytes of an expert weight [N, K] encoded along K: blockwise fp32
 // per 128 x 128 block, MX one byte per row and 32 columns.
@@ -123,7 +125,7 @@ size_t wscale_bytes(const moe_shape* s, int64_t N, int64_t K) {
 }
 int dw_blocks(const moe_shape* s) {
   if (s->dtype == MOE_F32) return f32_dw_blocks((int)s->I);
-  return is_fp8(s) ? fp8_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
+  return bwd_fp8(s) ? fp8_dw_blocks((int)s->I) : bf16_dw_blocks((int)s->I);
 }
 // upper bound of the 128-row token blocks over all experts
 int64_t nblk_max(const moe_shape* s) { return cdiv(s->T * s->k, kTokBlock) + s->E; }
@@ -137,6 +139,7 @@ struct Layout {
   size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
   size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
   size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0, Gf = 0;
+  size_t wgutq = 0, wguts = 0, wdtq = 0, wdts = 0;  // fp8_bwd: transposed weights
   size_t total = 0;
 };
 
@@ -167,12 +170,12 @@ Layout layout(const moe_shape* s, int op) {
     L.dwp = take(sizeof(float) * R * dw_blocks(s));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
   }
-  if (is_fp8(s)) {
+  if (bwd_fp8(s)) {
     // row scales take one 32-bit word per 128 columns in both formats (an
     // fp32 scale, or four E8M0 bytes)
     const int64_t T = s->T, d = s->d, I = s->I, E = s->E;
     const size_t w = sizeof(uint32_t);
-    if (op == MOE_OP_FORWARD) {
+    if (op == MOE_OP_FORWARD && fwd_fp8(s)) {
       L.xq = take(T * d);
       L.xs = take(w * T * (d / 128));
       L.wguq = take(E * 2 * I * d);
@@ -194,6 +197,12 @@ Layout layout(const moe_shape* s, int op) {
       L.tqb = take(rb * nb * kTokBlock);
       L.tsb = take(w * rb * nb);
       L.Gf = take(sizeof(float) * R * I);
+      if (!fwd_fp8(s)) {
+        L.wgutq = take(E * d * 2 * I);
+        L.wdtq = take(E * I * d);
+        L.wguts = take(wscale_bytes(s, d, 2 * I));
+        L.wdts = take(wscale_bytes(s, I, d));
+      }
     }
   }
   L.total = off;
@@ -213,7 +222,7 @@ SavedLayout saved_layout(const moe_shape* s) {
   L.H = 0;
   L.A = es * R * 2 * I;
   size_t off = L.A + es * R * I;
-  if (is_fp8(s)) {
+  if (fwd_fp8(s)) {
     auto take = [&](size_t bytes) {
       off = align256(off);
       const size_t o = off;
@@ -372,7 +381,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   void* Y = at(workspace, L.Y);
   if (shape->dtype == MOE_F32) {
     HIP_TRY(f32_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
-  } else if (is_fp8(shape)) {
+  } else if (fwd_fp8(shape)) {
     Fp8Fwd q;
     q.mx = is_mx(shape);
     q.xq = (uint8_t*)at(workspace, L.xq); q.xs = at(workspace, L.xs);
@@ -422,7 +431,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   (void)hipGetLastError();
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
                           (int32_t*)at(workspace, L.order),
-                          is_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr,
+                          bwd_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr,
                           (int4*)at(workspace, L.tiles)),
           "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
@@ -436,11 +445,17 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   if (shape->dtype == MOE_F32)
     HIP_TRY(f32_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down,
                           (float*)at(workspace, L.G)), "backward GEMMs");
-  else if (is_fp8(shape)) {
+  else if (bwd_fp8(shape)) {
     Fp8Bwd q;
     q.mx = is_mx(shape);
+    q.quant_weights = !fwd_fp8(shape);
     q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = at(workspace, L.douts);
-    q.sv = fp8_saved(shape, saved);
+    if (q.quant_weights) {
+      q.sv.wgutq = (uint8_t*)at(workspace, L.wgutq); q.sv.wguts = at(workspace, L.wguts);
+      q.sv.wdtq = (uint8_t*)at(workspace, L.wdtq); q.sv.wdts = at(workspace, L.wdts);
+    } else {
+      q.sv = fp8_saved(shape, saved);
+    }
     q.dhq = (uint8_t*)at(workspace, L.dhq); q.dhs = at(workspace, L.dhs);
     q.tqa = (uint8_t*)at(workspace, L.tqa); q.tsa = at(workspace, L.tsa);
     q.tqb = (uint8_t*)at(workspace, L.tqb); q.tsb = at(workspace, L.tsb);

@@ -194,6 +194,8 @@ struct Fp8Fwd {
 // ([max(d,2I)] and [max(I,d)] rows of 128 nblk_max bytes).
 struct Fp8Bwd {
   bool mx;
+  bool quant_weights;           // encode the transposed weights into sv first
+                                // (no fp8 forward ran)
   uint8_t* doutq; void* douts;  // [T,d]
   Fp8Saved sv;                  // from the forward's saved buffer
   uint8_t* dhq; void* dhs;      // [R,2I]

@@ -678,6 +678,12 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
                          void* dW_d) {
   const int64_t I = a.I, d = a.d;
   const bool mx = q.mx;
+  if (q.quant_weights) {  // the data-gradient (transposed) encodings only
+    HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, nullptr, nullptr,
+                          q.sv.wgutq, q.sv.wguts));
+    HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, nullptr, nullptr, q.sv.wdtq,
+                          q.sv.wdts));
+  }
   HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx));
   {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
      // <G, a> and dH's row codes

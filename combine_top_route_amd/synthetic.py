@@ -49,7 +49,7 @@ class Workload:
     I: int
     dtype: str            # storage dtype of x, weights, outputs, grads: "f32" | "bf16"
     logits_dtype: str     # "f32" | "bf16"
-    precision: str        # "native" | "fp8_block" | "mxfp8"
+    precision: str        # "native" | "fp8_block" | "mxfp8" | "fp8_bwd"
     bias: str             # "none" | "normal" | "zipf"
     bias_std: float = 0.0
 
@@ -75,6 +75,8 @@ WORKLOADS = {
     "fp8_skew": Workload("fp8_skew", 16384, 4096, 128, 8, 1536, "bf16", "bf16", "fp8_block", "zipf"),
     # the same skewed layer in MXFP8 (32-value blocks, power-of-two scales)
     "mxfp8_skew": Workload("mxfp8_skew", 16384, 4096, 128, 8, 1536, "bf16", "bf16", "mxfp8", "zipf"),
+    # bf16 forward, blockwise fp8 backward
+    "fp8_bwd_skew": Workload("fp8_bwd_skew", 16384, 4096, 128, 8, 1536, "bf16", "bf16", "fp8_bwd", "zipf"),
 }
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

@@ -75,10 +75,18 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * kernel integration" overview: an mxfp8 precision option): e4m3 values in
  * blocks of 32 along every GEMM operand's contraction dimension, each block
  * with a power-of-two scale stored as an E8M0 byte (see
- * moe_quantize_mxfp8), fp32 accumulation.  Both fp8 precisions require dtype
+ * moe_quantize_mxfp8), fp32 accumulation.  MOE_PREC_FP8_BWD (the PR's
+ * fp8_bwd option): FP8 in the backward only -- the forward of the bf16 layer,
+ * then the backward of MOE_PREC_FP8_BLOCK on the saved bf16 H and Aw (the
+ * backward quantises the weights itself).  The fp8 precisions require dtype
  * MOE_BF16, d and I multiples of 128 and T*k*max(d, 2I)/128 < 2^31; H, Aw
  * and dH stay bf16. */
-typedef enum { MOE_PREC_NATIVE = 0, MOE_PREC_FP8_BLOCK = 1, MOE_PREC_MXFP8 = 2 } moe_precision;
+typedef enum {
+  MOE_PREC_NATIVE = 0,
+  MOE_PREC_FP8_BLOCK = 1,
+  MOE_PREC_MXFP8 = 2,
+  MOE_PREC_FP8_BWD = 3
+} moe_precision;
 
 typedef enum { MOE_OP_ROUTE = 0, MOE_OP_FORWARD = 1, MOE_OP_BACKWARD = 2 } moe_op;
 
@@ -118,9 +126,10 @@ moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 /* Bytes of the `saved` buffer written by moe_forward and read by
  * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
  * Aw [T*k, I] (SwiGLU output times the row's top-k weight), both in dtype,
- * in expert-sorted row order.  With an fp8 precision the buffer also holds
- * the transposed e4m3 weight codes and scales that the backward's data
- * gradients use (both weights are quantised once, in the forward). */
+ * in expert-sorted row order.  With an fp8 forward (MOE_PREC_FP8_BLOCK,
+ * MOE_PREC_MXFP8) the buffer also holds the transposed e4m3 weight codes and
+ * scales that the backward's data gradients use (both weights are quantised
+ * once, in the forward). */
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
 
 /* Routing only: top-k (when logits != NULL), per-expert counts and offsets,

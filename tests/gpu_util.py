@@ -8,7 +8,9 @@ from combine_top_route_amd import synthetic as S
 from oracle import moe_oracle as O
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
-RECIPE = {"fp8_block": O.FP8_BLOCK, "mxfp8": O.MXFP8}
+# (forward, backward) quantisation recipes of each fp8 precision
+RECIPE = {"fp8_block": (O.FP8_BLOCK, O.FP8_BLOCK), "mxfp8": (O.MXFP8, O.MXFP8),
+          "fp8_bwd": (O.NO_QUANT, O.FP8_BLOCK)}
 
 
 def rel_err(got, ref):
@@ -56,17 +58,17 @@ def run_oracle(wl, inp, ids=None, w=None, backward=True):
     else:
         rt = O.route(None, wl.k, wl.E, ids=ids.numpy(), w=w.double().numpy())
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
-    recipe = RECIPE.get(wl.precision)
-    if recipe is None:
+    recipes = RECIPE.get(wl.precision)
+    if recipes is None:
         fw = O.forward(f(inp["x"]), rt, Wgu, Wd)
     else:
-        fw = O.forward_fp8(f(inp["x"]), rt, Wgu, Wd, recipe=recipe)
+        fw = O.forward_fp8(f(inp["x"]), rt, Wgu, Wd, recipe=recipes[0])
     res = {"rt": rt, "out": fw["out"]}
     if backward:
-        if recipe is None:
+        if recipes is None:
             bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
         else:
-            bw = O.backward_fp8(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, recipe=recipe)
+            bw = O.backward_fp8(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, recipe=recipes[1])
         res.update(bw)
     return res
 

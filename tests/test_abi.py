@@ -102,6 +102,25 @@ def test_mxfp8_requirements_and_sizes():
     assert sizes["mxfp8"] - sizes["fp8_block"] >= 3 * E * d * I // 32 - 1024   # 256-byte alignment
 
 
+def test_fp8_bwd_sizes():
+    """fp8_bwd: a bf16 forward (no weight codes saved), an fp8 backward that
+    encodes the transposed weights in its own workspace."""
+    bf = dict(dtype=torch.bfloat16, d=256, I=128)
+    assert _status(_shape(precision="fp8_bwd"))[0] == 2                                # f32 storage
+    assert _status(_shape(precision="fp8_bwd", **bf), op=B.OP_FORWARD) == \
+        _status(_shape(**bf), op=B.OP_FORWARD)
+    _, wb = _status(_shape(precision="fp8_bwd", **bf), op=B.OP_BACKWARD)
+    _, w8 = _status(_shape(precision="fp8_block", **bf), op=B.OP_BACKWARD)
+    assert wb >= w8 + 3 * 8 * 256 * 128
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    B.lib().moe_saved_size(ctypes.byref(_shape(precision="fp8_bwd", **bf)), ctypes.byref(n0))
+    B.lib().moe_saved_size(ctypes.byref(_shape(**bf)), ctypes.byref(n1))
+    assert n0.value == n1.value
+    s = _shape(**bf)
+    s.precision = 4
+    assert _status(s)[0] == 1
+
+
 def test_quantize_mxfp8_entry_points_validate():
     L = B.lib()
     q, sc = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)

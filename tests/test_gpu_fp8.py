@@ -138,3 +138,55 @@ def test_fp8_layer_parity_full_size_sampled():
             assert err <= TOL["fp8"], (n, e, err)
     for e in np.nonzero(counts == 0)[0]:
         assert np.all(gpu["dW_gate_up"][e] == 0) and np.all(gpu["dW_down"][e] == 0)
+
+
+# ------------------------------------------------------------ fp8_bwd option
+# bf16 forward (H, Aw stored in bf16), blockwise fp8 backward on them; the
+# backward encodes the weights itself.
+FP8_BWD = {
+    "fp8bwd_tiles": SMALL["fp8_tiles"].scaled(precision="fp8_bwd"),
+    "fp8bwd_one_token": SMALL["fp8_one_token"].scaled(precision="fp8_bwd"),
+    "fp8bwd_skew_small": S.WORKLOADS["fp8_bwd_skew"].scaled(T=1024, d=256, I=256),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_BWD))
+def test_fp8_bwd_layer_parity_small(name):
+    wl = FP8_BWD[name]
+    print(f"case {name}: {wl}", flush=True)
+    inp = S.make_inputs(wl, seed=2)
+    gpu = run_gpu(wl, inp)
+    ref = run_oracle(wl, inp)
+    check_routing(gpu, ref)
+    assert rel_err(gpu["out"], ref["out"]) <= TOL["bf16"]
+    errs = check_floats(gpu, ref, TOL["fp8"])
+    print(name, errs)
+
+
+def test_fp8_bwd_layer_parity_full_size_sampled():
+    """fp8_bwd on the skewed layer at 16,384 tokens, d=4096, I=1536: sampled
+    tokens and two experts' weight gradients, as for fp8."""
+    wl = S.WORKLOADS["fp8_bwd_skew"]
+    inp = S.make_inputs(wl, seed=0)
+    gpu = run_gpu(wl, inp)
+    lg = inp["logits"].double().numpy()
+    rt = O.route(lg, wl.k, wl.E)
+    check_routing(gpu, {"rt": rt})
+    counts = rt["counts"]
+    Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
+    x, dout = inp["x"].double().numpy(), inp["dout"].double().numpy()
+    toks = np.random.default_rng(1).choice(wl.T, 12, replace=False)
+    toks[:2] = [0, wl.T - 1]
+    s = O.forward_backward_tokens_fp8(x, lg, dout, Wgu, Wd, wl.k, toks, fwd_recipe=O.NO_QUANT)
+    for n in ("out", "dx", "d_topk_w", "dlogits"):
+        e = rel_err(gpu[n][toks], s[n])
+        print(n, e)
+        assert e <= TOL["bf16" if n == "out" else "fp8"], (n, e)
+    nz = np.nonzero(counts)[0]
+    order = nz[np.argsort(counts[nz])]
+    for e in (order[0], order[-1]):
+        dgu, dd = O.expert_weight_grads_fp8(x, dout, rt, Wgu, Wd, e, fwd_recipe=O.NO_QUANT)
+        for n, got, ref in (("dW_gate_up", gpu["dW_gate_up"][e], dgu), ("dW_down", gpu["dW_down"][e], dd)):
+            err = rel_err(got, ref)
+            print(n, e, counts[e], err)
+            assert err <= TOL["fp8"], (n, e, err)

@@ -360,6 +360,24 @@ def main():
         fwd_ms.append(a.elapsed_time(b))
         bwd_ms.append(b.elapsed_time(c))
 
+    # activation checkpointing: forward keeping nothing, then the backward
+    # that recomputes the gate/up half from x (moe_backward with saved = NULL)
+    del layer
+    torch.cuda.empty_cache()
+    ac = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt, logits_dtype=S.torch_dtype(wl.logits_dtype),
+                    precision=wl.precision, device=dev, save=False)
+    ac_ms = []
+    for i in range(args.warmup + args.steps):
+        a, b = ev(), ev()
+        a.record()
+        ac.forward(x, wgu, wd, logits=logits)
+        ac.backward(dout, x, wgu, wd)
+        b.record()
+        b.synchronize()
+        if i >= args.warmup:
+            ac_ms.append(a.elapsed_time(b))
+    del ac
+
     flops = wl.flops_fwd() + wl.flops_bwd()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     work = kernel_work(wl)
@@ -419,6 +437,8 @@ def main():
         "fwd_ms_mean": float(np.mean(fwd_ms)),
         "bwd_ms_mean": float(np.mean(bwd_ms)),
         "two_fwd_plus_bwd_ms": float(2 * np.median(fwd_ms) + np.median(bwd_ms)),
+        # measured: forward without saving + backward that recomputes H and Aw
+        "recompute_step_ms": float(np.median(ac_ms)),
         "gemm_ms_per_step": gemm_ms,
         "gemm_mfma_util": (wl.flops_fwd() + wl.flops_bwd()) / (gemm_ms * 1e-3) / 1e12 / mfma_peak(wl),
         "roofline": roof,

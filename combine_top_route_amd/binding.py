@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_F32, MOE_BF16 = 0, 1
 PREC_NATIVE, PREC_FP8_BLOCK, PREC_MXFP8, PREC_FP8_BWD = 0, 1, 2, 3
-OP_ROUTE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+OP_ROUTE, OP_FORWARD, OP_BACKWARD, OP_BACKWARD_RECOMPUTE = 0, 1, 2, 3
 QUANT_ROWS, QUANT_WEIGHT, QUANT_WEIGHT_T = 0, 1, 2
 
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
@@ -168,7 +168,9 @@ class Routing:
 
 class MoeLayer:
     """One layer shape with preallocated outputs and workspaces, so repeated
-    calls (benchmarks, training loops) allocate nothing."""
+    calls (benchmarks, training loops) allocate nothing.  save=False: the
+    forward keeps nothing and the backward recomputes H and Aw from x
+    (activation checkpointing)."""
 
     def __init__(self, T, d, E, k, I, dtype=torch.bfloat16, logits_dtype=None,
                  precision="native", device="cuda", save=True):
@@ -182,7 +184,8 @@ class MoeLayer:
         self.shape = make_shape(T, d, E, k, I, dtype, self.logits_dtype, precision)
         dev = self.device
         self.ws_fwd = torch.empty(workspace_size(self.shape, OP_FORWARD), dtype=torch.uint8, device=dev)
-        self.ws_bwd = torch.empty(workspace_size(self.shape, OP_BACKWARD), dtype=torch.uint8, device=dev)
+        self.ws_bwd = torch.empty(workspace_size(self.shape, OP_BACKWARD if save else OP_BACKWARD_RECOMPUTE),
+                                  dtype=torch.uint8, device=dev)
         self.saved = (torch.empty(saved_size(self.shape), dtype=torch.uint8, device=dev) if save else None)
         self.out = torch.empty((T, d), dtype=dtype, device=dev)
         self.routing = Routing.empty(T, E, k, dev)
@@ -221,8 +224,6 @@ class MoeLayer:
     def backward(self, dout, x, w_gate_up, w_down, want_dlogits=True):
         T, d, dt, dev = self.T, self.d, self.dtype, self.device
         _need(dout, "dout", (T, d), dt, dev)
-        if self.saved is None:
-            raise ValueError("layer was built with save=False")
         r = self.routing
         cr = r.c()
         dl = self.dlogits if (want_dlogits and r.logits is not None) else None

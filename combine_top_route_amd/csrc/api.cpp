@@ -131,84 +131,6 @@ int dw_blocks(const moe_shape* s) {
 int64_t nblk_max(const moe_shape* s) { return cdiv(s->T * s->k, kTokBlock) + s->E; }
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-struct Layout {
-  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0, tiles = 0;  // routing / schedule
-  size_t Y = 0, A = 0, H = 0;                             // forward
-  size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
-  // fp8: quantised operands (q) and their scales (s)
-  size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
-  size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
-  size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0, Gf = 0;
-  size_t wgutq = 0, wguts = 0, wdtq = 0, wdts = 0;  // fp8_bwd: transposed weights
-  size_t total = 0;
-};
-
-Layout layout(const moe_shape* s, int op) {
-  Layout L;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const int64_t R = s->T * s->k;
-  const size_t es = elem_size(s->dtype);
-  const int64_t nchunks = cdiv(R, kSortChunk);
-  L.tile_off = take(sizeof(int32_t) * (s->E + 1));
-  L.order = take(sizeof(int32_t) * s->E);
-  L.blk_off = take(sizeof(int32_t) * (s->E + 1));
-  L.tiles = take(sizeof(int4) * max_row_tiles(R, s->E));
-  if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
-  if (op == MOE_OP_FORWARD) {
-    L.Y = take(es * R * s->d);
-    L.A = take(es * R * s->I);
-    if (s->dtype == MOE_F32) L.H = take(es * R * 2 * s->I);
-  }
-  if (op == MOE_OP_BACKWARD) {
-    L.dH = take(es * R * 2 * s->I);
-    L.dXp = take(es * R * s->d);
-    L.dwp = take(sizeof(float) * R * dw_blocks(s));
-    if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
-  }
-  if (bwd_fp8(s)) {
-    // row scales take one 32-bit word per 128 columns in both formats (an
-    // fp32 scale, or four E8M0 bytes)
-    const int64_t T = s->T, d = s->d, I = s->I, E = s->E;
-    const size_t w = sizeof(uint32_t);
-    if (op == MOE_OP_FORWARD && fwd_fp8(s)) {
-      L.xq = take(T * d);
-      L.xs = take(w * T * (d / 128));
-      L.wguq = take(E * 2 * I * d);
-      L.wgus = take(wscale_bytes(s, 2 * I, d));
-      L.wdq = take(E * d * I);
-      L.wds = take(wscale_bytes(s, d, I));
-      L.awq = take(R * I);
-      L.aws = take(w * R * (I / 128));
-    }
-    if (op == MOE_OP_BACKWARD) {
-      const int64_t nb = nblk_max(s);
-      L.doutq = take(T * d);
-      L.douts = take(w * T * (d / 128));
-      L.dhq = take(R * 2 * I);
-      L.dhs = take(w * R * (2 * I / 128));
-      const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;
-      L.tqa = take(ra * nb * kTokBlock);
-      L.tsa = take(w * ra * nb);
-      L.tqb = take(rb * nb * kTokBlock);
-      L.tsb = take(w * rb * nb);
-      L.Gf = take(sizeof(float) * R * I);
-      if (!fwd_fp8(s)) {
-        L.wgutq = take(E * d * 2 * I);
-        L.wdtq = take(E * I * d);
-        L.wguts = take(wscale_bytes(s, d, 2 * I));
-        L.wdts = take(wscale_bytes(s, I, d));
-      }
-    }
-  }
-  L.total = off;
-  return L;
-}
-
 // `saved`: H [R,2I] then Aw [R,I] (dtype); for fp8 also the transposed weight
 // codes and scales the backward's dgrads read.
 struct SavedLayout {
@@ -234,6 +156,90 @@ SavedLayout saved_layout(const moe_shape* s) {
     L.wguts = take(wscale_bytes(s, d, 2 * I));
     L.wdts = take(wscale_bytes(s, I, d));
   }
+  L.total = off;
+  return L;
+}
+
+struct Layout {
+  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0, tiles = 0;  // routing / schedule
+  size_t Y = 0, A = 0, H = 0;                             // forward
+  size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
+  // fp8: quantised operands (q) and their scales (s)
+  size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
+  size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
+  size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0, Gf = 0;
+  size_t wgutq = 0, wguts = 0, wdtq = 0, wdts = 0;  // fp8_bwd: transposed weights
+  size_t rsaved = 0;                                // recompute: the saved buffer
+  size_t total = 0;
+};
+
+Layout layout(const moe_shape* s, int op) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int64_t R = s->T * s->k;
+  const size_t es = elem_size(s->dtype);
+  const int64_t nchunks = cdiv(R, kSortChunk);
+  L.tile_off = take(sizeof(int32_t) * (s->E + 1));
+  L.order = take(sizeof(int32_t) * s->E);
+  L.blk_off = take(sizeof(int32_t) * (s->E + 1));
+  L.tiles = take(sizeof(int4) * max_row_tiles(R, s->E));
+  if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
+  if (op == MOE_OP_FORWARD) {
+    L.Y = take(es * R * s->d);
+    L.A = take(es * R * s->I);
+    if (s->dtype == MOE_F32) L.H = take(es * R * 2 * s->I);
+  }
+  const bool bwd = op == MOE_OP_BACKWARD || op == MOE_OP_BACKWARD_RECOMPUTE;
+  if (bwd) {
+    L.dH = take(es * R * 2 * s->I);
+    L.dXp = take(es * R * s->d);
+    L.dwp = take(sizeof(float) * R * dw_blocks(s));
+    if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
+  }
+  if (bwd_fp8(s)) {
+    // row scales take one 32-bit word per 128 columns in both formats (an
+    // fp32 scale, or four E8M0 bytes)
+    const int64_t T = s->T, d = s->d, I = s->I, E = s->E;
+    const size_t w = sizeof(uint32_t);
+    // the recomputing backward reruns the gate/up GEMM with its x and weight codes
+    if ((op == MOE_OP_FORWARD || op == MOE_OP_BACKWARD_RECOMPUTE) && fwd_fp8(s)) {
+      L.xq = take(T * d);
+      L.xs = take(w * T * (d / 128));
+      L.wguq = take(E * 2 * I * d);
+      L.wgus = take(wscale_bytes(s, 2 * I, d));
+      if (op == MOE_OP_FORWARD) {
+        L.wdq = take(E * d * I);
+        L.wds = take(wscale_bytes(s, d, I));
+        L.awq = take(R * I);
+        L.aws = take(w * R * (I / 128));
+      }
+    }
+    if (bwd) {
+      const int64_t nb = nblk_max(s);
+      L.doutq = take(T * d);
+      L.douts = take(w * T * (d / 128));
+      L.dhq = take(R * 2 * I);
+      L.dhs = take(w * R * (2 * I / 128));
+      const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;
+      L.tqa = take(ra * nb * kTokBlock);
+      L.tsa = take(w * ra * nb);
+      L.tqb = take(rb * nb * kTokBlock);
+      L.tsb = take(w * rb * nb);
+      L.Gf = take(sizeof(float) * R * I);
+      if (!fwd_fp8(s)) {
+        L.wgutq = take(E * d * 2 * I);
+        L.wdtq = take(E * I * d);
+        L.wguts = take(wscale_bytes(s, d, 2 * I));
+        L.wdts = take(wscale_bytes(s, I, d));
+      }
+    }
+  }
+  if (op == MOE_OP_BACKWARD_RECOMPUTE) L.rsaved = take(saved_layout(s).total);
   L.total = off;
   return L;
 }
@@ -322,6 +328,24 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   return a;
 }
 
+// The forward's GEMMs (and, fp8, its encodings) writing H (may be null for
+// bf16), A and, unless Y is null, Y.  Y == null: the gate/up half alone,
+// as the recomputing backward needs it.  saved: where the fp8 forward leaves
+// the transposed weight codes (null: not kept).
+hipError_t forward_gemms(const moe_shape* shape, const LaunchCtx& c, const LayerArgs& a, void* ws,
+                         const Layout& L, void* saved, void* H, void* A, void* Y) {
+  if (shape->dtype == MOE_F32) return f32_fwd_gemms(c, a, H, A, Y);
+  if (!fwd_fp8(shape)) return bf16_fwd_gemms(c, a, H, A, Y);
+  Fp8Fwd q;
+  q.mx = is_mx(shape);
+  q.xq = (uint8_t*)at(ws, L.xq); q.xs = at(ws, L.xs);
+  q.wguq = (uint8_t*)at(ws, L.wguq); q.wgus = at(ws, L.wgus);
+  q.wdq = Y ? (uint8_t*)at(ws, L.wdq) : nullptr; q.wds = Y ? at(ws, L.wds) : nullptr;
+  q.awq = Y ? (uint8_t*)at(ws, L.awq) : nullptr; q.aws = Y ? at(ws, L.aws) : nullptr;
+  q.sv = fp8_saved(shape, saved);
+  return fp8_fwd_gemms(c, a, q, H, A, Y);
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,7 +353,7 @@ extern "C" {
 moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   TRY(check_shape(shape));
   CHECK_PTR(bytes);
-  if (op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) return fail(MOE_ERR_INVALID_ARGUMENT, "op=%d unknown", op);
+  if (op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD_RECOMPUTE) return fail(MOE_ERR_INVALID_ARGUMENT, "op=%d unknown", op);
   *bytes = layout(shape, op).total;
   return MOE_OK;
 }
@@ -379,20 +403,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   void* H = saved ? saved : (shape->dtype == MOE_F32 ? at(workspace, L.H) : nullptr);
   void* A = saved ? at(saved, es * R * 2 * shape->I) : at(workspace, L.A);
   void* Y = at(workspace, L.Y);
-  if (shape->dtype == MOE_F32) {
-    HIP_TRY(f32_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
-  } else if (fwd_fp8(shape)) {
-    Fp8Fwd q;
-    q.mx = is_mx(shape);
-    q.xq = (uint8_t*)at(workspace, L.xq); q.xs = at(workspace, L.xs);
-    q.wguq = (uint8_t*)at(workspace, L.wguq); q.wgus = at(workspace, L.wgus);
-    q.wdq = (uint8_t*)at(workspace, L.wdq); q.wds = at(workspace, L.wds);
-    q.awq = (uint8_t*)at(workspace, L.awq); q.aws = at(workspace, L.aws);
-    q.sv = fp8_saved(shape, saved);
-    HIP_TRY(fp8_fwd_gemms(c, a, q, H, A, Y), "forward GEMMs");
-  } else {
-    HIP_TRY(bf16_fwd_gemms(c, a, H, A, Y), "forward GEMMs");
-  }
+  HIP_TRY(forward_gemms(shape, c, a, workspace, L, saved, H, A, Y), "forward GEMMs");
   // rows already carry their top-k weight: the combine is a plain sum
   HIP_TRY(launch_combine(c, "combine", shape->dtype, Y, routing->row_of, nullptr, (int)shape->T,
                          (int)shape->k, (int)shape->d, out), "combine");
@@ -409,7 +420,6 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   CHECK_PTR(x);
   CHECK_PTR(w_gate_up);
   CHECK_PTR(w_down);
-  CHECK_PTR(saved);
   CHECK_PTR(dx);
   CHECK_PTR(dw_gate_up);
   CHECK_PTR(dw_down);
@@ -417,16 +427,17 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   TRY(check_routing(routing, true));
   if (dlogits && !routing->logits)
     return fail(MOE_ERR_INVALID_ARGUMENT, "dlogits needs the logits form of routing");
-  TRY(check_ws(shape, MOE_OP_BACKWARD, workspace, workspace_bytes));
+  const int op = saved ? MOE_OP_BACKWARD : MOE_OP_BACKWARD_RECOMPUTE;
+  TRY(check_ws(shape, op, workspace, workspace_bytes));
   TRY(check_aligned16(dout, "dout"));
   TRY(check_aligned16(x, "x"));
   TRY(check_aligned16(w_gate_up, "w_gate_up"));
   TRY(check_aligned16(w_down, "w_down"));
-  TRY(check_aligned16(saved, "saved"));
+  if (saved) TRY(check_aligned16(saved, "saved"));
   TRY(check_aligned16(dx, "dx"));
   TRY(check_aligned16(dw_gate_up, "dw_gate_up"));
   TRY(check_aligned16(dw_down, "dw_down"));
-  const Layout L = layout(shape, MOE_OP_BACKWARD);
+  const Layout L = layout(shape, op);
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
@@ -437,6 +448,12 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
   const int64_t R = shape->T * shape->k;
+  if (!saved) {  // recompute what the forward saves: H, Aw (and the fp8 weight codes)
+    void* rs = at(workspace, L.rsaved);
+    HIP_TRY(forward_gemms(shape, c, a, workspace, L, rs, rs, at(rs, es * R * 2 * shape->I), nullptr),
+            "recompute GEMMs");
+    saved = rs;
+  }
   const void* H = saved;
   const void* A = (const char*)saved + es * R * 2 * shape->I;
   void* dH = at(workspace, L.dH);

@@ -126,7 +126,8 @@ struct LayerArgs {
 
 // Forward GEMMs write H [R,2I] (gate|up, may be null), Aw [R,I] = w_row *
 // silu(gate) * up (each row already carries its top-k weight) and Yw [R,d] =
-// Aw W_down^T, so the combine is a plain sum of each token's k rows.
+// Aw W_down^T, so the combine is a plain sum of each token's k rows.  Yw ==
+// null: the gate/up GEMM alone (the recomputing backward).
 // bf16 MFMA path.
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw);
 // backward outputs dH [R,2I], dXp [R,d], dwp [R, bf16_dw_blocks(I)] fp32, dW_gu, dW_d.

@@ -666,6 +666,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
     hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R);
     if (err != hipSuccess) return err;
   }
+  if (!Yw) return hipSuccess;  // the gate/up half alone (recomputation)
   // down GEMM: Yw = Aw W_down[e]^T (rows already carry their top-k weight)
   RowsArgs q = {};
   q.offsets = a.offsets; q.tile_off = a.tile_off; q.tiles = a.tiles; q.E = a.E;

@@ -208,6 +208,7 @@ hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* 
   if (err != hipSuccess) return err;
   MOE_LAUNCH(c, "swiglu_fwd", f32_swiglu_fwd, dim3((unsigned)cdiv(R * I, 256)), dim3(256), 0,
              (const float*)H, a.topk_w, a.src_of, R, a.I, (float*)Aact);
+  if (!Y) return hipSuccess;  // the gate/up half alone (recomputation)
   return rows_gemm(c, "gemm_down_fwd", a, (const float*)Aact, I, nullptr, 1,
                    (const float*)a.w_down, d * I, I, 1, (float*)Y, d, a.d, a.I);
 }

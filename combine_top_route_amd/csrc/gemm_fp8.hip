@@ -660,6 +660,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R, mx));
   }
+  if (!Yw) return hipSuccess;  // the gate/up half alone (recomputation)
   HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws, mx));
   Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
   p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;

@@ -88,7 +88,14 @@ typedef enum {
   MOE_PREC_FP8_BWD = 3
 } moe_precision;
 
-typedef enum { MOE_OP_ROUTE = 0, MOE_OP_FORWARD = 1, MOE_OP_BACKWARD = 2 } moe_op;
+/* MOE_OP_BACKWARD_RECOMPUTE sizes a moe_backward call that gets saved ==
+ * NULL and recomputes what moe_forward would have saved. */
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_FORWARD = 1,
+  MOE_OP_BACKWARD = 2,
+  MOE_OP_BACKWARD_RECOMPUTE = 3
+} moe_op;
 
 typedef struct {
   int64_t T, d, E, k, I;
@@ -150,7 +157,16 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
  * dw_gate_up [E,2I,d], dw_down [E,d,I] (dtype; experts with no rows get
  * exact zeros), d_topk_w [T,k] float32, and dlogits [T,E] (logits_dtype;
  * zero outside the selected experts) or NULL.  dlogits requires the logits
- * form of routing (routing->logits != NULL). */
+ * form of routing (routing->logits != NULL).
+ * saved == NULL selects recomputation (activation checkpointing, where a
+ * layer costs two forwards and one backward: "Prime Intellect added the
+ * missing backward pass to DeepSeek's fused MoE kernel ..."; "Prime Mega MoE
+ * Trains Giant AI Models 55% Faster", section "Where MoE training loses
+ * time"): the call first reruns the gate/up GEMM (and, with an fp8 forward,
+ * the weight encodings) from x and the routing into its workspace, with the
+ * same kernels as moe_forward, so the results equal those from a saved
+ * buffer bit for bit; the workspace must then hold
+ * moe_workspace_size(shape, MOE_OP_BACKWARD_RECOMPUTE) bytes. */
 moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
                         const moe_routing* routing, const void* w_gate_up,
                         const void* w_down, const void* saved, void* dx,

@@ -1,0 +1,52 @@
+"""The layer's torch operators trace without a GPU: their fake (shape-only)
+implementations give the right output shapes and dtypes, and forward plus
+backward trace into one graph under fake tensors.  CPU only; the library is
+loaded for its host-side size queries."""
+import os
+
+import pytest
+import torch
+
+from combine_top_route_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+T, d, E, k, I = 64, 256, 8, 2, 128
+
+
+def _inputs(device, dtype=torch.bfloat16):
+    return (torch.empty(T, d, dtype=dtype, device=device), torch.empty(T, E, dtype=dtype, device=device),
+            torch.empty(E, 2 * I, d, dtype=dtype, device=device), torch.empty(E, d, I, dtype=dtype, device=device))
+
+
+@pytest.mark.parametrize("precision,save", [("native", True), ("native", False), ("fp8_block", True),
+                                            ("mxfp8", True)])
+def test_fake_shapes(precision, save):
+    from combine_top_route_amd import autograd  # noqa: F401  (registers the operators)
+    x, lg, wgu, wd = _inputs("meta")
+    outs = torch.ops.ctr_moe.moe_fwd(x, lg, wgu, wd, k, precision, save)
+    shape = B.make_shape(T, d, E, k, I, torch.bfloat16, torch.bfloat16, precision)
+    want = [((T, d), torch.bfloat16), ((B.saved_size(shape) if save else 0,), torch.uint8),
+            ((T, k), torch.int32), ((T, k), torch.float32), ((E,), torch.int32), ((E + 1,), torch.int32),
+            ((T * k,), torch.int32), ((T * k,), torch.int32)]
+    assert [(tuple(o.shape), o.dtype) for o in outs] == want
+    g = torch.ops.ctr_moe.moe_bwd(torch.empty(T, d, dtype=torch.bfloat16, device="meta"), x, lg, wgu, wd,
+                                  *outs[1:], k, precision)
+    assert [tuple(t.shape) for t in g] == [(T, d), (T, E), (E, 2 * I, d), (E, d, I)]
+
+
+def test_forward_and_backward_trace_into_one_graph():
+    from torch.fx.experimental.proxy_tensor import make_fx
+
+    from combine_top_route_amd.autograd import moe_layer
+
+    def step(x, lg, wgu, wd, dout):
+        out = moe_layer(x, lg, wgu, wd, k, recompute=True)
+        return torch.autograd.grad(out, (x, lg, wgu, wd), dout)
+
+    x, lg, wgu, wd = (t.requires_grad_() for t in _inputs("cpu"))
+    dout = torch.empty(T, d, dtype=torch.bfloat16)
+    gm = make_fx(step, tracing_mode="fake")(x, lg, wgu, wd, dout)
+    targets = [str(n.target) for n in gm.graph.nodes if n.op == "call_function"]
+    assert any("ctr_moe.moe_fwd" in t for t in targets)
+    assert any("ctr_moe.moe_bwd" in t for t in targets)

@@ -161,7 +161,7 @@ SavedLayout saved_layout(const moe_shape* s) {
 }
 
 struct Layout {
-  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0, tiles = 0;  // routing / schedule
+  size_t hist = 0, tile_off = 0, order = 0, blk_off = 0, tiles = 0, tok = 0;  // routing / schedule
   size_t Y = 0, A = 0, H = 0;                             // forward
   size_t dH = 0, dXp = 0, dwp = 0, G = 0;                 // backward
   // fp8: quantised operands (q) and their scales (s)
@@ -196,6 +196,7 @@ Layout layout(const moe_shape* s, int op) {
   }
   const bool bwd = op == MOE_OP_BACKWARD || op == MOE_OP_BACKWARD_RECOMPUTE;
   if (bwd) {
+    L.tok = take(sizeof(int32_t) * R);
     L.dH = take(es * R * 2 * s->I);
     L.dXp = take(es * R * s->d);
     L.dwp = take(sizeof(float) * R * dw_blocks(s));
@@ -325,6 +326,7 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   a.tile_off = (const int32_t*)at(ws, L.tile_off);
   a.tiles = (const int4*)at(ws, L.tiles);
   a.order = (const int32_t*)at(ws, L.order);
+  a.tok_of = L.tok ? (const int32_t*)at(ws, L.tok) : nullptr;  // backward layouts only
   return a;
 }
 
@@ -445,6 +447,8 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
                           bwd_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr,
                           (int4*)at(workspace, L.tiles)),
           "route_schedule");
+  HIP_TRY(launch_tok_of(c, routing->src_of, (int)(shape->T * shape->k), (int)shape->k,
+                        (int32_t*)at(workspace, L.tok)), "route_tok");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
   const int64_t R = shape->T * shape->k;

@@ -103,6 +103,8 @@ hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const
 // row's top-k-weight gradient dw [R] = <G, silu(g) u>.
 hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, const float* topk_w,
                              const int32_t* src_of, int R, int I, void* dH, float* dw);
+// tok[r] = src_of[r] / k: the token of each expert-sorted row.
+hipError_t launch_tok_of(const LaunchCtx& c, const int32_t* src_of, int R, int k, int32_t* tok);
 // d_topk_w[t,j] = sum_b dwp[row_of[t*k+j]*nblk + b]; dlogits (optional).
 hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, const int32_t* row_of,
                             const int32_t* ids, const float* w, int T, int k, int E,
@@ -122,6 +124,7 @@ struct LayerArgs {
   const int32_t* tile_off;  // [E+1], kRowTile tiles
   const int4* tiles;        // [tile_off[E]] row-tile descriptors
   const int32_t* order;     // [E]
+  const int32_t* tok_of;    // [R] token of each sorted row (backward only)
 };
 
 // Forward GEMMs write H [R,2I] (gate|up, may be null), Aw [R,I] = w_row *

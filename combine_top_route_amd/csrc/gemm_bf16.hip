@@ -100,6 +100,7 @@ __device__ __forceinline__ int km_swz(int krow) { return ((krow & 3) << 1) ^ ((k
 // ---------------------------------------------------------------------------
 template <int ROWS>
 struct OpMK {
+  static constexpr bool TR = false;  // fragments read with plain ds_read_b128
   static constexpr int NI = ROWS * BK * 2 / 1024 / NWAVE;
   static constexpr int BYTES = ROWS * BK * 2;
   const bf16_t* ptr[NI];  // address of this lane's chunk at the current K step
@@ -121,14 +122,17 @@ struct OpMK {
       ptr[i] = rowp_of(row) + koff(i);
     }
   }
-  __device__ bool full(int kt) const { return (kt + 1) * BK <= K; }
-  template <int I0, int I1>
-  __device__ void issue(int kt, lds_t* s, bool full_step) const {
+  // number of leading K steps (of nk) that need no bounds checks
+  __device__ int nfull(int nk) const { return K / BK < nk ? K / BK : nk; }
+  template <int I0, int I1, bool FULL>
+  __device__ void issue(int kt, lds_t* s) const {
     const int w = wave_id();
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
-      if (!full_step && kt * BK + koff(i) >= K) g = g_zero_page;
+      if constexpr (!FULL) {
+        if (kt * BK + koff(i) >= K) g = g_zero_page;
+      }
       dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
@@ -150,6 +154,7 @@ struct OpMK {
 // ---------------------------------------------------------------------------
 template <int COLS>
 struct OpKM {
+  static constexpr bool TR = true;          // fragments read with ds_read_b64_tr_b16
   static constexpr int RB = COLS * 2;       // bytes per k-row
   static constexpr int UPR = RB / 16;       // 16-byte units per k-row
   static constexpr int RPI = 1024 / RB;     // k-rows per instruction
@@ -177,14 +182,16 @@ struct OpKM {
 #pragma unroll
     for (int i = 0; i < NI; ++i) ptr[i] = base + (int64_t)krow(i) * ld + c0_ + ucol(i);
   }
-  __device__ bool full(int kt) const { return cfull && (kt + 1) * BK <= KR; }
-  template <int I0, int I1>
-  __device__ void issue(int kt, lds_t* s, bool full_step) const {
+  __device__ int nfull(int nk) const { return !cfull ? 0 : (KR / BK < nk ? KR / BK : nk); }
+  template <int I0, int I1, bool FULL>
+  __device__ void issue(int kt, lds_t* s) const {
     const int w = wave_id();
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const void* g = ptr[i];
-      if (!full_step && (kt * BK + krow(i) >= KR || c0 + ucol(i) >= N)) g = g_zero_page;
+      if constexpr (!FULL) {
+        if (kt * BK + krow(i) >= KR || c0 + ucol(i) >= N) g = g_zero_page;
+      }
       dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
@@ -211,11 +218,12 @@ struct OpKM {
 // ---------------------------------------------------------------------------
 // Column-contiguous operand whose k-rows are rows of an expert's segment:
 // element (col, k) = base[row(seg0 + k) * ld + col] for k < KR, with
-// row(r) = src_of[r] / kdiv (a token of x or dout) or r itself (src_of null).
-// The row indices of the next stage to issue are loaded one K step ahead.
+// row(r) = tok[r] (GATHER: the token of row r, a row of x or dout) or r.
+// The row indices of the next stage to issue are formed one K step ahead.
 // ---------------------------------------------------------------------------
-template <int COLS>
+template <int COLS, bool GATHER>
 struct OpKMg {
+  static constexpr bool TR = true;
   static constexpr int RB = COLS * 2;
   static constexpr int UPR = RB / 16;
   static constexpr int RPI = 1024 / RB;
@@ -223,10 +231,11 @@ struct OpKMg {
   static constexpr int BYTES = COLS * BK * 2;
   const bf16_t* base;
   int64_t ld;
-  const int32_t* src_of;
-  int kdiv, seg0, c0, KR, N;
-  int nkt;       // stage whose rows are in nrow[]
-  int nrow[NI];  // row of this lane's k-row in instruction i for stage nkt (-1: outside)
+  const int32_t* tok;
+  int seg0, c0, KR, N;
+  int nkt;         // stage whose rows are in nrow[]
+  int nrow[NI];    // row of this lane's k-row in instruction i for stage nkt
+  unsigned nmask;  // bit i: that k-row lies inside the segment
   bool cfull;
 
   __device__ static int krow(int i) {
@@ -236,45 +245,69 @@ struct OpKMg {
     const int p = (threadIdx.x & 63) % UPR;
     return ((((p >> 1) ^ km_swz(krow(i))) << 1) | (p & 1)) * 8;
   }
+  // The token loads are unconditional (k-rows past the segment read a row
+  // inside it, or row 0 of an empty segment) and nothing consumes their
+  // values before the next stage is issued, one K step later, after that
+  // step's wait: a load under a branch, or a select on its value, would make
+  // the compiler wait for every load in flight, the stage just issued
+  // included.
   __device__ void fetch_rows(int kt) {
     nkt = kt;
+    nmask = 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int k = kt * BK + krow(i);
-      nrow[i] = k < KR ? (src_of ? src_of[seg0 + k] / kdiv : seg0 + k) : -1;
+      const bool in = k < KR;
+      nmask |= (unsigned)in << i;
+      if constexpr (GATHER) nrow[i] = tok[KR > 0 ? seg0 + (in ? k : KR - 1) : 0];
+      else nrow[i] = seg0 + k;
     }
   }
-  __device__ void init(const bf16_t* base_, int64_t ld_, const int32_t* src_of_, int kdiv_, int seg0_,
-                       int c0_, int N_, int KR_) {
-    base = base_; ld = ld_; src_of = src_of_; kdiv = kdiv_; seg0 = seg0_;
+  __device__ void init(const bf16_t* base_, int64_t ld_, const int32_t* tok_, int seg0_, int c0_, int N_,
+                       int KR_) {
+    base = base_; ld = ld_; tok = tok_; seg0 = seg0_;
     c0 = c0_; N = N_; KR = KR_;
     cfull = c0_ + COLS <= N_;
     fetch_rows(0);
   }
-  __device__ bool full(int kt) const { return cfull && (kt + 1) * BK <= KR; }
-  template <int I0, int I1>
-  __device__ void issue(int, lds_t* s, bool full_step) const {
+  __device__ int nfull(int nk) const { return !cfull ? 0 : (KR / BK < nk ? KR / BK : nk); }
+  template <int I0, int I1, bool FULL>
+  __device__ void issue(int, lds_t* s) const {
     const int w = wave_id();
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const int c = c0 + ucol(i);
-      const bool ok = nrow[i] >= 0 && (full_step || c < N);
-      const void* g = ok ? (const void*)(base + (int64_t)nrow[i] * ld + c) : (const void*)g_zero_page;
+      const void* g;
+      if constexpr (FULL) {  // every k-row of the stage lies in the segment, every column in N
+        g = base + (int64_t)nrow[i] * ld + c;
+      } else {
+        const bool ok = ((nmask >> i) & 1) && c < N;
+        g = ok ? (const void*)(base + (int64_t)nrow[i] * ld + c) : (const void*)g_zero_page;
+      }
       dma16(g, s + (w + NWAVE * i) * 1024);
     }
   }
-  // the stage just issued is done with nrow[]: fetch the rows of the next one
+  // the stage just issued is done with nrow[]: form the rows of the next one
   __device__ void advance() { fetch_rows(nkt + 1); }
   __device__ static bf16x8_t frag(const lds_t* s, int cb, int kk) { return OpKM<COLS>::frag(s, cb, kk); }
 };
 
-// Issues part P (of 4) of a stage's direct loads of operand O.
-template <int P, class O>
-__device__ __forceinline__ void issue_part(const O& o, int kt, lds_t* s, bool full_step) {
+// Issues part P (of 4) of a stage's direct loads of operand O (FULL: the
+// stage needs no bounds checks).
+template <int P, bool FULL, class O>
+__device__ __forceinline__ void issue_part(const O& o, int kt, lds_t* s) {
   constexpr int per = (O::NI + 3) / 4;
   constexpr int i0 = P * per < O::NI ? P * per : O::NI;
   constexpr int i1 = (P + 1) * per < O::NI ? (P + 1) * per : O::NI;
-  if constexpr (i1 > i0) o.template issue<i0, i1>(kt, s, full_step);
+  if constexpr (i1 > i0) o.template issue<i0, i1, FULL>(kt, s);
+}
+
+template <bool FULL, class OA, class OB>
+__device__ __forceinline__ void issue_stage(const OA& oa, const OB& ob, int kt, lds_t* dst) {
+  issue_part<0, FULL>(oa, kt, dst); issue_part<0, FULL>(ob, kt, dst + OA::BYTES);
+  issue_part<1, FULL>(oa, kt, dst); issue_part<1, FULL>(ob, kt, dst + OA::BYTES);
+  issue_part<2, FULL>(oa, kt, dst); issue_part<2, FULL>(ob, kt, dst + OA::BYTES);
+  issue_part<3, FULL>(oa, kt, dst); issue_part<3, FULL>(ob, kt, dst + OA::BYTES);
 }
 
 // Wave position in the 2 x 4 wave grid.
@@ -284,13 +317,74 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 // ---------------------------------------------------------------------------
 // Main loop.  Per K step: wait for this wave's loads of the step, barrier
 // (all waves' loads landed, everybody done with the slot to be refilled),
-// then four 16-k sub-steps, each issuing a quarter of the next step's loads
-// and reading the fragments of the next sub-step while its MFMAs run.
+// then four 16-k sub-steps; the first issues all of the next step's loads,
+// and each reads the fragments of the next sub-step while its MFMAs run.
+// Steps are instantiated by whether they load a next stage (PRE) and whether
+// that stage needs bounds checks (!FULL), so the steady-state body has no
+// branches: the leading full stages run first, the checked tail after.
+//
+// Where the next stage's loads leave: the compiler cannot tell the
+// transposing LDS read (ds_read_b64_tr_b16) apart from the slot the direct
+// loads are filling, so it makes any such read wait for all direct loads in
+// flight.  No transposed read may therefore follow the loads within a step:
+// with only B transposed, the step's B fragments (two tiles) are all read
+// first and the loads leave at the start; with both transposed, the loads
+// leave in the last sub-step, after the step's last fragment read.
 // ---------------------------------------------------------------------------
+template <bool PRE, bool FULL, class OA, class OB>
+__device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
+                                      f32x16_t (&acc)[TM][TN]) {
+  constexpr int ST = OA::BYTES + OB::BYTES;
+  constexpr int NKK = BK / 16;
+  // only B transposed (the data gradients): all of the step's B fragments
+  // are read before the loads leave at the start; A and B transposed (the
+  // weight gradients): the loads leave in the last sub-step
+  constexpr bool B_FIRST = OB::TR && !OA::TR;
+  constexpr int ISSUE_KK = OA::TR ? NKK - 1 : 0;
+  constexpr int NB = B_FIRST ? NKK : 2;
+  const int wm = wave_m(), wn = wave_n();
+  wait_vmcnt<0>();
+  barrier_lds();
+  lds_t* const dst = base + (slot ^ 1) * ST;
+  const lds_t* As = base + slot * ST;
+  const lds_t* Bs = As + OA::BYTES;
+  bf16x8_t a[2][TM], b[NB][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (TBM / WM) + i * 32, 0);
+#pragma unroll
+  for (int q = 0; q < (B_FIRST ? NKK : 1); ++q)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[q][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, q);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int cur = kk & 1;
+    const int bc = B_FIRST ? kk : cur;
+    if (kk + 1 < NKK) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TBM / WM) + i * 32, kk + 1);
+      if constexpr (!B_FIRST) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[(cur ^ 1) % NB][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
+      }
+    }
+    if constexpr (PRE) {
+      if (kk == ISSUE_KK) issue_stage<FULL>(oa, ob, kt + 1, dst);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[bc][j], acc[i][j], 0, 0, 0);
+  }
+  if constexpr (PRE) {
+    oa.advance();
+    ob.advance();
+  }
+  slot ^= 1;
+}
+
 template <class OA, class OB>
 __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32x16_t (&acc)[TM][TN]) {
-  constexpr int ST = OA::BYTES + OB::BYTES;
-  const int wm = wave_m(), wn = wave_n();
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -299,56 +393,17 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (nk <= 0) return;
   lds_t* const base = (lds_t*)smem;
-  {
-    const bool f = oa.full(0) && ob.full(0);
-    issue_part<0>(oa, 0, base, f); issue_part<1>(oa, 0, base, f);
-    issue_part<2>(oa, 0, base, f); issue_part<3>(oa, 0, base, f);
-    issue_part<0>(ob, 0, base + OA::BYTES, f); issue_part<1>(ob, 0, base + OA::BYTES, f);
-    issue_part<2>(ob, 0, base + OA::BYTES, f); issue_part<3>(ob, 0, base + OA::BYTES, f);
-    oa.advance();
-    ob.advance();
-  }
-  int slot = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();
-    barrier_lds();
-    const bool pre = kt + 1 < nk;
-    lds_t* const dst = base + (slot ^ 1) * ST;
-    const bool f = pre && oa.full(kt + 1) && ob.full(kt + 1);
-    const lds_t* As = base + slot * ST;
-    const lds_t* Bs = As + OA::BYTES;
-    bf16x8_t a[2][TM], b[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (TBM / WM) + i * 32, 0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, 0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TBM / WM) + i * 32, kk + 1);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
-      }
-      if (pre && kk == 0) {
-        issue_part<0>(oa, kt + 1, dst, f); issue_part<0>(ob, kt + 1, dst + OA::BYTES, f);
-        issue_part<1>(oa, kt + 1, dst, f); issue_part<1>(ob, kt + 1, dst + OA::BYTES, f);
-        issue_part<2>(oa, kt + 1, dst, f); issue_part<2>(ob, kt + 1, dst + OA::BYTES, f);
-        issue_part<3>(oa, kt + 1, dst, f); issue_part<3>(ob, kt + 1, dst + OA::BYTES, f);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
-    }
-    if (pre) {
-      oa.advance();
-      ob.advance();
-    }
-    slot ^= 1;
-  }
+  // stages [0, nf) need no bounds checks
+  const int nfa = oa.nfull(nk), nfb = ob.nfull(nk);
+  const int nf = nfa < nfb ? nfa : nfb;
+  if (nf > 0) issue_stage<true>(oa, ob, 0, base);
+  else issue_stage<false>(oa, ob, 0, base);
+  oa.advance();
+  ob.advance();
+  int slot = 0, kt = 0;
+  for (; kt + 1 < nf; ++kt) kstep<true, true>(oa, ob, kt, base, slot, acc);
+  for (; kt + 1 < nk; ++kt) kstep<true, false>(oa, ob, kt, base, slot, acc);
+  kstep<false, false>(oa, ob, kt, base, slot, acc);
 }
 
 // Row inside the wave tile of accumulator register r of MFMA tile i; the
@@ -559,15 +614,13 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
 // rows in expert order (contiguous per expert).
 // ===========================================================================
 struct WgradArgs {
-  // A(m, r) = A[arow(r) * lda + m], arow(r) = a_src ? a_src[r] / kdiv : r
+  // A(m, r) = A[arow(r) * lda + m], B(n, r) = B[brow(r) * ldb + n]; the
+  // gathered side (TAG 0: A, TAG 1: B) reads row tok[r], the other row r
   const bf16_t* A;
   int64_t lda;
-  const int32_t* a_src;
-  // B(n, r) = B[brow(r) * ldb + n], brow(r) = b_src ? b_src[r] / kdiv : r
   const bf16_t* B;
   int64_t ldb;
-  const int32_t* b_src;
-  int kdiv;
+  const int32_t* tok;  // [R] token of each expert-sorted row
   int M, N, m_tiles, n_tiles, E;
   const int32_t* offsets;
   const int32_t* order;
@@ -578,7 +631,8 @@ struct WgradArgs {
 // Experts, largest first, are dealt round-robin to the 8 XCDs (work-groups
 // go to XCD bid % 8); all tiles of an expert run on one XCD, so its rows are
 // fetched into one L2.
-// TAG only tells the launch sites apart in profiles (0: down, 1: gate/up).
+// TAG 0: the down wgrad (A = dout gathered by token), 1: the gate/up wgrad
+// (B = x gathered by token).
 template <int TAG>
 __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -591,10 +645,10 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   const int e = p.order[oi];
   const int seg0 = p.offsets[e];
   const int len = p.offsets[e + 1] - seg0;
-  OpKMg<TBM> oa;
-  OpKMg<TBN> ob;
-  oa.init(p.A, p.lda, p.a_src, p.kdiv, seg0, mt * TBM, p.M, len);
-  ob.init(p.B, p.ldb, p.b_src, p.kdiv, seg0, nt * TBN, p.N, len);
+  OpKMg<TBM, TAG == 0> oa;
+  OpKMg<TBN, TAG == 1> ob;
+  oa.init(p.A, p.lda, p.tok, seg0, mt * TBM, p.M, len);
+  ob.init(p.B, p.ldb, p.tok, seg0, nt * TBN, p.N, len);
   f32x16_t acc[TM][TN];
   mainloop(oa, ob, (int)cdiv(len, BK), smem, acc);
   barrier_lds();
@@ -698,8 +752,8 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
   }
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
     WgradArgs p = {};
-    p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.kdiv = a.k;
-    p.B = (const bf16_t*)Aw; p.ldb = I; p.b_src = nullptr; p.E = a.E;
+    p.A = (const bf16_t*)dout; p.lda = d; p.tok = a.tok_of;
+    p.B = (const bf16_t*)Aw; p.ldb = I; p.E = a.E;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
@@ -718,8 +772,8 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
     WgradArgs p = {};
-    p.A = (const bf16_t*)dH; p.lda = 2 * I; p.a_src = nullptr; p.kdiv = a.k;
-    p.B = (const bf16_t*)a.x; p.ldb = d; p.b_src = a.src_of; p.E = a.E;
+    p.A = (const bf16_t*)dH; p.lda = 2 * I; p.tok = a.tok_of;
+    p.B = (const bf16_t*)a.x; p.ldb = d; p.E = a.E;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.offsets = a.offsets; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;

@@ -302,4 +302,18 @@ hipError_t launch_topk_grad(const LaunchCtx& c, const float* dwp, int nblk, cons
   return hipSuccess;
 }
 
+namespace {
+__global__ __launch_bounds__(256) void tok_of_kernel(const int32_t* __restrict__ src_of, int R, int k,
+                                                     int32_t* __restrict__ tok) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < R) tok[r] = src_of[r] / k;
+}
+}  // namespace
+
+hipError_t launch_tok_of(const LaunchCtx& c, const int32_t* src_of, int R, int k, int32_t* tok) {
+  if (R <= 0) return hipSuccess;
+  MOE_LAUNCH(c, "route_tok", tok_of_kernel, dim3((unsigned)cdiv(R, 256)), dim3(256), 0, src_of, R, k, tok);
+  return hipSuccess;
+}
+
 }  // namespace moe

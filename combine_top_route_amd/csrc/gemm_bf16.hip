@@ -329,7 +329,8 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 // flight.  No transposed read may therefore follow the loads within a step:
 // with only B transposed, the step's B fragments (two tiles) are all read
 // first and the loads leave at the start; with both transposed, the loads
-// leave in the last sub-step, after the step's last fragment read.
+// leave right after the step's last fragment read (in the next-to-last
+// sub-step, which prefetches the last one's).
 // ---------------------------------------------------------------------------
 template <bool PRE, bool FULL, class OA, class OB>
 __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
@@ -338,9 +339,10 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
   constexpr int NKK = BK / 16;
   // only B transposed (the data gradients): all of the step's B fragments
   // are read before the loads leave at the start; A and B transposed (the
-  // weight gradients): the loads leave in the last sub-step
+  // weight gradients): the loads leave in the next-to-last sub-step, right
+  // after it has read the last sub-step's fragments
   constexpr bool B_FIRST = OB::TR && !OA::TR;
-  constexpr int ISSUE_KK = OA::TR ? NKK - 1 : 0;
+  constexpr int ISSUE_KK = OA::TR ? NKK - 2 : 0;
   constexpr int NB = B_FIRST ? NKK : 2;
   const int wm = wave_m(), wn = wave_n();
   wait_vmcnt<0>();

@@ -357,10 +357,15 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
   for (int q = 0; q < (B_FIRST ? NKK : 1); ++q)
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[q][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, q);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const int cur = kk & 1;
     const int bc = B_FIRST ? kk : cur;
+    // this sub-step's fragments are all in registers before its first MFMA
+    // (read during the previous sub-step), so no MFMA below waits on reads
+    // issued after it
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (kk + 1 < NKK) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TBM / WM) + i * 32, kk + 1);
@@ -377,6 +382,20 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[bc][j], acc[i][j], 0, 0, 0);
+    // one fragment read (and direct load) after each MFMA, so the reads of
+    // the next sub-step and the loads of the next stage issue while this
+    // sub-step's MFMAs run, and nothing here waits for them
+    // (a transposed fragment takes two reads)
+    const int NR = (kk + 1 < NKK ? TM * (OA::TR ? 2 : 1) + (B_FIRST ? 0 : TN * (OB::TR ? 2 : 1)) : 0);
+    const int NG = (PRE && kk == ISSUE_KK) ? OA::NI + OB::NI : 0;
+#pragma unroll
+    for (int q = 0; q < TM * TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      if (q * 2 + 1 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+      else if (q * 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (PRE) {
     oa.advance();

@@ -332,9 +332,9 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 // leave right after the step's last fragment read (in the next-to-last
 // sub-step, which prefetches the last one's).
 // ---------------------------------------------------------------------------
-template <bool PRE, bool FULL, class OA, class OB>
+template <int TMX, bool PRE, bool FULL, class OA, class OB>
 __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
-                                      f32x16_t (&acc)[TM][TN]) {
+                                      f32x16_t (&acc)[TMX][TN]) {
   constexpr int ST = OA::BYTES + OB::BYTES;
   constexpr int NKK = BK / 16;
   // only B transposed (the data gradients): all of the step's B fragments
@@ -350,9 +350,9 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
   lds_t* const dst = base + (slot ^ 1) * ST;
   const lds_t* As = base + slot * ST;
   const lds_t* Bs = As + OA::BYTES;
-  bf16x8_t a[2][TM], b[NB][TN];
+  bf16x8_t a[2][TMX], b[NB][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a[0][i] = OA::frag(As, wm * (TBM / WM) + i * 32, 0);
+  for (int i = 0; i < TMX; ++i) a[0][i] = OA::frag(As, wm * (TMX * 32) + i * 32, 0);
 #pragma unroll
   for (int q = 0; q < (B_FIRST ? NKK : 1); ++q)
 #pragma unroll
@@ -368,7 +368,7 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (kk + 1 < NKK) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TBM / WM) + i * 32, kk + 1);
+      for (int i = 0; i < TMX; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TMX * 32) + i * 32, kk + 1);
       if constexpr (!B_FIRST) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) b[(cur ^ 1) % NB][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
@@ -378,7 +378,7 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
       if (kk == ISSUE_KK) issue_stage<FULL>(oa, ob, kt + 1, dst);
     }
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TMX; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[bc][j], acc[i][j], 0, 0, 0);
@@ -386,10 +386,10 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
     // the next sub-step and the loads of the next stage issue while this
     // sub-step's MFMAs run, and nothing here waits for them
     // (a transposed fragment takes two reads)
-    const int NR = (kk + 1 < NKK ? TM * (OA::TR ? 2 : 1) + (B_FIRST ? 0 : TN * (OB::TR ? 2 : 1)) : 0);
+    const int NR = (kk + 1 < NKK ? TMX * (OA::TR ? 2 : 1) + (B_FIRST ? 0 : TN * (OB::TR ? 2 : 1)) : 0);
     const int NG = (PRE && kk == ISSUE_KK) ? OA::NI + OB::NI : 0;
 #pragma unroll
-    for (int q = 0; q < TM * TN; ++q) {
+    for (int q = 0; q < TMX * TN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
       if (q * 2 + 1 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
       else if (q * 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -404,10 +404,12 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
   slot ^= 1;
 }
 
-template <class OA, class OB>
-__device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32x16_t (&acc)[TM][TN]) {
+// TMX: 32-row MFMA tiles per wave along M (a wave covers 32 TMX rows; the
+// A operand holds WM * 32 TMX rows).
+template <int TMX, class OA, class OB>
+__device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32x16_t (&acc)[TMX][TN]) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TMX; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -422,9 +424,9 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
   oa.advance();
   ob.advance();
   int slot = 0, kt = 0;
-  for (; kt + 1 < nf; ++kt) kstep<true, true>(oa, ob, kt, base, slot, acc);
-  for (; kt + 1 < nk; ++kt) kstep<true, false>(oa, ob, kt, base, slot, acc);
-  kstep<false, false>(oa, ob, kt, base, slot, acc);
+  for (; kt + 1 < nf; ++kt) kstep<TMX, true, true>(oa, ob, kt, base, slot, acc);
+  for (; kt + 1 < nk; ++kt) kstep<TMX, true, false>(oa, ob, kt, base, slot, acc);
+  kstep<TMX, false, false>(oa, ob, kt, base, slot, acc);
 }
 
 // Row inside the wave tile of accumulator register r of MFMA tile i; the
@@ -500,9 +502,10 @@ __device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t
 }
 
 // Weights of the tile's rows (topk_w of each row's flat entry; 0 past seg1).
+template <int ROWS>
 __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
                                                  const int32_t* src_of, int m0, int seg1) {
-  for (int t = threadIdx.x; t < TBM; t += NTHR) {
+  for (int t = threadIdx.x; t < ROWS; t += NTHR) {
     const int row = m0 + t;
     wl[t] = row < seg1 ? topk_w[src_of[row]] : 0.0f;
   }
@@ -542,21 +545,18 @@ struct RowsArgs {
   const int32_t* src_of;
 };
 
-// TAG only tells launch sites with the same epilogue and B layout apart in
-// profiles.
-template <int EPI, int BL, int TAG>
-__global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
-  if (L < 0) return;
-  const int nt = L % p.n_tiles;
-  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
-  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+// One row tile: ROWS = 256, or 128 for a segment's last tile when it holds
+// at most 128 rows (the waves then take 64 rows each: half the MFMA work
+// and half the A operand, where a full tile would spend most of it on rows
+// past the segment).
+template <int EPI, int BL, int ROWS>
+__device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt, int e, int m0, int seg1) {
+  constexpr int TMX = ROWS / WM / 32;
   const int seg0 = m0;  // rows past the segment repeat the tile's first row
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
 
-  OpMK<TBM> oa;
+  OpMK<ROWS> oa;
   oa.init([&](int row) {
     int r = m0 + row;
     if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
@@ -565,12 +565,12 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   }, p.K);
   const bf16_t* Be = p.B + (int64_t)e * p.b_estride;
 
-  f32x16_t acc[TM][TN];
+  f32x16_t acc[TMX][TN];
   const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
     OpKM<TBN> ob;
     ob.init(Be, p.ldb, nt * TBN, p.N, p.K);
-    mainloop(oa, ob, nk, smem, acc);
+    mainloop<TMX>(oa, ob, nk, smem, acc);
   } else {
     OpMK<TBN> ob;
     ob.init([&](int n) {
@@ -586,47 +586,61 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
       }
       return Be + (int64_t)wrow * p.ldb;
     }, p.K);
-    mainloop(oa, ob, nk, smem, acc);
+    mainloop<TMX>(oa, ob, nk, smem, acc);
   }
 
   // ------------------------------------------------------------- epilogues
   // The LDS ring is free once every wave has left the main loop.
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
-  const int rows_valid = seg1 - m0;  // rows of this tile inside the segment (may exceed 256)
-  const int r0w = wm * (TBM / WM);   // first tile row of this wave
+  const int rows_valid = seg1 - m0;  // rows of this tile inside the segment (may exceed ROWS)
+  const int r0w = wm * (ROWS / WM);  // first tile row of this wave
   if constexpr (EPI == EPI_STORE) {
     constexpr int S = ep_stride<TBN>();
-    stage_pairs<TM, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
+    stage_pairs<TMX, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
     barrier_lds();
-    lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
-                               p.N - nt * TBN);
+    lds_to_global<ROWS, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
+                                p.N - nt * TBN);
   } else if constexpr (EPI == EPI_GATEUP) {
     // acc[i][0] = gate, acc[i][1] = up, for the tile's gate column
     // wn * 32 + (lane & 31) (128 gate columns per tile)
     constexpr int S = ep_stride<TBN / 2>();
-    constexpr int TB = TBM * S;  // bytes of one staged 256 x 128 tile
+    constexpr int TB = ROWS * S;  // bytes of one staged ROWS x 128 tile
     lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
+    load_row_weights<ROWS>(wl, p.topk_w, p.src_of, m0, seg1);
     barrier_lds();
     const int c0w = wn * 32;
-    stage_pairs<TM, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
+    stage_pairs<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
       const float g = acc[i][0][r], u = acc[i][1][r];
       return wl[r0w + acc_row(i, r, lane)] * (g * sigmoidf_(g) * u);
     });
-    if (p.H) stage_pairs<TM, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
+    if (p.H) stage_pairs<TMX, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
     barrier_lds();
     const int gc0 = nt * (TBN / 2);
-    lds_to_global<TBM, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
+    lds_to_global<ROWS, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
     if (p.H) {
       bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
-      lds_to_global<TBM, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<ROWS, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
       barrier_lds();
-      stage_pairs<TM, 1, S>(lds, r0w, c0w, [&](int i, int, int r) { return acc[i][1][r]; });
+      stage_pairs<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) { return acc[i][1][r]; });
       barrier_lds();
-      lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<ROWS, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
   }
+}
+
+// TAG only tells launch sites with the same epilogue and B layout apart in
+// profiles.
+template <int EPI, int BL, int TAG>
+__global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
+  if (L < 0) return;
+  const int nt = L % p.n_tiles;
+  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
+  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+  if (seg1 - m0 <= TBM / 2) rows_tile<EPI, BL, TBM / 2>(p, smem, nt, e, m0, seg1);
+  else rows_tile<EPI, BL, TBM>(p, smem, nt, e, m0, seg1);
 }
 
 // ===========================================================================
@@ -671,7 +685,7 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   oa.init(p.A, p.lda, p.tok, seg0, mt * TBM, p.M, len);
   ob.init(p.B, p.ldb, p.tok, seg0, nt * TBN, p.N, len);
   f32x16_t acc[TM][TN];
-  mainloop(oa, ob, (int)cdiv(len, BK), smem, acc);
+  mainloop<TM>(oa, ob, (int)cdiv(len, BK), smem, acc);
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   constexpr int S = ep_stride<TBN>();

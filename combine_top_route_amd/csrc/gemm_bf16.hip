@@ -545,10 +545,10 @@ struct RowsArgs {
   const int32_t* src_of;
 };
 
-// One row tile: ROWS = 256, or 128 for a segment's last tile when it holds
-// at most 128 rows (the waves then take 64 rows each: half the MFMA work
-// and half the A operand, where a full tile would spend most of it on rows
-// past the segment).
+// One row tile: ROWS = 256, or 128 / 64 for a segment's last tile when it
+// holds at most that many rows (the waves then take 64 / 32 rows each: a
+// half / a quarter of the MFMA work and of the A operand, where a full tile
+// would spend most of it on rows past the segment).
 template <int EPI, int BL, int ROWS>
 __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt, int e, int m0, int seg1) {
   constexpr int TMX = ROWS / WM / 32;
@@ -639,7 +639,9 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   const int nt = L % p.n_tiles;
   const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
   const int e = desc.x, m0 = desc.y, seg1 = desc.z;
-  if (seg1 - m0 <= TBM / 2) rows_tile<EPI, BL, TBM / 2>(p, smem, nt, e, m0, seg1);
+  const int rows = seg1 - m0;
+  if (rows <= TBM / 4) rows_tile<EPI, BL, TBM / 4>(p, smem, nt, e, m0, seg1);
+  else if (rows <= TBM / 2) rows_tile<EPI, BL, TBM / 2>(p, smem, nt, e, m0, seg1);
   else rows_tile<EPI, BL, TBM>(p, smem, nt, e, m0, seg1);
 }
 

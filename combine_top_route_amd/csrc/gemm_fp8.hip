@@ -60,11 +60,13 @@ enum ScaleMode {
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 // ---------------------------------------------------------------------------
-// One operand: 256 rows x 128 bytes per stage.  Instruction q covers rows
-// 8q..8q+7 (1 KB); wave w issues q = w + 8i, i < 4.
+// One operand: 64 NI rows x 128 bytes per stage (NI = 4: 256 rows).
+// Instruction q covers rows 8q..8q+7 (1 KB); wave w issues q = w + 8i, i < NI.
 // ---------------------------------------------------------------------------
+template <int NI = 4>
 struct Op8 {
-  const uint8_t* ptr[4];  // this lane's 16-byte chunk at the current stage
+  static constexpr int N = NI;
+  const uint8_t* ptr[NI];  // this lane's 16-byte chunk at the current stage
 
   __device__ static int koff(int i) {
     const int lane = threadIdx.x & 63;
@@ -76,17 +78,17 @@ struct Op8 {
   __device__ void init(F rowp) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ptr[i] = rowp(8 * (w + NWAVE * i) + (lane >> 3)) + koff(i);
+    for (int i = 0; i < NI; ++i) ptr[i] = rowp(8 * (w + NWAVE * i) + (lane >> 3)) + koff(i);
   }
   template <int I0, int I1>
   __device__ void issue(lds_t* s) const {
     const int w = wave_id();
 #pragma unroll
-    for (int i = I0; i < I1; ++i) dma16(ptr[i], s + (w + NWAVE * i) * 1024);
+    for (int i = I0; i < (I1 < NI ? I1 : NI); ++i) dma16(ptr[i], s + (w + NWAVE * i) * 1024);
   }
   __device__ void advance() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ptr[i] += KB;
+    for (int i = 0; i < NI; ++i) ptr[i] += KB;
   }
 };
 
@@ -120,31 +122,37 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 
 // Part I of a stage's loads: token-operand instruction I / 2 (even I) or
 // feature-operand instruction I / 2 (odd I); part 0 adds the scales.
-template <int I>
-__device__ __forceinline__ void issue_step(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst) {
+template <int I, class OT, class OF>
+__device__ __forceinline__ void issue_step(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst) {
   constexpr int q = I / 2;
-  if constexpr (I % 2 == 0) ot.issue<q, q + 1>(dst);
-  else of.issue<q, q + 1>(dst + OPB);
+  if constexpr (I % 2 == 0) ot.template issue<q, q + 1>(dst);
+  else of.template issue<q, q + 1>(dst + OPB);
   if constexpr (I == 0) dma4(sp, dst + 2 * OPB + 256 * wave_id());
 }
 
+template <class OT, class OF>
+__device__ __forceinline__ void issue_stage(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst) {
+  issue_step<0>(ot, of, sp, dst); issue_step<1>(ot, of, sp, dst); issue_step<2>(ot, of, sp, dst);
+  issue_step<3>(ot, of, sp, dst); issue_step<4>(ot, of, sp, dst); issue_step<5>(ot, of, sp, dst);
+  issue_step<6>(ot, of, sp, dst); issue_step<7>(ot, of, sp, dst);
+}
+
 // ---------------------------------------------------------------------------
-// Main loop over nkb K steps.  SC_ROW: the feature side has a scale per row
-// (token-blocked operands) rather than per 128 rows (weights), so each of a
-// lane's four results takes its own feature scale.
-// acc[i][j][r]: token wave_m*128 + 16 i + lane % 16, feature
+// Main loop over nkb K steps.  TMX: 16-row MFMA tiles per wave along tokens
+// (8 for a 256-row tile; 4 / 2 for a segment tail of at most 128 / 64 rows,
+// whose token operand is loaded for 128 / 64 rows only).  SC_ROW: the
+// feature side has a scale per row (token-blocked operands) rather than per
+// 128 rows (weights), so each of a lane's four results takes its own
+// feature scale.
+// acc[i][j][r]: token wave_m*16*TMX + 16 i + lane % 16, feature
 // wave_n*64 + 16 j + 4 (lane / 16) + r.
 // ---------------------------------------------------------------------------
-template <int SC, bool PRE, int I>
-__device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst,
+template <int SC, int TMX, bool PRE, int I, class OT, class OF>
+__device__ __forceinline__ void substep(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
                                         const i32x8_t (&f)[TN], const i32x8_t& t,
                                         const lds_f32_t* SAw, float& sa, const f32x4_t (&sb)[TN],
-                                        f32x4_t (&acc)[TM][TN]) {
-  if constexpr (PRE && I == 0) {  // the whole next stage leaves at the start of the step
-    issue_step<0>(ot, of, sp, dst); issue_step<1>(ot, of, sp, dst); issue_step<2>(ot, of, sp, dst);
-    issue_step<3>(ot, of, sp, dst); issue_step<4>(ot, of, sp, dst); issue_step<5>(ot, of, sp, dst);
-    issue_step<6>(ot, of, sp, dst); issue_step<7>(ot, of, sp, dst);
-  }
+                                        f32x4_t (&acc)[TMX][TN]) {
+  if constexpr (PRE && I == 0) issue_stage(ot, of, sp, dst);  // the next stage leaves at the step's start
   const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -158,53 +166,89 @@ __device__ __forceinline__ void substep(const Op8& ot, const Op8& of, const uint
       for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r], s, acc[I][j][r]);
     }
   }
-  if constexpr (I + 1 < TM) sa = SAw[(I + 1) * 16];  // token scale of the next sub-step
+  if constexpr (I + 1 < TMX) sa = SAw[(I + 1) * 16];  // token scale of the next sub-step
   // keep the scheduler from hoisting later sub-steps' fragment reads and
   // MFMAs: each would hold its own registers live
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// MX sub-step I: the MFMA applies the E8M0 codes (byte 0 of each scale
+// operand) and accumulates in place.  st: this lane's token-row code of
+// sub-tile I; sf[j]: its feature-row code of sub-tile j.
+template <int TMX, bool PRE, int I, class OT, class OF>
+__device__ __forceinline__ void substep_mx(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
+                                           const i32x8_t (&f)[TN], const i32x8_t& t, const lds_u8_t* SAl,
+                                           int& st, const int (&sf)[TN], f32x4_t (&acc)[TMX][TN]) {
+  if constexpr (PRE && I == 0) issue_stage(ot, of, sp, dst);
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    acc[I][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, acc[I][j], 0, 0, 0, sf[j], 0, st);
+  if constexpr (I + 1 < TMX) st = SAl[(I + 1) * 16 * 4];  // token code of the next sub-step
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sub-steps I .. TMX-1 of a K step: t[I & 1] holds sub-step I's token
+// fragment, the other slot sub-step I + 1's; each slot is refilled for
+// I + 2 once its sub-step has issued.
+template <int SC, int TMX, bool PRE, int I, class OT, class OF>
+__device__ __forceinline__ void substeps(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
+                                         const i32x8_t (&f)[TN], i32x8_t (&t)[2], const lds_t* tb,
+                                         const FragOff& fo, const lds_f32_t* SAw, float& sa,
+                                         const f32x4_t (&sb)[TN], const lds_u8_t* SAl, int& st,
+                                         const int (&sf)[TN], f32x4_t (&acc)[TMX][TN]) {
+  if constexpr (I < TMX) {
+    if constexpr (SC == SC_MX) substep_mx<TMX, PRE, I>(ot, of, sp, dst, f, t[I & 1], SAl, st, sf, acc);
+    else substep<SC, TMX, PRE, I>(ot, of, sp, dst, f, t[I & 1], SAw, sa, sb, acc);
+    if constexpr (I + 2 < TMX) t[I & 1] = frag8(tb + (I + 2) * 16 * KB, fo);
+    substeps<SC, TMX, PRE, I + 1>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sb, SAl, st, sf, acc);
+  }
+}
+
 // One K step on the stage in `cur`; PRE: also load the next stage into `dst`
 // (a branch-free body, so the sub-step boundaries hold).
-template <int SC, bool PRE>
-__device__ __forceinline__ void kstep(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
-                                      lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
+template <int SC, int TMX, bool PRE, class OT, class OF>
+__device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, const lds_t* cur, lds_t* dst,
+                                      const FragOff& fo, f32x4_t (&acc)[TMX][TN]) {
   const int wm = wave_m(), wn = wave_n();
   const int lane = threadIdx.x & 63;
   wait_vmcnt<0>();
   barrier_lds();
-  const lds_f32_t* SA = (const lds_f32_t*)(cur + 2 * OPB);
-  const lds_f32_t* SB = (const lds_f32_t*)(cur + 2 * OPB + SCB);
-  const lds_f32_t* SAw = SA + wm * 128 + (lane & 15);
-  float sa = SAw[0];
+  const int trow = wm * TMX * 16;  // this wave's first token row
+  // blockwise scales: fp32 [row]; MX: words [row] of 4 codes, this lane's
+  // code at row lane % 16 of each sub-tile, block lane / 16
+  const lds_f32_t* SAw = nullptr;
+  const lds_u8_t* SAl = nullptr;
+  float sa = 0.0f;
+  int st = 0;
   f32x4_t sb[TN];
+  int sf[TN];
+  if constexpr (SC == SC_MX) {
+    const int lo = (lane & 15) * 4 + (lane >> 4);
+    SAl = (const lds_u8_t*)(cur + 2 * OPB) + trow * 4 + lo;
+    const lds_u8_t* SBl = (const lds_u8_t*)(cur + 2 * OPB + SCB) + wn * 64 * 4 + lo;
+    st = SAl[0];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int fr = wn * 64 + j * 16 + 4 * (lane >> 4);
-    if constexpr (SC == SC_ROW) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
-    else sb[j][0] = SB[fr];
+    for (int j = 0; j < TN; ++j) sf[j] = SBl[j * 16 * 4];
+  } else {
+    const lds_f32_t* SB = (const lds_f32_t*)(cur + 2 * OPB + SCB);
+    SAw = (const lds_f32_t*)(cur + 2 * OPB) + trow + (lane & 15);
+    sa = SAw[0];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int fr = wn * 64 + j * 16 + 4 * (lane >> 4);
+      if constexpr (SC == SC_ROW) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
+      else sb[j][0] = SB[fr];
+    }
   }
-  const lds_t* tb = cur + wm * 128 * KB;       // this wave's token rows
+  const lds_t* tb = cur + trow * KB;           // this wave's token rows
   const lds_t* fb = cur + OPB + wn * 64 * KB;  // this wave's feature rows
   i32x8_t f[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
-  i32x8_t t0 = frag8(tb, fo);
-  i32x8_t t1 = frag8(tb + 16 * KB, fo);
-  substep<SC, PRE, 0>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
-  t0 = frag8(tb + 32 * KB, fo);
-  substep<SC, PRE, 1>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
-  t1 = frag8(tb + 48 * KB, fo);
-  substep<SC, PRE, 2>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
-  t0 = frag8(tb + 64 * KB, fo);
-  substep<SC, PRE, 3>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
-  t1 = frag8(tb + 80 * KB, fo);
-  substep<SC, PRE, 4>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
-  t0 = frag8(tb + 96 * KB, fo);
-  substep<SC, PRE, 5>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
-  t1 = frag8(tb + 112 * KB, fo);
-  substep<SC, PRE, 6>(ot, of, sp, dst, f, t0, SAw, sa, sb, acc);
-  substep<SC, PRE, 7>(ot, of, sp, dst, f, t1, SAw, sa, sb, acc);
+  i32x8_t t[2];
+  t[0] = frag8(tb, fo);
+  if constexpr (TMX > 1) t[1] = frag8(tb + 16 * KB, fo);
+  substeps<SC, TMX, PRE, 0>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sb, SAl, st, sf, acc);
   if constexpr (PRE) {
     ot.advance();
     of.advance();
@@ -212,98 +256,26 @@ __device__ __forceinline__ void kstep(Op8& ot, Op8& of, const uint32_t*& sp, con
   }
 }
 
-// MX sub-step I: the MFMA applies the E8M0 codes (byte 0 of each scale
-// operand) and accumulates in place.  st: this lane's token-row code of
-// sub-tile I; sf[j]: its feature-row code of sub-tile j.
-template <bool PRE, int I>
-__device__ __forceinline__ void substep_mx(const Op8& ot, const Op8& of, const uint32_t* sp, lds_t* dst,
-                                           const i32x8_t (&f)[TN], const i32x8_t& t, const lds_u8_t* SAl,
-                                           int& st, const int (&sf)[TN], f32x4_t (&acc)[TM][TN]) {
-  if constexpr (PRE && I == 0) {
-    issue_step<0>(ot, of, sp, dst); issue_step<1>(ot, of, sp, dst); issue_step<2>(ot, of, sp, dst);
-    issue_step<3>(ot, of, sp, dst); issue_step<4>(ot, of, sp, dst); issue_step<5>(ot, of, sp, dst);
-    issue_step<6>(ot, of, sp, dst); issue_step<7>(ot, of, sp, dst);
-  }
+template <int SC, int TMX, class OT, class OF>
+__device__ __forceinline__ void mainloop8(OT& ot, OF& of, const uint32_t* sp, int nkb, char* smem,
+                                          f32x4_t (&acc)[TMX][TN]) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
-    acc[I][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, acc[I][j], 0, 0, 0, sf[j], 0, st);
-  if constexpr (I + 1 < TM) st = SAl[(I + 1) * 16 * 4];  // token code of the next sub-step
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <bool PRE>
-__device__ __forceinline__ void kstep_mx(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
-                                         lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
-  const int wm = wave_m(), wn = wave_n();
-  const int lane = threadIdx.x & 63;
-  wait_vmcnt<0>();
-  barrier_lds();
-  // scale words [row] of 4 codes; this lane's code: row lane % 16 of each
-  // sub-tile, block lane / 16
-  const int lo = (lane & 15) * 4 + (lane >> 4);
-  const lds_u8_t* SAl = (const lds_u8_t*)(cur + 2 * OPB) + wm * 128 * 4 + lo;
-  const lds_u8_t* SBl = (const lds_u8_t*)(cur + 2 * OPB + SCB) + wn * 64 * 4 + lo;
-  int st = SAl[0];
-  int sf[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) sf[j] = SBl[j * 16 * 4];
-  const lds_t* tb = cur + wm * 128 * KB;
-  const lds_t* fb = cur + OPB + wn * 64 * KB;
-  i32x8_t f[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
-  i32x8_t t0 = frag8(tb, fo);
-  i32x8_t t1 = frag8(tb + 16 * KB, fo);
-  substep_mx<PRE, 0>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
-  t0 = frag8(tb + 32 * KB, fo);
-  substep_mx<PRE, 1>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
-  t1 = frag8(tb + 48 * KB, fo);
-  substep_mx<PRE, 2>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
-  t0 = frag8(tb + 64 * KB, fo);
-  substep_mx<PRE, 3>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
-  t1 = frag8(tb + 80 * KB, fo);
-  substep_mx<PRE, 4>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
-  t0 = frag8(tb + 96 * KB, fo);
-  substep_mx<PRE, 5>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
-  t1 = frag8(tb + 112 * KB, fo);
-  substep_mx<PRE, 6>(ot, of, sp, dst, f, t0, SAl, st, sf, acc);
-  substep_mx<PRE, 7>(ot, of, sp, dst, f, t1, SAl, st, sf, acc);
-  if constexpr (PRE) {
-    ot.advance();
-    of.advance();
-    sp += 1;
-  }
-}
-
-template <int SC, bool PRE>
-__device__ __forceinline__ void any_kstep(Op8& ot, Op8& of, const uint32_t*& sp, const lds_t* cur,
-                                          lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TM][TN]) {
-  if constexpr (SC == SC_MX) kstep_mx<PRE>(ot, of, sp, cur, dst, fo, acc);
-  else kstep<SC, PRE>(ot, of, sp, cur, dst, fo, acc);
-}
-
-template <int SC>
-__device__ __forceinline__ void mainloop8(Op8& ot, Op8& of, const uint32_t* sp, int nkb, char* smem,
-                                          f32x4_t (&acc)[TM][TN]) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TMX; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   if (nkb <= 0) return;
   lds_t* const base = (lds_t*)smem;
   const FragOff fo;
-  issue_step<0>(ot, of, sp, base); issue_step<1>(ot, of, sp, base); issue_step<2>(ot, of, sp, base);
-  issue_step<3>(ot, of, sp, base); issue_step<4>(ot, of, sp, base); issue_step<5>(ot, of, sp, base);
-  issue_step<6>(ot, of, sp, base); issue_step<7>(ot, of, sp, base);
+  issue_stage(ot, of, sp, base);
   ot.advance();
   of.advance();
   sp += 1;
   int slot = 0;
   for (int kb = 0; kb + 1 < nkb; ++kb) {
-    any_kstep<SC, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+    kstep<SC, TMX, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
     slot ^= 1;
   }
-  any_kstep<SC, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+  kstep<SC, TMX, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,9 +327,10 @@ __device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t
   }
 }
 
+template <int ROWS>
 __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
                                                  const int32_t* src_of, int m0, int seg1) {
-  for (int t = threadIdx.x; t < TBM; t += NTHR) {
+  for (int t = threadIdx.x; t < ROWS; t += NTHR) {
     const int row = m0 + t;
     wl[t] = row < seg1 ? topk_w[src_of[row]] : 0.0f;
   }
@@ -407,16 +380,12 @@ struct Rows8Args {
   const int32_t* src_of;
 };
 
-// TAG only tells launch sites with the same epilogue apart in profiles.
-// SC: SC_WEIGHT (blockwise) or SC_MX.
-template <int EPI, int TAG, int SC>
-__global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
-  if (L < 0) return;
-  const int nt = L % p.n_tiles;
-  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
-  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+// One row tile of ROWS token rows: 256, or 128 / 64 for a segment's last
+// tile holding at most that many rows (the waves then take 64 / 32 rows:
+// a half / a quarter of the MFMA work and of the token operand).
+template <int EPI, int SC, int ROWS>
+__device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int nt, int e, int m0, int seg1) {
+  constexpr int TMX = ROWS / WM / 16;
   const int seg0 = m0;  // rows past the segment repeat the tile's first row
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
@@ -438,26 +407,27 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   };
   const uint8_t* Be = p.B + (int64_t)e * p.b_estride;
   const uint32_t* Bse = p.Bs + (int64_t)e * p.bs_estride;
-  Op8 ot, of;
+  Op8<ROWS / 64> ot;
+  Op8<> of;
   ot.init([&](int row) { return p.A + arow(row) * p.lda; });
   of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
   const int srow = 64 * (wave_id() & 3) + lane;
   const uint32_t* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_sld
                                      : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_sld;
-  f32x4_t acc[TM][TN];
-  mainloop8<SC>(ot, of, sp, p.K / KB, smem, acc);
+  f32x4_t acc[TMX][TN];
+  mainloop8<SC, TMX>(ot, of, sp, p.K / KB, smem, acc);
 
   // ------------------------------------------------------------- epilogues
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   const int rows_valid = seg1 - m0;
-  const int r0w = wm * (TBM / WM);
+  const int r0w = wm * (ROWS / WM);
   if constexpr (EPI == EPI_STORE) {
     constexpr int S = ep_stride<TBN>();
-    stage4<TM, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
+    stage4<TMX, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
     barrier_lds();
-    lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
-                               p.N - nt * TBN);
+    lds_to_global<ROWS, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
+                                p.N - nt * TBN);
   } else if constexpr (EPI == EPI_STORE_F32) {
     // two passes of 128 columns (the waves with wn = 2h, 2h + 1), 528-byte
     // LDS rows so that a lane group's 16 rows hit distinct banks
@@ -467,7 +437,7 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
       if (h) barrier_lds();
       if ((wn >> 1) == h) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TMX; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int row = r0w + i * 16 + (lane & 15);
@@ -479,7 +449,7 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
       float* Cb = p.Cf + (int64_t)m0 * p.ldc + nt * TBN + 128 * h;
       const int col_lim = p.N - nt * TBN - 128 * h;
 #pragma unroll 4
-      for (int q = threadIdx.x; q < TBM * 32; q += NTHR) {
+      for (int q = threadIdx.x; q < ROWS * 32; q += NTHR) {
         const int row = q >> 5, c4 = q & 31;
         if (row < rows_valid && c4 * 4 < col_lim)
           *(f32x4_t*)(Cb + (int64_t)row * p.ldc + c4 * 4) =
@@ -490,28 +460,44 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
     // features j = 0, 1 are gate columns wn*32 + 16 j + ..., j = 2, 3 the up
     // columns of the same gate columns
     constexpr int S = ep_stride<TBN / 2>();
-    constexpr int TB = TBM * S;
+    constexpr int TB = ROWS * S;
     lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    load_row_weights(wl, p.topk_w, p.src_of, m0, seg1);
+    load_row_weights<ROWS>(wl, p.topk_w, p.src_of, m0, seg1);
     barrier_lds();
     const int c0w = wn * 32;
-    stage4<TM, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) {
+    stage4<TMX, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) {
       const float g = acc[i][j][r], u = acc[i][j + 2][r];
       return wl[r0w + i * 16 + (lane & 15)] * (g * sigmoidf_(g) * u);
     });
-    if (p.H) stage4<TM, 2, S>(lds + TB, r0w, c0w, [&](int i, int j, int r) { return acc[i][j][r]; });
+    if (p.H) stage4<TMX, 2, S>(lds + TB, r0w, c0w, [&](int i, int j, int r) { return acc[i][j][r]; });
     barrier_lds();
     const int gc0 = nt * (TBN / 2);
-    lds_to_global<TBM, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
+    lds_to_global<ROWS, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
     if (p.H) {
       bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
-      lds_to_global<TBM, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<ROWS, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
       barrier_lds();
-      stage4<TM, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) { return acc[i][j + 2][r]; });
+      stage4<TMX, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) { return acc[i][j + 2][r]; });
       barrier_lds();
-      lds_to_global<TBM, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
+      lds_to_global<ROWS, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
   }
+}
+
+// TAG only tells launch sites with the same epilogue apart in profiles.
+// SC: SC_WEIGHT (blockwise) or SC_MX.
+template <int EPI, int TAG, int SC>
+__global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
+  if (L < 0) return;
+  const int nt = L % p.n_tiles;
+  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
+  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+  const int rows = seg1 - m0;
+  if (rows <= TBM / 4) rows8_tile<EPI, SC, TBM / 4>(p, smem, nt, e, m0, seg1);
+  else if (rows <= TBM / 2) rows8_tile<EPI, SC, TBM / 2>(p, smem, nt, e, m0, seg1);
+  else rows8_tile<EPI, SC, TBM>(p, smem, nt, e, m0, seg1);
 }
 
 // ===========================================================================
@@ -549,14 +535,14 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   const int nkb = p.blk_off[e + 1] - b0;
   auto mrow = [&](int row) { const int m = mt * TBM + row; return m < p.M ? m : 0; };
   auto nrow = [&](int row) { const int n = nt * TBN + row; return n < p.N ? n : 0; };
-  Op8 ot, of;
+  Op8<> ot, of;
   ot.init([&](int row) { return p.A + (int64_t)mrow(row) * p.ldk + (int64_t)b0 * KB; });
   of.init([&](int row) { return p.B + (int64_t)nrow(row) * p.ldk + (int64_t)b0 * KB; });
   const int srow = 64 * (wave_id() & 3) + (threadIdx.x & 63);
   const uint32_t* sp = wave_id() < 4 ? p.As + (int64_t)mrow(srow) * p.nblk + b0
                                      : p.Bs + (int64_t)nrow(srow) * p.nblk + b0;
   f32x4_t acc[TM][TN];
-  mainloop8<SC>(ot, of, sp, nkb, smem, acc);
+  mainloop8<SC, TM>(ot, of, sp, nkb, smem, acc);
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   constexpr int S = ep_stride<TBN>();

@@ -48,6 +48,7 @@ KERNEL_SITES = [
     ("combine_wide_kernel<", "combine + reduce_dx"), ("combine_kernel<", "combine + reduce_dx"),
     ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
+    ("tok_of_kernel", "route_tok"),
     ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
     ("quant_weight_kernel", "quant_w_*"), ("quant_weight_mx_kernel", "quant_w_*"),
     ("quant_tok_kernel", "quant_*_tok"),
@@ -150,7 +151,13 @@ def measured_traffic(wl, kernel: str):
 
 def cpu_baseline(wl, inp: dict, tokens: int):
     """The oracle (fp64 numpy) on the first `tokens` tokens of the workload,
-    all experts, forward + backward; rate in TFLOP/s of algorithmic work."""
+    all experts, forward + backward; rate in TFLOP/s of algorithmic work.
+
+    MXFP8 encodes every expert's two weights in two blockings, a fixed cost
+    (minutes in numpy) that no token sample bounds; its sample is instead the
+    rows of the two most-loaded experts among the first `tokens` tokens,
+    through the oracle's per-expert evaluator (gate/up forward, down dgrad,
+    both weight gradients), whose work is 12 rows d I."""
     from oracle import moe_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -164,6 +171,19 @@ def cpu_baseline(wl, inp: dict, tokens: int):
     fp8 = wl.precision in FP8
     recipe = O.MXFP8 if wl.precision == "mxfp8" else O.FP8_BLOCK
     fwd_recipe = O.NO_QUANT if wl.precision == "fp8_bwd" else recipe
+    if wl.precision == "mxfp8":
+        rt = O.route(lg, wl.k, wl.E)
+        top = np.argsort(-rt["counts"], kind="stable")[:2]
+        t0 = time.perf_counter()
+        for e in top:
+            O.expert_weight_grads_fp8(x, dout, rt, Wgu, Wd, int(e), recipe=recipe)
+        dt = time.perf_counter() - t0
+        rows = int(rt["counts"][top].sum())
+        return {"value": 12.0 * rows * wl.d * wl.I / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"rows of experts {[int(e) for e in top]} ({rows} rows) among the first {tokens} "
+                          f"tokens of the {wl.name} workload, per-expert fwd gate/up + down dgrad + both "
+                          f"weight gradients in float64 numpy emulating MXFP8, {dt:.1f} s"}
     t0 = time.perf_counter()
     rt = O.route(lg, wl.k, wl.E)
     if fp8:
@@ -446,6 +466,8 @@ def main():
     }
     if not args.no_cpu:
         n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(wl.name, wl.T)
+        print(f"bench: GPU timing done ({ms_per_step:.3f} ms/step); CPU oracle baseline on {min(n, wl.T)} "
+              f"tokens", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, min(n, wl.T))
     print(json.dumps(res), flush=True)
 

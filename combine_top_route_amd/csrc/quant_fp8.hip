@@ -146,6 +146,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
   }
 }
 
+// Staged code tiles: 128 rows of 32 words (+1 of padding) in LDS, leaving
+// as 16-byte pieces of 128-byte rows.
+constexpr int kWS = 33;  // staged code rows: 32 words + 1 of padding
+
+__device__ __forceinline__ void store_code_tile(const uint32_t* tile, uint8_t* dst, int64_t ld) {
+  // 128 rows x 128 bytes: chunk c = 16 bytes (4 words) of row c / 8
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = p * 256 + threadIdx.x;
+    const int row = c >> 3, w = (c & 7) * 4;
+    const uint32_t* src = tile + row * kWS + w;
+    *(u32x4_t*)(dst + (int64_t)row * ld + w * 4) = u32x4_t{src[0], src[1], src[2], src[3]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 128 x 128 weight blocks of W [E, N, K], written as q [E, N, K] with s [E,
 // N/128, K/128] and/or transposed as qt [E, K, N] with st [E, K/128, N/128]
@@ -157,7 +172,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
                                                           uint8_t* __restrict__ qt,
                                                           float* __restrict__ st) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint32_t codes[128 * 33];  // [n][32 words], padded
+  __shared__ __attribute__((aligned(16))) uint32_t fcodes[128 * kWS];  // [n][32 words]
+  __shared__ __attribute__((aligned(16))) uint32_t tcodes[128 * kWS];  // [k][32 words]
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
   const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
@@ -189,28 +205,26 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) f[j][i] = __fdiv_rn(f[j][i], sc);
+  // q, qt are kernel arguments: every branch on them is uniform
   if (qt) {  // a transposed row gets four consecutive codes from each of 32 lanes
-    uint8_t* qb = qt + (int64_t)e * K * N + (int64_t)(kb * 128 + k0) * N + nb * 128 + n0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *(uint32_t*)(qb + (int64_t)i * N) = e4m3x4(f[0][i], f[1][i], f[2][i], f[3][i]);
-    if (t == 0) st[((int64_t)e * nbk + kb) * nbn + nb] = sc;
+    for (int i = 0; i < 16; ++i) tcodes[(k0 + i) * kWS + (n0 >> 2)] = e4m3x4(f[0][i], f[1][i], f[2][i], f[3][i]);
   }
-  if (q) {  // rows go through LDS so that each row leaves as 128 contiguous bytes
+  if (q) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        codes[(n0 + j) * 33 + (k0 >> 2) + w] =
+        fcodes[(n0 + j) * kWS + (k0 >> 2) + w] =
             e4m3x4(f[j][4 * w], f[j][4 * w + 1], f[j][4 * w + 2], f[j][4 * w + 3]);
-    __syncthreads();
-    uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int idx = p * 256 + t;  // word idx % 32 of row idx / 32
-      const int n = idx >> 5, w = idx & 31;
-      *(uint32_t*)(qb + (int64_t)n * K + 4 * w) = codes[n * 33 + w];
-    }
+  }
+  __syncthreads();
+  if (qt) {
+    store_code_tile(tcodes, qt + (int64_t)e * K * N + (int64_t)(kb * 128) * N + nb * 128, N);
+    if (t == 0) st[((int64_t)e * nbk + kb) * nbn + nb] = sc;
+  }
+  if (q) {
+    store_code_tile(fcodes, q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128, K);
     if (t == 0) s[((int64_t)e * nbn + nb) * nbk + kb] = sc;
   }
 }
@@ -219,16 +233,20 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
 // MXFP8 weights W [E, N, K], encoded twice from one read: q [E, N, K] with
 // 1 x 32 blocks along K and scales s [E, N, K/32], and qt [E, K, N] (the
 // transpose) with 1 x 32 blocks along N and scales st [E, K, N/32]; either
-// pair may be null (not written).  One
-// work-group per 128 x 128 tile; thread t holds rows 4 (t % 32) .. +3 and
-// columns 16 (t / 32) .. +15 of it, so a row's 32-column block spans lanes
-// t and t ^ 32 and a column's 32-row block spans the 8 lanes t ^ 0..7.
+// pair may be null (not written).  One work-group per 128 x 128 tile; thread
+// t holds rows 4 (t % 32) .. +3 and columns 16 (t / 32) .. +15 of it, so a
+// row's 32-column block spans lanes t and t ^ 32 and a column's 32-row
+// block spans the 8 lanes t ^ 0..7.  Both code tiles and both scale tiles
+// are staged in LDS and leave as 16-byte rows (codes) and 32-bit words (a
+// row's or column's four scale bytes).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __restrict__ W, int N, int K,
                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                              uint8_t* __restrict__ qt,
                                                              uint8_t* __restrict__ st) {
-  __shared__ __attribute__((aligned(16))) uint32_t codes[128 * 33];  // [n][32 words], padded
+  __shared__ __attribute__((aligned(16))) uint32_t fcodes[128 * kWS];  // [n][32 words]
+  __shared__ __attribute__((aligned(16))) uint32_t tcodes[128 * kWS];  // [k][32 words]
+  __shared__ uint32_t fscale[128], tscale[128];                        // [n], [k]: 4 bytes each
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
   const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
@@ -248,30 +266,21 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
   const int nbk32 = K / 32, nbn32 = N / 32;
   // q, qt are kernel arguments: every branch on them is uniform
   if (q) {  // forward layout: row blocks along K
-    MxScale rs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float a = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[j][i]));
-      rs[j] = mx_scale(fmaxf(a, __shfl_xor(a, 32, kWave)));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+      const MxScale rs = mx_scale(fmaxf(a, __shfl_xor(a, 32, kWave)));
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        codes[(n0 + j) * 33 + (k0 >> 2) + w] =
-            e4m3x4(f[j][4 * w] * rs[j].inv, f[j][4 * w + 1] * rs[j].inv, f[j][4 * w + 2] * rs[j].inv,
-                   f[j][4 * w + 3] * rs[j].inv);
-    if (((t >> 5) & 1) == 0) {
-      uint8_t* sb = s + ((int64_t)e * N + nb * 128 + n0) * nbk32 + kb * 4 + (t >> 6);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[(int64_t)j * nbk32] = (uint8_t)rs[j].code;
+        fcodes[(n0 + j) * kWS + (k0 >> 2) + w] =
+            e4m3x4(f[j][4 * w] * rs.inv, f[j][4 * w + 1] * rs.inv, f[j][4 * w + 2] * rs.inv,
+                   f[j][4 * w + 3] * rs.inv);
+      if (((t >> 5) & 1) == 0) ((uint8_t*)fscale)[(n0 + j) * 4 + (t >> 6)] = (uint8_t)rs.code;
     }
   }
   if (qt) {  // transposed layout: column blocks along N, four rows' codes per word
-    uint8_t* qb = qt + (int64_t)e * K * N + (int64_t)(kb * 128 + k0) * N + nb * 128 + n0;
-    uint8_t* sb = st + ((int64_t)e * K + kb * 128 + k0) * nbn32 + nb * 4 + ((t & 31) >> 3);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float a = fmaxf(fmaxf(fabsf(f[0][i]), fabsf(f[1][i])), fmaxf(fabsf(f[2][i]), fabsf(f[3][i])));
@@ -279,20 +288,22 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
       a = fmaxf(a, __shfl_xor(a, 2, kWave));
       a = fmaxf(a, __shfl_xor(a, 4, kWave));
       const MxScale cs = mx_scale(a);
-      *(uint32_t*)(qb + (int64_t)i * N) =
+      tcodes[(k0 + i) * kWS + (n0 >> 2)] =
           e4m3x4(f[0][i] * cs.inv, f[1][i] * cs.inv, f[2][i] * cs.inv, f[3][i] * cs.inv);
-      if ((t & 7) == 0) sb[(int64_t)i * nbn32] = (uint8_t)cs.code;
+      if ((t & 7) == 0) ((uint8_t*)tscale)[(k0 + i) * 4 + ((t & 31) >> 3)] = (uint8_t)cs.code;
     }
   }
-  if (!q) return;
   __syncthreads();
-  // forward rows leave as 128 contiguous bytes each
-  uint8_t* qb = q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128;
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int idx = p * 256 + t;  // word idx % 32 of row idx / 32
-    const int n = idx >> 5, w = idx & 31;
-    *(uint32_t*)(qb + (int64_t)n * K + 4 * w) = codes[n * 33 + w];
+  if (q) {
+    store_code_tile(fcodes, q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128, K);
+    if (t < 128) *(uint32_t*)(s + ((int64_t)e * N + nb * 128 + t) * nbk32 + kb * 4) = fscale[t];
+  }
+  if (qt) {
+    store_code_tile(tcodes, qt + (int64_t)e * K * N + (int64_t)(kb * 128) * N + nb * 128, N);
+    if (t >= 128) {
+      const int k = t - 128;
+      *(uint32_t*)(st + ((int64_t)e * K + kb * 128 + k) * nbn32 + nb * 4) = tscale[k];
+    }
   }
 }
 

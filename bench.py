@@ -269,8 +269,11 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
                     continue
                 per.setdefault(site, {}).setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         cal = per.get("calibration copy")
-        if not cal:
+        if not cal or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
             raise SystemExit("no calibration copy kernel in the counter runs (bench.py --copy-calibration)")
+        # the 1 GiB copy is by far the largest dispatch outside the layer (the
+        # others are torch's small fills), so it is the maximum, not the mean
+        cal = {key: [max(v)] for key, v in cal.items()}
         f_fetch = COPY_BYTES / float(np.mean(cal["FETCH_SIZE"]))
         f_write = COPY_BYTES / float(np.mean(cal["WRITE_SIZE"]))
         lines += ["", "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, KiB per "

@@ -366,7 +366,7 @@ struct Rows8Args {
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
   const int32_t* offsets;
   const int32_t* tile_off;
-  const int4* tiles;  // row-tile descriptors {expert, first row, segment end, 0}
+  const int4* tiles;  // row-tile descriptors {expert, first row, segment end, expert's first tile}
   int E;
   // EPI_STORE: C [R, ldc] bf16; EPI_STORE_F32: Cf [R, ldc] fp32
   bf16_t* C;
@@ -491,9 +491,18 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
   if (L < 0) return;
-  const int nt = L % p.n_tiles;
-  const int4 desc = p.tiles[L / p.n_tiles];  // {expert, first row, segment end, 0}
-  const int e = desc.x, m0 = desc.y, seg1 = desc.z;
+  // An expert's (row tile, N tile) pairs are a contiguous range of L, taken
+  // N-tile-major (work-groups that start close together share a weight tile
+  // through L2); the descriptor of L's row-tile-major row tile lies in the
+  // same expert and gives the range.
+  const int T = L / p.n_tiles;
+  const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
+  const int e = d0.x, seg1 = d0.z, first = d0.w;
+  const int seg0 = d0.y - (T - first) * TBM;
+  const int nrt = (seg1 - seg0 + TBM - 1) / TBM;
+  const int j = L - first * p.n_tiles;
+  const int nt = j / nrt;
+  const int m0 = seg0 + (j - nt * nrt) * TBM;
   const int rows = seg1 - m0;
   if (rows <= TBM / 4) rows8_tile<EPI, SC, TBM / 4>(p, smem, nt, e, m0, seg1);
   else if (rows <= TBM / 2) rows8_tile<EPI, SC, TBM / 2>(p, smem, nt, e, m0, seg1);

@@ -322,9 +322,9 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
   int off = block_exclusive_scan(e < E ? tiles_e(c) : 0, sh_waves, &total);
   if (e < E) tile_off[e] = off;
   if (e == 0) tile_off[E] = total;
-  if (tiles && e < E) {  // one descriptor per row tile: expert, first row, end of segment
+  if (tiles && e < E) {  // one descriptor per row tile: expert, first row, end of segment, expert's first tile
     const int seg0 = offsets[e], seg1 = offsets[e + 1];
-    for (int t = 0; t < tiles_e(c); ++t) tiles[off + t] = make_int4(e, seg0 + t * kRowTile, seg1, 0);
+    for (int t = 0; t < tiles_e(c); ++t) tiles[off + t] = make_int4(e, seg0 + t * kRowTile, seg1, off);
   }
   __syncthreads();
   if (blk_off) {

@@ -556,7 +556,7 @@ moe_status quantize_common(bool mx, int kind, const void* src, int64_t n0, int64
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
   if (kind == MOE_QUANT_ROWS) {
-    HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s, mx), "quant_rows");
+    HIP_TRY(launch_quant_rows(c, "quant_rows", src, n1, n0, (int)n1, q, s, mx, false), "quant_rows");
     return MOE_OK;
   }
   const bool tr = kind == MOE_QUANT_WEIGHT_T;
@@ -566,7 +566,7 @@ moe_status quantize_common(bool mx, int kind, const void* src, int64_t n0, int64
   void* ts = tr ? s : nullptr;
   if (mx)
     HIP_TRY(launch_quant_weight_mx(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, fq, (uint8_t*)fs,
-                                   tq, (uint8_t*)ts), "quant_weight");
+                                   tq, (uint8_t*)ts, false), "quant_weight");
   else
     HIP_TRY(launch_quant_weight(c, "quant_weight", src, (int)n0, (int)n1, (int)n2, fq, (float*)fs, tq,
                                 (float*)ts), "quant_weight");
@@ -598,7 +598,7 @@ moe_status quantize_tokens_common(bool mx, const moe_shape* shape, const void* s
                           (int32_t*)at(workspace, L.order), blk_off, nullptr), "route_schedule");
   HIP_TRY(launch_quant_tok(c, "quant_tokens", src, C, gather ? routing->src_of : nullptr,
                            (int)shape->k, (int)C, routing->offsets, blk_off, (int)shape->E,
-                           (int)nblk_max(shape), q, s, mx), "quant_tokens");
+                           (int)nblk_max(shape), q, s, mx, false), "quant_tokens");
   return MOE_OK;
 }
 

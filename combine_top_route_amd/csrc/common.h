@@ -156,22 +156,26 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
 // along N, tokens 32-row blocks inside the 128-row runs).  Scale buffers are
 // typed void*: fp32 values or E8M0 bytes.
 //   rows:   src [rows, C] -> q [rows, C], s [rows, C/128] fp32 or [rows, C/32] bytes;
+//           run_major: the 32-bit words [C/128, rows] instead;
 //   weight: W [E, N, K] -> q [E, N, K] and/or qt [E, K, N]; blockwise scales
 //           s [E, N/128, K/128] / st [E, K/128, N/128]; MX s [E, N, K/32] /
-//           st [E, K, N/32];
+//           st [E, K, N/32], or with run_major the words [E, K/128, N] /
+//           [E, N/128, K];
 //   tok:    128-row runs of each expert's segment, written transposed q [C,
 //           128 nblk_max], one 32-bit scale word per run and column [C,
 //           nblk_max] (an fp32 scale, or four E8M0 codes).
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, void* s, bool mx);
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major);
 hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
                                int K, uint8_t* q, float* s, uint8_t* qt, float* st);
 hipError_t launch_quant_weight_mx(const LaunchCtx& c, const char* name, const void* W, int E, int N,
-                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st);
+                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st, bool run_major);
+// run_major: scale words [run][C] (as the weight-gradient GEMMs read them)
+// instead of [C][nblk_max]
 hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                             const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
                             const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
-                            bool mx);
+                            bool mx, bool run_major);
 
 // fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd from an fp32 G
 // [R,I], plus dH's e4m3 row codes dhq [R,2I] and scales dhs (I % 128 == 0).

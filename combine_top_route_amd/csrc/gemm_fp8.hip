@@ -118,7 +118,8 @@ __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 
 // Scales: waves 0-3 load the token rows' scale words (rows 64w .. 64w+63),
 // waves 4-7 the feature rows' (rows 64(w-4) ..); sp is the lane's source at
-// the current stage, advanced by one word per K step.
+// the current stage, advanced by sstep words per K step (1 for row-major
+// words, the row count for run-major ones).
 
 // Part I of a stage's loads: token-operand instruction I / 2 (even I) or
 // feature-operand instruction I / 2 (odd I); part 0 adds the scales.
@@ -207,8 +208,8 @@ __device__ __forceinline__ void substeps(const OT& ot, const OF& of, const uint3
 // One K step on the stage in `cur`; PRE: also load the next stage into `dst`
 // (a branch-free body, so the sub-step boundaries hold).
 template <int SC, int TMX, bool PRE, class OT, class OF>
-__device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, const lds_t* cur, lds_t* dst,
-                                      const FragOff& fo, f32x4_t (&acc)[TMX][TN]) {
+__device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, int sstep, const lds_t* cur,
+                                      lds_t* dst, const FragOff& fo, f32x4_t (&acc)[TMX][TN]) {
   const int wm = wave_m(), wn = wave_n();
   const int lane = threadIdx.x & 63;
   wait_vmcnt<0>();
@@ -252,12 +253,12 @@ __device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, const
   if constexpr (PRE) {
     ot.advance();
     of.advance();
-    sp += 1;
+    sp += sstep;
   }
 }
 
 template <int SC, int TMX, class OT, class OF>
-__device__ __forceinline__ void mainloop8(OT& ot, OF& of, const uint32_t* sp, int nkb, char* smem,
+__device__ __forceinline__ void mainloop8(OT& ot, OF& of, const uint32_t* sp, int sstep, int nkb, char* smem,
                                           f32x4_t (&acc)[TMX][TN]) {
 #pragma unroll
   for (int i = 0; i < TMX; ++i)
@@ -269,13 +270,13 @@ __device__ __forceinline__ void mainloop8(OT& ot, OF& of, const uint32_t* sp, in
   issue_stage(ot, of, sp, base);
   ot.advance();
   of.advance();
-  sp += 1;
+  sp += sstep;
   int slot = 0;
   for (int kb = 0; kb + 1 < nkb; ++kb) {
-    kstep<SC, TMX, true>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+    kstep<SC, TMX, true>(ot, of, sp, sstep, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
     slot ^= 1;
   }
-  kstep<SC, TMX, false>(ot, of, sp, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
+  kstep<SC, TMX, false>(ot, of, sp, sstep, base + slot * STB, base + (slot ^ 1) * STB, fo, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -346,21 +347,24 @@ enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_STORE_F32 = 2 };
 
 struct Rows8Args {
   // token side: row r reads A + arow(r) * lda, arow = a_src ? a_src[r] / a_div : r;
-  // its scale word at K step kb is As[arow * a_sld + kb]
+  // its scale word at K step kb is As[arow * a_srow + kb * a_skb] (row-major
+  // words for the gathered token rows; run-major, a_srow = 1, for the
+  // expert-sorted ones, whose words of one K step are then contiguous)
   const uint8_t* A;
   int64_t lda;
   const int32_t* a_src;
   int a_div;
   const uint32_t* As;
-  int64_t a_sld;
+  int64_t a_srow, a_skb;
   // feature side (expert e): row n reads B + e * b_estride + wrow(n) * ldb,
-  // scale word Bs[e * bs_estride + (wrow(n) >> b_rshift) * b_sld + kb]
-  // (b_rshift 7: one blockwise scale per 128 rows; 0: MX codes per row).
+  // scale word Bs[e * bs_estride + (wrow(n) >> b_rshift) * b_srow + kb * b_skb]
+  // (b_rshift 7: one blockwise scale per 128 rows, row-major; 0: MX codes
+  // per row, run-major).
   // gateup: 32-row blocks alternate gate rows (even) and up rows (odd).
   const uint8_t* B;
   int64_t b_estride, ldb;
   const uint32_t* Bs;
-  int64_t bs_estride, b_sld;
+  int64_t bs_estride, b_srow, b_skb;
   int b_rshift;
   int gateup;
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
@@ -412,10 +416,10 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
   ot.init([&](int row) { return p.A + arow(row) * p.lda; });
   of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
   const int srow = 64 * (wave_id() & 3) + lane;
-  const uint32_t* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_sld
-                                     : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_sld;
+  const uint32_t* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_srow
+                                     : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_srow;
   f32x4_t acc[TMX][TN];
-  mainloop8<SC, TMX>(ot, of, sp, p.K / KB, smem, acc);
+  mainloop8<SC, TMX>(ot, of, sp, (int)(wave_id() < 4 ? p.a_skb : p.b_skb), p.K / KB, smem, acc);
 
   // ------------------------------------------------------------- epilogues
   barrier_lds();
@@ -514,14 +518,15 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
 // A(m, k) B(n, k) s_A(m, blk) s_B(n, blk).  Both operands are transposed
 // token-blocked ([features][padded rows], see quant_fp8.hip): expert e owns
 // K bytes [128 blk_off[e], 128 blk_off[e+1]) of every row, and one scale
-// word per row and 128-row run.
+// word per row and 128-row run, stored run-major so that a K step's words
+// for 256 consecutive rows are one contiguous kilobyte.
 // ===========================================================================
 struct Wgrad8Args {
   const uint8_t* A;    // output-row side, [M][ldk]
-  const uint32_t* As;  // [M][nblk]
+  const uint32_t* As;  // [run][M]
   const uint8_t* B;    // output-column side, [N][ldk]
-  const uint32_t* Bs;  // [N][nblk]
-  int64_t ldk, nblk;
+  const uint32_t* Bs;  // [run][N]
+  int64_t ldk;
   int M, N, m_tiles, n_tiles, E;
   const int32_t* blk_off;
   const int32_t* order;
@@ -548,10 +553,9 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   ot.init([&](int row) { return p.A + (int64_t)mrow(row) * p.ldk + (int64_t)b0 * KB; });
   of.init([&](int row) { return p.B + (int64_t)nrow(row) * p.ldk + (int64_t)b0 * KB; });
   const int srow = 64 * (wave_id() & 3) + (threadIdx.x & 63);
-  const uint32_t* sp = wave_id() < 4 ? p.As + (int64_t)mrow(srow) * p.nblk + b0
-                                     : p.Bs + (int64_t)nrow(srow) * p.nblk + b0;
+  const uint32_t* sp = wave_id() < 4 ? p.As + (int64_t)b0 * p.M + mrow(srow) : p.Bs + (int64_t)b0 * p.N + nrow(srow);
   f32x4_t acc[TM][TN];
-  mainloop8<SC, TM>(ot, of, sp, nkb, smem, acc);
+  mainloop8<SC, TM>(ot, of, sp, wave_id() < 4 ? p.M : p.N, nkb, smem, acc);
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   constexpr int S = ep_stride<TBN>();
@@ -621,13 +625,14 @@ int fp8_dw_blocks(int) { return 1; }
 
 namespace {
 // Scale words per expert of a weight [N, K] encoded for a GEMM with K along
-// its rows: blockwise (N/128) x (K/128) fp32 scales, MX N x K/32 codes.
+// its rows: blockwise (N/128) x (K/128) fp32 scales (row-major), MX N x K/32
+// codes (words run-major, [K/128][N]).
 int64_t wscale_words(int64_t N, int64_t K, bool mx) { return (mx ? N : N / 128) * (K / 128); }
 
 hipError_t quant_weights(const LaunchCtx& c, const char* name, const void* W, int E, int N, int K,
                          bool mx, uint8_t* q, void* s, uint8_t* qt, void* st) {
-  if (mx)
-    return launch_quant_weight_mx(c, name, W, E, N, K, q, (uint8_t*)s, qt, (uint8_t*)st);
+  if (mx)  // run-major words: one K step's words of consecutive rows are contiguous
+    return launch_quant_weight_mx(c, name, W, E, N, K, q, (uint8_t*)s, qt, (uint8_t*)st, true);
   return launch_quant_weight(c, name, W, E, N, K, q, (float*)s, qt, (float*)st);
 }
 }  // namespace
@@ -636,7 +641,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
                          void* Yw) {
   const int64_t I = a.I, d = a.d;
   const bool mx = q.mx;
-  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx));
+  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx, false));
   // both layouts in one pass: the transposed codes serve the backward's dgrads
   HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, q.wguq, q.wgus,
                         q.sv.wgutq, q.sv.wguts));
@@ -646,9 +651,10 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
-    p.As = (const uint32_t*)q.xs; p.a_sld = d / 128;
+    p.As = (const uint32_t*)q.xs; p.a_srow = d / 128; p.a_skb = 1;
     p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
-    p.Bs = (const uint32_t*)q.wgus; p.bs_estride = wscale_words(2 * I, d, mx); p.b_sld = d / 128;
+    p.Bs = (const uint32_t*)q.wgus; p.bs_estride = wscale_words(2 * I, d, mx);
+    p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? 2 * I : 1;
     p.gateup = 1;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
@@ -656,13 +662,14 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R, mx));
   }
   if (!Yw) return hipSuccess;  // the gate/up half alone (recomputation)
-  HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws, mx));
+  HIP_RET(launch_quant_rows(c, "quant_aw", Aw, I, a.R, a.I, q.awq, q.aws, mx, true));
   Rows8Args p = {};  // down GEMM: Yw = Aw W_down[e]^T
   p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
   p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1;
-  p.As = (const uint32_t*)q.aws; p.a_sld = I / 128;
+  p.As = (const uint32_t*)q.aws; p.a_srow = 1; p.a_skb = a.R;
   p.B = q.wdq; p.b_estride = d * I; p.ldb = I;
-  p.Bs = (const uint32_t*)q.wds; p.bs_estride = wscale_words(d, I, mx); p.b_sld = I / 128;
+  p.Bs = (const uint32_t*)q.wds; p.bs_estride = wscale_words(d, I, mx);
+  p.b_srow = mx ? 1 : I / 128; p.b_skb = mx ? d : 1;
   p.gateup = 0;
   p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
   p.C = (bf16_t*)Yw; p.ldc = d;
@@ -680,15 +687,16 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, nullptr, nullptr, q.sv.wdtq,
                           q.sv.wdts));
   }
-  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx));
+  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx, false));
   {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
      // <G, a> and dH's row codes
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
-    p.As = (const uint32_t*)q.douts; p.a_sld = d / 128;
+    p.As = (const uint32_t*)q.douts; p.a_srow = d / 128; p.a_skb = 1;
     p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
-    p.Bs = (const uint32_t*)q.sv.wdts; p.bs_estride = wscale_words(I, d, mx); p.b_sld = d / 128;
+    p.Bs = (const uint32_t*)q.sv.wdts; p.bs_estride = wscale_words(I, d, mx);
+    p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? I : 1;
     p.gateup = 0;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Cf = q.G; p.ldc = I;
@@ -699,9 +707,10 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
-    p.As = (const uint32_t*)q.dhs; p.a_sld = 2 * I / 128;
+    p.As = (const uint32_t*)q.dhs; p.a_srow = 1; p.a_skb = a.R;  // run-major (swiglu_bwd_fp8)
     p.B = q.sv.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
-    p.Bs = (const uint32_t*)q.sv.wguts; p.bs_estride = wscale_words(d, 2 * I, mx); p.b_sld = 2 * I / 128;
+    p.Bs = (const uint32_t*)q.sv.wguts; p.bs_estride = wscale_words(d, 2 * I, mx);
+    p.b_srow = mx ? 1 : 2 * I / 128; p.b_skb = mx ? d : 1;
     p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
@@ -710,12 +719,12 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
   const int nb = q.nblk_max;
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
     HIP_RET(launch_quant_tok(c, "quant_dout_tok", dout, d, a.src_of, a.k, a.d, a.offsets, q.blk_off,
-                             a.E, nb, q.tqa, q.tsa, mx));
+                             a.E, nb, q.tqa, q.tsa, mx, true));
     HIP_RET(launch_quant_tok(c, "quant_aw_tok", Aw, I, nullptr, 1, a.I, a.offsets, q.blk_off, a.E, nb,
-                             q.tqb, q.tsb, mx));
+                             q.tqb, q.tsb, mx, true));
     Wgrad8Args p = {};
     p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
-    p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.ldk = (int64_t)nb * KB;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN); p.E = a.E;
     p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
@@ -723,12 +732,12 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
     HIP_RET(launch_quant_tok(c, "quant_dh_tok", dH, 2 * I, nullptr, 1, 2 * a.I, a.offsets, q.blk_off,
-                             a.E, nb, q.tqa, q.tsa, mx));
+                             a.E, nb, q.tqa, q.tsa, mx, true));
     HIP_RET(launch_quant_tok(c, "quant_x_tok", a.x, d, a.src_of, a.k, a.d, a.offsets, q.blk_off, a.E,
-                             nb, q.tqb, q.tsb, mx));
+                             nb, q.tqb, q.tsb, mx, true));
     Wgrad8Args p = {};
     p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
-    p.ldk = (int64_t)nb * KB; p.nblk = nb;
+    p.ldk = (int64_t)nb * KB;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.E = a.E; p.blk_off = q.blk_off; p.order = a.order;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;

@@ -105,13 +105,16 @@ __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
 
 // ---------------------------------------------------------------------------
 // Blocks along rows: src [rows, C] (leading dimension ld) -> q [rows, C] and
-// s [rows, C/128] fp32 (1 x 128 blocks) or, MX, s [rows, C/32] E8M0 bytes
-// (1 x 32 blocks).  A 16-lane group handles 128 columns, 8 values a lane.
+// one scale word per row and 128 columns: fp32 (1 x 128 blocks) or, MX, the
+// E8M0 bytes of four 1 x 32 blocks.  The word of (row r, column block cb)
+// sits at s[r * s_row + cb * s_blk]: row-major (C / 128, 1) or run-major
+// (1, rows), where one K step's words of consecutive rows are contiguous.
+// A 16-lane group handles 128 columns, 8 values a lane.
 // ---------------------------------------------------------------------------
 template <bool MX>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restrict__ src, int64_t ld,
                                                         int64_t rows, int C, uint8_t* __restrict__ q,
-                                                        void* __restrict__ s) {
+                                                        void* __restrict__ s, int64_t s_row, int64_t s_blk) {
   const int nbc = C / 128;
   const int64_t nb = rows * nbc;
   const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -135,14 +138,14 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
     const uint32_t word = gather4_codes(sc.code, lane & ~15, 4);
     if (!ok) return;
     *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8_mx(f, sc.inv);
-    if (sl == 0) ((uint32_t*)s)[r * nbc + cb] = word;
+    if (sl == 0) ((uint32_t*)s)[r * s_row + cb * s_blk] = word;
   } else {
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
     const float sc = block_scale(amax);
     if (!ok) return;
     *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8(f, sc);
-    if (sl == 0) ((float*)s)[r * nbc + cb] = sc;
+    if (sl == 0) ((float*)s)[r * s_row + cb * s_blk] = sc;
   }
 }
 
@@ -233,7 +236,10 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
 // MXFP8 weights W [E, N, K], encoded twice from one read: q [E, N, K] with
 // 1 x 32 blocks along K and scales s [E, N, K/32], and qt [E, K, N] (the
 // transpose) with 1 x 32 blocks along N and scales st [E, K, N/32]; either
-// pair may be null (not written).  One work-group per 128 x 128 tile; thread
+// pair may be null (not written).  run_major: the scale words (four codes
+// each) are stored [E, K/128, N] and [E, N/128, K] instead, so that the
+// words of one 128-wide K step for consecutive rows are contiguous.  One
+// work-group per 128 x 128 tile; thread
 // t holds rows 4 (t % 32) .. +3 and columns 16 (t / 32) .. +15 of it, so a
 // row's 32-column block spans lanes t and t ^ 32 and a column's 32-row
 // block spans the 8 lanes t ^ 0..7.  Both code tiles and both scale tiles
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
 __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __restrict__ W, int N, int K,
                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                              uint8_t* __restrict__ qt,
-                                                             uint8_t* __restrict__ st) {
+                                                             uint8_t* __restrict__ st, int run_major) {
   __shared__ __attribute__((aligned(16))) uint32_t fcodes[128 * kWS];  // [n][32 words]
   __shared__ __attribute__((aligned(16))) uint32_t tcodes[128 * kWS];  // [k][32 words]
   __shared__ uint32_t fscale[128], tscale[128];                        // [n], [k]: 4 bytes each
@@ -263,7 +269,6 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
       f[j][8 + i] = hi[i];
     }
   }
-  const int nbk32 = K / 32, nbn32 = N / 32;
   // q, qt are kernel arguments: every branch on them is uniform
   if (q) {  // forward layout: row blocks along K
 #pragma unroll
@@ -296,13 +301,19 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
   __syncthreads();
   if (q) {
     store_code_tile(fcodes, q + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128, K);
-    if (t < 128) *(uint32_t*)(s + ((int64_t)e * N + nb * 128 + t) * nbk32 + kb * 4) = fscale[t];
+    if (t < 128) {
+      const int64_t n = nb * 128 + t;
+      const int64_t w = run_major ? ((int64_t)e * (K / 128) + kb) * N + n : ((int64_t)e * N + n) * (K / 128) + kb;
+      ((uint32_t*)s)[w] = fscale[t];
+    }
   }
   if (qt) {
     store_code_tile(tcodes, qt + (int64_t)e * K * N + (int64_t)(kb * 128) * N + nb * 128, N);
     if (t >= 128) {
       const int k = t - 128;
-      *(uint32_t*)(st + ((int64_t)e * K + kb * 128 + k) * nbn32 + nb * 4) = tscale[k];
+      const int64_t kk = kb * 128 + k;
+      const int64_t w = run_major ? ((int64_t)e * (N / 128) + nb) * K + kk : ((int64_t)e * K + kk) * (N / 128) + nb;
+      ((uint32_t*)st)[w] = tscale[k];
     }
   }
 }
@@ -312,9 +323,11 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
 // (b - blk_off[e])-th run of 128 rows of expert e's segment; row i of the run
 // is src row srow(offsets[e] + 128 * (b - blk_off[e]) + i), with srow(r) =
 // src_of[r] / kdiv (token rows of x or dout) or r.  A work-group handles 64
-// columns: q[c][128 b + i] = code (0 past the segment) and word b of scale
-// row c (ldw words per row): the run's fp32 scale or, MX, the E8M0 codes of
-// its four 32-row blocks.
+// columns: q[c][128 b + i] = code (0 past the segment) and the scale word
+// of (column c, run b) at s[c * s_row + b * s_blk]: the run's fp32 scale or,
+// MX, the E8M0 codes of its four 32-row blocks.  Run-major words (s_row = 1,
+// s_blk = columns) put the words of one run for consecutive columns side by
+// side, as one K step of the weight-gradient GEMMs reads them.
 // ---------------------------------------------------------------------------
 constexpr int kTokCols = 64;
 
@@ -324,7 +337,7 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
                                                        const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ blk_off, int E,
                                                        uint8_t* __restrict__ q, int64_t ldq,
-                                                       uint32_t* __restrict__ s, int64_t ldw) {
+                                                       uint32_t* __restrict__ s, int64_t s_row, int64_t s_blk) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 136];  // [row][64 bf16], 136-byte rows
   const int b = blockIdx.x;
   if (b >= blk_off[E]) return;
@@ -399,15 +412,16 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
   *(u32x4_t*)(q + (int64_t)c * ldq + (int64_t)b * 128 + rg * 16) = q0;
   *(u32x4_t*)(q + (int64_t)(c + 1) * ldq + (int64_t)b * 128 + rg * 16) = q1;
   if (rg == 0) {
-    s[(int64_t)c * ldw + b] = w0;
-    s[(int64_t)(c + 1) * ldw + b] = w1;
+    s[(int64_t)c * s_row + (int64_t)b * s_blk] = w0;
+    s[(int64_t)(c + 1) * s_row + (int64_t)b * s_blk] = w1;
   }
 }
 
 // SwiGLU backward of one row per wave from G = dout_t W_down[e] (fp32), as
 // in the bf16 path, that also encodes the bf16-rounded dH in 1 x 128 blocks
 // (fp32 scales) or, MX, 1 x 32 blocks (a word of four E8M0 codes per 128
-// columns): the A operand of the gate/up dgrad.  Lane l handles the 8-column
+// columns), the words stored run-major ([I/64][R]): the A operand of the
+// gate/up dgrad.  Lane l handles the 8-column
 // chunks l, l + 64, ... of the gate and of the up half; a 16-lane group
 // covers 128 columns.  Requires I % 128 == 0.
 template <bool MX>
@@ -415,6 +429,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
     const f32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
     const int32_t* __restrict__ src_of, int R, int chunks, u32x4_t* __restrict__ dH,
     float* __restrict__ dw, uint8_t* __restrict__ dhq, uint32_t* __restrict__ dhs) {
+  // dH scale words run-major: word (row r, 128-column block j) at dhs[j * R + r]
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   const int lane = threadIdx.x & 63;
@@ -423,7 +438,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
   const u32x4_t* Hg = H + (int64_t)r * 2 * chunks;
   u32x4_t* Dr = dH + (int64_t)r * 2 * chunks;
   uint8_t* Qr = dhq + (int64_t)r * 2 * chunks * 8;
-  uint32_t* Sr = dhs + (int64_t)r * (2 * chunks / 16);
+  uint32_t* Sr = dhs + r;
   float part = 0.0f;
   for (int c0 = 0; c0 < chunks; c0 += kWave) {  // uniform trip count
     const int c = c0 + lane;
@@ -493,8 +508,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
       *(u32x2_t*)(Qr + c * 8) = qg;
       *(u32x2_t*)(Qr + (chunks + c) * 8) = qu;
       if ((lane & 15) == 0) {
-        Sr[c / 16] = wg;
-        Sr[(chunks + c) / 16] = wu;
+        Sr[(int64_t)(c / 16) * R] = wg;
+        Sr[(int64_t)((chunks + c) / 16) * R] = wu;
       }
     }
   }
@@ -520,15 +535,16 @@ hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void*
 }
 
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, void* s, bool mx) {
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major) {
   const int64_t nb = rows * (C / 128);
   if (nb == 0) return hipSuccess;
+  const int64_t s_row = run_major ? 1 : C / 128, s_blk = run_major ? rows : 1;
   if (mx)
     MOE_LAUNCH(c, name, quant_rows_kernel<true>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
-               (const bf16_t*)src, ld, rows, C, q, s);
+               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk);
   else
     MOE_LAUNCH(c, name, quant_rows_kernel<false>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
-               (const bf16_t*)src, ld, rows, C, q, s);
+               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk);
   return hipSuccess;
 }
 
@@ -540,24 +556,25 @@ hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void*
 }
 
 hipError_t launch_quant_weight_mx(const LaunchCtx& c, const char* name, const void* W, int E, int N,
-                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st) {
+                                  int K, uint8_t* q, uint8_t* s, uint8_t* qt, uint8_t* st, bool run_major) {
   MOE_LAUNCH(c, name, quant_weight_mx_kernel, dim3(K / 128, N / 128, E), dim3(256), 0,
-             (const bf16_t*)W, N, K, q, s, qt, st);
+             (const bf16_t*)W, N, K, q, s, qt, st, (int)run_major);
   return hipSuccess;
 }
 
 hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
                             const int32_t* src_of, int kdiv, int C, const int32_t* offsets,
                             const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
-                            bool mx) {
+                            bool mx, bool run_major) {
+  const int64_t s_row = run_major ? 1 : nblk_max, s_blk = run_major ? C : 1;
   if (mx)
     MOE_LAUNCH(c, name, quant_tok_kernel<true>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
                (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
-               (uint32_t*)s, (int64_t)nblk_max);
+               (uint32_t*)s, s_row, s_blk);
   else
     MOE_LAUNCH(c, name, quant_tok_kernel<false>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
                (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
-               (uint32_t*)s, (int64_t)nblk_max);
+               (uint32_t*)s, s_row, s_blk);
   return hipSuccess;
 }
 

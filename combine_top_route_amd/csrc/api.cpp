@@ -210,7 +210,7 @@ Layout layout(const moe_shape* s, int op) {
     // the recomputing backward reruns the gate/up GEMM with its x and weight codes
     if ((op == MOE_OP_FORWARD || op == MOE_OP_BACKWARD_RECOMPUTE) && fwd_fp8(s)) {
       L.xq = take(T * d);
-      L.xs = take(w * T * (d / 128));
+      L.xs = take(w * R * (d / 128));  // per expert-sorted row
       L.wguq = take(E * 2 * I * d);
       L.wgus = take(wscale_bytes(s, 2 * I, d));
       if (op == MOE_OP_FORWARD) {
@@ -223,7 +223,7 @@ Layout layout(const moe_shape* s, int op) {
     if (bwd) {
       const int64_t nb = nblk_max(s);
       L.doutq = take(T * d);
-      L.douts = take(w * T * (d / 128));
+      L.douts = take(w * R * (d / 128));  // per expert-sorted row
       L.dhq = take(R * 2 * I);
       L.dhs = take(w * R * (2 * I / 128));
       const int64_t ra = d > 2 * I ? d : 2 * I, rb = d > I ? d : I;

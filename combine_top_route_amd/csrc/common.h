@@ -156,7 +156,9 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
 // along N, tokens 32-row blocks inside the 128-row runs).  Scale buffers are
 // typed void*: fp32 values or E8M0 bytes.
 //   rows:   src [rows, C] -> q [rows, C], s [rows, C/128] fp32 or [rows, C/32] bytes;
-//           run_major: the 32-bit words [C/128, rows] instead;
+//           run_major: the 32-bit words [C/128, rows] instead; with row_of
+//           (and k), the words [C/128, rows k] of the expert-sorted rows
+//           row_of[r k + j] that gather token row r;
 //   weight: W [E, N, K] -> q [E, N, K] and/or qt [E, K, N]; blockwise scales
 //           s [E, N/128, K/128] / st [E, K/128, N/128]; MX s [E, N, K/32] /
 //           st [E, K, N/32], or with run_major the words [E, K/128, N] /
@@ -165,7 +167,8 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
 //           128 nblk_max], one 32-bit scale word per run and column [C,
 //           nblk_max] (an fp32 scale, or four E8M0 codes).
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major);
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major,
+                             const int32_t* row_of = nullptr, int k = 1);
 hipError_t launch_quant_weight(const LaunchCtx& c, const char* name, const void* W, int E, int N,
                                int K, uint8_t* q, float* s, uint8_t* qt, float* st);
 hipError_t launch_quant_weight_mx(const LaunchCtx& c, const char* name, const void* W, int E, int N,
@@ -178,7 +181,8 @@ hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* sr
                             bool mx, bool run_major);
 
 // fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd from an fp32 G
-// [R,I], plus dH's e4m3 row codes dhq [R,2I] and scales dhs (I % 128 == 0).
+// [R,I], plus dH's e4m3 row codes dhq [R,2I] and scale words dhs, run-major
+// [2I/128, R] (I % 128 == 0).
 hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
                                  const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
                                  float* dw, uint8_t* dhq, void* dhs, bool mx);
@@ -191,10 +195,10 @@ struct Fp8Saved {
 // Workspace of the fp8 forward: quantised x, weights and Aw with their scales.
 struct Fp8Fwd {
   bool mx;                     // MXFP8 rather than blockwise
-  uint8_t* xq; void* xs;       // [T,d]
+  uint8_t* xq; void* xs;       // codes [T,d]; scale words [d/128, R] per expert-sorted row
   uint8_t* wguq; void* wgus;   // [E,2I,d]
   uint8_t* wdq; void* wds;     // [E,d,I]
-  uint8_t* awq; void* aws;     // [R,I]
+  uint8_t* awq; void* aws;     // codes [R,I]; scale words run-major [I/128, R]
   Fp8Saved sv;                 // written when saving for the backward (else null)
 };
 // Workspace of the fp8 backward.  tqa/tsa and tqb/tsb hold the two
@@ -204,9 +208,9 @@ struct Fp8Bwd {
   bool mx;
   bool quant_weights;           // encode the transposed weights into sv first
                                 // (no fp8 forward ran)
-  uint8_t* doutq; void* douts;  // [T,d]
+  uint8_t* doutq; void* douts;  // codes [T,d]; scale words [d/128, R] per expert-sorted row
   Fp8Saved sv;                  // from the forward's saved buffer
-  uint8_t* dhq; void* dhs;      // [R,2I]
+  uint8_t* dhq; void* dhs;      // codes [R,2I]; scale words run-major [2I/128, R]
   uint8_t* tqa; void* tsa;
   uint8_t* tqb; void* tsb;
   float* G;                     // [R,I] the down dgrad's output

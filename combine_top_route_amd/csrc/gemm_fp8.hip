@@ -347,15 +347,17 @@ enum Epi { EPI_STORE = 0, EPI_GATEUP = 1, EPI_STORE_F32 = 2 };
 
 struct Rows8Args {
   // token side: row r reads A + arow(r) * lda, arow = a_src ? a_src[r] / a_div : r;
-  // its scale word at K step kb is As[arow * a_srow + kb * a_skb] (row-major
-  // words for the gathered token rows; run-major, a_srow = 1, for the
-  // expert-sorted ones, whose words of one K step are then contiguous)
+  // its scale word at K step kb is As[srow * a_srow + kb * a_skb], srow = r
+  // (a_s_sorted: words stored per expert-sorted row, also for gathered token
+  // rows) or arow; run-major words (a_srow = 1) put one K step's words of
+  // consecutive rows side by side
   const uint8_t* A;
   int64_t lda;
   const int32_t* a_src;
   int a_div;
   const uint32_t* As;
   int64_t a_srow, a_skb;
+  int a_s_sorted;
   // feature side (expert e): row n reads B + e * b_estride + wrow(n) * ldb,
   // scale word Bs[e * bs_estride + (wrow(n) >> b_rshift) * b_srow + kb * b_skb]
   // (b_rshift 7: one blockwise scale per 128 rows, row-major; 0: MX codes
@@ -394,10 +396,13 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
 
+  auto srt = [&](int row) -> int64_t {  // expert-sorted row of tile row `row`
+    const int r = m0 + row;
+    return r < seg1 ? r : seg0;  // rows past the segment: computed, never stored
+  };
   auto arow = [&](int row) -> int64_t {
-    int r = m0 + row;
-    if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
-    return p.a_src ? (int64_t)(p.a_src[r] / p.a_div) : (int64_t)r;
+    const int64_t r = srt(row);
+    return p.a_src ? (int64_t)(p.a_src[r] / p.a_div) : r;
   };
   auto wrow = [&](int n) -> int {
     if (p.gateup) {
@@ -416,7 +421,7 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
   ot.init([&](int row) { return p.A + arow(row) * p.lda; });
   of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
   const int srow = 64 * (wave_id() & 3) + lane;
-  const uint32_t* sp = wave_id() < 4 ? p.As + arow(srow) * p.a_srow
+  const uint32_t* sp = wave_id() < 4 ? p.As + (p.a_s_sorted ? srt(srow) : arow(srow)) * p.a_srow
                                      : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_srow;
   f32x4_t acc[TMX][TN];
   mainloop8<SC, TMX>(ot, of, sp, (int)(wave_id() < 4 ? p.a_skb : p.b_skb), p.K / KB, smem, acc);
@@ -641,7 +646,9 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
                          void* Yw) {
   const int64_t I = a.I, d = a.d;
   const bool mx = q.mx;
-  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx, false));
+  // x's scale words per expert-sorted row (run-major), so that the gathering
+  // gate/up GEMM reads one K step's words contiguously
+  HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx, true, a.row_of, a.k));
   // both layouts in one pass: the transposed codes serve the backward's dgrads
   HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, q.wguq, q.wgus,
                         q.sv.wgutq, q.sv.wguts));
@@ -651,7 +658,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
-    p.As = (const uint32_t*)q.xs; p.a_srow = d / 128; p.a_skb = 1;
+    p.As = (const uint32_t*)q.xs; p.a_srow = 1; p.a_skb = a.R; p.a_s_sorted = 1;
     p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
     p.Bs = (const uint32_t*)q.wgus; p.bs_estride = wscale_words(2 * I, d, mx);
     p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? 2 * I : 1;
@@ -687,13 +694,13 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, nullptr, nullptr, q.sv.wdtq,
                           q.sv.wdts));
   }
-  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx, false));
+  HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx, true, a.row_of, a.k));
   {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
      // <G, a> and dH's row codes
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
-    p.As = (const uint32_t*)q.douts; p.a_srow = d / 128; p.a_skb = 1;
+    p.As = (const uint32_t*)q.douts; p.a_srow = 1; p.a_skb = a.R; p.a_s_sorted = 1;
     p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
     p.Bs = (const uint32_t*)q.sv.wdts; p.bs_estride = wscale_words(I, d, mx);
     p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? I : 1;

@@ -109,12 +109,16 @@ __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
 // E8M0 bytes of four 1 x 32 blocks.  The word of (row r, column block cb)
 // sits at s[r * s_row + cb * s_blk]: row-major (C / 128, 1) or run-major
 // (1, rows), where one K step's words of consecutive rows are contiguous.
+// With row_of (token rows of x or dout), each token row's word goes to the
+// k expert-sorted rows row_of[r k + j] instead, run-major over those rows:
+// a GEMM that gathers the token rows then reads its words contiguously.
 // A 16-lane group handles 128 columns, 8 values a lane.
 // ---------------------------------------------------------------------------
 template <bool MX>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restrict__ src, int64_t ld,
                                                         int64_t rows, int C, uint8_t* __restrict__ q,
-                                                        void* __restrict__ s, int64_t s_row, int64_t s_blk) {
+                                                        void* __restrict__ s, int64_t s_row, int64_t s_blk,
+                                                        const int32_t* __restrict__ row_of, int k) {
   const int nbc = C / 128;
   const int64_t nb = rows * nbc;
   const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -138,14 +142,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
     const uint32_t word = gather4_codes(sc.code, lane & ~15, 4);
     if (!ok) return;
     *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8_mx(f, sc.inv);
-    if (sl == 0) ((uint32_t*)s)[r * s_row + cb * s_blk] = word;
+    if (sl == 0) {
+      if (row_of)
+        for (int j = 0; j < k; ++j) ((uint32_t*)s)[(int64_t)row_of[r * k + j] * s_row + cb * s_blk] = word;
+      else
+        ((uint32_t*)s)[r * s_row + cb * s_blk] = word;
+    }
   } else {
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
     const float sc = block_scale(amax);
     if (!ok) return;
     *(u32x2_t*)(q + r * C + cb * 128 + sl * 8) = quant8(f, sc);
-    if (sl == 0) ((float*)s)[r * s_row + cb * s_blk] = sc;
+    if (sl == 0) {
+      if (row_of)
+        for (int j = 0; j < k; ++j) ((float*)s)[(int64_t)row_of[r * k + j] * s_row + cb * s_blk] = sc;
+      else
+        ((float*)s)[r * s_row + cb * s_blk] = sc;
+    }
   }
 }
 
@@ -535,16 +549,18 @@ hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void*
 }
 
 hipError_t launch_quant_rows(const LaunchCtx& c, const char* name, const void* src, int64_t ld,
-                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major) {
+                             int64_t rows, int C, uint8_t* q, void* s, bool mx, bool run_major,
+                             const int32_t* row_of, int k) {
   const int64_t nb = rows * (C / 128);
   if (nb == 0) return hipSuccess;
-  const int64_t s_row = run_major ? 1 : C / 128, s_blk = run_major ? rows : 1;
+  const int64_t srows = row_of ? rows * k : rows;  // rows of the scale words
+  const int64_t s_row = (run_major || row_of) ? 1 : C / 128, s_blk = (run_major || row_of) ? srows : 1;
   if (mx)
     MOE_LAUNCH(c, name, quant_rows_kernel<true>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
-               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk);
+               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk, row_of, k);
   else
     MOE_LAUNCH(c, name, quant_rows_kernel<false>, dim3((unsigned)cdiv(nb, 16)), dim3(256), 0,
-               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk);
+               (const bf16_t*)src, ld, rows, C, q, s, s_row, s_blk, row_of, k);
   return hipSuccess;
 }
 

@@ -88,20 +88,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const LT* __restrict__ logits
   }
 }
 
-// One lane per token: the lane walks its token's logits once and keeps the
-// KMAX largest keys in a register list sorted descending (branch-free
-// bubble insert), so no cross-lane reduction is needed.  Used for k <= KMAX.
-template <typename LT, int KMAX>
+// LPT lanes per token (adjacent lanes): lane p of a token walks the p-th
+// contiguous E/LPT of its logits once and keeps the KMAX largest keys in a
+// register list sorted descending (branch-free bubble insert); the LPT
+// lists then merge pairwise through lane shuffles, each key of the partner's
+// list inserted into one's own.  Keys are (ordered logit bits, ~expert), all
+// distinct, so the merged list is the token's top KMAX whatever the split.
+// Used for k <= KMAX; LPT > 1 needs E % (LPT * 16 bytes of logits) == 0.
+template <typename LT, int KMAX, int LPT>
 __global__ __launch_bounds__(256) void topk_lane_kernel(const LT* __restrict__ logits, int T, int E,
                                                         int k, int32_t* __restrict__ ids,
                                                         float* __restrict__ w) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  const int t = gt / LPT, part = gt % LPT;
+  // the token's LPT lanes exit together (t is shared), so the shuffles below
+  // see only live partners
   if (t >= T) return;
   uint64_t top[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) top[j] = 0;
-  auto push = [&](float v, int e) {
-    uint64_t x = ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e);
+  auto insert = [&](uint64_t x) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const uint64_t hi = top[j] > x ? top[j] : x;
@@ -109,10 +115,12 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const LT* __restrict__ l
       top[j] = hi;
     }
   };
+  auto push = [&](float v, int e) { insert(((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e)); };
   const LT* row = logits + (int64_t)t * E;
   constexpr int VEC = 16 / sizeof(LT);
-  if (E % VEC == 0 && ((uintptr_t)logits & 15) == 0) {
-    for (int e0 = 0; e0 < E; e0 += VEC) {
+  if (LPT > 1 || (E % VEC == 0 && ((uintptr_t)logits & 15) == 0)) {
+    const int span = E / LPT, e_lo = part * span;
+    for (int e0 = e_lo; e0 < e_lo + span; e0 += VEC) {
       const uint4 v = *(const uint4*)(row + e0);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
       if constexpr (sizeof(LT) == 4) {
@@ -129,6 +137,19 @@ __global__ __launch_bounds__(256) void topk_lane_kernel(const LT* __restrict__ l
   } else {
     for (int e = 0; e < E; ++e) push(to_f32<LT>(row[e]), e);
   }
+#pragma unroll
+  for (int off = 1; off < LPT; off <<= 1) {
+    uint64_t other[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const uint32_t lo = __shfl_xor((uint32_t)top[j], off, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(top[j] >> 32), off, 64);
+      other[j] = ((uint64_t)hi << 32) | lo;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) insert(other[j]);
+  }
+  if (part != 0) return;
   // softmax over the k selected logits (float32), summed in slot order
   const float top0 = unordered_bits((uint32_t)(top[0] >> 32));
   float ex[KMAX];
@@ -349,22 +370,28 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 hipError_t launch_topk(const LaunchCtx& c, const void* logits, int logits_dtype, int T, int E,
                        int k, int32_t* ids, float* w) {
   if (k <= 16) {
-    dim3 grid((T + 255) / 256);
+    // four lanes per token when each takes whole 16-byte runs of logits (and
+    // the logits are 16-byte aligned), else one
+    const int run = logits_dtype == F32 ? 4 : 8;
+    const bool split = E % (4 * run) == 0 && ((uintptr_t)logits & 15) == 0;
+    const dim3 grid((unsigned)cdiv((int64_t)T * (split ? 4 : 1), 256));
+#define MOE_TOPK_LANE(LT, KM)                                                                     \
+  do {                                                                                            \
+    if (split)                                                                                    \
+      MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<LT, KM, 4>), grid, dim3(256), 0,              \
+                 (const LT*)logits, T, E, k, ids, w);                                             \
+    else                                                                                          \
+      MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<LT, KM, 1>), grid, dim3(256), 0,              \
+                 (const LT*)logits, T, E, k, ids, w);                                             \
+  } while (0)
     if (k <= 8) {
-      if (logits_dtype == F32)
-        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<float, 8>), grid, dim3(256), 0,
-                   (const float*)logits, T, E, k, ids, w);
-      else
-        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<bf16_t, 8>), grid, dim3(256), 0,
-                   (const bf16_t*)logits, T, E, k, ids, w);
+      if (logits_dtype == F32) MOE_TOPK_LANE(float, 8);
+      else MOE_TOPK_LANE(bf16_t, 8);
     } else {
-      if (logits_dtype == F32)
-        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<float, 16>), grid, dim3(256), 0,
-                   (const float*)logits, T, E, k, ids, w);
-      else
-        MOE_LAUNCH(c, "route_topk", (topk_lane_kernel<bf16_t, 16>), grid, dim3(256), 0,
-                   (const bf16_t*)logits, T, E, k, ids, w);
+      if (logits_dtype == F32) MOE_TOPK_LANE(float, 16);
+      else MOE_TOPK_LANE(bf16_t, 16);
     }
+#undef MOE_TOPK_LANE
   } else if (k <= kWave) {
     dim3 grid((T + 3) / 4);
     if (logits_dtype == F32)

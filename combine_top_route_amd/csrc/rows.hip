@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const uint4* __restri
 
 // d_topk_w[t,j] = sum over the partial dot products of row row_of[t*k+j]
 // (fixed order); dlogits[t,e] = w_e (dw_e - sum_j w_j dw_j) on the selected
-// experts, 0 elsewhere.  One wave per token.
+// experts, 0 elsewhere.  One wave per token; lane j holds slot j's gradient,
+// which the expert lanes pick up through shuffles.
 template <typename LT>
 __global__ __launch_bounds__(256) void topk_grad_kernel(const float* __restrict__ dwp, int nblk,
                                                         const int32_t* __restrict__ row_of,
@@ -191,6 +192,30 @@ __global__ __launch_bounds__(256) void topk_grad_kernel(const float* __restrict_
     for (int q = 0; q < lim; ++q) inner += __shfl(wj * dw, q, kWave);
   }
   if (!dlogits) return;
+  if (k <= kWave) {
+    // lane j < k: slot j's expert and gradient (dw of slot j recomputed in
+    // the same order as above, so bit-equal)
+    int idj = -1;
+    float gj = 0.0f;
+    if (lane < k) {
+      const int64_t r = row_of[(int64_t)t * k + lane];
+      float dw = 0.0f;
+      for (int b = 0; b < nblk; ++b) dw += dwp[r * nblk + b];
+      idj = ids[(int64_t)t * k + lane];
+      gj = w[(int64_t)t * k + lane] * (dw - inner);
+    }
+    for (int e0 = 0; e0 < E; e0 += kWave) {  // every lane runs every pass: the shuffles read live lanes
+      const int e = e0 + lane;
+      float g = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int id = __shfl(idj, j, kWave);
+        const float gv = __shfl(gj, j, kWave);
+        if (id == e) g = gv;
+      }
+      if (e < E) dlogits[(int64_t)t * E + e] = from_f32<LT>(g);
+    }
+    return;
+  }
   for (int e = lane; e < E; e += kWave) {
     float g = 0.0f;
     for (int j = 0; j < k; ++j) {

@@ -90,7 +90,8 @@ constexpr int64_t kMaxR = int64_t(1) << 27;
 moe_status check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
   if (s->T < 1 || s->T > kMaxT) return fail(MOE_ERR_INVALID_ARGUMENT, "T=%lld outside [1, 2^24]", (long long)s->T);
-  if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARGUMENT, "E=%lld outside [1, 1024]", (long long)s->E);
+  if (s->E < 1 || s->E > kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "E=%lld outside [1, %d]", (long long)s->E, kMaxExperts);
   if (s->k < 1 || s->k > s->E) return fail(MOE_ERR_INVALID_ARGUMENT, "k=%lld outside [1, E=%lld]", (long long)s->k, (long long)s->E);
   if (s->T * s->k > kMaxR) return fail(MOE_ERR_INVALID_ARGUMENT, "T*k=%lld above 2^27", (long long)(s->T * s->k));
   if (s->d < 8 || s->d > 16384 || s->d % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "d=%lld must be a multiple of 8 in [8, 16384]", (long long)s->d);

@@ -73,6 +73,7 @@ struct LaunchCtx {
 constexpr int kRowTile = 256;
 // Flat entries handled by one wave in the counting sort.
 constexpr int kSortChunk = 1024;
+constexpr int kMaxExperts = 1024;  // the C ABI rejects E outside [1, kMaxExperts]
 
 hipError_t launch_topk(const LaunchCtx& c, const void* logits, int logits_dtype, int T, int E,
                        int k, int32_t* ids, float* w);

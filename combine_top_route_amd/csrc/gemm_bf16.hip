@@ -480,9 +480,9 @@ __device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t
 #pragma unroll 4
   for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
     const int row = q / CPR, c8 = q % CPR;
-    if (row < row_lim && c8 * 8 < col_lim)
-      *(u32x4_t*)(C + (int64_t)row * ldc + c8 * 8) =
-          *(const __attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16);
+    if (row < row_lim && c8 * 8 < col_lim)  // streamed out: no L2 line kept for the output
+      __builtin_nontemporal_store(*(const __attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16),
+                                  (u32x4_t*)(C + (int64_t)row * ldc + c8 * 8));
   }
 }
 

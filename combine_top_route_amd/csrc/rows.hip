@@ -161,7 +161,11 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const uint4* __restri
     }
   }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) out[(int64_t)t * RV + c * 64 + lane] = pack<T>(acc[c]);
+  for (int c = 0; c < CPL; ++c) {  // streamed out: no L2 line kept for the output
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const uint4 v = pack<T>(acc[c]);
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, (u32x4v*)(out + (int64_t)t * RV + c * 64 + lane));
+  }
 }
 
 // d_topk_w[t,j] = sum over the partial dot products of row row_of[t*k+j]

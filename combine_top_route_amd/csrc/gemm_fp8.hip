@@ -315,19 +315,6 @@ __device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t
   }
 }
 
-template <int ROWS, int COLS, int S>
-__device__ __forceinline__ void global_to_lds(lds_t* t, const bf16_t* G, int64_t ld, int row_lim,
-                                              int col_lim) {
-  constexpr int CPR = COLS / 8;
-#pragma unroll 4
-  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
-    const int row = q / CPR, c8 = q % CPR;
-    if (row < row_lim && c8 * 8 < col_lim)
-      *(__attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16) =
-          *(const u32x4_t*)(G + (int64_t)row * ld + c8 * 8);
-  }
-}
-
 template <int ROWS>
 __device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
                                                  const int32_t* src_of, int m0, int seg1) {

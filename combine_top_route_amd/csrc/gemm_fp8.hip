@@ -148,25 +148,40 @@ __device__ __forceinline__ void issue_stage(const OT& ot, const OF& of, const ui
 // acc[i][j][r]: token wave_m*16*TMX + 16 i + lane % 16, feature
 // wave_n*64 + 16 j + 4 (lane / 16) + r.
 // ---------------------------------------------------------------------------
-template <int SC, int TMX, bool PRE, int I, class OT, class OF>
-__device__ __forceinline__ void substep(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
-                                        const i32x8_t (&f)[TN], const i32x8_t& t,
-                                        const lds_f32_t* SAw, float& sa, const f32x4_t (&sb)[TN],
-                                        f32x4_t (&acc)[TMX][TN]) {
-  if constexpr (PRE && I == 0) issue_stage(ot, of, sp, dst);  // the next stage leaves at the step's start
-  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+// acc += P s_token s_feature for one sub-tile row's TN partials.
+template <int SC>
+__device__ __forceinline__ void promote(f32x4_t (&acc)[TN], const f32x4_t (&P)[TN], float sa,
+                                        const f32x4_t (&sb)[TN]) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const f32x4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, zero, 0, 0, 0, 127, 0, 127);
     if constexpr (SC == SC_ROW) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r] * sb[j][r], sa, acc[I][j][r]);
+      for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[j][r] * sb[j][r], sa, acc[j][r]);
     } else {
       const float s = sa * sb[j][0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[I][j][r] = __builtin_fmaf(P[r], s, acc[I][j][r]);
+      for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[j][r], s, acc[j][r]);
     }
   }
+}
+
+// Blockwise sub-step I: its MFMAs write fresh partials P[I & 1]; the
+// partials of sub-step I - 1, whose MFMAs issued a whole sub-step earlier,
+// are promoted after them (so no FMA waits on the MFMA it follows), with
+// that sub-step's token scale sap.  The last sub-step's partials are
+// promoted by the caller.
+template <int SC, int TMX, bool PRE, int I, class OT, class OF>
+__device__ __forceinline__ void substep(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
+                                        const i32x8_t (&f)[TN], const i32x8_t& t,
+                                        const lds_f32_t* SAw, float& sa, float& sap, const f32x4_t (&sb)[TN],
+                                        f32x4_t (&P)[2][TN], f32x4_t (&acc)[TMX][TN]) {
+  if constexpr (PRE && I == 0) issue_stage(ot, of, sp, dst);  // the next stage leaves at the step's start
+  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    P[I & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[j], t, zero, 0, 0, 0, 127, 0, 127);
+  if constexpr (I > 0) promote<SC>(acc[I - 1], P[(I - 1) & 1], sap, sb);
+  sap = sa;
   if constexpr (I + 1 < TMX) sa = SAw[(I + 1) * 16];  // token scale of the next sub-step
   // keep the scheduler from hoisting later sub-steps' fragment reads and
   // MFMAs: each would hold its own registers live
@@ -194,14 +209,14 @@ __device__ __forceinline__ void substep_mx(const OT& ot, const OF& of, const uin
 template <int SC, int TMX, bool PRE, int I, class OT, class OF>
 __device__ __forceinline__ void substeps(const OT& ot, const OF& of, const uint32_t* sp, lds_t* dst,
                                          const i32x8_t (&f)[TN], i32x8_t (&t)[2], const lds_t* tb,
-                                         const FragOff& fo, const lds_f32_t* SAw, float& sa,
-                                         const f32x4_t (&sb)[TN], const lds_u8_t* SAl, int& st,
-                                         const int (&sf)[TN], f32x4_t (&acc)[TMX][TN]) {
+                                         const FragOff& fo, const lds_f32_t* SAw, float& sa, float& sap,
+                                         const f32x4_t (&sb)[TN], f32x4_t (&P)[2][TN], const lds_u8_t* SAl,
+                                         int& st, const int (&sf)[TN], f32x4_t (&acc)[TMX][TN]) {
   if constexpr (I < TMX) {
     if constexpr (SC == SC_MX) substep_mx<TMX, PRE, I>(ot, of, sp, dst, f, t[I & 1], SAl, st, sf, acc);
-    else substep<SC, TMX, PRE, I>(ot, of, sp, dst, f, t[I & 1], SAw, sa, sb, acc);
+    else substep<SC, TMX, PRE, I>(ot, of, sp, dst, f, t[I & 1], SAw, sa, sap, sb, P, acc);
     if constexpr (I + 2 < TMX) t[I & 1] = frag8(tb + (I + 2) * 16 * KB, fo);
-    substeps<SC, TMX, PRE, I + 1>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sb, SAl, st, sf, acc);
+    substeps<SC, TMX, PRE, I + 1>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sap, sb, P, SAl, st, sf, acc);
   }
 }
 
@@ -249,7 +264,10 @@ __device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, int s
   i32x8_t t[2];
   t[0] = frag8(tb, fo);
   if constexpr (TMX > 1) t[1] = frag8(tb + 16 * KB, fo);
-  substeps<SC, TMX, PRE, 0>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sb, SAl, st, sf, acc);
+  float sap = 0.0f;
+  f32x4_t P[2][TN];
+  substeps<SC, TMX, PRE, 0>(ot, of, sp, dst, f, t, tb, fo, SAw, sa, sap, sb, P, SAl, st, sf, acc);
+  if constexpr (SC != SC_MX) promote<SC>(acc[TMX - 1], P[(TMX - 1) & 1], sap, sb);
   if constexpr (PRE) {
     ot.advance();
     of.advance();

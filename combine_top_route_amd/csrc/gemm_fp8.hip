@@ -19,10 +19,14 @@
 // of 128 x 64, 128 bytes of K per stage for both operands (the same 64 KB
 // per stage as the bf16 engine, for twice the MFMA work).  Operands and one
 // 32-bit scale word per row and K step (an fp32 scale, or four E8M0 codes)
-// move global -> LDS with direct loads into a two-stage ring.  The MFMA's A
-// operand is the feature side and its B operand the token side, so a lane's
-// four results share one token row: the blockwise promotion costs one
-// multiply-add per result.
+// move global -> LDS with direct loads into a two-stage ring.  The scale
+// words are stored run-major wherever a step's words would otherwise sit one
+// per cache line (expert-sorted activations, x's and dout's words written
+// per expert-sorted row, MX weights, token runs), so a step's 256 words are
+// one contiguous kilobyte.  The MFMA's A operand is the feature side and its
+// B operand the token side, so a lane's four results share one token row:
+// the blockwise promotion costs one multiply-add per result, and it runs a
+// sub-step behind the MFMAs that produced the partial.
 #include "common.h"
 #include "tile.h"
 

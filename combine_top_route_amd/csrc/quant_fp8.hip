@@ -27,6 +27,10 @@
 // gradients; token operands take 32-row blocks inside the same 128-row
 // padded runs.  Four consecutive blocks' codes form one 32-bit word, so a
 // 128-wide K step of the GEMMs reads one word per row, as with fp32 scales.
+//
+// The kernels can write the scale words row-major (the layouts of the C
+// ABI's quantise entry points) or run-major, [K/128][rows], for the GEMMs:
+// there one K step's words for consecutive rows are contiguous.
 #include "common.h"
 
 namespace moe {

@@ -700,19 +700,11 @@ constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
 constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
-template <class K>
-hipError_t allow_smem(K kernel) {
-  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)kSmem);
-}
-
 template <int EPI, int BL, int TAG = 0>
 hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = allow_smem(rows_gemm_kernel<EPI, BL, TAG>);
+  {
+    hipError_t e = allow_smem_once<rows_gemm_kernel<EPI, BL, TAG>>(kSmem);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   // upper bound of the tile count (the kernel reads the exact one)
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
@@ -723,11 +715,9 @@ hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) 
 
 template <int TAG>
 hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p, int E) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = allow_smem(wgrad_kernel<TAG>);
+  {
+    hipError_t e = allow_smem_once<wgrad_kernel<TAG>>(kSmem);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const unsigned nblocks = (unsigned)(cdiv(E, 8) * 8 * p.m_tiles * p.n_tiles);
   MOE_LAUNCH(c, name, wgrad_kernel<TAG>, dim3(nblocks), dim3(NTHR), kSmem, p);

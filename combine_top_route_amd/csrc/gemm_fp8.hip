@@ -588,19 +588,11 @@ constexpr size_t kStoreF32Epi = (size_t)TBM * (128 * 4 + 16);
 constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreF32Epi), cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
-template <class K>
-hipError_t allow_smem(K kernel) {
-  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)kSmem);
-}
-
 template <int EPI, int TAG, int SC>
 hipError_t launch_rows8_sc(const LaunchCtx& c, const char* name, const Rows8Args& p, int R) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = allow_smem(rows8_kernel<EPI, TAG, SC>);
+  {
+    hipError_t e = allow_smem_once<rows8_kernel<EPI, TAG, SC>>(kSmem);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
@@ -617,11 +609,9 @@ hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R
 
 template <int TAG, int SC>
 hipError_t launch_wgrad8_sc(const LaunchCtx& c, const char* name, const Wgrad8Args& p) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = allow_smem(wgrad8_kernel<TAG, SC>);
+  {
+    hipError_t e = allow_smem_once<wgrad8_kernel<TAG, SC>>(kSmem);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const unsigned nblocks = (unsigned)(cdiv(p.E, 8) * 8 * p.m_tiles * p.n_tiles);
   MOE_LAUNCH(c, name, (wgrad8_kernel<TAG, SC>), dim3(nblocks), dim3(NTHR), kSmem, p);

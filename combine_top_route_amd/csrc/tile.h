@@ -3,6 +3,9 @@
 // swizzle and the mapping of work-groups to tiles.
 #pragma once
 
+#include <atomic>
+#include <cstdint>
+
 #include "common.h"
 
 namespace moe {
@@ -73,6 +76,22 @@ __device__ __forceinline__ int xcd_tile(int bid, int real) {
   if (idx >= per) return -1;
   const int L = (bid & 7) * per + idx;
   return L < real ? L : -1;
+}
+
+// Raises KERNEL's dynamic LDS limit to BYTES on the current device, once per
+// device and kernel (attributes are per device; the bit set makes repeat
+// launches free and is safe to race on: the call itself is idempotent).
+template <auto KERNEL>
+hipError_t allow_smem_once(size_t bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 }  // namespace tile

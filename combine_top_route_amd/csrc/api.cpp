@@ -55,19 +55,21 @@ hipEvent_t pooled_event() {
   return e;
 }
 
-void prof_before(const char* name, hipStream_t s) {
+// Start and stop events for one kernel dispatch (see MOE_LAUNCH); a kernel
+// whose events could not be created runs untimed and counts with 0 ms.
+void prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r;
   r.name = name;
   r.a = pooled_event();
-  r.b = pooled_event();
-  if (r.a) (void)hipEventRecord(r.a, s);
+  r.b = r.a ? pooled_event() : nullptr;
+  if (!r.b) {
+    if (r.a) g_pool.push_back(r.a);
+    r.a = nullptr;
+  }
+  *start = r.a;
+  *stop = r.b;
   g_recs.push_back(r);
-}
-
-void prof_after(const char*, hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_recs.empty() && g_recs.back().b) (void)hipEventRecord(g_recs.back().b, s);
 }
 
 LaunchCtx make_ctx(void* stream) {
@@ -78,8 +80,7 @@ LaunchCtx make_ctx(void* stream) {
     std::lock_guard<std::mutex> lk(g_mu);
     prof = g_prof;
   }
-  c.before = prof ? prof_before : nullptr;
-  c.after = prof ? prof_after : nullptr;
+  c.events = prof ? prof_events : nullptr;
   return c;
 }
 

@@ -1,6 +1,7 @@
 // Shared definitions of the HIP kernels (gfx950) and the host launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,23 +44,29 @@ __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rc
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ----------------------------------------------------------------------------
-// Host side: every launcher reports its kernel through `launched` so the API
-// layer can time it (profiling) and check the launch status.
+// Host side: every launcher enqueues through MOE_LAUNCH, which checks the
+// launch status and, while the API layer is timing kernels, hands the
+// dispatch a start and a stop event: the runtime stamps them with the
+// kernel's own start and end, with no extra packets on the stream.
 // ----------------------------------------------------------------------------
 struct LaunchCtx {
   hipStream_t stream;
-  // called before and after each kernel enqueue with the kernel's name
-  void (*before)(const char* name, hipStream_t s);
-  void (*after)(const char* name, hipStream_t s);
+  // while timing: the events to attach to the named kernel's dispatch (both
+  // null when none are available)
+  void (*events)(const char* name, hipEvent_t* start, hipEvent_t* stop);
 };
 
-#define MOE_LAUNCH(ctx, name, kernel, grid, block, shmem, ...)                     \
-  do {                                                                             \
-    if ((ctx).before) (ctx).before(name, (ctx).stream);                            \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, (ctx).stream, __VA_ARGS__);     \
-    hipError_t _e = hipGetLastError();                                             \
-    if ((ctx).after) (ctx).after(name, (ctx).stream);                              \
-    if (_e != hipSuccess) return _e;                                               \
+#define MOE_LAUNCH(ctx, name, kernel, grid, block, shmem, ...)                               \
+  do {                                                                                       \
+    hipEvent_t _start = nullptr, _stop = nullptr;                                            \
+    if ((ctx).events) (ctx).events(name, &_start, &_stop);                                   \
+    if (_start)                                                                              \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, (ctx).stream, _start, _stop, 0,     \
+                            __VA_ARGS__);                                                    \
+    else                                                                                     \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, (ctx).stream, __VA_ARGS__);             \
+    hipError_t _e = hipGetLastError();                                                       \
+    if (_e != hipSuccess) return _e;                                                         \
   } while (0)
 
 #define HIP_RET(...)                        \

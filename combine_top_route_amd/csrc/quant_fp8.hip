@@ -32,6 +32,7 @@
 // ABI's quantise entry points) or run-major, [K/128][rows], for the GEMMs:
 // there one K step's words for consecutive rows are contiguous.
 #include "common.h"
+#include "tile.h"
 
 namespace moe {
 namespace {
@@ -182,6 +183,42 @@ __device__ __forceinline__ void store_code_tile(const uint32_t* tile, uint8_t* d
   }
 }
 
+// The 128 x 128 bf16 block at Wb (row stride K elements) as floats: thread
+// t gets rows 4 (t % 32) .. +3, columns 16 (t / 32) .. +15.  The block goes
+// through LDS (stage: 32 KB) on direct loads that read whole 256-byte rows,
+// 16-byte chunk c of row r landing at chunk c ^ ((r / 4) % 16) of its LDS
+// row, so that the 32 rows one half-wave reads at a column are spread over
+// the banks.  Read straight from memory, each load instruction took 16 bytes
+// from each of 32 rows.  Ends with a barrier: stage may be reused at once.
+__device__ __forceinline__ void load_block_staged(const bf16_t* Wb, int K, tile::lds_t* stage,
+                                                  float (&f)[4][16]) {
+  const int t = threadIdx.x, w = tile::wave_id(), l = t & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = w * 8 + i;  // 1 KB of LDS: rows 4q .. 4q+3
+    const int row = 4 * q + (l >> 4);
+    const int c = (l & 15) ^ ((row >> 2) & 15);
+    tile::dma16(Wb + (int64_t)row * K + c * 8, stage + q * 1024);
+  }
+  tile::wait_vmcnt<0>();
+  __syncthreads();
+  const int n0 = 4 * (t & 31), c0 = 2 * (t >> 5);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = n0 + j, sw = (row >> 2) & 15;
+    const tile::lds_t* r = stage + row * 256;
+    float lo[8], hi[8];
+    unpack8(*(const __attribute__((address_space(3))) u32x4_t*)(r + ((c0 ^ sw) << 4)), lo);
+    unpack8(*(const __attribute__((address_space(3))) u32x4_t*)(r + (((c0 + 1) ^ sw) << 4)), hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[j][i] = lo[i];
+      f[j][8 + i] = hi[i];
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // 128 x 128 weight blocks of W [E, N, K], written as q [E, N, K] with s [E,
 // N/128, K/128] and/or transposed as qt [E, K, N] with st [E, K/128, N/128]
@@ -193,24 +230,16 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
                                                           uint8_t* __restrict__ qt,
                                                           float* __restrict__ st) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint32_t fcodes[128 * kWS];  // [n][32 words]
-  __shared__ __attribute__((aligned(16))) uint32_t tcodes[128 * kWS];  // [k][32 words]
+  // the staged bf16 block, then the code tiles fcodes [n][32 words] and
+  // tcodes [k][32 words]
+  __shared__ __attribute__((aligned(16))) uint32_t smem[2 * 128 * kWS];
+  uint32_t* const fcodes = smem;
+  uint32_t* const tcodes = smem + 128 * kWS;
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
   const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
-  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128 + n0) * K + kb * 128 + k0;
   float f[4][16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float lo[8], hi[8];
-    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K), lo);
-    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K + 8), hi);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f[j][i] = lo[i];
-      f[j][8 + i] = hi[i];
-    }
-  }
+  load_block_staged(W + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128, K, (tile::lds_t*)smem, f);
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -268,25 +297,17 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                              uint8_t* __restrict__ qt,
                                                              uint8_t* __restrict__ st, int run_major) {
-  __shared__ __attribute__((aligned(16))) uint32_t fcodes[128 * kWS];  // [n][32 words]
-  __shared__ __attribute__((aligned(16))) uint32_t tcodes[128 * kWS];  // [k][32 words]
-  __shared__ uint32_t fscale[128], tscale[128];                        // [n], [k]: 4 bytes each
+  // the staged bf16 block, then the code tiles fcodes [n][32 words] and
+  // tcodes [k][32 words]
+  __shared__ __attribute__((aligned(16))) uint32_t smem[2 * 128 * kWS];
+  __shared__ uint32_t fscale[128], tscale[128];  // [n], [k]: 4 bytes each
+  uint32_t* const fcodes = smem;
+  uint32_t* const tcodes = smem + 128 * kWS;
   const int kb = blockIdx.x, nb = blockIdx.y, e = blockIdx.z;
   const int t = threadIdx.x;
   const int n0 = 4 * (t & 31), k0 = 16 * (t >> 5);
-  const bf16_t* Wb = W + (int64_t)e * N * K + (int64_t)(nb * 128 + n0) * K + kb * 128 + k0;
   float f[4][16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float lo[8], hi[8];
-    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K), lo);
-    unpack8(*(const u32x4_t*)(Wb + (int64_t)j * K + 8), hi);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f[j][i] = lo[i];
-      f[j][8 + i] = hi[i];
-    }
-  }
+  load_block_staged(W + (int64_t)e * N * K + (int64_t)(nb * 128) * K + kb * 128, K, (tile::lds_t*)smem, f);
   // q, qt are kernel arguments: every branch on them is uniform
   if (q) {  // forward layout: row blocks along K
 #pragma unroll

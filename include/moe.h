@@ -254,9 +254,11 @@ const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
 
 /* Kernel timing for measurement: between moe_profile_begin and
- * moe_profile_end every kernel the library enqueues is bracketed by HIP
- * events on its stream.  moe_profile_end waits for those events and returns,
- * per kernel name, the number of launches and their summed duration. */
+ * moe_profile_end every kernel the library enqueues carries a start and a
+ * stop HIP event on its stream, stamped by the runtime with the kernel's
+ * own start and end (hipExtLaunchKernel), so timing adds no packets between
+ * kernels.  moe_profile_end waits for those events and returns, per kernel
+ * name, the number of launches and their summed duration. */
 typedef struct {
   char name[48];
   int64_t launches;

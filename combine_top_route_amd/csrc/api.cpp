@@ -187,7 +187,7 @@ Layout layout(const moe_shape* s, int op) {
   const size_t es = elem_size(s->dtype);
   const int64_t nchunks = cdiv(R, kSortChunk);
   L.tile_off = take(sizeof(int32_t) * (s->E + 1));
-  L.order = take(sizeof(int32_t) * s->E);
+  L.order = take(sizeof(int32_t) * (s->E + 8 * cdiv(s->E, 8)));  // order, then xorder
   L.blk_off = take(sizeof(int32_t) * (s->E + 1));
   L.tiles = take(sizeof(int4) * max_row_tiles(R, s->E));
   if (op == MOE_OP_ROUTE || op == MOE_OP_FORWARD) L.hist = take(sizeof(int32_t) * nchunks * s->E);
@@ -328,6 +328,7 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   a.tile_off = (const int32_t*)at(ws, L.tile_off);
   a.tiles = (const int4*)at(ws, L.tiles);
   a.order = (const int32_t*)at(ws, L.order);
+  a.xorder = a.order + s->E;
   a.tok_of = L.tok ? (const int32_t*)at(ws, L.tok) : nullptr;  // backward layouts only
   return a;
 }
@@ -399,7 +400,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   (void)hipGetLastError();
   TRY(run_route(shape, routing, workspace, L, c));
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order), nullptr, (int4*)at(workspace, L.tiles)),
+                          (int32_t*)at(workspace, L.order), nullptr, nullptr, (int4*)at(workspace, L.tiles)),
           "route_schedule");
   const LayerArgs a = layer_args(shape, routing, x, w_gate_up, w_down, workspace, L);
   const size_t es = elem_size(shape->dtype);
@@ -445,7 +446,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order),
+                          (int32_t*)at(workspace, L.order), (int32_t*)at(workspace, L.order) + shape->E,
                           bwd_fp8(shape) ? (int32_t*)at(workspace, L.blk_off) : nullptr,
                           (int4*)at(workspace, L.tiles)),
           "route_schedule");
@@ -597,7 +598,7 @@ moe_status quantize_tokens_common(bool mx, const moe_shape* shape, const void* s
   (void)hipGetLastError();
   int32_t* blk_off = (int32_t*)at(workspace, L.blk_off);
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
-                          (int32_t*)at(workspace, L.order), blk_off, nullptr), "route_schedule");
+                          (int32_t*)at(workspace, L.order), nullptr, blk_off, nullptr), "route_schedule");
   HIP_TRY(launch_quant_tok(c, "quant_tokens", src, C, gather ? routing->src_of : nullptr,
                            (int)shape->k, (int)C, routing->offsets, blk_off, (int)shape->E,
                            (int)nblk_max(shape), q, s, mx, false), "quant_tokens");

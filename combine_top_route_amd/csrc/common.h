@@ -95,8 +95,12 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
 constexpr int kTokBlock = 128;
 // tiles (optional) [tile_off[E]]: per row tile {expert, first row, end of the
 // expert's segment, 0}.
+// Per expert: row-tile offsets (tile_off, and tiles when non-null), order
+// (experts by row count, largest first), xorder when non-null (the weight
+// gradients' experts per XCD: slot s of XCD x at 8 s + x, -1 when empty; 8
+// ceil(E/8) entries) and blk_off when non-null (128-row token blocks).
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order, int32_t* blk_off, int4* tiles);
+                           int32_t* order, int32_t* xorder, int32_t* blk_off, int4* tiles);
 // Upper bound of the row-tile count.
 inline int64_t max_row_tiles(int64_t R, int64_t E) { return R / kRowTile + E; }
 
@@ -131,7 +135,8 @@ struct LayerArgs {
   const int32_t* row_of;
   const int32_t* tile_off;  // [E+1], kRowTile tiles
   const int4* tiles;        // [tile_off[E]] row-tile descriptors
-  const int32_t* order;     // [E]
+  const int32_t* order;     // [E] experts by row count, largest first
+  const int32_t* xorder;    // [8 ceil(E/8)] weight-gradient slot s of XCD x at 8 s + x (-1: empty)
   const int32_t* tok_of;    // [R] token of each sorted row (backward only)
 };
 

@@ -654,26 +654,26 @@ struct WgradArgs {
   const int32_t* tok;  // [R] token of each expert-sorted row
   int M, N, m_tiles, n_tiles, E;
   const int32_t* offsets;
-  const int32_t* order;
+  const int32_t* xorder;  // expert of each (slot, XCD): see the schedule
   bf16_t* C;  // dW[e] = C + e * c_estride, row-major [M, N]
   int64_t c_estride;
 };
 
-// Experts, largest first, are dealt round-robin to the 8 XCDs (work-groups
-// go to XCD bid % 8); all tiles of an expert run on one XCD, so its rows are
-// fetched into one L2.
+// All tiles of an expert run on one XCD (work-groups go to XCD bid % 8), so
+// its rows are fetched into one L2; the schedule deals the experts to the
+// XCDs so that their rows balance (xorder).
 // TAG 0: the down wgrad (A = dout gathered by token), 1: the gate/up wgrad
 // (B = x gathered by token).
 template <int TAG>
 __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int oi = (idx / per) * 8 + xcd;
-  if (oi >= p.E) return;
-  const int rem = idx % per;
+  const int slot = (blockIdx.x >> 3) / per;  // the work-group runs on XCD blockIdx.x % 8
+  if (slot >= (p.E + 7) / 8) return;
+  const int e = p.xorder[slot * 8 + (blockIdx.x & 7)];
+  if (e < 0) return;
+  const int rem = (blockIdx.x >> 3) % per;
   const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
-  const int e = p.order[oi];
   const int seg0 = p.offsets[e];
   const int len = p.offsets[e + 1] - seg0;
   OpKMg<TBM, TAG == 0> oa;
@@ -776,7 +776,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.A = (const bf16_t*)dout; p.lda = d; p.tok = a.tok_of;
     p.B = (const bf16_t*)Aw; p.ldb = I; p.E = a.E;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
-    p.offsets = a.offsets; p.order = a.order;
+    p.offsets = a.offsets; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
     err = launch_wgrad<0>(c, "gemm_down_wgrad", p, a.E);
     if (err != hipSuccess) return err;
@@ -796,7 +796,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.A = (const bf16_t*)dH; p.lda = 2 * I; p.tok = a.tok_of;
     p.B = (const bf16_t*)a.x; p.ldb = d; p.E = a.E;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
-    p.offsets = a.offsets; p.order = a.order;
+    p.offsets = a.offsets; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
     err = launch_wgrad<1>(c, "gemm_gateup_wgrad", p, a.E);
     if (err != hipSuccess) return err;

@@ -543,7 +543,7 @@ struct Wgrad8Args {
   int64_t ldk;
   int M, N, m_tiles, n_tiles, E;
   const int32_t* blk_off;
-  const int32_t* order;
+  const int32_t* xorder;  // expert of each (slot, XCD): see the schedule
   bf16_t* C;  // dW[e] = C + e * c_estride, row-major [M, N]
   int64_t c_estride;
 };
@@ -553,12 +553,12 @@ template <int TAG, int SC>
 __global__ __launch_bounds__(NTHR, 1) void wgrad8_kernel(Wgrad8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int per = p.m_tiles * p.n_tiles;
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int oi = (idx / per) * 8 + xcd;
-  if (oi >= p.E) return;
-  const int rem = idx % per;
+  const int slot = (blockIdx.x >> 3) / per;  // the work-group runs on XCD blockIdx.x % 8
+  if (slot >= (p.E + 7) / 8) return;
+  const int e = p.xorder[slot * 8 + (blockIdx.x & 7)];
+  if (e < 0) return;
+  const int rem = (blockIdx.x >> 3) % per;
   const int mt = rem / p.n_tiles, nt = rem % p.n_tiles;
-  const int e = p.order[oi];
   const int b0 = p.blk_off[e];
   const int nkb = p.blk_off[e + 1] - b0;
   auto mrow = [&](int row) { const int m = mt * TBM + row; return m < p.M ? m : 0; };
@@ -732,7 +732,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
     p.ldk = (int64_t)nb * KB;
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN); p.E = a.E;
-    p.blk_off = q.blk_off; p.order = a.order;
+    p.blk_off = q.blk_off; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
     HIP_RET(launch_wgrad8<0>(c, "gemm_down_wgrad", p, mx));
   }
@@ -745,7 +745,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.A = q.tqa; p.As = (const uint32_t*)q.tsa; p.B = q.tqb; p.Bs = (const uint32_t*)q.tsb;
     p.ldk = (int64_t)nb * KB;
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
-    p.E = a.E; p.blk_off = q.blk_off; p.order = a.order;
+    p.E = a.E; p.blk_off = q.blk_off; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
     HIP_RET(launch_wgrad8<1>(c, "gemm_gateup_wgrad", p, mx));
   }

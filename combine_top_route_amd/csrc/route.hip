@@ -7,6 +7,8 @@
 // routing tensors are top scores, selected expert indices and per-expert
 // token counts ("Mario/overlap moe kernel integration", commit on
 // GroupedExperts.forward).
+#include <climits>
+
 #include "common.h"
 
 namespace moe {
@@ -331,6 +333,7 @@ __device__ __forceinline__ int tiles_e(int rows) { return (rows + kRowTile - 1) 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
                                                         int32_t* __restrict__ tile_off,
                                                         int32_t* __restrict__ order,
+                                                        int32_t* __restrict__ xorder,
                                                         int32_t* __restrict__ blk_off,
                                                         int4* __restrict__ tiles) {
   __shared__ int sh_waves[16];
@@ -355,6 +358,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
     if (e == 0) blk_off[E] = total;
     __syncthreads();
   }
+  __shared__ int ord[1024];
   if (e < E) {
     int rank = 0;
     for (int o = 0; o < E; ++o) {
@@ -362,6 +366,51 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
       rank += (co > c) || (co == c && o < e);
     }
     order[rank] = e;
+    ord[rank] = e;
+  }
+  __syncthreads();
+  // Experts to XCDs for the weight gradients, where all tiles of an expert
+  // run on one XCD: largest first, each to the least loaded XCD that has
+  // fewer than ceil(E/8) experts (ties: lowest XCD).  An expert's cost is
+  // its rows plus a fixed 192 for its tiles' prologue and epilogue.  Dealt
+  // round-robin instead, a Zipf-skewed routing left the busiest XCD 26%
+  // above the mean; this way it stays within about 2%.  Slot s of XCD x
+  // lands at xorder[8 s + x] (-1: empty), as work-group 8 s + x runs on XCD
+  // x.  Lane x of the first wave keeps XCD x's load and count in registers;
+  // the experts go one at a time, to the lane that wins an argmin over the
+  // eight lanes taken with DPP moves (the pass is serial, so each step
+  // avoids the LDS round trip of a shuffle).
+  if (xorder) {  // a kernel argument: uniform
+    __shared__ int cost[1024];
+    if (e < E) cost[e] = cnt[ord[e]] + 192;  // loads stay below R + 192 E < 2^28
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      const int cap = (E + 7) / 8;
+      int load = 0, n = 0;
+      for (int c0 = 0; c0 < E; c0 += kWave) {
+        // 64 experts' costs and ids in registers, taken lane by lane below
+        const int cr = c0 + lane < E ? cost[c0 + lane] : 0;
+        const int er = c0 + lane < E ? ord[c0 + lane] : 0;
+        const int nn = E - c0 < kWave ? E - c0 : kWave;
+        for (int j = 0; j < nn; ++j) {
+          const int ci = __builtin_amdgcn_readlane(cr, j), ex = __builtin_amdgcn_readlane(er, j);
+          // (load, lane) packed so that one integer min is the argmin
+          // (loads stay below 2^28)
+          int m = lane < 8 && n < cap ? load << 3 | lane : INT_MAX;
+          m = min(m, __builtin_amdgcn_mov_dpp(m, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+          m = min(m, __builtin_amdgcn_mov_dpp(m, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+          m = min(m, __builtin_amdgcn_mov_dpp(m, 0x141, 0xF, 0xF, false));  // the other half of the eight
+          if (lane < 8 && lane == (m & 7)) {
+            xorder[n * 8 + lane] = ex;
+            load += ci;
+            ++n;
+          }
+        }
+      }
+      if (lane < 8)
+        for (int slot = n; slot < cap; ++slot) xorder[slot * 8 + lane] = -1;
+    }
   }
 }
 
@@ -424,9 +473,9 @@ hipError_t launch_sort(const LaunchCtx& c, const int32_t* ids, int T, int E, int
 }
 
 hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, int32_t* tile_off,
-                           int32_t* order, int32_t* blk_off, int4* tiles) {
+                           int32_t* order, int32_t* xorder, int32_t* blk_off, int4* tiles) {
   MOE_LAUNCH(c, "route_schedule", schedule_kernel, dim3(1), dim3(1024), 0, offsets, E, tile_off,
-             order, blk_off, tiles);
+             order, xorder, blk_off, tiles);
   return hipSuccess;
 }
 

@@ -381,7 +381,7 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
     for (int i = 0; i < TMX; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[bc][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[bc][j], a[cur][i], acc[i][j], 0, 0, 0);
     // one fragment read (and direct load) after each MFMA, so the reads of
     // the next sub-step and the loads of the next stage issue while this
     // sub-step's MFMAs run, and nothing here waits for them
@@ -429,11 +429,13 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
   kstep<TMX, false, false>(oa, ob, kt, base, slot, acc);
 }
 
-// Row inside the wave tile of accumulator register r of MFMA tile i; the
-// column is (lane & 31) + 32 * j.
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
+// Accumulator layout.  The MFMAs take the B fragment as their first
+// operand, so tile (i, j) holds the transpose of the usual output: lane l
+// has row i * 32 + (l & 31) of the wave tile, and register r its column
+// j * 32 + 8 (r / 4) + 4 (l / 32) + r % 4.  Each group of four registers is
+// four consecutive columns of one row: one 8-byte bf16 write.
+__device__ __forceinline__ int acc_row(int i, int lane) { return i * 32 + (lane & 31); }
+__device__ __forceinline__ int acc_col(int j, int g, int lane) { return j * 32 + 8 * g + 4 * (lane >> 5); }
 
 // ---------------------------------------------------------------------------
 // Epilogue staging: accumulators -> bf16 tile in LDS (row stride S bytes) ->
@@ -442,32 +444,21 @@ __device__ __forceinline__ int acc_row(int i, int r, int lane) {
 template <int COLS>
 constexpr int ep_stride() { return COLS * 2 + 16; }
 
-// Swaps a value with the neighbouring lane (lane ^ 1) through DPP.
-__device__ __forceinline__ float swap_adjacent(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-
 // Writes the wave's MFMA tiles i in [0, NI), j in [0, NJ), value v(i, j, r),
-// at tile rows row0.. and columns col0.. .  Adjacent lanes hold adjacent
-// columns of the same rows, and registers r, r+1 (r even) adjacent rows: one
-// lane swap lets the even lane store the column pair of row r and the odd
-// lane that of row r+1, as 32-bit writes.
+// at tile rows row0.. and columns col0.., four columns (8 bytes) a write.
 template <int NI, int NJ, int S, class V>
-__device__ __forceinline__ void stage_pairs(lds_t* t, int row0, int col0, V v) {
+__device__ __forceinline__ void stage_quads(lds_t* t, int row0, int col0, V v) {
   const int lane = threadIdx.x & 63;
-  const bool odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float a0 = v(i, j, r), a1 = v(i, j, r + 1);
-        const float recv = swap_adjacent(odd ? a0 : a1);
-        const uint32_t packed = pack_bf16x2(odd ? recv : a0, odd ? a1 : recv);
-        const int row = row0 + acc_row(i, r, lane) + (lane & 1);
-        const int col = col0 + j * 32 + ((lane & 31) & ~1);
-        *(__attribute__((address_space(3))) uint32_t*)(t + row * S + col * 2) = packed;
+      for (int g = 0; g < 4; ++g) {
+        const u32x2_t w = {pack_bf16x2(v(i, j, 4 * g), v(i, j, 4 * g + 1)),
+                           pack_bf16x2(v(i, j, 4 * g + 2), v(i, j, 4 * g + 3))};
+        const int row = row0 + acc_row(i, lane), col = col0 + acc_col(j, g, lane);
+        *(__attribute__((address_space(3))) u32x2_t*)(t + row * S + col * 2) = w;
       }
 }
 
@@ -582,24 +573,25 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
   const int r0w = wm * (ROWS / WM);  // first tile row of this wave
   if constexpr (EPI == EPI_STORE) {
     constexpr int S = ep_stride<TBN>();
-    stage_pairs<TMX, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
+    stage_quads<TMX, TN, S>(lds, r0w, wn * (TBN / WN), [&](int i, int j, int r) { return acc[i][j][r]; });
     barrier_lds();
     lds_to_global<ROWS, TBN, S>(lds, p.C + (int64_t)m0 * p.ldc + nt * TBN, p.ldc, rows_valid,
                                 p.N - nt * TBN);
   } else if constexpr (EPI == EPI_GATEUP) {
-    // acc[i][0] = gate, acc[i][1] = up, for the tile's gate column
-    // wn * 32 + (lane & 31) (128 gate columns per tile)
+    // acc[i][0] = gate, acc[i][1] = up, register by register for the same
+    // gate column wn * 32 + acc_col(0, r / 4, lane) + r % 4 (128 gate columns
+    // per tile)
     constexpr int S = ep_stride<TBN / 2>();
     constexpr int TB = ROWS * S;  // bytes of one staged ROWS x 128 tile
     lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
     load_row_weights<ROWS>(wl, p.topk_w, p.src_of, m0, seg1);
     barrier_lds();
     const int c0w = wn * 32;
-    stage_pairs<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
+    stage_quads<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
       const float g = acc[i][0][r], u = acc[i][1][r];
-      return wl[r0w + acc_row(i, r, lane)] * (g * sigmoidf_(g) * u);
+      return wl[r0w + acc_row(i, lane)] * (g * sigmoidf_(g) * u);
     });
-    if (p.H) stage_pairs<TMX, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
+    if (p.H) stage_quads<TMX, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
     barrier_lds();
     const int gc0 = nt * (TBN / 2);
     lds_to_global<ROWS, TBN / 2, S>(lds, p.Aout + (int64_t)m0 * p.I + gc0, p.I, rows_valid, p.I - gc0);
@@ -607,7 +599,7 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
       bf16_t* H0 = p.H + (int64_t)m0 * 2 * p.I + gc0;
       lds_to_global<ROWS, TBN / 2, S>(lds + TB, H0, 2 * p.I, rows_valid, p.I - gc0);
       barrier_lds();
-      stage_pairs<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) { return acc[i][1][r]; });
+      stage_quads<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) { return acc[i][1][r]; });
       barrier_lds();
       lds_to_global<ROWS, TBN / 2, S>(lds, H0 + p.I, 2 * p.I, rows_valid, p.I - gc0);
     }
@@ -685,7 +677,7 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
   barrier_lds();
   lds_t* const lds = (lds_t*)smem;
   constexpr int S = ep_stride<TBN>();
-  stage_pairs<TM, TN, S>(lds, wave_m() * (TBM / WM), wave_n() * (TBN / WN),
+  stage_quads<TM, TN, S>(lds, wave_m() * (TBM / WM), wave_n() * (TBN / WN),
                          [&](int i, int j, int r) { return acc[i][j][r]; });
   barrier_lds();
   lds_to_global<TBM, TBN, S>(lds, p.C + (int64_t)e * p.c_estride + (int64_t)mt * TBM * p.N + nt * TBN,

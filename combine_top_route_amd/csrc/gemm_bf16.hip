@@ -112,15 +112,14 @@ struct OpMK {
     const int row = 8 * ((threadIdx.x >> 6) + NWAVE * i) + (lane >> 3);
     return ((lane & 7) ^ mk_swz(row)) << 3;
   }
+  // tile row of this lane's chunk in instruction i
+  __device__ static int lane_row(int i) { return 8 * ((threadIdx.x >> 6) + NWAVE * i) + ((threadIdx.x & 63) >> 3); }
+  // rowp_of(i, row): the address of tile row `row`, which instruction i loads
   template <class F>
   __device__ void init(F rowp_of, int K_) {
     K = K_;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = 8 * (w + NWAVE * i) + (lane >> 3);
-      ptr[i] = rowp_of(row) + koff(i);
-    }
+    for (int i = 0; i < NI; ++i) ptr[i] = rowp_of(i, lane_row(i)) + koff(i);
   }
   // number of leading K steps (of nk) that need no bounds checks
   __device__ int nfull(int nk) const { return K / BK < nk ? K / BK : nk; }
@@ -468,22 +467,21 @@ template <int ROWS, int COLS, int S>
 __device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t ldc, int row_lim,
                                               int col_lim) {
   constexpr int CPR = COLS / 8;  // 16-byte chunks per row
-#pragma unroll 4
-  for (int q = threadIdx.x; q < ROWS * CPR; q += NTHR) {
+  constexpr int NQ = ROWS * CPR / NTHR;
+  static_assert(ROWS * CPR % NTHR == 0, "whole chunks per thread");
+  // all of the thread's LDS reads first, so the stores leave back to back
+  u32x4_t v[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = threadIdx.x + i * NTHR;
+    v[i] = *(const __attribute__((address_space(3))) u32x4_t*)(t + (q / CPR) * S + (q % CPR) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = threadIdx.x + i * NTHR;
     const int row = q / CPR, c8 = q % CPR;
     if (row < row_lim && c8 * 8 < col_lim)  // streamed out: no L2 line kept for the output
-      __builtin_nontemporal_store(*(const __attribute__((address_space(3))) u32x4_t*)(t + row * S + c8 * 16),
-                                  (u32x4_t*)(C + (int64_t)row * ldc + c8 * 8));
-  }
-}
-
-// Weights of the tile's rows (topk_w of each row's flat entry; 0 past seg1).
-template <int ROWS>
-__device__ __forceinline__ void load_row_weights(lds_f32_t* wl, const float* topk_w,
-                                                 const int32_t* src_of, int m0, int seg1) {
-  for (int t = threadIdx.x; t < ROWS; t += NTHR) {
-    const int row = m0 + t;
-    wl[t] = row < seg1 ? topk_w[src_of[row]] : 0.0f;
+      __builtin_nontemporal_store(v[i], (u32x4_t*)(C + (int64_t)row * ldc + c8 * 8));
   }
 }
 
@@ -532,15 +530,32 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
   const int lane = threadIdx.x & 63;
   const int wm = wave_m(), wn = wave_n();
 
-  OpMK<ROWS> oa;
-  oa.init([&](int row) {
-    int r = m0 + row;
+  // The loads whose results the prologue needs leave together: the gate/up
+  // epilogue's row weights (flat entry first; the main loop hides the
+  // second, dependent load) and the gathered A rows.  Address math between
+  // loads made the compiler wait for each before issuing the next.
+  int wsrc = 0;
+  if constexpr (EPI == EPI_GATEUP) {
+    if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < seg1) wsrc = p.src_of[m0 + threadIdx.x] + 1;
+  }
+  constexpr int NIA = OpMK<ROWS>::NI;
+  int arow[NIA];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    int r = m0 + OpMK<ROWS>::lane_row(i);
     if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
-    const int64_t ar = p.a_src ? (int64_t)(p.a_src[r] / p.a_div) : (int64_t)r;
+    arow[i] = p.a_src ? p.a_src[r] : r;
+  }
+  float wrow = 0.0f;
+  if constexpr (EPI == EPI_GATEUP) {
+    if (wsrc) wrow = p.topk_w[wsrc - 1];
+  }
+  OpMK<ROWS> oa;
+  oa.init([&](int i, int) {
+    const int64_t ar = p.a_src ? (int64_t)(arow[i] / p.a_div) : (int64_t)arow[i];
     return p.A + ar * p.lda;
   }, p.K);
   const bf16_t* Be = p.B + (int64_t)e * p.b_estride;
-
   f32x16_t acc[TMX][TN];
   const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
@@ -549,7 +564,7 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
     mainloop<TMX>(oa, ob, nk, smem, acc);
   } else {
     OpMK<TBN> ob;
-    ob.init([&](int n) {
+    ob.init([&](int, int n) {
       int wrow;
       if constexpr (BL == B_MK_GATEUP) {
         const int blk = n >> 5;
@@ -584,7 +599,7 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
     constexpr int S = ep_stride<TBN / 2>();
     constexpr int TB = ROWS * S;  // bytes of one staged ROWS x 128 tile
     lds_f32_t* wl = (lds_f32_t*)(lds + 2 * TB);
-    load_row_weights<ROWS>(wl, p.topk_w, p.src_of, m0, seg1);
+    if (threadIdx.x < ROWS) wl[threadIdx.x] = wrow;
     barrier_lds();
     const int c0w = wn * 32;
     stage_quads<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {

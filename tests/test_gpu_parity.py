@@ -32,6 +32,8 @@ SMALL_CASES = {
     "bf16_k80": TINY.scaled(T=16, d=64, E=128, k=80, I=64, **BF),
     "bf16_k12": TINY.scaled(T=200, d=128, E=32, k=12, I=64, **BF),
     "bf16_k20": TINY.scaled(T=100, d=128, E=64, k=20, I=64, **BF),
+    # 12 experts: two weight-gradient slots per XCD, four of the 16 empty
+    "bf16_e12": TINY.scaled(T=300, d=128, E=12, k=3, I=64, **BF),
     "bf16_d4096": TINY.scaled(T=64, d=4096, E=8, k=2, I=256, **BF),
     "bf16_f32_logits": TINY.scaled(T=300, d=256, E=16, k=4, I=128, dtype="bf16", logits_dtype="f32"),
 }

@@ -101,6 +101,7 @@ __device__ __forceinline__ int km_swz(int krow) { return ((krow & 3) << 1) ^ ((k
 template <int ROWS>
 struct OpMK {
   static constexpr bool TR = false;  // fragments read with plain ds_read_b128
+  static constexpr bool GATHERED = false;
   static constexpr int NI = ROWS * BK * 2 / 1024 / NWAVE;
   static constexpr int BYTES = ROWS * BK * 2;
   const bf16_t* ptr[NI];  // address of this lane's chunk at the current K step
@@ -154,6 +155,7 @@ struct OpMK {
 template <int COLS>
 struct OpKM {
   static constexpr bool TR = true;          // fragments read with ds_read_b64_tr_b16
+  static constexpr bool GATHERED = false;
   static constexpr int RB = COLS * 2;       // bytes per k-row
   static constexpr int UPR = RB / 16;       // 16-byte units per k-row
   static constexpr int RPI = 1024 / RB;     // k-rows per instruction
@@ -223,6 +225,7 @@ struct OpKM {
 template <int COLS, bool GATHER>
 struct OpKMg {
   static constexpr bool TR = true;
+  static constexpr bool GATHERED = GATHER;  // stage addresses come from loaded row indices
   static constexpr int RB = COLS * 2;
   static constexpr int UPR = RB / 16;
   static constexpr int RPI = 1024 / RB;
@@ -418,8 +421,26 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
   // stages [0, nf) need no bounds checks
   const int nfa = oa.nfull(nk), nfb = ob.nfull(nk);
   const int nf = nfa < nfb ? nfa : nfb;
-  if (nf > 0) issue_stage<true>(oa, ob, 0, base);
-  else issue_stage<false>(oa, ob, 0, base);
+  if constexpr (OA::GATHERED || OB::GATHERED) {
+    // the first stage of a gathered operand needs its row indices: wait for
+    // them once, while nothing else is in flight (the compiler's own waits
+    // would also cover each direct load issued in between), then issue that
+    // operand first
+    wait_vmcnt<0>();
+    if constexpr (OB::GATHERED) {
+      if (nf > 0) ob.template issue<0, OB::NI, true>(0, base + OA::BYTES);
+      else ob.template issue<0, OB::NI, false>(0, base + OA::BYTES);
+    }
+    if (nf > 0) oa.template issue<0, OA::NI, true>(0, base);
+    else oa.template issue<0, OA::NI, false>(0, base);
+    if constexpr (!OB::GATHERED) {
+      if (nf > 0) ob.template issue<0, OB::NI, true>(0, base + OA::BYTES);
+      else ob.template issue<0, OB::NI, false>(0, base + OA::BYTES);
+    }
+  } else {
+    if (nf > 0) issue_stage<true>(oa, ob, 0, base);
+    else issue_stage<false>(oa, ob, 0, base);
+  }
   oa.advance();
   ob.advance();
   int slot = 0, kt = 0;

@@ -47,6 +47,22 @@ __device__ __forceinline__ float block_scale(float amax) {
   return amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
 }
 
+// v / s as the e4m3 encoding sees it, without a full division per value.
+// q = v * rs, with rs the rounded reciprocal of s, lies within 2.5 fp32
+// ulps of the rounded quotient: two roundings of relative size 2^-24, plus
+// the quotient's own half ulp.  e4m3 keeps three mantissa bits, so its
+// rounding decides on the 20 bits below them; unless those bits of q lie
+// within 8 ulps of the midpoint pattern 0x80000, q and the rounded quotient
+// are on the same side of every e4m3 midpoint, with no tie, and give the
+// same code.  Near a midpoint, and below e4m3's normal range (2^-6, where
+// its grid is fixed at 2^-9), the exact quotient is taken.
+__device__ __forceinline__ float quot_e4m3(float v, float s, float rs) {
+  const float q = v * rs;
+  const int d = (int)(__float_as_uint(q) & 0xFFFFFu) - 0x80000;
+  const bool safe = v == 0.0f || ((d > 8 || d < -8) && fabsf(q) >= 0x1p-6f);
+  return safe ? q : __fdiv_rn(v, s);
+}
+
 // e4m3 codes of four quotients packed little-endian.  v_cvt_pk_fp8_f32
 // rounds to nearest even; the operand is clamped to +-448 first, so values a
 // rounding of s pushed just past 448 saturate instead of overflowing.
@@ -103,8 +119,9 @@ __device__ __forceinline__ uint32_t gather4_codes(uint32_t code, int base, int s
 // Eight values divided by s, as eight e4m3 codes.
 __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
   u32x2_t q;
-  q[0] = e4m3x4(__fdiv_rn(f[0], s), __fdiv_rn(f[1], s), __fdiv_rn(f[2], s), __fdiv_rn(f[3], s));
-  q[1] = e4m3x4(__fdiv_rn(f[4], s), __fdiv_rn(f[5], s), __fdiv_rn(f[6], s), __fdiv_rn(f[7], s));
+  const float rs = __fdiv_rn(1.0f, s);
+  q[0] = e4m3x4(quot_e4m3(f[0], s, rs), quot_e4m3(f[1], s, rs), quot_e4m3(f[2], s, rs), quot_e4m3(f[3], s, rs));
+  q[1] = e4m3x4(quot_e4m3(f[4], s, rs), quot_e4m3(f[5], s, rs), quot_e4m3(f[6], s, rs), quot_e4m3(f[7], s, rs));
   return q;
 }
 
@@ -250,11 +267,12 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   const float sc = block_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  const float rsc = __fdiv_rn(1.0f, sc);
   const int nbn = N / 128, nbk = K / 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) f[j][i] = __fdiv_rn(f[j][i], sc);
+    for (int i = 0; i < 16; ++i) f[j][i] = quot_e4m3(f[j][i], sc, rsc);
   // q, qt are kernel arguments: every branch on them is uniform
   if (qt) {  // a transposed row gets four consecutive codes from each of 32 lanes
 #pragma unroll
@@ -438,12 +456,13 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
       a1 = fmaxf(a1, __shfl_xor(a1, off, kWave));
     }
     const float s0 = block_scale(a0), s1 = block_scale(a1);
+    const float r0 = __fdiv_rn(1.0f, s0), r1 = __fdiv_rn(1.0f, s1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      q0[w] = e4m3x4(__fdiv_rn(f0[4 * w], s0), __fdiv_rn(f0[4 * w + 1], s0), __fdiv_rn(f0[4 * w + 2], s0),
-                     __fdiv_rn(f0[4 * w + 3], s0));
-      q1[w] = e4m3x4(__fdiv_rn(f1[4 * w], s1), __fdiv_rn(f1[4 * w + 1], s1), __fdiv_rn(f1[4 * w + 2], s1),
-                     __fdiv_rn(f1[4 * w + 3], s1));
+      q0[w] = e4m3x4(quot_e4m3(f0[4 * w], s0, r0), quot_e4m3(f0[4 * w + 1], s0, r0),
+                     quot_e4m3(f0[4 * w + 2], s0, r0), quot_e4m3(f0[4 * w + 3], s0, r0));
+      q1[w] = e4m3x4(quot_e4m3(f1[4 * w], s1, r1), quot_e4m3(f1[4 * w + 1], s1, r1),
+                     quot_e4m3(f1[4 * w + 2], s1, r1), quot_e4m3(f1[4 * w + 3], s1, r1));
     }
     w0 = __float_as_uint(s0);
     w1 = __float_as_uint(s1);

@@ -32,6 +32,62 @@ from . import binding as B
 _NS = "ctr_moe"
 
 
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def _require(ok: bool, msg: str):
+    if not ok:
+        raise ValueError(msg)
+
+
+def _check_layer_args(x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, k: int,
+                      precision: str):
+    """Shapes, dtypes and contiguity of the layer's inputs, checked before
+    anything is launched: x [T,d], logits [T,E], w_gate_up [E,2I,d],
+    w_down [E,d,I], 1 <= k <= E."""
+    _require(x.dim() == 2, f"x must be [T, d], got {tuple(x.shape)}")
+    T, d = x.shape
+    _require(w_gate_up.dim() == 3 and w_gate_up.shape[2] == d and w_gate_up.shape[1] % 2 == 0,
+             f"w_gate_up must be [E, 2I, d={d}], got {tuple(w_gate_up.shape)}")
+    E, two_i, _ = w_gate_up.shape
+    _require(tuple(w_down.shape) == (E, d, two_i // 2),
+             f"w_down must be [E={E}, d={d}, I={two_i // 2}], got {tuple(w_down.shape)}")
+    _require(tuple(logits.shape) == (T, E), f"logits must be [T={T}, E={E}], got {tuple(logits.shape)}")
+    _require(1 <= k <= E, f"k={k} outside [1, E={E}]")
+    _require(precision in B._PREC, f"precision {precision!r} unknown")
+    _require(x.dtype in _FLOATS and w_gate_up.dtype == x.dtype and w_down.dtype == x.dtype,
+             f"x and both weights need one dtype of {_FLOATS}, got {x.dtype}, {w_gate_up.dtype}, "
+             f"{w_down.dtype}")
+    _require(logits.dtype in _FLOATS, f"logits dtype {logits.dtype} not in {_FLOATS}")
+    for name, t in (("x", x), ("logits", logits), ("w_gate_up", w_gate_up), ("w_down", w_down)):
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_devices(**tensors):
+    """Every tensor on the first one's GPU (checked last, after the shapes)."""
+    dev = next(iter(tensors.values())).device
+    for name, t in tensors.items():
+        _require(t.device.type == "cuda" and t.device == dev, f"{name} is on {t.device}; every tensor "
+                 f"must be on one GPU ({dev})")
+
+
+def _check_backward_args(dout: Tensor, x: Tensor, saved: Tensor, routing, k: int, precision: str):
+    """dout [T,d] in x's dtype, `saved` empty or of the forward's size, and the
+    routing tensors the forward returned, on x's device."""
+    T, d = x.shape
+    _require(tuple(dout.shape) == (T, d) and dout.dtype == x.dtype,
+             f"dout must be [T={T}, d={d}] {x.dtype}, got {tuple(dout.shape)} {dout.dtype}")
+    ids, w, counts, offsets, row_of, src_of = routing
+    E = counts.numel()
+    for name, t, shape, dt in (("topk_ids", ids, (T, k), torch.int32), ("topk_w", w, (T, k), torch.float32),
+                               ("counts", counts, (E,), torch.int32), ("offsets", offsets, (E + 1,), torch.int32),
+                               ("row_of", row_of, (T * k,), torch.int32), ("src_of", src_of, (T * k,), torch.int32),
+                               ("saved", saved, (saved.numel(),), torch.uint8)):
+        _require(tuple(t.shape) == shape and t.dtype == dt, f"{name} must be {shape} {dt}, got "
+                 f"{tuple(t.shape)} {t.dtype}")
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
 def _shape(x: Tensor, logits: Tensor, w_gate_up: Tensor, k: int, precision: str):
     T, d = x.shape
     E, two_i, _ = w_gate_up.shape
@@ -54,6 +110,8 @@ def moe_fwd(x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, k: int
             save: bool) -> tuple[Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor]:
     """Layer forward.  Returns (out [T,d], saved (uint8; empty unless save),
     topk_ids, topk_w, counts, offsets, row_of, src_of)."""
+    _check_layer_args(x, logits, w_gate_up, w_down, k, precision)
+    _check_devices(x=x, logits=logits, w_gate_up=w_gate_up, w_down=w_down)
     shape = _shape(x, logits, w_gate_up, k, precision)
     T, d = x.shape
     E = w_gate_up.shape[0]
@@ -88,11 +146,18 @@ def moe_bwd(dout: Tensor, x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: 
             src_of: Tensor, k: int, precision: str) -> tuple[Tensor, Tensor, Tensor, Tensor]:
     """Layer backward: (dx, dlogits, dw_gate_up, dw_down).  An empty `saved`
     selects recomputation."""
+    _check_layer_args(x, logits, w_gate_up, w_down, k, precision)
+    dout = dout.contiguous()
+    _check_backward_args(dout, x, saved, (topk_ids, topk_w, counts, offsets, row_of, src_of), k, precision)
     shape = _shape(x, logits, w_gate_up, k, precision)
+    _require(saved.numel() in (0, B.saved_size(shape)),
+             f"saved holds {saved.numel()} bytes, expected 0 or {B.saved_size(shape)}")
+    _check_devices(x=x, dout=dout, logits=logits, w_gate_up=w_gate_up, w_down=w_down, saved=saved,
+                   topk_ids=topk_ids, topk_w=topk_w, counts=counts, offsets=offsets, row_of=row_of,
+                   src_of=src_of)
     T, d = x.shape
     E, two_i, _ = w_gate_up.shape
     dev = x.device
-    dout = dout.contiguous()
     recompute = saved.numel() == 0
     dx = torch.empty_like(x)
     dlogits = torch.empty_like(logits)

@@ -48,6 +48,8 @@ class MoeKernelStat(ctypes.Structure):
 # exported entry points: (name, restype, argtypes)
 _P = ctypes.c_void_p
 _SIGS = [
+    ("moe_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(MoeShape), ctypes.c_int]),
+    ("moe_saved_bytes", ctypes.c_size_t, [ctypes.POINTER(MoeShape)]),
     ("moe_workspace_size", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     ("moe_saved_size", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(ctypes.c_size_t)]),
     ("moe_route", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeRouting), _P, ctypes.c_size_t, _P]),
@@ -109,15 +111,17 @@ def make_shape(T, d, E, k, I, dtype=torch.bfloat16, logits_dtype=None, precision
 
 
 def workspace_size(shape: MoeShape, op: int) -> int:
-    n = ctypes.c_size_t()
-    _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(shape), op, ctypes.byref(n)))
-    return n.value
+    n = lib().moe_workspace_bytes(ctypes.byref(shape), op)
+    if n == 0:
+        raise ValueError(f"moe_workspace_bytes: {lib().moe_last_error().decode()}")
+    return n
 
 
 def saved_size(shape: MoeShape) -> int:
-    n = ctypes.c_size_t()
-    _check("moe_saved_size", lib().moe_saved_size(ctypes.byref(shape), ctypes.byref(n)))
-    return n.value
+    n = lib().moe_saved_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise ValueError(f"moe_saved_bytes: {lib().moe_last_error().decode()}")
+    return n
 
 
 def _ptr(t):

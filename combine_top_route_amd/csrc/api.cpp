@@ -370,6 +370,16 @@ moe_status moe_saved_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
+size_t moe_workspace_bytes(const moe_shape* shape, int op) {
+  size_t n = 0;
+  return moe_workspace_size(shape, op, &n) == MOE_OK ? n : 0;
+}
+
+size_t moe_saved_bytes(const moe_shape* shape) {
+  size_t n = 0;
+  return moe_saved_size(shape, &n) == MOE_OK ? n : 0;
+}
+
 moe_status moe_route(const moe_shape* shape, moe_routing* routing, void* workspace,
                      size_t workspace_bytes, void* stream) {
   TRY(check_shape(shape));

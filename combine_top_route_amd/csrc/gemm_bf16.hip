@@ -47,44 +47,9 @@ constexpr int TM = TBM / WM / 32;      // MFMA tiles per wave along M (4)
 constexpr int TN = TBN / WN / 32;      // MFMA tiles per wave along N (2)
 static_assert(TBM == kRowTile, "tile table is built for 256-row tiles");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_t;  // byte pointer into LDS (32-bit)
-typedef __attribute__((address_space(3))) float lds_f32_t;
-typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
 // Source of the direct loads that fall outside an operand (K tail, columns
 // past N, rows past an expert's segment in the weight gradients).
 __device__ __attribute__((aligned(64))) uint8_t g_zero_page[64] = {0};
-
-__device__ __forceinline__ void dma16(const void* g, lds_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-
-// Index of this thread's wave, as a scalar (uniform) value.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier that does not drain outstanding global loads (a
-// __syncthreads fence would wait for the whole ring).  The empty asm keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// [row][k] layout: 64 bf16 = 128 bytes per row, 16-byte chunks XOR-swizzled.
-__device__ __forceinline__ int mk_swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int mk_off(int row, int kc) { return row * 128 + ((kc ^ mk_swz(row)) << 4); }
 
 // [k][cols] layout: 32-byte chunks XOR-swizzled by k-row so that the four
 // rows read together by a 16-lane group, and the two column halves of a

@@ -37,8 +37,8 @@
 namespace moe {
 namespace {
 
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+using tile::u32x2_t;
+using tile::u32x4_t;
 
 constexpr float kE4M3Max = 448.0f;
 
@@ -55,11 +55,13 @@ __device__ __forceinline__ float block_scale(float amax) {
 // within 8 ulps of the midpoint pattern 0x80000, q and the rounded quotient
 // are on the same side of every e4m3 midpoint, with no tie, and give the
 // same code.  Near a midpoint, and below e4m3's normal range (2^-6, where
-// its grid is fixed at 2^-9), the exact quotient is taken.
+// its grid is fixed at 2^-9), the exact quotient is taken; so it is for a
+// whole block whose scale lies below 2^-128 (amax under 448 * 2^-128),
+// where the reciprocal overflows to infinity.
 __device__ __forceinline__ float quot_e4m3(float v, float s, float rs) {
   const float q = v * rs;
   const int d = (int)(__float_as_uint(q) & 0xFFFFFu) - 0x80000;
-  const bool safe = v == 0.0f || ((d > 8 || d < -8) && fabsf(q) >= 0x1p-6f);
+  const bool safe = rs <= 0x1.fffffep+127f && (v == 0.0f || ((d > 8 || d < -8) && fabsf(q) >= 0x1p-6f));
   return safe ? q : __fdiv_rn(v, s);
 }
 

@@ -59,7 +59,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad extent, k > E, ...     */
   MOE_ERR_UNSUPPORTED = 2,      /* valid but not built (dtype, alignment)   */
-  MOE_ERR_WORKSPACE = 3,        /* workspace smaller than moe_workspace_size */
+  MOE_ERR_WORKSPACE = 3,        /* workspace smaller than moe_workspace_bytes */
   MOE_ERR_HIP = 4               /* a kernel launch failed                   */
 } moe_status;
 
@@ -127,26 +127,57 @@ typedef struct {
   int32_t* src_of;
 } moe_routing;
 
-/* Bytes of device workspace a call with this shape needs (op: moe_op). */
-moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
+/* Bytes of device workspace a call with this shape needs (op: moe_op);
+ * 0 when the shape or op is invalid (moe_last_error() says why).  The
+ * caller owns the workspace: the pages' layer owns persistent buffers
+ * ("Mario/overlap moe kernel integration", commit list: symmetric buffers
+ * that the layer allocates and destroys itself),
+ * whereas on one GPU nothing has to outlive a call, so here every call takes
+ * its scratch memory from the caller. */
+size_t moe_workspace_bytes(const moe_shape* shape, int op);
 
 /* Bytes of the `saved` buffer written by moe_forward and read by
- * moe_backward: H [T*k, 2I] (gate|up pre-activations) followed by
- * Aw [T*k, I] (SwiGLU output times the row's top-k weight), both in dtype,
- * in expert-sorted row order.  With an fp8 forward (MOE_PREC_FP8_BLOCK,
- * MOE_PREC_MXFP8) the buffer also holds the transposed e4m3 weight codes and
- * scales that the backward's data gradients use (both weights are quantised
- * once, in the forward). */
+ * moe_backward (0 for an invalid shape): H [T*k, 2I] (gate|up
+ * pre-activations) followed by Aw [T*k, I] (SwiGLU output times the row's
+ * top-k weight), both in dtype, in expert-sorted row order.  With an fp8
+ * forward (MOE_PREC_FP8_BLOCK, MOE_PREC_MXFP8) the buffer also holds the
+ * transposed e4m3 weight codes and scales that the backward's data
+ * gradients use (both weights are quantised once, in the forward).  The
+ * forward keeps these so that the backward, which repeats the layer's
+ * exchange for gradients ("Prime Mega MoE Trains Giant AI Models 55%
+ * Faster", section "Where MoE training loses time"), need not recompute
+ * them; moe_backward with saved == NULL recomputes instead. */
+size_t moe_saved_bytes(const moe_shape* shape);
+
+/* The same sizes with a status: MOE_OK and *bytes set, or the reason the
+ * shape or op is rejected. */
+moe_status moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
 
 /* Routing only: top-k (when logits != NULL), per-expert counts and offsets,
- * and the stable expert-order permutation. */
+ * and the stable expert-order permutation.  The router sends each token to
+ * a small subset of experts, and dispatch sorts the tokens into expert
+ * order ("Prime Mega MoE Trains Giant AI Models 55% Faster", section "Where
+ * MoE training loses time"); the routing tensors are the per-token top
+ * scores and selected expert indices, or the per-expert token counts
+ * ("Mario/overlap moe kernel integration", commit on
+ * GroupedExperts.forward(x, *routing)).  Logits in: the k largest per
+ * token, weights the softmax over them (see the math above); ids in
+ * (logits == NULL): topk_ids and topk_w are read as given, and only counts,
+ * offsets, row_of and src_of are written. */
 moe_status moe_route(const moe_shape* shape, moe_routing* routing,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Layer forward: routing as moe_route, then out [T,d] (dtype).
- * x [T,d], w_gate_up [E,2I,d], w_down [E,d,I] in dtype.  saved: NULL, or a
- * buffer of moe_saved_size bytes that moe_backward will read. */
+/* Layer forward: routing as moe_route, then out [T,d] (dtype): dispatch
+ * into expert order, both expert linear layers with SwiGLU, and the combine
+ * that returns each token's k expert outputs to its position, weighted by
+ * topk_w ("Prime Intellect Fused MoE Kernel: 3.11x MoE Training Speed",
+ * section "What a mixture-of-experts layer actually does"; "Prime Mega MoE
+ * Trains Giant AI Models 55% Faster", section "Where MoE training loses
+ * time").  x [T,d], w_gate_up [E,2I,d], w_down [E,d,I] in dtype.  saved:
+ * NULL, or a buffer of moe_saved_bytes bytes that moe_backward will read.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_FORWARD) bytes, 256-byte
+ * aligned; x, the weights, out and saved 16-byte aligned. */
 moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routing,
                        const void* w_gate_up, const void* w_down, void* out,
                        void* saved, void* workspace, size_t workspace_bytes,
@@ -166,7 +197,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
  * the weight encodings) from x and the routing into its workspace, with the
  * same kernels as moe_forward, so the results equal those from a saved
  * buffer bit for bit; the workspace must then hold
- * moe_workspace_size(shape, MOE_OP_BACKWARD_RECOMPUTE) bytes. */
+ * moe_workspace_bytes(shape, MOE_OP_BACKWARD_RECOMPUTE) bytes. */
 moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
                         const moe_routing* routing, const void* w_gate_up,
                         const void* w_down, const void* saved, void* dx,
@@ -174,12 +205,21 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
                         void* dlogits, void* workspace, size_t workspace_bytes,
                         void* stream);
 
-/* Dispatch alone: xp[r] = x[src_of[r] / k], xp [T*k, d] (dtype). */
+/* Dispatch alone ("token sorting": "Prime Mega MoE Trains Giant AI Models
+ * 55% Faster", section "Where MoE training loses time"): xp[r] =
+ * x[src_of[r] / k], xp [T*k, d] (dtype), rows in expert order; reads only
+ * routing->src_of (as moe_route wrote it).  x and xp 16-byte aligned. */
 moe_status moe_permute(const moe_shape* shape, const void* x,
                        const moe_routing* routing, void* xp, void* stream);
 
-/* Combine alone: out[t] = sum_j topk_w[t][j] * rows[row_of[t*k+j]],
- * summed in float32 in slot order; rows [T*k, d], out [T,d] (dtype). */
+/* Combine alone (outputs returned to their original positions: "Prime Mega
+ * MoE Trains Giant AI Models 55% Faster", section "Where MoE training loses
+ * time"; the weighted sum of a token's expert outputs: "Prime Intellect
+ * Fused MoE Kernel: 3.11x MoE Training Speed", section "What a
+ * mixture-of-experts layer actually does"): out[t] = sum_j topk_w[t][j] *
+ * rows[row_of[t*k+j]], summed in float32 in slot order; rows [T*k, d], out
+ * [T,d] (dtype); reads routing->row_of and topk_w.  rows and out 16-byte
+ * aligned. */
 moe_status moe_combine(const moe_shape* shape, const void* rows,
                        const moe_routing* routing, void* out, void* stream);
 

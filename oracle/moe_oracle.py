@@ -601,13 +601,26 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
     return res
 
 
+def encode_expert_weights(w_gate_up, w_down, e: int, recipe=FP8_BLOCK, fwd_recipe=None):
+    """Expert e's weights as the fp8 layer's GEMMs see them: (gate/up, down)
+    in the forward encoding of fwd_recipe (default recipe), then in the
+    data-gradient encoding of recipe."""
+    fr = recipe if fwd_recipe is None else fwd_recipe
+    fw = (fr["w_fwd"](w_gate_up[e]), fr["w_fwd"](w_down[e]))
+    bw = fw if recipe["w_bwd"] is fr["w_fwd"] else \
+        (recipe["w_bwd"](w_gate_up[e]), recipe["w_bwd"](w_down[e]))
+    return fw + bw
+
+
 def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
                                 tokens: np.ndarray, ids=None, w=None,
-                                recipe=FP8_BLOCK, fwd_recipe=None) -> dict:
+                                recipe=FP8_BLOCK, fwd_recipe=None, encoded=None) -> dict:
     """forward_fp8 (with fwd_recipe, default recipe) / backward_fp8 (with
     recipe) results (out, dx, d_topk_w, dlogits) for a subset of tokens.  Activation blocks lie within one row and weight
     blocks depend only on the weights, so each token's results follow from
-    its own rows; the same steps as the full functions, row by row."""
+    its own rows; the same steps as the full functions, row by row.
+    encoded: optional {expert: encode_expert_weights(...)} computed ahead
+    (for instance in parallel) with the same recipes."""
     tokens = np.asarray(tokens)
     E = w_gate_up.shape[0]
     I = w_gate_up.shape[1] // 2
@@ -619,14 +632,11 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
         ids_t = np.asarray(ids)[tokens].astype(np.int64)
         w_t = np.asarray(w, F64)[tokens]
     fr = recipe if fwd_recipe is None else fwd_recipe
-    qw = {}
+    qw = dict(encoded) if encoded is not None else {}
 
     def weights(e):  # (gate/up, down) forward and data-gradient forms
         if e not in qw:
-            fw = (fr["w_fwd"](w_gate_up[e]), fr["w_fwd"](w_down[e]))
-            bw = fw if recipe["w_bwd"] is fr["w_fwd"] else \
-                (recipe["w_bwd"](w_gate_up[e]), recipe["w_bwd"](w_down[e]))
-            qw[e] = fw + bw
+            qw[e] = encode_expert_weights(w_gate_up, w_down, e, recipe, fwd_recipe)
         return qw[e]
 
     n, d = tokens.size, w_down.shape[1]

@@ -75,9 +75,22 @@ def run_oracle(wl, inp, ids=None, w=None, backward=True):
 
 def bf16_test_matrix(shape, seed):
     """bf16 values spanning e4m3's normal and subnormal ranges after
-    scaling: per-row magnitudes from 1e-6 to 1e3, a zero block, exact ties."""
+    scaling: per-row magnitudes from 1e-6 to 1e3, a zero block, exact ties,
+    and blocks whose largest magnitude is about 1e-37, so that their
+    blockwise scale (amax / 448) lies below 2^-128 and has no finite float32
+    reciprocal: the 128 x 128 block of rows 0..127 and columns 256..383 of
+    the flattened matrix (a weight block, or 1 x 128 row blocks), with zeros
+    in it, and column 130 (every 128-token run of it)."""
     g = np.random.default_rng(seed)
     a = g.standard_normal(shape) * np.exp(g.uniform(np.log(1e-6), np.log(1e3), shape[:-1] + (1,)))
+    flat = a.reshape(-1, a.shape[-1])
+    if flat.shape[0] >= 128 and flat.shape[1] >= 384:
+        tiny = g.standard_normal((128, 128)) * 1e-37
+        tiny[::7, 3] = 0.0
+        flat[:128, 256:384] = tiny
+    if flat.shape[1] > 130:
+        flat[:, 130] = g.standard_normal(flat.shape[0]) * 1e-37
+        flat[::5, 130] = 0.0
     a = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
     flat = a.view(-1, a.shape[-1])
     flat[0, :128] = 0.0                         # an all-zero block

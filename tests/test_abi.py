@@ -23,12 +23,39 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
 
 
+# The calls of the boundary as the scope table names them (routing, forward,
+# backward, the sizing queries, the standalone dispatch and combine, status
+# strings), plus this library's status-returning sizes and timing hooks.
+BOUNDARY = ("moe_route", "moe_forward", "moe_backward", "moe_workspace_bytes", "moe_saved_bytes",
+            "moe_permute", "moe_combine", "moe_status_string")
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("moe_route", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
-              "moe_workspace_size", "moe_saved_size", "moe_status_string", "moe_last_error",
-              "moe_profile_begin", "moe_profile_end"):
+    for n in BOUNDARY + ("moe_workspace_size", "moe_saved_size", "moe_last_error", "moe_profile_begin",
+                         "moe_profile_end"):
         assert n in names
+
+
+def test_sizing_calls_match_their_status_forms():
+    """moe_workspace_bytes / moe_saved_bytes return the sizes the status
+    forms report, and 0 (with a message) for a rejected shape or op."""
+    lib = B.lib()
+    for kw in (dict(), dict(dtype=torch.bfloat16, d=256, I=256, precision="fp8_block"),
+               dict(dtype=torch.bfloat16, d=256, I=256, precision="mxfp8")):
+        sh = _shape(**kw)
+        for op in (B.OP_ROUTE, B.OP_FORWARD, B.OP_BACKWARD, B.OP_BACKWARD_RECOMPUTE):
+            st, n = _status(sh, op)
+            assert st == 0 and lib.moe_workspace_bytes(ctypes.byref(sh), op) == n > 0
+        m = ctypes.c_size_t()
+        assert lib.moe_saved_size(ctypes.byref(sh), ctypes.byref(m)) == 0
+        assert lib.moe_saved_bytes(ctypes.byref(sh)) == m.value > 0
+    bad = _shape(k=9)
+    assert lib.moe_workspace_bytes(ctypes.byref(bad), B.OP_FORWARD) == 0
+    assert b"k=9" in lib.moe_last_error()
+    assert lib.moe_saved_bytes(ctypes.byref(bad)) == 0
+    assert lib.moe_workspace_bytes(ctypes.byref(_shape()), 7) == 0
+    assert lib.moe_workspace_bytes(None, 0) == 0
 
 
 def test_library_exports_every_declared_symbol():

@@ -5,6 +5,8 @@ Quantisation is byte work and must match bit for bit: every e4m3 code and
 every scale byte.  Layer outputs and gradients match the oracle's emulation
 of the same quantisation within max|err|/max|ref| <= 6e-2.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -116,11 +118,12 @@ def test_mx_layer_parity_full_size_sampled():
     """Skewed-routing MXFP8 layer at 16,384 tokens, d=4096, I=1536 in the
     benchmark's launch configuration: routing bit-exact, out/dx/top-k-weight/
     logit gradients on sampled tokens, weight gradients of the smallest
-    non-empty expert and of a mid-sized one, zeros for empty experts.  The
-    oracle encodes each touched expert's weights four ways (about 5 s per
-    expert), so besides the first and last tokens the samples are tokens
-    that route only to those two tokens' experts and the 12 busiest ones:
-    about 22 experts, each with many row tiles."""
+    non-empty expert, a mid-sized one and the hottest one (about ten times
+    the mean load), zeros for empty experts.  The oracle encodes each touched
+    expert's weights four ways (a few seconds per expert), so the sampled
+    tokens are the first and last ones plus tokens routed only to the eight
+    busiest experts and 24 experts drawn at random from the non-empty ones:
+    about twenty experts whose loads span the whole range, hot to cold."""
     wl = S.WORKLOADS["mxfp8_skew"]
     inp = S.make_inputs(wl, seed=0)
     gpu = run_gpu(wl, inp)
@@ -131,18 +134,29 @@ def test_mx_layer_parity_full_size_sampled():
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
     x, dout = inp["x"].double().numpy(), inp["dout"].double().numpy()
     ids = rt["ids"]
-    allowed = set(np.argsort(-counts, kind="stable")[:12].tolist()) | set(ids[0].tolist()) | set(ids[-1].tolist())
+    g = np.random.default_rng(0)
+    busiest = np.argsort(-counts, kind="stable")[:8]
+    drawn = g.choice(np.nonzero(counts)[0], 24, replace=False)
+    allowed = set(busiest.tolist()) | set(drawn.tolist()) | set(ids[0].tolist()) | set(ids[-1].tolist())
     cand = [t for t in range(1, wl.T - 1) if set(ids[t].tolist()) <= allowed]
     assert len(cand) >= 10, len(cand)
-    toks = np.concatenate([[0, wl.T - 1], np.random.default_rng(0).choice(cand, 10, replace=False)])
-    s = O.forward_backward_tokens_fp8(x, lg, dout, Wgu, Wd, wl.k, toks, recipe=O.MXFP8)
+    toks = np.concatenate([[0, wl.T - 1], g.choice(cand, 10, replace=False)])
+    used = np.unique(ids[toks])
+    rank = np.argsort(np.argsort(-counts, kind="stable"), kind="stable")
+    print("experts sampled", used.size, "load ranks", sorted(rank[used].tolist()))
+    assert rank[used].max() >= 64          # the sample reaches the cold half of the experts
+    with ThreadPoolExecutor(max_workers=8) as ex:   # the encodings, expert by expert, in parallel
+        enc = dict(zip(used.tolist(), ex.map(
+            lambda e: O.encode_expert_weights(Wgu, Wd, e, recipe=O.MXFP8), used.tolist())))
+    s = O.forward_backward_tokens_fp8(x, lg, dout, Wgu, Wd, wl.k, toks, recipe=O.MXFP8, encoded=enc)
     for n in ("out", "dx", "d_topk_w", "dlogits"):
         e = rel_err(gpu[n][toks], s[n])
         print(n, e)
         assert e <= TOL["fp8"], (n, e)
     nz = np.nonzero(counts)[0]
     order = nz[np.argsort(counts[nz])]
-    for e in (order[0], order[len(order) // 2]):
+    assert counts[order[-1]] >= 8 * counts.mean()
+    for e in (order[0], order[len(order) // 2], order[-1]):
         dgu, dd = O.expert_weight_grads_fp8(x, dout, rt, Wgu, Wd, e, recipe=O.MXFP8)
         for n, got, ref in (("dW_gate_up", gpu["dW_gate_up"][e], dgu), ("dW_down", gpu["dW_down"][e], dd)):
             err = rel_err(got, ref)

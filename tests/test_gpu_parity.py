@@ -85,8 +85,8 @@ def test_layer_parity_full_size_sampled(name):
     """Qwen3-30B-A3B and Qwen3-235B-A22B layer shapes at 16,384 tokens in the
     benchmark's launch configuration: all routing artefacts bit-exact; out,
     dx, top-k-weight and logit gradients on sampled tokens; weight gradients
-    of expert 0 and of the busiest expert (q30b) or a median one (q235b,
-    whose busiest expert is too large for the float64 oracle in a test)."""
+    of expert 0, of the busiest expert (q235b's router bias gives it about
+    five times the mean load) and, for q235b, of a median one."""
     wl = S.WORKLOADS[name]
     print(f"case {name}: {wl}", flush=True)
     inp = S.make_inputs(wl, seed=0)
@@ -103,11 +103,16 @@ def test_layer_parity_full_size_sampled(name):
         e = rel_err(gpu[n][toks], s[n])
         assert e <= TOL["bf16"], (n, e)
     c = rt["counts"]
-    other = int(np.argmax(c)) if name == "q30b" else int(np.argsort(c)[len(c) // 2])
-    for e in (0, other):
+    experts = [0, int(np.argmax(c))]
+    if name == "q235b":
+        assert c.max() >= 4 * c.mean()
+        experts.append(int(np.argsort(c)[len(c) // 2]))
+    for e in experts:
         dgu, dd = O.expert_weight_grads(x, dout, rt, Wgu, Wd, e)
-        assert rel_err(gpu["dW_gate_up"][e], dgu) <= TOL["bf16"]
-        assert rel_err(gpu["dW_down"][e], dd) <= TOL["bf16"]
+        for n, got, ref in (("dW_gate_up", gpu["dW_gate_up"][e], dgu), ("dW_down", gpu["dW_down"][e], dd)):
+            err = rel_err(got, ref)
+            print(n, e, c[e], err)
+            assert err <= TOL["bf16"], (n, e, err)
 
 
 def test_deterministic_bitwise():
@@ -141,3 +146,42 @@ def test_permute_combine_identity(dtype):
     ref = inp["x"].double().numpy()
     ulp = 2.0 ** -23 if dtype == "f32" else 2.0 ** -8
     assert np.max(np.abs(to_np(out4) - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2 * ulp
+
+
+@pytest.mark.parametrize("ldt", ["f32", "bf16"])
+@pytest.mark.parametrize("E,k", [(16, 2), (128, 8), (12, 5), (40, 12), (64, 20), (128, 80)])
+def test_routing_signed_zeros_and_minus_inf(ldt, E, k):
+    """Logits with +0.0 / -0.0 ties at the selection boundary and -inf
+    entries, including rows with fewer than k finite logits (their -inf
+    experts are selected lowest index first, with weight exactly 0): ids,
+    counts, offsets and the permutation bit-exact against the oracle, on
+    every top-k kernel (k <= 8, <= 16 with and without the four-lane split,
+    <= 64, and above)."""
+    dev = torch.device("cuda", 0)
+    T = 301
+    g = np.random.default_rng(E * 1000 + k)
+    lg = np.round(g.standard_normal((T, E)))          # small integers: ties everywhere
+    lg[g.random((T, E)) < 0.3] = 0.0
+    neg = g.random((T, E)) < 0.5
+    lg[(lg == 0) & neg] = -0.0                        # signed zeros tie with +0.0
+    lg[g.random((T, E)) < 0.1] = -np.inf
+    for t in range(0, T, 5):                          # rows with 1..k finite logits
+        nfin = int(g.integers(1, k + 1))
+        row = np.full(E, -np.inf)
+        keep = g.choice(E, nfin, replace=False)
+        row[keep] = np.round(g.standard_normal(nfin))
+        lg[t] = row
+    lg[1] = 0.0
+    lg[1, ::2] = -0.0                                 # a row of zeros only
+    lg[:, 0][np.isinf(lg).all(axis=1)] = 0.0          # at least one finite logit per row
+    assert np.signbit(lg[lg == 0]).any() and np.isinf(lg).any()
+    logits = torch.from_numpy(lg.astype(np.float32)).to(S.torch_dtype(ldt))
+    assert np.array_equal(logits.double().numpy(), lg)
+    r = B.route(logits.to(dev), k)
+    torch.cuda.synchronize()
+    rt = O.route(lg, k, E)
+    check_routing({n: to_np(getattr(r, n)) for n in ("topk_ids", "topk_w", "counts", "offsets",
+                                                      "row_of", "src_of")}, {"rt": rt})
+    w = to_np(r.topk_w)
+    sel = np.take_along_axis(lg, rt["ids"], axis=1)
+    assert np.all(w[np.isinf(sel)] == 0.0) and np.all(w[~np.isinf(sel)] > 0.0)

@@ -53,6 +53,7 @@ _SIGS = [
     ("moe_workspace_size", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     ("moe_saved_size", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(ctypes.c_size_t)]),
     ("moe_route", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeRouting), _P, ctypes.c_size_t, _P]),
+    ("moe_route_noalloc", ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeRouting), _P]),
     ("moe_forward", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.POINTER(MoeRouting), _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]),
     ("moe_backward", ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, ctypes.POINTER(MoeRouting), _P, _P, _P, _P,
@@ -266,6 +267,16 @@ def route_ids(topk_ids, topk_w, E):
     cr = r.c()
     _check("moe_route", lib().moe_route(ctypes.byref(shape), ctypes.byref(cr), _ptr(ws), ws.numel(),
                                          _stream(dev)))
+    return r
+
+
+def route_noalloc(r: Routing, T, E, k, logits_dtype=torch.bfloat16):
+    """moe_route_noalloc into the caller's routing tensors r (logits in when
+    r.logits is set, else r.topk_ids / r.topk_w in); no workspace."""
+    shape = make_shape(T, 8, E, k, 8, torch.bfloat16, logits_dtype)
+    cr = r.c()
+    _check("moe_route_noalloc", lib().moe_route_noalloc(ctypes.byref(shape), ctypes.byref(cr),
+                                                         _stream(r.counts.device)))
     return r
 
 

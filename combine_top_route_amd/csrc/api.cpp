@@ -298,13 +298,43 @@ moe_status check_aligned16(const void* p, const char* name) {
 
 char* at(void* base, size_t off) { return (char*)base + off; }
 
-// routing launches shared by moe_route and moe_forward
-moe_status run_route(const moe_shape* s, moe_routing* r, void* ws, const Layout& L,
-                     const LaunchCtx& c) {
+// routing launches shared by moe_route, moe_route_noalloc and moe_forward;
+// hist: the counting sort's per-chunk histograms [ceil(T*k/kSortChunk), E]
+moe_status run_route(const moe_shape* s, moe_routing* r, int32_t* hist, const LaunchCtx& c) {
   const int T = (int)s->T, E = (int)s->E, k = (int)s->k;
   if (r->logits) HIP_TRY(launch_topk(c, r->logits, s->logits_dtype, T, E, k, r->topk_ids, r->topk_w), "route_topk");
-  HIP_TRY(launch_sort(c, r->topk_ids, T, E, k, (int32_t*)at(ws, L.hist), r->counts, r->offsets,
-                      r->row_of, r->src_of), "route_sort");
+  HIP_TRY(launch_sort(c, r->topk_ids, T, E, k, hist, r->counts, r->offsets, r->row_of, r->src_of),
+          "route_sort");
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ no-allocation routing
+// moe_route_noalloc keeps the histograms in this file-scope device array
+// instead of a caller workspace.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the
+// first call per device).
+moe_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return MOE_OK;
 }
 
@@ -387,7 +417,22 @@ moe_status moe_route(const moe_shape* shape, moe_routing* routing, void* workspa
   TRY(check_ws(shape, MOE_OP_ROUTE, workspace, workspace_bytes));
   const Layout L = layout(shape, MOE_OP_ROUTE);
   (void)hipGetLastError();
-  return run_route(shape, routing, workspace, L, make_ctx(stream));
+  return run_route(shape, routing, (int32_t*)at(workspace, L.hist), make_ctx(stream));
+}
+
+moe_status moe_route_noalloc(const moe_shape* shape, moe_routing* routing, void* stream) {
+  TRY(check_shape(shape));
+  TRY(check_routing(routing, true));
+  const size_t need = sizeof(int32_t) * cdiv(shape->T * shape->k, kSortChunk) * shape->E;
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_route_noalloc: T*k=%lld, E=%lld need %zu bytes of scratch, above its %zu; "
+                "use moe_route with a workspace", (long long)(shape->T * shape->k), (long long)shape->E,
+                need, kNoAllocScratchBytes);
+  void* hist = nullptr;
+  TRY(scratch_on_current_device(&hist));
+  (void)hipGetLastError();
+  return run_route(shape, routing, (int32_t*)hist, make_ctx(stream));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routing,
@@ -408,7 +453,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, moe_routing* routi
   const Layout L = layout(shape, MOE_OP_FORWARD);
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
-  TRY(run_route(shape, routing, workspace, L, c));
+  TRY(run_route(shape, routing, (int32_t*)at(workspace, L.hist), c));
   HIP_TRY(launch_schedule(c, routing->offsets, (int)shape->E, (int32_t*)at(workspace, L.tile_off),
                           (int32_t*)at(workspace, L.order), nullptr, nullptr, (int4*)at(workspace, L.tiles)),
           "route_schedule");

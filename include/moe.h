@@ -168,6 +168,20 @@ moe_status moe_saved_size(const moe_shape* shape, size_t* bytes);
 moe_status moe_route(const moe_shape* shape, moe_routing* routing,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and results, with no workspace argument.  The counting
+ * sort's per-chunk histograms live in a 4 MiB array of device memory that
+ * the library holds on each GPU it runs on until the process ends, so
+ * 4 * ceil(T*k / 1024) * E must not exceed 4 MiB (T*k*E <= 2^30); larger
+ * shapes get MOE_ERR_UNSUPPORTED before anything is enqueued.  Every call on
+ * one GPU uses that GPU's one array: calls that overlap in time on the same
+ * GPU (different streams, or host threads) race and must be serialised by
+ * the caller.  The array needs no clearing between calls (each call writes
+ * every histogram it reads).  The first call on a device looks the array up
+ * (hipGetSymbolAddress); no call allocates. */
+moe_status moe_route_noalloc(const moe_shape* shape, moe_routing* routing, void* stream);
+
 /* Layer forward: routing as moe_route, then out [T,d] (dtype): dispatch
  * into expert order, both expert linear layers with SwiGLU, and the combine
  * that returns each token's k expert outputs to its position, weighted by

@@ -243,3 +243,17 @@ def test_status_strings():
     lib = B.lib()
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_route_noalloc_rejects_shapes_beyond_its_scratch():
+    """Above 4 MiB of histograms (4 * ceil(T*k/1024) * E bytes) the
+    no-allocation routing call refuses before touching the device."""
+    lib = B.lib()
+    sh = _shape(T=1 << 20, E=1024, k=2, d=64, I=64)   # 2048 chunks x 1024 experts x 4 B = 8 MiB
+    r = B.MoeRouting(None, *([ctypes.c_void_p(16)] * 6))
+    st = lib.moe_route_noalloc(ctypes.byref(sh), ctypes.byref(r), None)
+    assert st == 2 and b"use moe_route with a workspace" in lib.moe_last_error()
+    st = lib.moe_route_noalloc(ctypes.byref(_shape(k=9)), ctypes.byref(r), None)
+    assert st == 1
+    rn = B.MoeRouting(None, None, *([ctypes.c_void_p(16)] * 5))
+    assert lib.moe_route_noalloc(ctypes.byref(_shape()), ctypes.byref(rn), None) == 1

@@ -88,10 +88,10 @@ def _check_backward_args(dout: Tensor, x: Tensor, saved: Tensor, routing, k: int
         _require(t.is_contiguous(), f"{name} must be contiguous")
 
 
-def _shape(x: Tensor, logits: Tensor, w_gate_up: Tensor, k: int, precision: str):
+def _shape(x: Tensor, logits: Tensor, w_gate_up: Tensor, k: int, precision: str, swiglu_limit: float = 0.0):
     T, d = x.shape
     E, two_i, _ = w_gate_up.shape
-    return B.make_shape(T, d, E, k, two_i // 2, x.dtype, logits.dtype, precision)
+    return B.make_shape(T, d, E, k, two_i // 2, x.dtype, logits.dtype, precision, swiglu_limit)
 
 
 def _workspace(shape, op, device) -> Tensor:
@@ -107,12 +107,14 @@ def _routing_empty(T, E, k, device):
 
 @torch.library.custom_op(f"{_NS}::moe_fwd", mutates_args=())
 def moe_fwd(x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, k: int, precision: str,
-            save: bool) -> tuple[Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor]:
+            save: bool, swiglu_limit: float = 0.0
+            ) -> tuple[Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor, Tensor]:
     """Layer forward.  Returns (out [T,d], saved (uint8; empty unless save),
-    topk_ids, topk_w, counts, offsets, row_of, src_of)."""
+    topk_ids, topk_w, counts, offsets, row_of, src_of).  swiglu_limit > 0:
+    the clamped SwiGLU."""
     _check_layer_args(x, logits, w_gate_up, w_down, k, precision)
     _check_devices(x=x, logits=logits, w_gate_up=w_gate_up, w_down=w_down)
-    shape = _shape(x, logits, w_gate_up, k, precision)
+    shape = _shape(x, logits, w_gate_up, k, precision, swiglu_limit)
     T, d = x.shape
     E = w_gate_up.shape[0]
     dev = x.device
@@ -129,10 +131,10 @@ def moe_fwd(x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, k: int
 
 
 @moe_fwd.register_fake
-def _(x, logits, w_gate_up, w_down, k, precision, save):
+def _(x, logits, w_gate_up, w_down, k, precision, save, swiglu_limit=0.0):
     T, d = x.shape
     E = w_gate_up.shape[0]
-    shape = _shape(x, logits, w_gate_up, k, precision)
+    shape = _shape(x, logits, w_gate_up, k, precision, swiglu_limit)
     n = B.saved_size(shape) if save else 0
     i32 = dict(dtype=torch.int32)
     return (x.new_empty((T, d)), x.new_empty((n,), dtype=torch.uint8), x.new_empty((T, k), **i32),
@@ -143,13 +145,14 @@ def _(x, logits, w_gate_up, w_down, k, precision, save):
 @torch.library.custom_op(f"{_NS}::moe_bwd", mutates_args=())
 def moe_bwd(dout: Tensor, x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, saved: Tensor,
             topk_ids: Tensor, topk_w: Tensor, counts: Tensor, offsets: Tensor, row_of: Tensor,
-            src_of: Tensor, k: int, precision: str) -> tuple[Tensor, Tensor, Tensor, Tensor]:
+            src_of: Tensor, k: int, precision: str, swiglu_limit: float = 0.0
+            ) -> tuple[Tensor, Tensor, Tensor, Tensor]:
     """Layer backward: (dx, dlogits, dw_gate_up, dw_down).  An empty `saved`
     selects recomputation."""
     _check_layer_args(x, logits, w_gate_up, w_down, k, precision)
     dout = dout.contiguous()
     _check_backward_args(dout, x, saved, (topk_ids, topk_w, counts, offsets, row_of, src_of), k, precision)
-    shape = _shape(x, logits, w_gate_up, k, precision)
+    shape = _shape(x, logits, w_gate_up, k, precision, swiglu_limit)
     _require(saved.numel() in (0, B.saved_size(shape)),
              f"saved holds {saved.numel()} bytes, expected 0 or {B.saved_size(shape)}")
     _check_devices(x=x, dout=dout, logits=logits, w_gate_up=w_gate_up, w_down=w_down, saved=saved,
@@ -176,33 +179,34 @@ def moe_bwd(dout: Tensor, x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: 
 
 @moe_bwd.register_fake
 def _(dout, x, logits, w_gate_up, w_down, saved, topk_ids, topk_w, counts, offsets, row_of, src_of,
-      k, precision):
+      k, precision, swiglu_limit=0.0):
     return (torch.empty_like(x), torch.empty_like(logits), torch.empty_like(w_gate_up),
             torch.empty_like(w_down))
 
 
 def _setup_context(ctx, inputs, output):
-    x, logits, w_gate_up, w_down, k, precision, save = inputs
+    x, logits, w_gate_up, w_down, k, precision, save, swiglu_limit = inputs
     ctx.save_for_backward(x, logits, w_gate_up, w_down, *output[1:])
-    ctx.k, ctx.precision = k, precision
+    ctx.k, ctx.precision, ctx.swiglu_limit = k, precision, swiglu_limit
 
 
 def _backward(ctx, dout, *unused):
     x, logits, w_gate_up, w_down, saved, ids, w, counts, offsets, row_of, src_of = ctx.saved_tensors
     dx, dlogits, dwgu, dwd = moe_bwd(dout, x, logits, w_gate_up, w_down, saved, ids, w, counts, offsets,
-                                     row_of, src_of, ctx.k, ctx.precision)
-    return dx, dlogits, dwgu, dwd, None, None, None
+                                     row_of, src_of, ctx.k, ctx.precision, ctx.swiglu_limit)
+    return dx, dlogits, dwgu, dwd, None, None, None, None
 
 
 moe_fwd.register_autograd(_backward, setup_context=_setup_context)
 
 
 def moe_layer(x: Tensor, logits: Tensor, w_gate_up: Tensor, w_down: Tensor, k: int,
-              precision: str = "native", recompute: bool = False) -> Tensor:
+              precision: str = "native", recompute: bool = False, swiglu_limit: float = 0.0) -> Tensor:
     """out [T,d] of the layer, differentiable in x, logits and both weights.
     recompute=True: activation checkpointing inside the operator (nothing
-    kept between forward and backward but the routing)."""
+    kept between forward and backward but the routing).  swiglu_limit > 0:
+    the clamped SwiGLU with that limit."""
     for name, t in (("x", x), ("logits", logits), ("w_gate_up", w_gate_up), ("w_down", w_down)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    return moe_fwd(x, logits, w_gate_up, w_down, k, precision, not recompute)[0]
+    return moe_fwd(x, logits, w_gate_up, w_down, k, precision, not recompute, swiglu_limit)[0]

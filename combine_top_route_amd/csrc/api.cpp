@@ -101,7 +101,9 @@ moe_status check_shape(const moe_shape* s) {
   if (s->logits_dtype != MOE_F32 && s->logits_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_dtype=%d unknown", s->logits_dtype);
   if (s->precision < MOE_PREC_NATIVE || s->precision > MOE_PREC_FP8_BWD)
     return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
-  if (s->reserved != 0) return fail(MOE_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "swiglu_limit=%g must be 0 (plain SwiGLU) or a positive finite clamp",
+                (double)s->swiglu_limit);
   if (s->precision != MOE_PREC_NATIVE) {
     if (s->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 precisions need dtype bf16");
     if (s->d % 128 || s->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 precisions need d and I multiples of 128");
@@ -360,6 +362,7 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   a.order = (const int32_t*)at(ws, L.order);
   a.xorder = a.order + s->E;
   a.tok_of = L.tok ? (const int32_t*)at(ws, L.tok) : nullptr;  // backward layouts only
+  a.swiglu_lim = s->swiglu_limit > 0.0f ? s->swiglu_limit : __builtin_huge_valf();
   return a;
 }
 

@@ -41,6 +41,14 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return
 // Logistic function with the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// Clamped SwiGLU (DeepSeek V4's, as "Mario/overlap moe kernel integration"
+// names it in its commit on activations.ClampedSilu): a = silu(min(g, lim))
+// * clamp(u, -lim, lim).  lim = +inf gives the plain SwiGLU, bit for bit
+// (min and max with +-inf leave finite values unchanged).  In the backward
+// a gradient passes only where its clamp is inactive (at lim inclusive).
+__device__ __forceinline__ float clamp_gate(float g, float lim) { return fminf(g, lim); }
+__device__ __forceinline__ float clamp_up(float u, float lim) { return fminf(fmaxf(u, -lim), lim); }
+
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ----------------------------------------------------------------------------
@@ -113,8 +121,9 @@ hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const
                           const int32_t* row_of, const float* w, int T, int k, int d, void* out);
 // bf16 SwiGLU backward per row from G [R,I] and H [R,2I]: dH [R,2I] and the
 // row's top-k-weight gradient dw [R] = <G, silu(g) u>.
+// lim: the SwiGLU clamp (+inf: none).
 hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, const float* topk_w,
-                             const int32_t* src_of, int R, int I, void* dH, float* dw);
+                             const int32_t* src_of, int R, int I, float lim, void* dH, float* dw);
 // tok[r] = src_of[r] / k: the token of each expert-sorted row.
 hipError_t launch_tok_of(const LaunchCtx& c, const int32_t* src_of, int R, int k, int32_t* tok);
 // d_topk_w[t,j] = sum_b dwp[row_of[t*k+j]*nblk + b]; dlogits (optional).
@@ -138,6 +147,7 @@ struct LayerArgs {
   const int32_t* order;     // [E] experts by row count, largest first
   const int32_t* xorder;    // [8 ceil(E/8)] weight-gradient slot s of XCD x at 8 s + x (-1: empty)
   const int32_t* tok_of;    // [R] token of each sorted row (backward only)
+  float swiglu_lim;         // SwiGLU clamp limit, +inf for the plain SwiGLU
 };
 
 // Forward GEMMs write H [R,2I] (gate|up, may be null), Aw [R,I] = w_row *
@@ -197,8 +207,8 @@ hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* sr
 // [R,I], plus dH's e4m3 row codes dhq [R,2I] and scale words dhs, run-major
 // [2I/128, R] (I % 128 == 0).
 hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
-                                 const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
-                                 float* dw, uint8_t* dhq, void* dhs, bool mx);
+                                 const float* topk_w, const int32_t* src_of, int R, int I, float lim,
+                                 void* dH, float* dw, uint8_t* dhq, void* dhs, bool mx);
 
 // Transposed weight codes the fp8 forward leaves in `saved` for the backward.
 struct Fp8Saved {

@@ -497,10 +497,12 @@ struct RowsArgs {
   // EPI_STORE: C [R, ldc]
   bf16_t* C;
   int64_t ldc;
-  // EPI_GATEUP: H [R,2I] (optional), Aw [R,I] = w_row * silu(g) * u
+  // EPI_GATEUP: H [R,2I] (optional), Aw [R,I] = w_row * silu(g) * u (g, u
+  // clamped at lim: +inf for the plain SwiGLU)
   bf16_t* H;
   bf16_t* Aout;
   int I;
+  float lim;
   const float* topk_w;
   const int32_t* src_of;
 };
@@ -589,7 +591,7 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
     barrier_lds();
     const int c0w = wn * 32;
     stage_quads<TMX, 1, S>(lds, r0w, c0w, [&](int i, int, int r) {
-      const float g = acc[i][0][r], u = acc[i][1][r];
+      const float g = clamp_gate(acc[i][0][r], p.lim), u = clamp_up(acc[i][1][r], p.lim);
       return wl[r0w + acc_row(i, lane)] * (g * sigmoidf_(g) * u);
     });
     if (p.H) stage_quads<TMX, 1, S>(lds + TB, r0w, c0w, [&](int i, int, int r) { return acc[i][0][r]; });
@@ -729,7 +731,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
     p.A = (const bf16_t*)a.x; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
-    p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
+    p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I; p.lim = a.swiglu_lim;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R);
     if (err != hipSuccess) return err;
@@ -761,7 +763,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.C = G; p.ldc = I;
     err = launch_rows<EPI_STORE, B_KM, 1>(c, "gemm_down_dgrad", p, a.R);
     if (err != hipSuccess) return err;
-    err = launch_swiglu_bwd(c, G, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp);
+    err = launch_swiglu_bwd(c, G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, dH, dwp);
     if (err != hipSuccess) return err;
   }
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]

@@ -138,25 +138,27 @@ __global__ __launch_bounds__(256) void f32_wgrad(const float* __restrict__ A, in
 }
 
 // Aw[r, i] = w_r * silu(H[r, i]) * H[r, I + i], w_r = topk_w[src_of[r]]
+// (gate and up clamped at lim; +inf: none)
 __global__ __launch_bounds__(256) void f32_swiglu_fwd(const float* __restrict__ H,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ src_of, int64_t R,
-                                                      int I, float* __restrict__ Aout) {
+                                                      int I, float lim, float* __restrict__ Aout) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= R * I) return;
   const int64_t r = q / I;
   const int i = (int)(q % I);
-  const float g = H[r * 2 * I + i], u = H[r * 2 * I + I + i];
+  const float g = clamp_gate(H[r * 2 * I + i], lim), u = clamp_up(H[r * 2 * I + I + i], lim);
   Aout[q] = topk_w[src_of[r]] * (g / (1.0f + expf(-g)) * u);
 }
 
 // From G = dout_t W_down[e] (per row): dwp[r, b] = sum over the 128 columns of
-// block b of G * silu(g) * u; dA = w_r G; dH = (dA u s (1 + g (1 - s)), dA silu(g)).
+// block b of G * silu(g) * u; dA = w_r G; dH = (dA u s (1 + g (1 - s)), dA silu(g))
+// (g, u clamped at lim, no gradient through an active clamp).
 __global__ __launch_bounds__(256) void f32_swiglu_bwd(const float* __restrict__ G,
                                                       const float* __restrict__ H,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ src_of, int64_t R,
-                                                      int I, int nblk, float* __restrict__ dH,
+                                                      int I, int nblk, float lim, float* __restrict__ dH,
                                                       float* __restrict__ dwp) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= R * nblk) return;
@@ -166,12 +168,13 @@ __global__ __launch_bounds__(256) void f32_swiglu_bwd(const float* __restrict__ 
   float part = 0.0f;
   for (int i = b * 128; i < min(I, b * 128 + 128); ++i) {
     const float Gv = G[r * I + i];
-    const float g = H[r * 2 * I + i], u = H[r * 2 * I + I + i];
+    const float g0 = H[r * 2 * I + i], u0 = H[r * 2 * I + I + i];
+    const float g = clamp_gate(g0, lim), u = clamp_up(u0, lim);
     const float s = 1.0f / (1.0f + expf(-g));
     part += Gv * (g * s * u);
     const float dA = w * Gv;
-    dH[r * 2 * I + i] = dA * u * s * (1.0f + g * (1.0f - s));
-    dH[r * 2 * I + I + i] = dA * g * s;
+    dH[r * 2 * I + i] = g0 <= lim ? dA * u * s * (1.0f + g * (1.0f - s)) : 0.0f;
+    dH[r * 2 * I + I + i] = fabsf(u0) <= lim ? dA * g * s : 0.0f;
   }
   dwp[q] = part;
 }
@@ -207,7 +210,7 @@ hipError_t f32_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* 
                              (int)(2 * I), a.d);
   if (err != hipSuccess) return err;
   MOE_LAUNCH(c, "swiglu_fwd", f32_swiglu_fwd, dim3((unsigned)cdiv(R * I, 256)), dim3(256), 0,
-             (const float*)H, a.topk_w, a.src_of, R, a.I, (float*)Aact);
+             (const float*)H, a.topk_w, a.src_of, R, a.I, a.swiglu_lim, (float*)Aact);
   if (!Y) return hipSuccess;  // the gate/up half alone (recomputation)
   return rows_gemm(c, "gemm_down_fwd", a, (const float*)Aact, I, nullptr, 1,
                    (const float*)a.w_down, d * I, I, 1, (float*)Y, d, a.d, a.I);
@@ -223,7 +226,8 @@ hipError_t f32_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dou
                              (const float*)a.w_down, d * I, 1, I, G, I, a.I, a.d);
   if (err != hipSuccess) return err;
   MOE_LAUNCH(c, "swiglu_bwd", f32_swiglu_bwd, dim3((unsigned)cdiv(R * nblk, 256)), dim3(256), 0,
-             (const float*)G, (const float*)H, a.topk_w, a.src_of, R, a.I, nblk, (float*)dH, dwp);
+             (const float*)G, (const float*)H, a.topk_w, a.src_of, R, a.I, nblk, a.swiglu_lim,
+             (float*)dH, dwp);
   // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]  (Aw carries w_r)
   err = wgrad(c, "gemm_down_wgrad", a, (const float*)dout, d, 1, nullptr, (const float*)Aact, I,
               0, a.d, a.I, (float*)dW_d);

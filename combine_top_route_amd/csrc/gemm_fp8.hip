@@ -387,10 +387,12 @@ struct Rows8Args {
   bf16_t* C;
   float* Cf;
   int64_t ldc;
-  // EPI_GATEUP: H [R,2I] (optional), Aout [R,I] = w_row * silu(g) * u
+  // EPI_GATEUP: H [R,2I] (optional), Aout [R,I] = w_row * silu(g) * u (g, u
+  // clamped at lim: +inf for the plain SwiGLU)
   bf16_t* H;
   bf16_t* Aout;
   int I;
+  float lim;
   const float* topk_w;
   const int32_t* src_of;
 };
@@ -484,7 +486,7 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
     barrier_lds();
     const int c0w = wn * 32;
     stage4<TMX, 2, S>(lds, r0w, c0w, [&](int i, int j, int r) {
-      const float g = acc[i][j][r], u = acc[i][j + 2][r];
+      const float g = clamp_gate(acc[i][j][r], p.lim), u = clamp_up(acc[i][j + 2][r], p.lim);
       return wl[r0w + i * 16 + (lane & 15)] * (g * sigmoidf_(g) * u);
     });
     if (p.H) stage4<TMX, 2, S>(lds + TB, r0w, c0w, [&](int i, int j, int r) { return acc[i][j][r]; });
@@ -663,7 +665,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? 2 * I : 1;
     p.gateup = 1;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
-    p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I;
+    p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I; p.lim = a.swiglu_lim;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R, mx));
   }
@@ -707,7 +709,8 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Cf = q.G; p.ldc = I;
     HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx));
-    HIP_RET(launch_swiglu_bwd_fp8(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, dH, dwp, q.dhq, q.dhs, mx));
+    HIP_RET(launch_swiglu_bwd_fp8(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, dH, dwp, q.dhq,
+                                  q.dhs, mx));
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
     Rows8Args p = {};

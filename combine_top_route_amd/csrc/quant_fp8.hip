@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
 }
 
 // SwiGLU backward of one row per wave from G = dout_t W_down[e] (fp32), as
-// in the bf16 path, that also encodes the bf16-rounded dH in 1 x 128 blocks
+// in the bf16 path (clamp lim included), that also encodes the bf16-rounded dH in 1 x 128 blocks
 // (fp32 scales) or, MX, 1 x 32 blocks (a word of four E8M0 codes per 128
 // columns), the words stored run-major ([I/64][R]): the A operand of the
 // gate/up dgrad.  Lane l handles the 8-column
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
 template <bool MX>
 __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
     const f32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
-    const int32_t* __restrict__ src_of, int R, int chunks, u32x4_t* __restrict__ dH,
+    const int32_t* __restrict__ src_of, int R, int chunks, float lim, u32x4_t* __restrict__ dH,
     float* __restrict__ dw, uint8_t* __restrict__ dhq, uint32_t* __restrict__ dhs) {
   // dH scale words run-major: word (row r, 128-column block j) at dhs[j * R + r]
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -516,11 +516,12 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
     unpack8(ok ? Hg[chunks + c] : zero, u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sg = sigmoidf_(g[i]);
-      part += gv[i] * (g[i] * sg * u[i]);
+      const float gc = clamp_gate(g[i], lim), uc = clamp_up(u[i], lim);
+      const float sg = sigmoidf_(gc);
+      part += gv[i] * (gc * sg * uc);
       const float dA = wr * gv[i];
-      dg[i] = dA * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
-      du[i] = dA * g[i] * sg;
+      dg[i] = g[i] <= lim ? dA * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+      du[i] = fabsf(u[i]) <= lim ? dA * gc * sg : 0.0f;
     }
     // bf16 rounding first: the codes encode the stored dH
     u32x4_t pg, pu;
@@ -581,16 +582,16 @@ __global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
 }  // namespace
 
 hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
-                                 const float* topk_w, const int32_t* src_of, int R, int I, void* dH,
-                                 float* dw, uint8_t* dhq, void* dhs, bool mx) {
+                                 const float* topk_w, const int32_t* src_of, int R, int I, float lim,
+                                 void* dH, float* dw, uint8_t* dhq, void* dhs, bool mx) {
   if (mx)
     MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<true>, dim3((R + 3) / 4), dim3(256), 0,
-               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
-               (uint32_t*)dhs);
+               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, lim, (u32x4_t*)dH, dw,
+               dhq, (uint32_t*)dhs);
   else
     MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<false>, dim3((R + 3) / 4), dim3(256), 0,
-               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, (u32x4_t*)dH, dw, dhq,
-               (uint32_t*)dhs);
+               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, lim, (u32x4_t*)dH, dw,
+               dhq, (uint32_t*)dhs);
   return hipSuccess;
 }
 

@@ -237,14 +237,15 @@ __global__ __launch_bounds__(256) void topk_grad_kernel(const float* __restrict_
 
 // SwiGLU backward of one row per wave, from G = dout_t W_down[e] (bf16):
 // a = silu(g) u, dw_r = <G, a> (the row's top-k-weight gradient), dA = w_r G,
-// dH = (dA u s (1 + g (1 - s)), dA silu(g)) with s = sigmoid(g).  Lane l
+// dH = (dA u s (1 + g (1 - s)), dA silu(g)) with s = sigmoid(g); with a
+// clamp lim, g and u as clamped and no gradient through an active clamp.  Lane l
 // handles the 8-column chunks l, l + 64, ...; the float32 dot product is
 // reduced across the wave in a fixed order.
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict__ G,
                                                          const uint4* __restrict__ H,
                                                          const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ src_of, int R,
-                                                         int chunks, uint4* __restrict__ dH,
+                                                         int chunks, float lim, uint4* __restrict__ dH,
                                                          float* __restrict__ dw) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
@@ -263,12 +264,13 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
     unpack<bf16_t>(Hu[c], u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sg = sigmoidf_(g[i]);
-      const float a = g[i] * sg * u[i];
+      const float gc = clamp_gate(g[i], lim), uc = clamp_up(u[i], lim);
+      const float sg = sigmoidf_(gc);
+      const float a = gc * sg * uc;
       part += gv[i] * a;
       const float dA = wr * gv[i];
-      dg[i] = dA * u[i] * sg * (1.0f + g[i] * (1.0f - sg));
-      du[i] = dA * g[i] * sg;
+      dg[i] = g[i] <= lim ? dA * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+      du[i] = fabsf(u[i]) <= lim ? dA * gc * sg : 0.0f;
     }
     dg_out[c] = pack<bf16_t>(dg);
     du_out[c] = pack<bf16_t>(du);
@@ -281,9 +283,9 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
 }  // namespace
 
 hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, const float* topk_w,
-                             const int32_t* src_of, int R, int I, void* dH, float* dw) {
+                             const int32_t* src_of, int R, int I, float lim, void* dH, float* dw) {
   MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)G,
-             (const uint4*)H, topk_w, src_of, R, I / 8, (uint4*)dH, dw);
+             (const uint4*)H, topk_w, src_of, R, I / 8, lim, (uint4*)dH, dw);
   return hipSuccess;
 }
 

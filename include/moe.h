@@ -102,8 +102,16 @@ typedef struct {
   int32_t dtype;        /* moe_dtype of x, weights, out, saved, dout, grads */
   int32_t logits_dtype; /* moe_dtype of logits and dlogits                  */
   int32_t precision;    /* moe_precision                                    */
-  int32_t reserved;     /* must be 0                                        */
+  float swiglu_limit;   /* 0: SwiGLU; > 0 (finite): clamped SwiGLU, below   */
 } moe_shape;
+
+/* swiglu_limit > 0 selects the clamped SwiGLU that "Mario/overlap moe kernel
+ * integration" names for DeepSeek V4 (commit on activations.ClampedSilu);
+ * the pages give neither its form nor its constant, so the limit L is an
+ * argument and the form is read as a = silu(min(g, L)) * clamp(u, -L, L),
+ * with no gradient through an active clamp (g > L, |u| > L).  The pages'
+ * other clamped variant (sigmoid of 1.702 g, up + 1) is not computed.  H in
+ * `saved` holds the unclamped pre-activations. */
 
 /* Limits checked by every call: 1 <= T <= 2^24, 1 <= k <= E <= 1024,
  * T*k <= 2^27, d and I multiples of 8 in [8, 16384]. */

@@ -31,8 +31,13 @@ What the pages fix, and the readings taken where they leave a step open:
   * each expert is a two-layer MLP with SwiGLU [P3 "What a mixture-of-experts
     layer actually does"; P4 overview "SwiGLU expert GEMMs"].  Reading:
     W_gate_up[e] rows [0, I) are the gate, rows [I, 2I) the up projection;
-    A = silu(gate) * up, no clamp (the pages say the kernel does not compute
-    the clamped variant [P4 commit on ClampedSwiglu]).
+    A = silu(gate) * up.  The pages also name DeepSeek V4's clamped SwiGLU
+    (activations.ClampedSilu) as one the layer takes, and reject a
+    differently defined ClampedSwiglu (sigmoid of 1.702 gate, up + 1) [P4
+    commit on ClampedSwiglu]; they give neither the clamped form nor its
+    constant.  Reading, with the constant an argument (limit > 0):
+    A = silu(min(gate, limit)) * clamp(up, -limit, limit), no gradient
+    through an active clamp.
   * combine returns expert outputs to their original positions [P2 "Where MoE
     training loses time"], summed with the top-k weights.
   * the backward repeats the exchange for gradients [P2 "Where MoE training
@@ -171,17 +176,39 @@ def sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def swiglu(H: np.ndarray, I: int) -> np.ndarray:
-    """A = silu(gate) * up with gate = H[:, :I], up = H[:, I:]."""
-    return silu(H[:, :I]) * H[:, I:]
+def swiglu(H: np.ndarray, I: int, limit: float = 0.0) -> np.ndarray:
+    """A = silu(gate) * up with gate = H[:, :I], up = H[:, I:].
 
-
-def swiglu_backward(H: np.ndarray, dA: np.ndarray, I: int) -> np.ndarray:
-    """d/dgate = dA * up * s(g) * (1 + g (1 - s(g))), d/dup = dA * silu(g)."""
+    limit > 0: the clamped SwiGLU that the pages name for DeepSeek V4 (the
+    PR's commit on activations.ClampedSilu), whose form and constant they
+    do not give.  Reading: the gate is clamped from above and the up
+    projection to [-limit, limit] before the product,
+    A = silu(min(gate, limit)) * clamp(up, -limit, limit); the pages' other
+    clamped variant (sigmoid of 1.702 gate, up + 1) is the one the kernel
+    does not compute."""
     g, u = H[:, :I], H[:, I:]
+    if limit > 0:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
+    return silu(g) * u
+
+
+def swiglu_backward(H: np.ndarray, dA: np.ndarray, I: int, limit: float = 0.0) -> np.ndarray:
+    """d/dgate = dA * up * s(g) * (1 + g (1 - s(g))), d/dup = dA * silu(g).
+    Clamped (limit > 0): g and up as clamped in the forward, and no gradient
+    through a clamp that is active (gate above limit, |up| above limit); at
+    the limit itself the gradient passes, as a clamp's derivative is taken
+    one-sided from inside."""
+    g, u = H[:, :I], H[:, I:]
+    keep_g = keep_u = 1.0
+    if limit > 0:
+        keep_g = (g <= limit).astype(F64)
+        keep_u = (np.abs(u) <= limit).astype(F64)
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
     s = sigmoid(g)
-    dg = dA * u * s * (1.0 + g * (1.0 - s))
-    du = dA * g * s
+    dg = dA * u * s * (1.0 + g * (1.0 - s)) * keep_g
+    du = dA * g * s * keep_u
     return np.concatenate([dg, du], axis=1)
 
 
@@ -205,7 +232,7 @@ def combine(rows: np.ndarray, rt: dict) -> np.ndarray:
     return out
 
 
-def forward(x, rt: dict, w_gate_up, w_down, expert_fn=None) -> dict:
+def forward(x, rt: dict, w_gate_up, w_down, expert_fn=None, limit: float = 0.0) -> dict:
     """Layer forward.  expert_fn(e, Xp_e) -> Y_e replaces the expert MLP when
     given (used by the identity-expert invariant)."""
     off = rt["offsets"]
@@ -230,7 +257,7 @@ def forward(x, rt: dict, w_gate_up, w_down, expert_fn=None) -> dict:
         if off[e + 1] == off[e]:
             continue
         H[s] = Xp[s] @ np.asarray(Wgu[e], F64).T          # gate/up GEMM
-        A[s] = swiglu(H[s], I)                              # SwiGLU
+        A[s] = swiglu(H[s], I, limit)                       # SwiGLU
         Y[s] = A[s] @ np.asarray(Wd[e], F64).T              # down GEMM
     return dict(out=combine(Y, rt), H=H, A=A, Y=Y, Xp=Xp)
 
@@ -240,7 +267,7 @@ def forward(x, rt: dict, w_gate_up, w_down, expert_fn=None) -> dict:
 # --------------------------------------------------------------------------
 
 def backward(dout, rt: dict, w_gate_up, w_down, fwd: dict,
-             logits=None) -> dict:
+             logits=None, limit: float = 0.0) -> dict:
     """Exact gradient of L = sum(dout * out)."""
     dout = np.asarray(dout, F64)
     T, k, E = rt["ids"].shape[0], rt["k"], rt["E"]
@@ -270,7 +297,7 @@ def backward(dout, rt: dict, w_gate_up, w_down, fwd: dict,
         Wgu_e = np.asarray(Wgu[e], F64)
         dA = dY[s] @ Wd_e                               # down dgrad
         dW_down[e] = dY[s].T @ A[s]                     # down wgrad
-        dH = swiglu_backward(H[s], dA, I)               # SwiGLU backward
+        dH = swiglu_backward(H[s], dA, I, limit)        # SwiGLU backward
         dXp[s] = dH @ Wgu_e                             # gate/up dgrad
         dW_gate_up[e] = dH.T @ Xp[s]                    # gate/up wgrad
 
@@ -304,7 +331,7 @@ def router_logit_grad(rt: dict, d_topk_w: np.ndarray, E: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def forward_backward_tokens(x, logits, dout, w_gate_up, w_down, k: int,
-                            tokens: np.ndarray, ids=None, w=None) -> dict:
+                            tokens: np.ndarray, ids=None, w=None, limit: float = 0.0) -> dict:
     """out, dx, d_topk_w (and dlogits when logits are given) for a subset of
     tokens.  Every token's result depends only on its own routing and on the
     weights, so this evaluates the same definitions row by row."""
@@ -330,12 +357,12 @@ def forward_backward_tokens(x, logits, dout, w_gate_up, w_down, k: int,
             Wgu_e = np.asarray(w_gate_up[e], F64)
             Wd_e = np.asarray(w_down[e], F64)
             h = Wgu_e @ x_t[i]
-            a = swiglu(h[None, :], I)[0]
+            a = swiglu(h[None, :], I, limit)[0]
             y = Wd_e @ a
             out[i] += w_t[i, j] * y
             dtw[i, j] = g_t[i] @ y
             dA = w_t[i, j] * (Wd_e.T @ g_t[i])
-            dh = swiglu_backward(h[None, :], dA[None, :], I)[0]
+            dh = swiglu_backward(h[None, :], dA[None, :], I, limit)[0]
             dx[i] += Wgu_e.T @ dh
     res = dict(out=out, dx=dx, d_topk_w=dtw, ids=ids_t, w=w_t)
     if logits is not None:
@@ -344,7 +371,7 @@ def forward_backward_tokens(x, logits, dout, w_gate_up, w_down, k: int,
     return res
 
 
-def expert_weight_grads(x, dout, rt: dict, w_gate_up, w_down, e: int):
+def expert_weight_grads(x, dout, rt: dict, w_gate_up, w_down, e: int, limit: float = 0.0):
     """dW_gate_up[e], dW_down[e] from the rows routed to expert e."""
     k = rt["k"]
     s = slice(rt["offsets"][e], rt["offsets"][e + 1])
@@ -356,9 +383,9 @@ def expert_weight_grads(x, dout, rt: dict, w_gate_up, w_down, e: int):
     wr = rt["w"].ravel()[src]
     dY = wr[:, None] * np.asarray(dout, F64)[src // k]
     H = Xp @ Wgu_e.T
-    A = swiglu(H, I)
+    A = swiglu(H, I, limit)
     dA = dY @ Wd_e
-    dH = swiglu_backward(H, dA, I)
+    dH = swiglu_backward(H, dA, I, limit)
     return dH.T @ Xp, dY.T @ A
 
 
@@ -530,7 +557,7 @@ def no_quant(X: np.ndarray) -> np.ndarray:
 NO_QUANT = dict(act=no_quant, w_fwd=no_quant, w_bwd=no_quant, tok=no_quant)
 
 
-def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK) -> dict:
+def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK, limit: float = 0.0) -> dict:
     """Forward with both GEMMs on block-quantised e4m3 operands (block
     shapes from `recipe`: FP8_BLOCK or MXFP8).  The top-k
     weight of each row is folded into the SwiGLU output before the down GEMM
@@ -549,7 +576,7 @@ def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK) -> dict:
         if off[e + 1] == off[e]:
             continue
         Hs = recipe["act"](Xp[s]) @ recipe["w_fwd"](w_gate_up[e]).T
-        Aw[s] = bf16_round(w_row[s, None] * swiglu(Hs, I))
+        Aw[s] = bf16_round(w_row[s, None] * swiglu(Hs, I, limit))
         H[s] = bf16_round(Hs)
         Yw[s] = recipe["act"](Aw[s]) @ recipe["w_fwd"](w_down[e]).T
     T, k = rt["ids"].shape
@@ -560,7 +587,7 @@ def forward_fp8(x, rt: dict, w_gate_up, w_down, recipe=FP8_BLOCK) -> dict:
 
 
 def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
-                 logits=None, recipe=FP8_BLOCK) -> dict:
+                 logits=None, recipe=FP8_BLOCK, limit: float = 0.0) -> dict:
     """Backward with all four GEMMs on block-quantised e4m3 operands.  The
     top-k-weight gradient is <G_r, a_r> with G_r the quantised down dgrad
     (the backward's estimate of W_down^T dout_t) and a_r = silu(g) * up from
@@ -585,10 +612,10 @@ def backward_fp8(dout, rt: dict, w_gate_up, w_down, fwd: dict,
         Wd_q = recipe["w_bwd"](w_down[e])
         Wgu_q = recipe["w_bwd"](w_gate_up[e])
         G = recipe["act"](dout[tok[s]]) @ Wd_q               # down dgrad
-        dw_row[s] = np.sum(G * swiglu(H[s], I), axis=1)
+        dw_row[s] = np.sum(G * swiglu(H[s], I, limit), axis=1)
         dA = w_row[s, None] * G
         dW_down[e] = recipe["tok"](dout[tok[s]]).T @ recipe["tok"](Aw[s])
-        dH = bf16_round(swiglu_backward(H[s], dA, I))
+        dH = bf16_round(swiglu_backward(H[s], dA, I, limit))
         dXp[s] = recipe["act"](dH) @ Wgu_q                    # gate/up dgrad
         dW_gate_up[e] = recipe["tok"](dH).T @ recipe["tok"](Xp[s])
     d_topk_w = dw_row[row_of].reshape(T, k)
@@ -614,7 +641,8 @@ def encode_expert_weights(w_gate_up, w_down, e: int, recipe=FP8_BLOCK, fwd_recip
 
 def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
                                 tokens: np.ndarray, ids=None, w=None,
-                                recipe=FP8_BLOCK, fwd_recipe=None, encoded=None) -> dict:
+                                recipe=FP8_BLOCK, fwd_recipe=None, encoded=None,
+                                limit: float = 0.0) -> dict:
     """forward_fp8 (with fwd_recipe, default recipe) / backward_fp8 (with
     recipe) results (out, dx, d_topk_w, dlogits) for a subset of tokens.  Activation blocks lie within one row and weight
     blocks depend only on the weights, so each token's results follow from
@@ -649,11 +677,11 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
             Wgu_f, Wd_f, Wgu_b, Wd_b = weights(ids_t[i, j])
             Hs = xq @ Wgu_f.T
             H = bf16_round(Hs)
-            Aw = bf16_round(w_t[i, j] * swiglu(Hs, I))
+            Aw = bf16_round(w_t[i, j] * swiglu(Hs, I, limit))
             out[i] += (fr["act"](Aw) @ Wd_f.T)[0]
             G = gq @ Wd_b
-            dtw[i, j] = np.sum(G * swiglu(H, I))
-            dH = bf16_round(swiglu_backward(H, w_t[i, j] * G, I))
+            dtw[i, j] = np.sum(G * swiglu(H, I, limit))
+            dH = bf16_round(swiglu_backward(H, w_t[i, j] * G, I, limit))
             dx[i] += (recipe["act"](dH) @ Wgu_b)[0]
     res = dict(out=out, dx=dx, d_topk_w=dtw, ids=ids_t, w=w_t)
     if logits is not None:
@@ -662,7 +690,7 @@ def forward_backward_tokens_fp8(x, logits, dout, w_gate_up, w_down, k: int,
 
 
 def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int,
-                            recipe=FP8_BLOCK, fwd_recipe=None):
+                            recipe=FP8_BLOCK, fwd_recipe=None, limit: float = 0.0):
     """backward_fp8's dW_gate_up[e], dW_down[e] from the rows of expert e
     alone (token blocks are counted from the expert's first row); the
     forward's H and Aw with fwd_recipe (default recipe)."""
@@ -678,9 +706,9 @@ def expert_weight_grads_fp8(x, dout, rt: dict, w_gate_up, w_down, e: int,
     wr = rt["w"].ravel()[src]
     Hs = fr["act"](Xp) @ Wgu_f.T
     H = bf16_round(Hs)
-    Aw = bf16_round(wr[:, None] * swiglu(Hs, I))
+    Aw = bf16_round(wr[:, None] * swiglu(Hs, I, limit))
     G = recipe["act"](g) @ Wd_b
-    dH = bf16_round(swiglu_backward(H, wr[:, None] * G, I))
+    dH = bf16_round(swiglu_backward(H, wr[:, None] * G, I, limit))
     dW_down = recipe["tok"](g).T @ recipe["tok"](Aw)
     dW_gate_up = recipe["tok"](dH).T @ recipe["tok"](Xp)
     return dW_gate_up, dW_down

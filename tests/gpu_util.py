@@ -24,13 +24,13 @@ def to_np(t):
     return t.detach().cpu().double().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
 
 
-def run_gpu(wl, inp, ids=None, w=None, backward=True):
+def run_gpu(wl, inp, ids=None, w=None, backward=True, limit=0.0):
     """Runs forward (+ backward) of the layer on cuda:0; returns CPU numpy
-    results and the routing artefacts."""
+    results and the routing artefacts.  limit > 0: clamped SwiGLU."""
     dev = torch.device("cuda", 0)
     dt = S.torch_dtype(wl.dtype)
     layer = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt, logits_dtype=S.torch_dtype(wl.logits_dtype),
-                       precision=wl.precision, device=dev)
+                       precision=wl.precision, device=dev, swiglu_limit=limit)
     x = inp["x"].to(dev)
     wgu = inp["w_gate_up"].to(dev)
     wd = inp["w_down"].to(dev)
@@ -50,7 +50,7 @@ def run_gpu(wl, inp, ids=None, w=None, backward=True):
     return res
 
 
-def run_oracle(wl, inp, ids=None, w=None, backward=True):
+def run_oracle(wl, inp, ids=None, w=None, backward=True, limit=0.0):
     f = lambda t: t.double().numpy()
     logits = f(inp["logits"]) if ids is None else None
     if ids is None:
@@ -60,15 +60,16 @@ def run_oracle(wl, inp, ids=None, w=None, backward=True):
     Wgu, Wd = inp["w_gate_up"].float().numpy(), inp["w_down"].float().numpy()
     recipes = RECIPE.get(wl.precision)
     if recipes is None:
-        fw = O.forward(f(inp["x"]), rt, Wgu, Wd)
+        fw = O.forward(f(inp["x"]), rt, Wgu, Wd, limit=limit)
     else:
-        fw = O.forward_fp8(f(inp["x"]), rt, Wgu, Wd, recipe=recipes[0])
+        fw = O.forward_fp8(f(inp["x"]), rt, Wgu, Wd, recipe=recipes[0], limit=limit)
     res = {"rt": rt, "out": fw["out"]}
     if backward:
         if recipes is None:
-            bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits)
+            bw = O.backward(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, limit=limit)
         else:
-            bw = O.backward_fp8(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, recipe=recipes[1])
+            bw = O.backward_fp8(f(inp["dout"]), rt, Wgu, Wd, fw, logits=logits, recipe=recipes[1],
+                                limit=limit)
         res.update(bw)
     return res
 

@@ -92,9 +92,12 @@ def test_bad_enums_rejected():
     s = _shape()
     s.dtype = 7
     assert _status(s)[0] == 1
-    s = _shape()
-    s.reserved = 1
-    assert _status(s)[0] == 1
+    for bad in (-1.0, float("nan"), float("inf")):      # the SwiGLU clamp: 0 or a positive finite limit
+        s = _shape()
+        s.swiglu_limit = bad
+        assert _status(s)[0] == 1 and b"swiglu_limit" in B.lib().moe_last_error()
+    s = _shape(swiglu_limit=7.0)
+    assert _status(s)[0] == 0
 
 
 def test_fp8_requirements():

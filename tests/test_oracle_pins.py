@@ -298,7 +298,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert fd_gap() < 1e-6
     real = O.swiglu_backward
 
-    def dropped(H, dA, I):
+    def dropped(H, dA, I, limit=0.0):
         g, u = H[:, :I], H[:, I:]
         s = O.sigmoid(g)
         return np.concatenate([dA * u * s, dA * g * s], axis=1)   # missing (1 + g(1-s))
@@ -306,7 +306,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert fd_gap() > 1e-3
     monkeypatch.setattr(O, "swiglu_backward", real)
 
-    def swapped(H, I):
+    def swapped(H, I, limit=0.0):
         return O.silu(H[:, I:]) * H[:, :I]
     monkeypatch.setattr(O, "swiglu", swapped)
     rng = np.random.default_rng(5)

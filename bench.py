@@ -49,7 +49,7 @@ KERNEL_SITES = [
     ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
     ("tok_of_kernel", "route_tok"),
-    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
+    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("permute_scatter_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
     ("quant_weight_kernel", "quant_w_*"), ("quant_weight_mx_kernel", "quant_w_*"),
     ("quant_tok_kernel", "quant_*_tok"),
 ]
@@ -361,6 +361,18 @@ def main():
     kstats = B.profile_end()
     ms_per_step = elapsed * 1e3 / args.steps
 
+    # the dispatch alone (moe_permute: each token's row copied to its k
+    # expert-sorted rows), outside the layer step, on the step's routing
+    xp = torch.empty((wl.R, wl.d), dtype=dt, device=dev)
+    B.permute(x, layer.routing, wl.k, out=xp)
+    torch.cuda.synchronize()
+    B.profile_begin()
+    for _ in range(args.steps):
+        B.permute(x, layer.routing, wl.k, out=xp)
+    torch.cuda.synchronize()
+    kstats.update(B.profile_end())
+    del xp
+
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
@@ -407,7 +419,8 @@ def main():
     kernels = {}
     for name, (n, tot) in kstats.items():
         avg = tot / max(n, 1)
-        entry = {"launches_per_step": n / args.steps, "avg_ms": avg}
+        # the dispatch is timed on its own, outside the step
+        entry = {"launches_per_step": 0.0 if name == "permute" else n / args.steps, "avg_ms": avg}
         if name in work:
             kind, amt = work[name]
             if kind == "flop":

@@ -282,11 +282,13 @@ def route_noalloc(r: Routing, T, E, k, logits_dtype=torch.bfloat16):
     return r
 
 
-def permute(x, routing: Routing, k):
+def permute(x, routing: Routing, k, out=None):
+    """Dispatch: xp [T*k, d] with xp[r] = x[src_of[r] / k] (into `out` when given)."""
     T, d = x.shape
     E = routing.counts.numel()
     shape = make_shape(T, d, E, k, 8, x.dtype)
-    xp = torch.empty((T * k, d), dtype=x.dtype, device=x.device)
+    xp = torch.empty((T * k, d), dtype=x.dtype, device=x.device) if out is None else out
+    _need(xp, "out", (T * k, d), x.dtype, x.device)
     cr = routing.c()
     _check("moe_permute", lib().moe_permute(ctypes.byref(shape), _ptr(x), ctypes.byref(cr), _ptr(xp),
                                              _stream(x.device)))

@@ -562,12 +562,13 @@ moe_status moe_permute(const moe_shape* shape, const void* x, const moe_routing*
   CHECK_PTR(xp);
   CHECK_PTR(routing);
   CHECK_PTR(routing->src_of);
+  CHECK_PTR(routing->row_of);
   TRY(check_aligned16(x, "x"));
   TRY(check_aligned16(xp, "xp"));
   const LaunchCtx c = make_ctx(stream);
   (void)hipGetLastError();
-  HIP_TRY(launch_permute(c, "permute", shape->dtype, x, routing->src_of, (int)(shape->T * shape->k),
-                         (int)shape->k, (int)shape->d, xp), "permute");
+  HIP_TRY(launch_permute(c, "permute", shape->dtype, x, routing->src_of, routing->row_of,
+                         (int)(shape->T * shape->k), (int)shape->k, (int)shape->d, xp), "permute");
   return MOE_OK;
 }
 

@@ -113,8 +113,10 @@ hipError_t launch_schedule(const LaunchCtx& c, const int32_t* offsets, int E, in
 inline int64_t max_row_tiles(int64_t R, int64_t E) { return R / kRowTile + E; }
 
 // ---------------------------------------------------------------- row passes
+// xp[r] = x[src_of[r] / k]; rows of 4 or 8 KB are written as a scatter
+// through row_of (x read once), others gathered through src_of.
 hipError_t launch_permute(const LaunchCtx& c, const char* name, int dtype, const void* x,
-                          const int32_t* src_of,
+                          const int32_t* src_of, const int32_t* row_of,
                           int R, int k, int d, void* xp);
 // out[t] = sum_j (w ? w[t*k+j] : 1) * rows[row_of[t*k+j]]
 hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const void* rows,

@@ -109,10 +109,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   }
 }
 
+// Dispatch as a scatter, for rows of 64 * CPL 16-byte chunks: one wave per
+// token reads its row once and writes it to the token's k expert-sorted
+// rows (row_of), so x is read once instead of k times.  Same result as
+// permute_kernel; stores are non-temporal (the copies are read later, by
+// another kernel).
+template <int CPL>
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const uint4* __restrict__ x,
+                                                              const int32_t* __restrict__ row_of, int Tn,
+                                                              int k, uint4* __restrict__ xp) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int RV = 64 * CPL;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int lane = threadIdx.x & 63;
+  u32x4v v[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) v[c] = *(const u32x4v*)(x + (int64_t)t * RV + c * 64 + lane);
+  const int32_t* ro = row_of + (int64_t)t * k;
+  for (int j = 0; j < k; ++j) {
+    u32x4v* dst = (u32x4v*)(xp + (int64_t)ro[j] * RV + lane);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(v[c], dst + c * 64);
+  }
+}
+
 // Same sum with CPL 16-byte chunks per lane known at compile time (row width
-// 64 * CPL chunks): every lane issues the loads of four rows x CPL chunks
-// before accumulating, so more of each token's rows are in flight.
-template <typename T, int CPL>
+// 64 * CPL chunks): every lane issues the loads of RB rows x CPL chunks
+// before accumulating, so more of each token's rows are in flight.  Each
+// expert row is read exactly once, so the loads are non-temporal: they do
+// not evict lines that other kernels' operands reuse.
+template <typename T, int CPL, int RB>
 __global__ __launch_bounds__(256) void combine_wide_kernel(const uint4* __restrict__ rows,
                                                            const int32_t* __restrict__ row_of,
                                                            const float* __restrict__ w, int Tn, int k,
@@ -128,19 +155,23 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const uint4* __restri
   for (int c = 0; c < CPL; ++c)
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[c][i] = 0.0f;
+  typedef unsigned int u32x4l __attribute__((ext_vector_type(4)));
   int j = 0;
-  for (; j + 4 <= k; j += 4) {
-    uint4 v[4][CPL];
-    float s[4];
+  for (; j + RB <= k; j += RB) {
+    uint4 v[RB][CPL];
+    float s[RB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < RB; ++q) {
       const uint4* src = rows + (int64_t)ro[j + q] * RV + lane;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) v[q][c] = src[c * 64];
+      for (int c = 0; c < CPL; ++c) {
+        const u32x4l x = __builtin_nontemporal_load((const u32x4l*)(src + c * 64));
+        v[q][c] = uint4{x[0], x[1], x[2], x[3]};
+      }
       s[q] = w ? w[(int64_t)t * k + j + q] : 1.0f;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < RB; ++q)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         float f[N];
@@ -290,9 +321,20 @@ hipError_t launch_swiglu_bwd(const LaunchCtx& c, const void* G, const void* H, c
 }
 
 hipError_t launch_permute(const LaunchCtx& c, const char* name, int dtype, const void* x,
-                          const int32_t* src_of,
+                          const int32_t* src_of, const int32_t* row_of,
                           int R, int k, int d, void* xp) {
   const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
+  const int T = R / k;
+  if (row_vecs == 256) {
+    MOE_LAUNCH(c, name, permute_scatter_kernel<4>, dim3((T + 3) / 4), dim3(256), 0, (const uint4*)x,
+               row_of, T, k, (uint4*)xp);
+    return hipSuccess;
+  }
+  if (row_vecs == 512) {
+    MOE_LAUNCH(c, name, permute_scatter_kernel<8>, dim3((T + 3) / 4), dim3(256), 0, (const uint4*)x,
+               row_of, T, k, (uint4*)xp);
+    return hipSuccess;
+  }
   MOE_LAUNCH(c, name, permute_kernel, dim3((R + 3) / 4), dim3(256), 0, (const uint4*)x,
              src_of, R, k, row_vecs, (uint4*)xp);
   return hipSuccess;
@@ -302,13 +344,15 @@ hipError_t launch_combine(const LaunchCtx& c, const char* name, int dtype, const
                           const int32_t* row_of, const float* w, int T, int k, int d, void* out) {
   const int row_vecs = d * (dtype == F32 ? 4 : 2) / 16;
   const dim3 grid((T + 3) / 4);
+  // eight rows in flight per lane where a row takes four chunks a lane, four
+  // at eight chunks (register budget)
   if (dtype == BF16 && row_vecs == 256) {
-    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 4>), grid, dim3(256), 0, (const uint4*)rows,
+    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 4, 8>), grid, dim3(256), 0, (const uint4*)rows,
                row_of, w, T, k, (uint4*)out);
     return hipSuccess;
   }
   if (dtype == BF16 && row_vecs == 512) {
-    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 8>), grid, dim3(256), 0, (const uint4*)rows,
+    MOE_LAUNCH(c, name, (combine_wide_kernel<bf16_t, 8, 4>), grid, dim3(256), 0, (const uint4*)rows,
                row_of, w, T, k, (uint4*)out);
     return hipSuccess;
   }

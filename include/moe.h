@@ -229,8 +229,9 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
 
 /* Dispatch alone ("token sorting": "Prime Mega MoE Trains Giant AI Models
  * 55% Faster", section "Where MoE training loses time"): xp[r] =
- * x[src_of[r] / k], xp [T*k, d] (dtype), rows in expert order; reads only
- * routing->src_of (as moe_route wrote it).  x and xp 16-byte aligned. */
+ * x[src_of[r] / k], xp [T*k, d] (dtype), rows in expert order; reads
+ * routing->src_of and routing->row_of (as moe_route wrote them: each token's
+ * row is copied to its k expert-sorted rows).  x and xp 16-byte aligned. */
 moe_status moe_permute(const moe_shape* shape, const void* x,
                        const moe_routing* routing, void* xp, void* stream);
 

@@ -185,3 +185,22 @@ def test_routing_signed_zeros_and_minus_inf(ldt, E, k):
     w = to_np(r.topk_w)
     sel = np.take_along_axis(lg, rt["ids"], axis=1)
     assert np.all(w[np.isinf(sel)] == 0.0) and np.all(w[~np.isinf(sel)] > 0.0)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(4096, 2048, 128, 8), (1000, 4096, 64, 6), (300, 256, 16, 4)])
+def test_permute_bit_exact(T, d, E, k):
+    """moe_permute (dispatch alone) against the oracle's dispatch, every
+    element: rows of 4 and 8 KB take the token scatter (each token's row
+    written to its k expert-sorted rows), other widths the row gather."""
+    dev = torch.device("cuda", 0)
+    print(f"case permute T={T} d={d} E={E} k={k}", flush=True)
+    wl = S.WORKLOADS["q30b"].scaled(T=T, d=d, E=E, k=k)
+    logits = S.make_logits(wl, seed=7)
+    g = np.random.default_rng(7)
+    x = torch.from_numpy(g.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    r = B.route(logits.to(dev), k)
+    xp = B.permute(x.to(dev), r, k)
+    torch.cuda.synchronize()
+    rt = O.route(logits.double().numpy(), k, E)
+    assert np.array_equal(to_np(r.src_of), rt["src_of"])
+    assert np.array_equal(to_np(xp), O.dispatch(x.double().numpy(), rt))

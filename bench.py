@@ -41,6 +41,8 @@ CSRC = os.path.join(HERE, "combine_top_route_amd", "csrc")
 KERNEL_SITES = [
     ("rows_gemm_kernel<1, 1, 0>(", "gemm_gateup_fwd"), ("rows_gemm_kernel<0, 0, 0>(", "gemm_down_fwd"),
     ("rows_gemm_kernel<0, 2, 1>(", "gemm_down_dgrad"), ("rows_gemm_kernel<0, 2, 0>(", "gemm_gateup_dgrad"),
+    ("rows_persist_kernel<1, 1, 0>(", "gemm_gateup_fwd"), ("rows_persist_kernel<0, 0, 0>(", "gemm_down_fwd"),
+    ("rows_persist_kernel<0, 2, 1>(", "gemm_down_dgrad"), ("rows_persist_kernel<0, 2, 0>(", "gemm_gateup_dgrad"),
     ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
     ("rows8_kernel<1, 0, ", "gemm_gateup_fwd"), ("rows8_kernel<0, 0, ", "gemm_down_fwd"),
     ("rows8_kernel<2, 2, ", "gemm_down_dgrad"), ("rows8_kernel<0, 1, ", "gemm_gateup_dgrad"),
@@ -311,6 +313,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the oracle's CPU sample (default: sized for roughly 10-30 s)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--persistent", action="store_true",
+                    help="bf16 row GEMMs as persistent kernels (MOE_FLAG_PERSISTENT)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 1 GiB once (a plain copy kernel of known size "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -336,8 +340,8 @@ def main():
     wgu = inp["w_gate_up"].to(dev)
     wd = inp["w_down"].to(dev)
     dout = inp["dout"].to(dev)
-    layer = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt,
-                       logits_dtype=S.torch_dtype(wl.logits_dtype), precision=wl.precision, device=dev)
+    layer = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt, logits_dtype=S.torch_dtype(wl.logits_dtype),
+                       precision=wl.precision, device=dev, persistent=args.persistent)
 
     def step():
         layer.forward(x, wgu, wd, logits=logits)
@@ -400,7 +404,7 @@ def main():
     del layer
     torch.cuda.empty_cache()
     ac = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=dt, logits_dtype=S.torch_dtype(wl.logits_dtype),
-                    precision=wl.precision, device=dev, save=False)
+                    precision=wl.precision, device=dev, save=False, persistent=args.persistent)
     ac_ms = []
     for i in range(args.warmup + args.steps):
         a, b = ev(), ev()
@@ -466,7 +470,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: MoE layer fwd+bwd, T={wl.T} tokens, d={wl.d}, E={wl.E}, "
                                f"top-{wl.k}, I={wl.I}, {wl.dtype}, {wl.precision}",
-                   "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "I": wl.I, "precision": wl.precision},
+                   "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "I": wl.I, "precision": wl.precision,
+                   "row_gemms": "persistent" if args.persistent else "one tile per work-group"},
         "mfma_util": tflops / mfma_peak(wl),
         "fwd_ms": float(np.median(fwd_ms)),
         "bwd_ms": float(np.median(bwd_ms)),

@@ -30,7 +30,7 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("I", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("logits_dtype", ctypes.c_int32), ("precision", ctypes.c_int32),
-                ("swiglu_limit", ctypes.c_float)]
+                ("swiglu_limit", ctypes.c_float), ("flags", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -106,11 +106,16 @@ def _check(call: str, status: int):
         raise MoeError(call, status)
 
 
+FLAG_PERSISTENT = 1
+
+
 def make_shape(T, d, E, k, I, dtype=torch.bfloat16, logits_dtype=None, precision="native",
-               swiglu_limit=0.0) -> MoeShape:
-    """swiglu_limit > 0: the clamped SwiGLU with that limit (see moe.h)."""
+               swiglu_limit=0.0, persistent=False) -> MoeShape:
+    """swiglu_limit > 0: the clamped SwiGLU with that limit; persistent: the
+    bf16 row GEMMs as persistent kernels (MOE_FLAG_PERSISTENT; see moe.h)."""
     logits_dtype = dtype if logits_dtype is None else logits_dtype
-    return MoeShape(T, d, E, k, I, _DT[dtype], _DT[logits_dtype], _PREC[precision], float(swiglu_limit))
+    return MoeShape(T, d, E, k, I, _DT[dtype], _DT[logits_dtype], _PREC[precision], float(swiglu_limit),
+                    FLAG_PERSISTENT if persistent else 0)
 
 
 def workspace_size(shape: MoeShape, op: int) -> int:
@@ -180,7 +185,7 @@ class MoeLayer:
     (activation checkpointing)."""
 
     def __init__(self, T, d, E, k, I, dtype=torch.bfloat16, logits_dtype=None,
-                 precision="native", device="cuda", save=True, swiglu_limit=0.0):
+                 precision="native", device="cuda", save=True, swiglu_limit=0.0, persistent=False):
         self.T, self.d, self.E, self.k, self.I = T, d, E, k, I
         self.dtype = dtype
         self.logits_dtype = dtype if logits_dtype is None else logits_dtype
@@ -188,7 +193,7 @@ class MoeLayer:
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.device = dev
-        self.shape = make_shape(T, d, E, k, I, dtype, self.logits_dtype, precision, swiglu_limit)
+        self.shape = make_shape(T, d, E, k, I, dtype, self.logits_dtype, precision, swiglu_limit, persistent)
         dev = self.device
         self.ws_fwd = torch.empty(workspace_size(self.shape, OP_FORWARD), dtype=torch.uint8, device=dev)
         self.ws_bwd = torch.empty(workspace_size(self.shape, OP_BACKWARD if save else OP_BACKWARD_RECOMPUTE),

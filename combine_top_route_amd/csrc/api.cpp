@@ -101,6 +101,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->logits_dtype != MOE_F32 && s->logits_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_dtype=%d unknown", s->logits_dtype);
   if (s->precision < MOE_PREC_NATIVE || s->precision > MOE_PREC_FP8_BWD)
     return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
+  if (s->flags & ~MOE_FLAG_PERSISTENT) return fail(MOE_ERR_INVALID_ARGUMENT, "flags=%d has unknown bits", (int)s->flags);
   if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f))
     return fail(MOE_ERR_INVALID_ARGUMENT, "swiglu_limit=%g must be 0 (plain SwiGLU) or a positive finite clamp",
                 (double)s->swiglu_limit);
@@ -363,6 +364,7 @@ LayerArgs layer_args(const moe_shape* s, const moe_routing* r, const void* x, co
   a.xorder = a.order + s->E;
   a.tok_of = L.tok ? (const int32_t*)at(ws, L.tok) : nullptr;  // backward layouts only
   a.swiglu_lim = s->swiglu_limit > 0.0f ? s->swiglu_limit : __builtin_huge_valf();
+  a.persistent = (s->flags & MOE_FLAG_PERSISTENT) != 0;
   return a;
 }
 

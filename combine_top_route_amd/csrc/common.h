@@ -150,6 +150,7 @@ struct LayerArgs {
   const int32_t* xorder;    // [8 ceil(E/8)] weight-gradient slot s of XCD x at 8 s + x (-1: empty)
   const int32_t* tok_of;    // [R] token of each sorted row (backward only)
   float swiglu_lim;         // SwiGLU clamp limit, +inf for the plain SwiGLU
+  bool persistent;          // bf16 row GEMMs as persistent kernels
 };
 
 // Forward GEMMs write H [R,2I] (gate|up, may be null), Aw [R,I] = w_row *

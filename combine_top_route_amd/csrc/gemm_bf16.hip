@@ -33,6 +33,8 @@
 #include "common.h"
 #include "tile.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 using namespace tile;
@@ -281,39 +283,26 @@ __device__ __forceinline__ void issue_stage(const OA& oa, const OB& ob, int kt, 
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 
-// ---------------------------------------------------------------------------
-// Main loop.  Per K step: wait for this wave's loads of the step, barrier
-// (all waves' loads landed, everybody done with the slot to be refilled),
-// then four 16-k sub-steps; the first issues all of the next step's loads,
-// and each reads the fragments of the next sub-step while its MFMAs run.
-// Steps are instantiated by whether they load a next stage (PRE) and whether
-// that stage needs bounds checks (!FULL), so the steady-state body has no
-// branches: the leading full stages run first, the checked tail after.
-//
-// Where the next stage's loads leave: the compiler cannot tell the
-// transposing LDS read (ds_read_b64_tr_b16) apart from the slot the direct
-// loads are filling, so it makes any such read wait for all direct loads in
-// flight.  No transposed read may therefore follow the loads within a step:
-// with only B transposed, the step's B fragments (two tiles) are all read
-// first and the loads leave at the start; with both transposed, the loads
-// leave right after the step's last fragment read (in the next-to-last
-// sub-step, which prefetches the last one's).
-// ---------------------------------------------------------------------------
-template <int TMX, bool PRE, bool FULL, class OA, class OB>
-__device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
-                                      f32x16_t (&acc)[TMX][TN]) {
-  constexpr int ST = OA::BYTES + OB::BYTES;
+// One K step.  SS is the byte distance between the ring's two slots (0: one
+// stage apart).  IS issues the next stage: IS::early() runs right after the
+// step's barrier, IS::issue(dst) in sub-step IK (-1: where the step's reads
+// allow, as below).
+template <int TMX, bool PRE, int SS, int IK, class OA, class OB, class IS>
+__device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x16_t (&acc)[TMX][TN]) {
+  constexpr int ST = SS ? SS : OA::BYTES + OB::BYTES;
   constexpr int NKK = BK / 16;
   // only B transposed (the data gradients): all of the step's B fragments
   // are read before the loads leave at the start; A and B transposed (the
   // weight gradients): the loads leave in the next-to-last sub-step, right
   // after it has read the last sub-step's fragments
   constexpr bool B_FIRST = OB::TR && !OA::TR;
-  constexpr int ISSUE_KK = OA::TR ? NKK - 2 : 0;
+  constexpr int ISSUE_KK = IK >= 0 ? IK : (OA::TR ? NKK - 2 : 0);
+  static_assert(IK < 0 || !OA::TR || IK >= NKK - 2, "no transposed read after the loads");
   constexpr int NB = B_FIRST ? NKK : 2;
   const int wm = wave_m(), wn = wave_n();
   wait_vmcnt<0>();
   barrier_lds();
+  if constexpr (PRE) is.early();
   lds_t* const dst = base + (slot ^ 1) * ST;
   const lds_t* As = base + slot * ST;
   const lds_t* Bs = As + OA::BYTES;
@@ -342,7 +331,7 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
       }
     }
     if constexpr (PRE) {
-      if (kk == ISSUE_KK) issue_stage<FULL>(oa, ob, kt + 1, dst);
+      if (kk == ISSUE_KK) is.issue(dst);
     }
 #pragma unroll
     for (int i = 0; i < TMX; ++i)
@@ -364,11 +353,28 @@ __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  slot ^= 1;
+}
+
+// The next stage of the tile's own operands.
+template <bool FULL, class OA, class OB>
+struct SelfIssue {
+  const OA& oa;
+  const OB& ob;
+  int kt;
+  __device__ void early() {}
+  __device__ void issue(lds_t* dst) { issue_stage<FULL>(oa, ob, kt + 1, dst); }
+};
+
+template <int TMX, bool PRE, bool FULL, int SS = 0, class OA, class OB>
+__device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
+                                      f32x16_t (&acc)[TMX][TN]) {
+  SelfIssue<FULL, OA, OB> is{oa, ob, kt};
+  kstep_core<TMX, PRE, SS, -1, OA, OB>(is, base, slot, acc);
   if constexpr (PRE) {
     oa.advance();
     ob.advance();
   }
-  slot ^= 1;
 }
 
 // TMX: 32-row MFMA tiles per wave along M (a wave covers 32 TMX rows; the
@@ -432,8 +438,8 @@ constexpr int ep_stride() { return COLS * 2 + 16; }
 // Writes the wave's MFMA tiles i in [0, NI), j in [0, NJ), value v(i, j, r),
 // at tile rows row0.. and columns col0.., four columns (8 bytes) a write.
 template <int NI, int NJ, int S, class V>
-__device__ __forceinline__ void stage_quads(lds_t* t, int row0, int col0, V v) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void stage_quads(lds_t* t, int row0, int col0, V v, int tid = threadIdx.x) {
+  const int lane = tid & 63;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -447,11 +453,16 @@ __device__ __forceinline__ void stage_quads(lds_t* t, int row0, int col0, V v) {
       }
 }
 
+struct RowId {
+  __device__ int operator()(int r) const { return r; }
+};
+
 // Copies the staged ROWS x COLS tile to C (leading dimension ldc elements):
-// rows >= row_lim and columns >= col_lim are skipped.
-template <int ROWS, int COLS, int S>
+// staged row s is row map(s) of C; rows >= row_lim and columns >= col_lim
+// are skipped.
+template <int ROWS, int COLS, int S, class M = RowId>
 __device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t ldc, int row_lim,
-                                              int col_lim) {
+                                              int col_lim, M map = M(), int tid = threadIdx.x) {
   constexpr int CPR = COLS / 8;  // 16-byte chunks per row
   constexpr int NQ = ROWS * CPR / NTHR;
   static_assert(ROWS * CPR % NTHR == 0, "whole chunks per thread");
@@ -459,13 +470,13 @@ __device__ __forceinline__ void lds_to_global(const lds_t* t, bf16_t* C, int64_t
   u32x4_t v[NQ];
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int q = threadIdx.x + i * NTHR;
+    const int q = tid + i * NTHR;
     v[i] = *(const __attribute__((address_space(3))) u32x4_t*)(t + (q / CPR) * S + (q % CPR) * 16);
   }
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int q = threadIdx.x + i * NTHR;
-    const int row = q / CPR, c8 = q % CPR;
+    const int q = tid + i * NTHR;
+    const int row = map(q / CPR), c8 = q % CPR;
     if (row < row_lim && c8 * 8 < col_lim)  // streamed out: no L2 line kept for the output
       __builtin_nontemporal_store(v[i], (u32x4_t*)(C + (int64_t)row * ldc + c8 * 8));
   }
@@ -507,51 +518,37 @@ struct RowsArgs {
   const int32_t* src_of;
 };
 
-// One row tile: ROWS = 256, or 128 / 64 for a segment's last tile when it
-// holds at most that many rows (the waves then take 64 / 32 rows each: a
-// half / a quarter of the MFMA work and of the A operand, where a full tile
-// would spend most of it on rows past the segment).
-template <int EPI, int BL, int ROWS>
-__device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt, int e, int m0, int seg1) {
-  constexpr int TMX = ROWS / WM / 32;
-  const int seg0 = m0;  // rows past the segment repeat the tile's first row
-  const int lane = threadIdx.x & 63;
-  const int wm = wave_m(), wn = wave_n();
-
-  // The loads whose results the prologue needs leave together: the gate/up
-  // epilogue's row weights (flat entry first; the main loop hides the
-  // second, dependent load) and the gathered A rows.  Address math between
-  // loads made the compiler wait for each before issuing the next.
-  int wsrc = 0;
-  if constexpr (EPI == EPI_GATEUP) {
-    if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < seg1) wsrc = p.src_of[m0 + threadIdx.x] + 1;
-  }
-  constexpr int NIA = OpMK<ROWS>::NI;
-  int arow[NIA];
+// Rows of a row tile that instruction i of OpMK<ROWS> loads: through a_src
+// (the gather) or plain; rows past the segment repeat the tile's first row
+// (computed, never stored).
+template <int ROWS>
+__device__ __forceinline__ void fetch_arow(const RowsArgs& p, int m0, int seg1, int (&arow)[OpMK<ROWS>::NI]) {
 #pragma unroll
-  for (int i = 0; i < NIA; ++i) {
+  for (int i = 0; i < OpMK<ROWS>::NI; ++i) {
     int r = m0 + OpMK<ROWS>::lane_row(i);
-    if (r >= seg1) r = seg0;  // rows past the segment: computed, never stored
+    if (r >= seg1) r = m0;
     arow[i] = p.a_src ? p.a_src[r] : r;
   }
-  float wrow = 0.0f;
-  if constexpr (EPI == EPI_GATEUP) {
-    if (wsrc) wrow = p.topk_w[wsrc - 1];
-  }
-  OpMK<ROWS> oa;
+}
+
+template <int ROWS>
+__device__ __forceinline__ void init_a(const RowsArgs& p, OpMK<ROWS>& oa, const int (&arow)[OpMK<ROWS>::NI]) {
   oa.init([&](int i, int) {
     const int64_t ar = p.a_src ? (int64_t)(arow[i] / p.a_div) : (int64_t)arow[i];
     return p.A + ar * p.lda;
   }, p.K);
+}
+
+// The B operand of expert e's N tile nt.
+template <int BL> struct BOperand { using type = OpMK<TBN>; };
+template <> struct BOperand<B_KM> { using type = OpKM<TBN>; };
+
+template <int BL>
+__device__ __forceinline__ void init_b(const RowsArgs& p, typename BOperand<BL>::type& ob, int e, int nt) {
   const bf16_t* Be = p.B + (int64_t)e * p.b_estride;
-  f32x16_t acc[TMX][TN];
-  const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
-    OpKM<TBN> ob;
     ob.init(Be, p.ldb, nt * TBN, p.N, p.K);
-    mainloop<TMX>(oa, ob, nk, smem, acc);
   } else {
-    OpMK<TBN> ob;
     ob.init([&](int, int n) {
       int wrow;
       if constexpr (BL == B_MK_GATEUP) {
@@ -565,8 +562,44 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
       }
       return Be + (int64_t)wrow * p.ldb;
     }, p.K);
-    mainloop<TMX>(oa, ob, nk, smem, acc);
   }
+}
+
+// 1 + the flat (token, slot) entry of tile row threadIdx.x, 0 for none: the
+// gate/up epilogue's row weight is topk_w at that entry.
+template <int ROWS>
+__device__ __forceinline__ int fetch_wsrc(const RowsArgs& p, int m0, int seg1) {
+  return threadIdx.x < ROWS && m0 + (int)threadIdx.x < seg1 ? p.src_of[m0 + threadIdx.x] + 1 : 0;
+}
+
+// One row tile: ROWS = 256, or 128 / 64 for a segment's last tile when it
+// holds at most that many rows (the waves then take 64 / 32 rows each: a
+// half / a quarter of the MFMA work and of the A operand, where a full tile
+// would spend most of it on rows past the segment).
+template <int EPI, int BL, int ROWS>
+__device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt, int e, int m0, int seg1) {
+  constexpr int TMX = ROWS / WM / 32;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave_m(), wn = wave_n();
+
+  // The loads whose results the prologue needs leave together: the gate/up
+  // epilogue's row weights (flat entry first; the main loop hides the
+  // second, dependent load) and the gathered A rows.  Address math between
+  // loads made the compiler wait for each before issuing the next.
+  int wsrc = 0;
+  if constexpr (EPI == EPI_GATEUP) wsrc = fetch_wsrc<ROWS>(p, m0, seg1);
+  int arow[OpMK<ROWS>::NI];
+  fetch_arow<ROWS>(p, m0, seg1, arow);
+  float wrow = 0.0f;
+  if constexpr (EPI == EPI_GATEUP) {
+    if (wsrc) wrow = p.topk_w[wsrc - 1];
+  }
+  OpMK<ROWS> oa;
+  init_a<ROWS>(p, oa, arow);
+  typename BOperand<BL>::type ob;
+  init_b<BL>(p, ob, e, nt);
+  f32x16_t acc[TMX][TN];
+  mainloop<TMX>(oa, ob, (int)cdiv(p.K, BK), smem, acc);
 
   // ------------------------------------------------------------- epilogues
   // The LDS ring is free once every wave has left the main loop.
@@ -609,6 +642,29 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
   }
 }
 
+struct RowTile {
+  int e, nt, m0, seg1;
+};
+
+// Logical tile L: an expert's (row tile, N tile) pairs are a contiguous
+// range of L, taken N-tile-major (work-groups that run close together share
+// a weight tile through L2); the descriptor of L's row-tile-major row tile
+// lies in the same expert and gives the range.
+__device__ __forceinline__ RowTile decode_tile(const RowsArgs& p, int L) {
+  const int T = L / p.n_tiles;
+  const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
+  const int first = d0.w;
+  const int seg0 = d0.y - (T - first) * TBM;
+  const int nrt = (d0.z - seg0 + TBM - 1) / TBM;
+  const int j = L - first * p.n_tiles;
+  RowTile t;
+  t.e = d0.x;
+  t.seg1 = d0.z;
+  t.nt = j / nrt;
+  t.m0 = seg0 + (j - t.nt * nrt) * TBM;
+  return t;
+}
+
 // TAG only tells launch sites with the same epilogue and B layout apart in
 // profiles.
 template <int EPI, int BL, int TAG>
@@ -616,22 +672,191 @@ __global__ __launch_bounds__(NTHR, 1) void rows_gemm_kernel(RowsArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
   if (L < 0) return;
-  // An expert's (row tile, N tile) pairs are a contiguous range of L, taken
-  // N-tile-major (work-groups that start close together share a weight tile
-  // through L2); the descriptor of L's row-tile-major row tile lies in the
-  // same expert and gives the range.
-  const int T = L / p.n_tiles;
-  const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
-  const int e = d0.x, seg1 = d0.z, first = d0.w;
-  const int seg0 = d0.y - (T - first) * TBM;
-  const int nrt = (seg1 - seg0 + TBM - 1) / TBM;
-  const int j = L - first * p.n_tiles;
-  const int nt = j / nrt;
-  const int m0 = seg0 + (j - nt * nrt) * TBM;
+  const RowTile t = decode_tile(p, L);
+  const int e = t.e, nt = t.nt, m0 = t.m0, seg1 = t.seg1;
   const int rows = seg1 - m0;
   if (rows <= TBM / 4) rows_tile<EPI, BL, TBM / 4>(p, smem, nt, e, m0, seg1);
   else if (rows <= TBM / 2) rows_tile<EPI, BL, TBM / 2>(p, smem, nt, e, m0, seg1);
   else rows_tile<EPI, BL, TBM>(p, smem, nt, e, m0, seg1);
+}
+
+// ===========================================================================
+// Persistent ragged-M GEMM: one work-group per CU walks its XCD's tiles
+// (the same contiguous eighth of the launch's tiles as above, dealt
+// round-robin to the XCD's work-groups), all at full height.  The first
+// stage of the next tile - its gathered token rows and its weight slice -
+// is issued in the current tile's last K step, so it loads while that
+// step's MFMAs run and while the epilogue stages and stores; the next tile
+// starts on a landed stage.  This is the one-GPU form of a persistent
+// kernel that moves the next token group while it computes on the current
+// one ("Prime Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster",
+// section "One kernel overlaps the pipeline").
+//
+// LDS: slot 0 at [0, 64K), slot 1 at [96K, 160K).  The 32 KB between them
+// joins the slot the last step read to give the epilogue a 96 KB staging
+// area that the next tile's first stage, in the other slot, never touches.
+// ===========================================================================
+constexpr int kPSlot = 96 * 1024;
+constexpr size_t kPSmem = (size_t)kPSlot + (size_t)(TBM + TBN) * BK * 2;
+static_assert(kPSmem <= 160 * 1024, "LDS");
+
+// Issues the next tile's first stage (if there is one: `more`) in the
+// current tile's last K step: its row indices (and the gate/up epilogue's
+// row-weight entries) load right after the step's barrier, its direct loads
+// leave in the last sub-step, bounds-checked (once per tile: one form of the
+// step serves every tile).  oa / ob become the next tile's operands,
+// advanced past that stage.
+template <int EPI, int BL>
+struct NextIssue {
+  const RowsArgs& p;
+  const RowTile& t;
+  bool more;
+  OpMK<TBM>& oa;
+  typename BOperand<BL>::type& ob;
+  float& wrow;
+  int arow[OpMK<TBM>::NI];
+  int wsrc;
+  __device__ void early() {
+    if (!more) return;
+    fetch_arow<TBM>(p, t.m0, t.seg1, arow);
+    if constexpr (EPI == EPI_GATEUP) wsrc = fetch_wsrc<TBM>(p, t.m0, t.seg1);
+  }
+  __device__ void issue(lds_t* dst) {
+    if (!more) return;
+    init_a<TBM>(p, oa, arow);
+    init_b<BL>(p, ob, t.e, t.nt);
+    issue_stage<false>(oa, ob, 0, dst);
+    oa.advance();
+    ob.advance();
+    if constexpr (EPI == EPI_GATEUP) wrow = wsrc ? p.topk_w[wsrc - 1] : 0.0f;
+  }
+};
+
+// threadIdx.x, taken afresh: values derived from it in a tile's epilogue
+// are not hoisted out of the persistent loop (where they would stay live
+// through the main loop).
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Epilogue of a full-height tile, staged inside the 96 KB area beside slot
+// `last ^ 1` (which holds the next tile's first stage).
+template <int EPI>
+__device__ __forceinline__ void persist_epilogue(const RowsArgs& p, const RowTile& t, lds_t* base, int last,
+                                                 f32x16_t (&acc)[TM][TN], float wrow) {
+  const int tid = fresh_tid(), lane = tid & 63;
+  const int wm = (tid >> 6) / WN, wn = (tid >> 6) % WN;
+  const int rows_valid = t.seg1 - t.m0;
+  if constexpr (EPI == EPI_STORE) {
+    // two rounds of 128 rows: round h holds the waves' MFMA row tiles 2h and
+    // 2h + 1, so staged row s is tile row (s / 64) * 128 + 64 h + s % 64
+    constexpr int S = ep_stride<TBN>();
+    static_assert(128 * S <= kPSlot && 64 * 1024 + 128 * S <= (int)kPSmem, "staging area beside either slot");
+    lds_t* const stg = base + (last ? 64 * 1024 : 0);
+    bf16_t* const C0 = p.C + (int64_t)t.m0 * p.ldc + t.nt * TBN;
+    barrier_lds();  // every wave is done with the last step's slot
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h) barrier_lds();
+      stage_quads<2, TN, S>(stg, wm * 64, wn * (TBN / WN), [&](int i, int j, int r) { return acc[2 * h + i][j][r]; }, tid);
+      barrier_lds();
+      lds_to_global<128, TBN, S>(stg, C0, p.ldc, rows_valid, p.N - t.nt * TBN,
+                                 [h](int s) { return (s >> 6) * 128 + h * 64 + (s & 63); }, tid);
+    }
+  } else {
+    // three rounds of 256 x 128: Aw, then H's gate and up columns; the row
+    // weights sit in the 32 KB gap, clear of both the staged tile and the
+    // slots, so they are written before the first barrier
+    constexpr int S = ep_stride<TBN / 2>();
+    constexpr int TB = TBM * S;
+    static_assert(TB + 1024 <= kPSlot && 65 * 1024 + TB <= (int)kPSmem, "staging area beside either slot");
+    lds_t* const stg = base + (last ? 65 * 1024 : 0);
+    lds_f32_t* const wl = (lds_f32_t*)(base + (last ? 64 * 1024 : TB));
+    if (tid < TBM) wl[tid] = wrow;
+    barrier_lds();
+    const int r0w = wm * (TBM / WM), c0w = wn * 32;
+    const int gc0 = t.nt * (TBN / 2);
+    stage_quads<TM, 1, S>(stg, r0w, c0w, [&](int i, int, int r) {
+      const float g = clamp_gate(acc[i][0][r], p.lim), u = clamp_up(acc[i][1][r], p.lim);
+      return wl[r0w + acc_row(i, lane)] * (g * sigmoidf_(g) * u);
+    }, tid);
+    barrier_lds();
+    lds_to_global<TBM, TBN / 2, S>(stg, p.Aout + (int64_t)t.m0 * p.I + gc0, p.I, rows_valid, p.I - gc0, RowId(), tid);
+    if (p.H) {
+      bf16_t* H0 = p.H + (int64_t)t.m0 * 2 * p.I + gc0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        barrier_lds();
+        stage_quads<TM, 1, S>(stg, r0w, c0w, [&](int i, int, int r) { return acc[i][h][r]; }, tid);
+        barrier_lds();
+        lds_to_global<TBM, TBN / 2, S>(stg, H0 + h * p.I, 2 * p.I, rows_valid, p.I - gc0, RowId(), tid);
+      }
+    }
+  }
+}
+
+template <int EPI, int BL, int TAG>
+__global__ __launch_bounds__(NTHR, 1) void rows_persist_kernel(RowsArgs p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  using OB = typename BOperand<BL>::type;
+  const int real = p.tile_off[p.E] * p.n_tiles;
+  const int per = (real + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int P = (int)(gridDim.x >> 3);  // work-groups per XCD
+  const int end = min(xcd * per + per, real);
+  int L = xcd * per + (int)(blockIdx.x >> 3);
+  if (L >= end) return;
+  lds_t* const base = (lds_t*)smem;
+  const int nk = (int)cdiv(p.K, BK);  // >= 1 (the host launches K >= 1 only)
+  RowTile t = decode_tile(p, L);
+  OpMK<TBM> oa;
+  OB ob;
+  float wrow = 0.0f;
+  {  // the first tile's first stage
+    int wsrc = 0;
+    if constexpr (EPI == EPI_GATEUP) wsrc = fetch_wsrc<TBM>(p, t.m0, t.seg1);
+    int arow[OpMK<TBM>::NI];
+    fetch_arow<TBM>(p, t.m0, t.seg1, arow);
+    if constexpr (EPI == EPI_GATEUP) {
+      if (wsrc) wrow = p.topk_w[wsrc - 1];
+    }
+    init_a<TBM>(p, oa, arow);
+    init_b<BL>(p, ob, t.e, t.nt);
+    issue_stage<false>(oa, ob, 0, base);
+    oa.advance();
+    ob.advance();
+  }
+  int slot = 0;
+  for (;;) {
+    const int Ln = L + P;
+    const bool more = Ln < end;
+    const RowTile tn = decode_tile(p, more ? Ln : L);
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int nfa = oa.nfull(nk), nfb = ob.nfull(nk);
+    const int nf = nfa < nfb ? nfa : nfb;
+    int kt = 0;
+    for (; kt + 1 < nf; ++kt) kstep<TM, true, true, kPSlot>(oa, ob, kt, base, slot, acc);
+    for (; kt + 1 < nk; ++kt) kstep<TM, true, false, kPSlot>(oa, ob, kt, base, slot, acc);
+    const int last = slot;
+    float wnext = 0.0f;
+    {
+      NextIssue<EPI, BL> is{p, tn, more, oa, ob, wnext};
+      kstep_core<TM, true, kPSlot, BK / 16 - 1, OpMK<TBM>, OB>(is, base, slot, acc);
+    }
+    persist_epilogue<EPI>(p, t, base, last, acc, wrow);
+    if (!more) break;
+    L = Ln;
+    t = tn;
+    wrow = wnext;
+  }
 }
 
 // ===========================================================================
@@ -696,7 +921,7 @@ constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <int EPI, int BL, int TAG = 0>
-hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
+hipError_t launch_rows_tiles(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
   {
     hipError_t e = allow_smem_once<rows_gemm_kernel<EPI, BL, TAG>>(kSmem);
     if (e != hipSuccess) return e;
@@ -705,6 +930,33 @@ hipError_t launch_rows(const LaunchCtx& c, const char* name, RowsArgs p, int R) 
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
   MOE_LAUNCH(c, name, (rows_gemm_kernel<EPI, BL, TAG>), dim3(nblocks), dim3(NTHR), kSmem, p);
+  return hipSuccess;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The persistent form: one work-group per CU, at most as many per XCD as
+// the XCD can have tiles.
+template <int EPI, int BL, int TAG = 0>
+hipError_t launch_rows_persist(const LaunchCtx& c, const char* name, RowsArgs p, int R) {
+  {
+    hipError_t e = allow_smem_once<rows_persist_kernel<EPI, BL, TAG>>(kPSmem);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;  // upper bound of the tile count
+  const int64_t per_xcd = std::min<int64_t>(std::max(cu_count() / 8, 1), cdiv(tiles, 8));
+  MOE_LAUNCH(c, name, (rows_persist_kernel<EPI, BL, TAG>), dim3((unsigned)(8 * per_xcd)), dim3(NTHR), kPSmem, p);
   return hipSuccess;
 }
 
@@ -721,6 +973,13 @@ hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p
 
 }  // namespace
 
+// Row GEMMs: the persistent form on request (K >= 1 always holds here).
+template <int EPI, int BL, int TAG = 0>
+hipError_t launch_rows(const LaunchCtx& c, const char* name, const RowsArgs& p, int R, bool persistent) {
+  if (persistent && p.K >= 1) return launch_rows_persist<EPI, BL, TAG>(c, name, p, R);
+  return launch_rows_tiles<EPI, BL, TAG>(c, name, p, R);
+}
+
 int bf16_dw_blocks(int) { return 1; }
 
 hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void* Aw, void* Yw) {
@@ -733,7 +992,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I; p.lim = a.swiglu_lim;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
-    hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R);
+    hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R, a.persistent);
     if (err != hipSuccess) return err;
   }
   if (!Yw) return hipSuccess;  // the gate/up half alone (recomputation)
@@ -744,7 +1003,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
   q.B = (const bf16_t*)a.w_down; q.b_estride = d * I; q.ldb = I;
   q.N = a.d; q.K = a.I; q.n_tiles = (int)cdiv(a.d, TBN);
   q.C = (bf16_t*)Yw; q.ldc = d;
-  return launch_rows<EPI_STORE, B_MK>(c, "gemm_down_fwd", q, a.R);
+  return launch_rows<EPI_STORE, B_MK>(c, "gemm_down_fwd", q, a.R, a.persistent);
 }
 
 hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* dout,
@@ -761,7 +1020,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.C = G; p.ldc = I;
-    err = launch_rows<EPI_STORE, B_KM, 1>(c, "gemm_down_dgrad", p, a.R);
+    err = launch_rows<EPI_STORE, B_KM, 1>(c, "gemm_down_dgrad", p, a.R, a.persistent);
     if (err != hipSuccess) return err;
     err = launch_swiglu_bwd(c, G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, dH, dwp);
     if (err != hipSuccess) return err;
@@ -783,7 +1042,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
-    err = launch_rows<EPI_STORE, B_KM>(c, "gemm_gateup_dgrad", p, a.R);
+    err = launch_rows<EPI_STORE, B_KM>(c, "gemm_gateup_dgrad", p, a.R, a.persistent);
     if (err != hipSuccess) return err;
   }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]

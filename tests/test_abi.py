@@ -98,6 +98,11 @@ def test_bad_enums_rejected():
         assert _status(s)[0] == 1 and b"swiglu_limit" in B.lib().moe_last_error()
     s = _shape(swiglu_limit=7.0)
     assert _status(s)[0] == 0
+    for bad in (2, -1, 1 << 30):                        # flags: MOE_FLAG_PERSISTENT only
+        s = _shape()
+        s.flags = bad
+        assert _status(s)[0] == 1 and b"flags" in B.lib().moe_last_error()
+    assert _status(_shape(persistent=True))[0] == 0
 
 
 def test_fp8_requirements():

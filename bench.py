@@ -49,9 +49,10 @@ KERNEL_SITES = [
     ("wgrad8_kernel<0, ", "gemm_down_wgrad"), ("wgrad8_kernel<1, ", "gemm_gateup_wgrad"),
     ("combine_wide_kernel<", "combine + reduce_dx"), ("combine_kernel<", "combine + reduce_dx"),
     ("topk_lane_kernel<", "route_topk"), ("topk_kernel<", "route_topk"), ("count_kernel", "route_count"),
+    ("permute_kernel", "permute"), ("permute_scatter_kernel", "permute"),  # before route's scatter_kernel
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
     ("tok_of_kernel", "route_tok"),
-    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("permute_kernel", "permute"), ("permute_scatter_kernel", "permute"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
+    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
     ("quant_weight_kernel", "quant_w_*"), ("quant_weight_mx_kernel", "quant_w_*"),
     ("quant_tok_kernel", "quant_*_tok"),
 ]
@@ -234,7 +235,8 @@ def _csv_rows(d: str, suffix: str):
     return rows
 
 
-def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, write_dir: str | None = None):
+def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, write_dir: str | None = None,
+                    flags: str = ""):
     """Markdown summary of rocprofv3 output: per-kernel durations from
     --kernel-trace --stats and, given two --pmc runs (FETCH_SIZE, WRITE_SIZE),
     HBM bytes per launch scaled by the same counters on the 1 GiB copy."""
@@ -243,12 +245,12 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
              f"I={wl.I}, {wl.dtype}, {wl.precision})", "",
              "Commands (repository root, TMPDIR=/tmp):", "",
              f"    rocprofv3 --kernel-trace --stats --output-format csv -d {stats_dir} -o {n} -- "
-             f"python3 bench.py --workload {n} --steps 5 --warmup 2 --no-cpu"]
+             f"python3 bench.py --workload {n} --steps 5 --warmup 2 --no-cpu{flags}"]
     if fetch_dir and write_dir:
         for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             lines.append(f"    rocprofv3 --pmc {key} --output-format csv -d {d} -o {n} -- python3 bench.py "
-                         f"--workload {n} --steps 2 --warmup 1 --no-cpu --copy-calibration")
-    lines += [f"    python3 bench.py --workload {n} --rocprof-summary {out} {stats_dir}"
+                         f"--workload {n} --steps 2 --warmup 1 --no-cpu --copy-calibration{flags}")
+    lines += [f"    python3 bench.py --workload {n}{flags} --rocprof-summary {out} {stats_dir}"
               + (f" {fetch_dir} {write_dir}" if fetch_dir and write_dir else ""), ""]
     stats = _csv_rows(stats_dir, "kernel_stats.csv")
     lines += ["Kernel durations (rocprofv3 --kernel-trace --stats):", "",
@@ -323,7 +325,8 @@ def main():
                          "--kernel-trace --stats output (and of two --pmc runs) for --workload")
     args = ap.parse_args()
     if args.rocprof_summary:
-        rocprof_summary(S.WORKLOADS[args.workload], *args.rocprof_summary)
+        rocprof_summary(S.WORKLOADS[args.workload], *args.rocprof_summary,
+                        flags=" --persistent" if args.persistent else "")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the layer: this build runs on exactly one GPU "

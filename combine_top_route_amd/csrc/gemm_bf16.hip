@@ -420,6 +420,108 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
   kstep<TMX, false, false>(oa, ob, kt, base, slot, acc);
 }
 
+// ---------------------------------------------------------------------------
+// Five-slot ring for the forward GEMMs, whose operands are both
+// K-contiguous: five 32 KB slots of half stages, the weight slice (B) two K
+// steps ahead and the token rows (A) one.  B_k sits in slot 2k mod 5 and
+// A_k in slot 2k+1 mod 5; step k computes on slots s = 2k mod 5 and s+1 and
+// issues A_{k+1} into slot s+3 and B_{k+2} into slot s+4, which held step
+// k-1's operands (free after this step's barrier).  Against the two-stage
+// ring this keeps half a stage more in flight in the same 160 KB, with one
+// barrier per step.  Step k waits until only B_{k+1}'s loads are
+// outstanding (loads complete in issue order): A_k and B_k have landed.
+// CHK: the steady-state stages need bounds checks (K is not a multiple of
+// the step).
+// ---------------------------------------------------------------------------
+constexpr int kSlot5 = 32 * 1024;
+__device__ __forceinline__ int mod5(int v) { return v >= 5 ? v - 5 : v; }
+
+template <int TMX, bool WAIT_B, bool PRE_A, bool PRE_B, bool FULL, class OA, class OB>
+__device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& s, f32x16_t (&acc)[TMX][TN]) {
+  static_assert(OA::BYTES <= kSlot5 && OB::BYTES <= kSlot5 && !OA::TR && !OB::TR, "five-slot ring operands");
+  constexpr int NKK = BK / 16;
+  const int wm = wave_m(), wn = wave_n();
+  if constexpr (WAIT_B) wait_vmcnt<OB::NI>();
+  else wait_vmcnt<0>();
+  barrier_lds();
+  const lds_t* Bs = base + s * kSlot5;
+  const lds_t* As = base + mod5(s + 1) * kSlot5;
+  lds_t* const da = base + mod5(s + 3) * kSlot5;
+  lds_t* const db = base + mod5(s + 4) * kSlot5;
+  bf16x8_t a[2][TMX], b[2][TN];
+#pragma unroll
+  for (int i = 0; i < TMX; ++i) a[0][i] = OA::frag(As, wm * (TMX * 32) + i * 32, 0);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int cur = kk & 1;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (kk + 1 < NKK) {
+#pragma unroll
+      for (int i = 0; i < TMX; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TMX * 32) + i * 32, kk + 1);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
+    }
+    if (kk == 0) {
+      if constexpr (PRE_A) {
+        oa.template issue<0, OA::NI, FULL>(k + 1, da);
+        oa.advance();
+      }
+      if constexpr (PRE_B) {
+        ob.template issue<0, OB::NI, FULL>(k + 2, db);
+        ob.advance();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TMX; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cur][j], a[cur][i], acc[i][j], 0, 0, 0);
+    const int NR = kk + 1 < NKK ? TMX + TN : 0;
+    const int NG = kk == 0 ? (PRE_A ? OA::NI : 0) + (PRE_B ? OB::NI : 0) : 0;
+#pragma unroll
+    for (int q = 0; q < TMX * TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      if (q * 2 + 1 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+      else if (q * 2 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  s = mod5(s + 2);
+}
+
+template <int TMX, bool CHK, class OA, class OB>
+__device__ __forceinline__ void mainloop5(OA& oa, OB& ob, int nk, char* smem, f32x16_t (&acc)[TMX][TN]) {
+#pragma unroll
+  for (int i = 0; i < TMX; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (nk <= 0) return;
+  lds_t* const base = (lds_t*)smem;
+  // prologue: B_0 (slot 0), A_0 (slot 1), B_1 (slot 2); with !CHK every
+  // stage is whole
+  ob.template issue<0, OB::NI, !CHK>(0, base);
+  ob.advance();
+  oa.template issue<0, OA::NI, !CHK>(0, base + kSlot5);
+  oa.advance();
+  if (nk > 1) {
+    ob.template issue<0, OB::NI, !CHK>(1, base + 2 * kSlot5);
+    ob.advance();
+  }
+  int s = 0, k = 0;
+  for (; k + 2 < nk; ++k) kstep5<TMX, true, true, true, !CHK>(oa, ob, k, base, s, acc);
+  if (k + 1 < nk) {
+    kstep5<TMX, true, true, false, !CHK>(oa, ob, k, base, s, acc);
+    ++k;
+  }
+  kstep5<TMX, false, false, false, false>(oa, ob, k, base, s, acc);
+}
+
 // Accumulator layout.  The MFMAs take the B fragment as their first
 // operand, so tile (i, j) holds the transpose of the usual output: lane l
 // has row i * 32 + (l & 31) of the wave tile, and register r its column
@@ -599,7 +701,13 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
   typename BOperand<BL>::type ob;
   init_b<BL>(p, ob, e, nt);
   f32x16_t acc[TMX][TN];
-  mainloop<TMX>(oa, ob, (int)cdiv(p.K, BK), smem, acc);
+  const int nk = (int)cdiv(p.K, BK);
+  if constexpr (BL == B_KM) {
+    mainloop<TMX>(oa, ob, nk, smem, acc);
+  } else {  // the forward GEMMs: both operands K-contiguous
+    if (p.K % BK == 0) mainloop5<TMX, false>(oa, ob, nk, smem, acc);
+    else mainloop5<TMX, true>(oa, ob, nk, smem, acc);
+  }
 
   // ------------------------------------------------------------- epilogues
   // The LDS ring is free once every wave has left the main loop.
@@ -917,7 +1025,7 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kRingBytes = (size_t)NSTAGE * (TBM + TBN) * BK * 2;
 constexpr size_t kStoreEpi = (size_t)TBM * ep_stride<TBN>();
 constexpr size_t kGateupEpi = (size_t)2 * TBM * ep_stride<TBN / 2>() + TBM * 4;
-constexpr size_t kSmem = cmax(kRingBytes, cmax(kStoreEpi, kGateupEpi));
+constexpr size_t kSmem = cmax(cmax(kRingBytes, (size_t)5 * kSlot5), cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
 template <int EPI, int BL, int TAG = 0>

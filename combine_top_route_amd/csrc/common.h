@@ -46,8 +46,19 @@ __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rc
 // * clamp(u, -lim, lim).  lim = +inf gives the plain SwiGLU, bit for bit
 // (min and max with +-inf leave finite values unchanged).  In the backward
 // a gradient passes only where its clamp is inactive (at lim inclusive).
-__device__ __forceinline__ float clamp_gate(float g, float lim) { return fminf(g, lim); }
-__device__ __forceinline__ float clamp_up(float u, float lim) { return fminf(fmaxf(u, -lim), lim); }
+// One median-of-three each (v_med3_f32): fminf / fmaxf in IEEE mode cost a
+// canonicalising max per operand on top of the min and max themselves.  The
+// gate's lower bound -inf comes from an opaque move: with a literal -inf the
+// compiler turns the median back into that min-with-canonicalise pair.
+__device__ __forceinline__ float opaque_neg_inf() {
+  float v;
+  asm("s_mov_b32 %0, 0xff800000" : "=s"(v));
+  return v;
+}
+__device__ __forceinline__ float clamp_gate(float g, float lim) {
+  return __builtin_amdgcn_fmed3f(g, opaque_neg_inf(), lim);
+}
+__device__ __forceinline__ float clamp_up(float u, float lim) { return __builtin_amdgcn_fmed3f(u, -lim, lim); }
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -283,41 +283,34 @@ __device__ __forceinline__ void issue_stage(const OA& oa, const OB& ob, int kt, 
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
 
-// One K step.  SS is the byte distance between the ring's two slots (0: one
-// stage apart).  IS issues the next stage: IS::early() runs right after the
-// step's barrier, IS::issue(dst) in sub-step IK (-1: where the step's reads
-// allow, as below).
-template <int TMX, bool PRE, int SS, int IK, class OA, class OB, class IS>
-__device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x16_t (&acc)[TMX][TN]) {
-  constexpr int ST = SS ? SS : OA::BYTES + OB::BYTES;
+// One K step: wait for this wave's loads of the step, barrier (every wave's
+// loads have landed and every wave is done with the slot to be refilled),
+// then four 16-k sub-steps, each reading the next sub-step's fragments while
+// its MFMAs run.  SS is the byte distance between the ring's two slots (0:
+// one stage apart).  IS issues the next stage: IS::early() runs right after
+// the barrier, IS::issue(dst) in sub-step IK (the first when IK < 0).
+//
+// The body takes the slot it reads and the slot the loads fill as
+// __restrict__ parameters.  Without that, the compiler cannot tell a
+// transposing LDS read (ds_read_b64_tr_b16) apart from the slot that direct
+// loads are filling, and makes every such read wait for all direct loads in
+// flight; with it, the next stage's loads leave at the start of the step in
+// all six GEMMs and have the whole step to land.
+template <int TMX, bool PRE, int ISSUE_KK, class OA, class OB, class IS>
+__device__ __forceinline__ void kstep_body(IS& is, const lds_t* __restrict__ As, const lds_t* __restrict__ Bs,
+                                           lds_t* __restrict__ dst, f32x16_t (&acc)[TMX][TN]) {
   constexpr int NKK = BK / 16;
-  // only B transposed (the data gradients): all of the step's B fragments
-  // are read before the loads leave at the start; A and B transposed (the
-  // weight gradients): the loads leave in the next-to-last sub-step, right
-  // after it has read the last sub-step's fragments
-  constexpr bool B_FIRST = OB::TR && !OA::TR;
-  constexpr int ISSUE_KK = IK >= 0 ? IK : (OA::TR ? NKK - 2 : 0);
-  static_assert(IK < 0 || !OA::TR || IK >= NKK - 2, "no transposed read after the loads");
-  constexpr int NB = B_FIRST ? NKK : 2;
   const int wm = wave_m(), wn = wave_n();
-  wait_vmcnt<0>();
-  barrier_lds();
   if constexpr (PRE) is.early();
-  lds_t* const dst = base + (slot ^ 1) * ST;
-  const lds_t* As = base + slot * ST;
-  const lds_t* Bs = As + OA::BYTES;
-  bf16x8_t a[2][TMX], b[NB][TN];
+  bf16x8_t a[2][TMX], b[2][TN];
 #pragma unroll
   for (int i = 0; i < TMX; ++i) a[0][i] = OA::frag(As, wm * (TMX * 32) + i * 32, 0);
 #pragma unroll
-  for (int q = 0; q < (B_FIRST ? NKK : 1); ++q)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[q][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, q);
+  for (int j = 0; j < TN; ++j) b[0][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const int cur = kk & 1;
-    const int bc = B_FIRST ? kk : cur;
     // this sub-step's fragments are all in registers before its first MFMA
     // (read during the previous sub-step), so no MFMA below waits on reads
     // issued after it
@@ -325,10 +318,8 @@ __device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x1
     if (kk + 1 < NKK) {
 #pragma unroll
       for (int i = 0; i < TMX; ++i) a[cur ^ 1][i] = OA::frag(As, wm * (TMX * 32) + i * 32, kk + 1);
-      if constexpr (!B_FIRST) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[(cur ^ 1) % NB][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
-      }
+      for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
     }
     if constexpr (PRE) {
       if (kk == ISSUE_KK) is.issue(dst);
@@ -337,12 +328,12 @@ __device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x1
     for (int i = 0; i < TMX; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[bc][j], a[cur][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cur][j], a[cur][i], acc[i][j], 0, 0, 0);
     // one fragment read (and direct load) after each MFMA, so the reads of
     // the next sub-step and the loads of the next stage issue while this
     // sub-step's MFMAs run, and nothing here waits for them
     // (a transposed fragment takes two reads)
-    const int NR = (kk + 1 < NKK ? TMX * (OA::TR ? 2 : 1) + (B_FIRST ? 0 : TN * (OB::TR ? 2 : 1)) : 0);
+    const int NR = (kk + 1 < NKK ? TMX * (OA::TR ? 2 : 1) + TN * (OB::TR ? 2 : 1) : 0);
     const int NG = (PRE && kk == ISSUE_KK) ? OA::NI + OB::NI : 0;
 #pragma unroll
     for (int q = 0; q < TMX * TN; ++q) {
@@ -353,6 +344,15 @@ __device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x1
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+template <int TMX, bool PRE, int SS, int IK, class OA, class OB, class IS>
+__device__ __forceinline__ void kstep_core(IS& is, lds_t* base, int& slot, f32x16_t (&acc)[TMX][TN]) {
+  constexpr int ST = SS ? SS : OA::BYTES + OB::BYTES;
+  wait_vmcnt<0>();
+  barrier_lds();
+  const lds_t* As = base + slot * ST;
+  kstep_body<TMX, PRE, (IK >= 0 ? IK : 0), OA, OB>(is, As, As + OA::BYTES, base + (slot ^ 1) * ST, acc);
   slot ^= 1;
 }
 
@@ -366,6 +366,10 @@ struct SelfIssue {
   __device__ void issue(lds_t* dst) { issue_stage<FULL>(oa, ob, kt + 1, dst); }
 };
 
+// Main loop steps are instantiated by whether they load a next stage (PRE)
+// and whether that stage needs bounds checks (!FULL), so the steady-state
+// body has no branches: the leading full stages run first, the checked tail
+// after.
 template <int TMX, bool PRE, bool FULL, int SS = 0, class OA, class OB>
 __device__ __forceinline__ void kstep(OA& oa, OB& ob, int kt, lds_t* base, int& slot,
                                       f32x16_t (&acc)[TMX][TN]) {

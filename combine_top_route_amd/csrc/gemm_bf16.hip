@@ -425,33 +425,28 @@ __device__ __forceinline__ void mainloop(OA& oa, OB& ob, int nk, char* smem, f32
 }
 
 // ---------------------------------------------------------------------------
-// Five-slot ring for the forward GEMMs, whose operands are both
-// K-contiguous: five 32 KB slots of half stages, the weight slice (B) two K
-// steps ahead and the token rows (A) one.  B_k sits in slot 2k mod 5 and
-// A_k in slot 2k+1 mod 5; step k computes on slots s = 2k mod 5 and s+1 and
-// issues A_{k+1} into slot s+3 and B_{k+2} into slot s+4, which held step
-// k-1's operands (free after this step's barrier).  Against the two-stage
-// ring this keeps half a stage more in flight in the same 160 KB, with one
-// barrier per step.  Step k waits until only B_{k+1}'s loads are
-// outstanding (loads complete in issue order): A_k and B_k have landed.
+// Five-slot ring for the forward GEMMs: five 32 KB slots of half stages, the
+// weight slice (B) two K steps ahead and the token rows (A) one.  B_k sits
+// in slot 2k mod 5 and A_k in slot 2k+1 mod 5; step k computes on slots
+// s = 2k mod 5 and s+1, and issues A_{k+1} into slot s+3 (sub-step 0), then
+// B_{k+2} into slot s+4 (sub-step 1); both slots held step k-1's operands,
+// free after this step's barrier.  Against the two-stage ring this keeps
+// half a stage more in flight in the same 160 KB, with one barrier per step.
+// Step k waits until only B_{k+1}'s loads are outstanding (loads complete
+// in issue order, and A_k left before them): A_k and B_k have landed.
 // CHK: the steady-state stages need bounds checks (K is not a multiple of
-// the step).
+// the step, or the tile's weight columns run past N).
 // ---------------------------------------------------------------------------
 constexpr int kSlot5 = 32 * 1024;
 __device__ __forceinline__ int mod5(int v) { return v >= 5 ? v - 5 : v; }
 
-template <int TMX, bool WAIT_B, bool PRE_A, bool PRE_B, bool FULL, class OA, class OB>
-__device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& s, f32x16_t (&acc)[TMX][TN]) {
-  static_assert(OA::BYTES <= kSlot5 && OB::BYTES <= kSlot5 && !OA::TR && !OB::TR, "five-slot ring operands");
+template <int TMX, bool PRE_A, bool PRE_B, bool FULL, class OA, class OB>
+__device__ __forceinline__ void kstep5_body(OA& oa, OB& ob, int k, const lds_t* __restrict__ As,
+                                            const lds_t* __restrict__ Bs, lds_t* __restrict__ da,
+                                            lds_t* __restrict__ db, f32x16_t (&acc)[TMX][TN]) {
+  static_assert(OA::BYTES <= kSlot5 && OB::BYTES <= kSlot5, "five-slot ring operands");
   constexpr int NKK = BK / 16;
   const int wm = wave_m(), wn = wave_n();
-  if constexpr (WAIT_B) wait_vmcnt<OB::NI>();
-  else wait_vmcnt<0>();
-  barrier_lds();
-  const lds_t* Bs = base + s * kSlot5;
-  const lds_t* As = base + mod5(s + 1) * kSlot5;
-  lds_t* const da = base + mod5(s + 3) * kSlot5;
-  lds_t* const db = base + mod5(s + 4) * kSlot5;
   bf16x8_t a[2][TMX], b[2][TN];
 #pragma unroll
   for (int i = 0; i < TMX; ++i) a[0][i] = OA::frag(As, wm * (TMX * 32) + i * 32, 0);
@@ -468,12 +463,18 @@ __device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& 
 #pragma unroll
       for (int j = 0; j < TN; ++j) b[cur ^ 1][j] = OB::frag(Bs, wn * (TBN / WN) + j * 32, kk + 1);
     }
-    if (kk == 0) {
-      if constexpr (PRE_A) {
+    // A's loads in sub-step 0, B's in sub-step 1: the sub-step boundary
+    // (sched_barrier) keeps them in that order, which the next step's
+    // partial wait relies on (the __restrict__ slots would otherwise let
+    // the compiler issue them in either order)
+    if constexpr (PRE_A) {
+      if (kk == 0) {
         oa.template issue<0, OA::NI, FULL>(k + 1, da);
         oa.advance();
       }
-      if constexpr (PRE_B) {
+    }
+    if constexpr (PRE_B) {
+      if (kk == 1) {
         ob.template issue<0, OB::NI, FULL>(k + 2, db);
         ob.advance();
       }
@@ -483,8 +484,9 @@ __device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& 
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cur][j], a[cur][i], acc[i][j], 0, 0, 0);
-    const int NR = kk + 1 < NKK ? TMX + TN : 0;
-    const int NG = kk == 0 ? (PRE_A ? OA::NI : 0) + (PRE_B ? OB::NI : 0) : 0;
+    // (a transposed fragment takes two reads)
+    const int NR = kk + 1 < NKK ? TMX * (OA::TR ? 2 : 1) + TN * (OB::TR ? 2 : 1) : 0;
+    const int NG = kk == 0 ? (PRE_A ? OA::NI : 0) : kk == 1 ? (PRE_B ? OB::NI : 0) : 0;
 #pragma unroll
     for (int q = 0; q < TMX * TN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
@@ -494,6 +496,17 @@ __device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// (The slots reach the body as __restrict__ parameters, as in kstep_body.)
+template <int TMX, bool WAIT_B, bool PRE_A, bool PRE_B, bool FULL, class OA, class OB>
+__device__ __forceinline__ void kstep5(OA& oa, OB& ob, int k, lds_t* base, int& s, f32x16_t (&acc)[TMX][TN]) {
+  if constexpr (WAIT_B) wait_vmcnt<OB::NI>();
+  else wait_vmcnt<0>();
+  barrier_lds();
+  // A_k in slot s + 1, B_k in slot s; A_{k+1} into s + 3, B_{k+2} into s + 4
+  kstep5_body<TMX, PRE_A, PRE_B, FULL>(oa, ob, k, base + mod5(s + 1) * kSlot5, base + s * kSlot5,
+                                       base + mod5(s + 3) * kSlot5, base + mod5(s + 4) * kSlot5, acc);
   s = mod5(s + 2);
 }
 
@@ -707,10 +720,13 @@ __device__ __forceinline__ void rows_tile(const RowsArgs& p, char* smem, int nt,
   f32x16_t acc[TMX][TN];
   const int nk = (int)cdiv(p.K, BK);
   if constexpr (BL == B_KM) {
+    // the data gradients stay on the two-stage ring: on the five-slot ring
+    // they ran 1-5% slower (q235b: both; q30b: the down dgrad)
     mainloop<TMX>(oa, ob, nk, smem, acc);
-  } else {  // the forward GEMMs: both operands K-contiguous
-    if (p.K % BK == 0) mainloop5<TMX, false>(oa, ob, nk, smem, acc);
-    else mainloop5<TMX, true>(oa, ob, nk, smem, acc);
+  } else if (oa.nfull(nk) == nk && ob.nfull(nk) == nk) {
+    mainloop5<TMX, false>(oa, ob, nk, smem, acc);
+  } else {
+    mainloop5<TMX, true>(oa, ob, nk, smem, acc);
   }
 
   // ------------------------------------------------------------- epilogues

@@ -235,6 +235,54 @@ def _csv_rows(d: str, suffix: str):
     return rows
 
 
+MFMA_COUNTERS = "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT"
+
+
+def mfma_summary(wl, out: str, pmc_dir: str):
+    """Markdown summary of one rocprofv3 --pmc run of MFMA_COUNTERS: per
+    launch, the sustained clock, the MFMA units' busy share and LDS activity."""
+    import collections
+    n = wl.name
+    per = collections.defaultdict(dict)
+    for r in _csv_rows(pmc_dir, "counter_collection.csv"):
+        site = site_of(r["Kernel_Name"])
+        if site is None:
+            continue
+        key = (site, r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        d = per[key]
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = collections.defaultdict(list)
+    for (site, _), d in per.items():
+        if d.get("GRBM_GUI_ACTIVE", 0) > 0 and d["ns"] > 0:
+            cyc = d["GRBM_GUI_ACTIVE"] / 8  # summed over the 8 XCDs
+            agg[site].append((d["ns"] / 1e3, cyc / d["ns"], d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * 1024),
+                              d.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * 256),
+                              d.get("SQ_LDS_BANK_CONFLICT", 0.0) / (cyc * 256)))
+    lines = [f"# rocprofv3 summary: MFMA busy cycles, LDS activity and sustained clock, {n} workload "
+             f"(T={wl.T}, d={wl.d}, E={wl.E}, k={wl.k}, I={wl.I}, {wl.dtype}, {wl.precision})", "",
+             "Commands (repository root, TMPDIR=/tmp):", "",
+             f"    rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d {pmc_dir} -o {n} -- python3 bench.py "
+             f"--workload {n} --steps 2 --warmup 1 --no-cpu",
+             f"    python3 bench.py --workload {n} --mfma-summary {out} {pmc_dir}", "",
+             "Per dispatch (one CSV row per dispatch and counter):",
+             "- GRBM_GUI_ACTIVE is summed over the 8 XCDs; one XCD's busy cycles are the value / 8.",
+             "- clock = (GRBM_GUI_ACTIVE / 8) / (End_Timestamp - Start_Timestamp).",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ((GRBM_GUI_ACTIVE / 8) * 1024 SIMDs).",
+             "- LDS active = SQ_LDS_IDX_ACTIVE / ((GRBM_GUI_ACTIVE / 8) * 256 CUs); bank conflicts likewise.",
+             "- The clock is meaningful for long dispatches only: GRBM_GUI_ACTIVE also counts launch overhead.", "",
+             "| launch | dispatches | avg us | clock GHz | MFMA busy | LDS active | LDS bank conflict |",
+             "|---|---|---|---|---|---|---|"]
+    for site, v in sorted(agg.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        m = np.mean(np.array(v), axis=0)
+        mf = f"{100 * m[2]:.1f}%" if site.startswith("gemm") else "-"
+        ghz = f"{m[1]:.2f}" if m[0] >= 50 else "-"  # launch overhead dominates short dispatches
+        lines.append(f"| {site} | {len(v)} | {m[0]:.1f} | {ghz} | {mf} | {100 * m[3]:.1f}% | {100 * m[4]:.2f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, write_dir: str | None = None,
                     flags: str = ""):
     """Markdown summary of rocprofv3 output: per-kernel durations from
@@ -320,10 +368,16 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 1 GiB once (a plain copy kernel of known size "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("OUT.md", "PMC_DIR"),
+                    help="write the clock / MFMA busy / LDS summary of a rocprofv3 --pmc run of "
+                         + MFMA_COUNTERS)
     ap.add_argument("--rocprof-summary", nargs="+", metavar="ARG",
                     help="OUT.md STATS_DIR [FETCH_DIR WRITE_DIR]: write the summary of rocprofv3 "
                          "--kernel-trace --stats output (and of two --pmc runs) for --workload")
     args = ap.parse_args()
+    if args.mfma_summary:
+        mfma_summary(S.WORKLOADS[args.workload], *args.mfma_summary)
+        return
     if args.rocprof_summary:
         rocprof_summary(S.WORKLOADS[args.workload], *args.rocprof_summary,
                         flags=" --persistent" if args.persistent else "")

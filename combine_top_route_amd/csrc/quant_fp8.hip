@@ -47,22 +47,66 @@ __device__ __forceinline__ float block_scale(float amax) {
   return amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
 }
 
-// v / s as the e4m3 encoding sees it, without a full division per value.
-// q = v * rs, with rs the rounded reciprocal of s, lies within 2.5 fp32
-// ulps of the rounded quotient: two roundings of relative size 2^-24, plus
-// the quotient's own half ulp.  e4m3 keeps three mantissa bits, so its
-// rounding decides on the 20 bits below them; unless those bits of q lie
-// within 8 ulps of the midpoint pattern 0x80000, q and the rounded quotient
-// are on the same side of every e4m3 midpoint, with no tie, and give the
-// same code.  Near a midpoint, and below e4m3's normal range (2^-6, where
-// its grid is fixed at 2^-9), the exact quotient is taken; so it is for a
-// whole block whose scale lies below 2^-128 (amax under 448 * 2^-128),
-// where the reciprocal overflows to infinity.
-__device__ __forceinline__ float quot_e4m3(float v, float s, float rs) {
-  const float q = v * rs;
-  const int d = (int)(__float_as_uint(q) & 0xFFFFFu) - 0x80000;
-  const bool safe = rs <= 0x1.fffffep+127f && (v == 0.0f || ((d > 8 || d < -8) && fabsf(q) >= 0x1p-6f));
-  return safe ? q : __fdiv_rn(v, s);
+// Blockwise quotients f[i] <- RN(f[i] / s), i < N, for the e4m3 encoding
+// (whose codes are the e4m3 rounding of the rounded quotient).  With
+// rs = RN(1 / s), q = RN(f rs) lies within an ulp of the quotient, and one
+// FMA correction, RN(q + RN(f - q s) rs), gives the rounded quotient
+// exactly (Markstein's theorem on FMA-based division) as long as the
+// residual f - q s does not underflow: here |f| >= 2^-100, and rs finite.
+// Zero keeps its sign through q.  A wave with any other value in any lane
+// (a nonzero magnitude below 2^-100, or a block whose scale lies below
+// 2^-128, where rs overflows) divides all of its values instead: one
+// wave-uniform branch, which ordinary data never enters.
+//
+// quot_run divides f[0, N) by s, and quot_run2 two runs by their own
+// scales; then `use` consumes the quotients, inside each branch.  Uniform,
+// and with nothing merging after it, the branch costs no registers: a
+// divergent one would keep every original value live through the division
+// side for the other lanes (50 more registers in the weight quantiser).
+__device__ __forceinline__ bool quot_slow(float v) { return v != 0.0f && fabsf(v) < 0x1p-100f; }
+__device__ __forceinline__ bool quot_rs_ok(float rs) { return rs <= 0x1.fffffep+127f; }
+
+template <int N>
+__device__ __forceinline__ void quot_divide(float* f, float s) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    f[i] = __fdiv_rn(f[i], s);
+    __builtin_amdgcn_sched_barrier(0);  // one at a time: interleaved, they would set the register budget
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void quot_fma(float* f, float s, float rs) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float q = f[i] * rs;
+    f[i] = f[i] == 0.0f ? q : fmaf(fmaf(-q, s, f[i]), rs, q);
+  }
+}
+
+template <int N, class F>
+__device__ __forceinline__ void quot_run(float* f, float s, float rs, F&& use) {
+  bool slow = !quot_rs_ok(rs);
+#pragma unroll
+  for (int i = 0; i < N; ++i) slow |= quot_slow(f[i]);
+  if (__builtin_amdgcn_ballot_w64(slow)) quot_divide<N>(f, s);
+  else quot_fma<N>(f, s, rs);
+  use();
+}
+
+template <int N, class F>
+__device__ __forceinline__ void quot_run2(float* f0, float s0, float r0, float* f1, float s1, float r1, F&& use) {
+  bool slow = !quot_rs_ok(r0) || !quot_rs_ok(r1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) slow |= quot_slow(f0[i]) || quot_slow(f1[i]);
+  if (__builtin_amdgcn_ballot_w64(slow)) {
+    quot_divide<N>(f0, s0);
+    quot_divide<N>(f1, s1);
+  } else {
+    quot_fma<N>(f0, s0, r0);
+    quot_fma<N>(f1, s1, r1);
+  }
+  use();
 }
 
 // e4m3 codes of four quotients packed little-endian.  v_cvt_pk_fp8_f32
@@ -120,10 +164,14 @@ __device__ __forceinline__ uint32_t gather4_codes(uint32_t code, int base, int s
 
 // Eight values divided by s, as eight e4m3 codes.
 __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
+  float g[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) g[i] = f[i];
   u32x2_t q;
-  const float rs = __fdiv_rn(1.0f, s);
-  q[0] = e4m3x4(quot_e4m3(f[0], s, rs), quot_e4m3(f[1], s, rs), quot_e4m3(f[2], s, rs), quot_e4m3(f[3], s, rs));
-  q[1] = e4m3x4(quot_e4m3(f[4], s, rs), quot_e4m3(f[5], s, rs), quot_e4m3(f[6], s, rs), quot_e4m3(f[7], s, rs));
+  quot_run<8>(g, s, __fdiv_rn(1.0f, s), [&] {
+    q[0] = e4m3x4(g[0], g[1], g[2], g[3]);
+    q[1] = e4m3x4(g[4], g[5], g[6], g[7]);
+  });
   return q;
 }
 
@@ -271,23 +319,21 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const bf16_t* __restr
   const float sc = block_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
   const float rsc = __fdiv_rn(1.0f, sc);
   const int nbn = N / 128, nbk = K / 128;
+  quot_run<64>(&f[0][0], sc, rsc, [&] {
+    // q, qt are kernel arguments: every branch on them is uniform
+    if (qt) {  // a transposed row gets four consecutive codes from each of 32 lanes
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 16; ++i) tcodes[(k0 + i) * kWS + (n0 >> 2)] = e4m3x4(f[0][i], f[1][i], f[2][i], f[3][i]);
+    }
+    if (q) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) f[j][i] = quot_e4m3(f[j][i], sc, rsc);
-  // q, qt are kernel arguments: every branch on them is uniform
-  if (qt) {  // a transposed row gets four consecutive codes from each of 32 lanes
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tcodes[(k0 + i) * kWS + (n0 >> 2)] = e4m3x4(f[0][i], f[1][i], f[2][i], f[3][i]);
-  }
-  if (q) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        fcodes[(n0 + j) * kWS + (k0 >> 2) + w] =
-            e4m3x4(f[j][4 * w], f[j][4 * w + 1], f[j][4 * w + 2], f[j][4 * w + 3]);
-  }
+        for (int w = 0; w < 4; ++w)
+          fcodes[(n0 + j) * kWS + (k0 >> 2) + w] =
+              e4m3x4(f[j][4 * w], f[j][4 * w + 1], f[j][4 * w + 2], f[j][4 * w + 3]);
+    }
+  });
   __syncthreads();
   if (qt) {
     store_code_tile(tcodes, qt + (int64_t)e * K * N + (int64_t)(kb * 128) * N + nb * 128, N);
@@ -459,13 +505,13 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
     }
     const float s0 = block_scale(a0), s1 = block_scale(a1);
     const float r0 = __fdiv_rn(1.0f, s0), r1 = __fdiv_rn(1.0f, s1);
+    quot_run2<16>(f0, s0, r0, f1, s1, r1, [&] {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      q0[w] = e4m3x4(quot_e4m3(f0[4 * w], s0, r0), quot_e4m3(f0[4 * w + 1], s0, r0),
-                     quot_e4m3(f0[4 * w + 2], s0, r0), quot_e4m3(f0[4 * w + 3], s0, r0));
-      q1[w] = e4m3x4(quot_e4m3(f1[4 * w], s1, r1), quot_e4m3(f1[4 * w + 1], s1, r1),
-                     quot_e4m3(f1[4 * w + 2], s1, r1), quot_e4m3(f1[4 * w + 3], s1, r1));
-    }
+      for (int w = 0; w < 4; ++w) {
+        q0[w] = e4m3x4(f0[4 * w], f0[4 * w + 1], f0[4 * w + 2], f0[4 * w + 3]);
+        q1[w] = e4m3x4(f1[4 * w], f1[4 * w + 1], f1[4 * w + 2], f1[4 * w + 3]);
+      }
+    });
     w0 = __float_as_uint(s0);
     w1 = __float_as_uint(s1);
   }

@@ -79,16 +79,20 @@ def test_autograd_equals_direct_calls(name, recompute):
     _equal(_direct(wl, inp, save=True), _autograd(wl, inp, recompute))
 
 
-def test_compile_fullgraph_matches_eager():
+@pytest.mark.parametrize("backend", ["aot_eager", "inductor"])
+def test_compile_fullgraph_matches_eager(backend):
     """The forward compiles as one graph (no breaks); AOT autograd traces the
-    backward through the backward operator."""
+    backward through the backward operator.  inductor is the default
+    compiler: it generates the surrounding elementwise kernels and calls the
+    layer's operators as they are."""
     wl = CASES["bf16"]
     inp = S.make_inputs(wl, seed=5)
+    print(f"compile backend {backend}", flush=True)
 
     def fwd(x, lg, wgu, wd):
         return moe_layer(x, lg, wgu, wd, wl.k, "native", True) * 2.0
     torch._dynamo.reset()
-    compiled = torch.compile(fwd, fullgraph=True, backend="aot_eager")
+    compiled = torch.compile(fwd, fullgraph=True, backend=backend)
     res = []
     for f in (fwd, compiled):
         x, lg, wgu, wd = (inp[n].to(DEV).requires_grad_() for n in ("x", "logits", "w_gate_up", "w_down"))

@@ -81,7 +81,12 @@ def bf16_test_matrix(shape, seed):
     blockwise scale (amax / 448) lies below 2^-128 and has no finite float32
     reciprocal: the 128 x 128 block of rows 0..127 and columns 256..383 of
     the flattened matrix (a weight block, or 1 x 128 row blocks), with zeros
-    in it, and column 130 (every 128-token run of it)."""
+    in it, and column 130 (every 128-token run of it).  Blocks around 1e-31
+    have a finite reciprocal scale but values below 2^-100, where one FMA
+    correction of v / s is not exact and the quantisers divide, with nonzero
+    codes: row 2, column 132 (its token runs) and, for weights, the block of
+    rows 128..255, columns 0..127.  Column 131 spans 1e-38..1e-28 inside
+    ordinary blocks, across that 2^-100 boundary."""
     g = np.random.default_rng(seed)
     a = g.standard_normal(shape) * np.exp(g.uniform(np.log(1e-6), np.log(1e3), shape[:-1] + (1,)))
     flat = a.reshape(-1, a.shape[-1])
@@ -89,9 +94,15 @@ def bf16_test_matrix(shape, seed):
         tiny = g.standard_normal((128, 128)) * 1e-37
         tiny[::7, 3] = 0.0
         flat[:128, 256:384] = tiny
-    if flat.shape[1] > 130:
+    if flat.shape[0] >= 256 and flat.shape[1] >= 128:
+        flat[128:256, :128] = g.standard_normal((128, 128)) * 1e-31
+    if flat.shape[1] > 132:
         flat[:, 130] = g.standard_normal(flat.shape[0]) * 1e-37
         flat[::5, 130] = 0.0
+        flat[:, 131] = g.standard_normal(flat.shape[0]) * 10.0 ** g.uniform(-38, -28, flat.shape[0])
+        flat[:, 132] = g.standard_normal(flat.shape[0]) * 1e-31
+    if flat.shape[0] > 2:
+        flat[2] = g.standard_normal(flat.shape[1]) * 1e-31
     a = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
     flat = a.view(-1, a.shape[-1])
     flat[0, :128] = 0.0                         # an all-zero block

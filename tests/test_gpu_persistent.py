@@ -10,8 +10,8 @@ results must equal the default engine's bit for bit, and the oracle's
 within the layer tolerance.  The cases cover K and N tails in every row
 GEMM, single-step K loops (d = 64, I = 40), a one-token layer, empty
 experts next to a hot one, the bf16 forward of fp8_bwd, the recomputing
-backward, and q30b at full size (bit equality only: the oracle at that
-size is covered by the full-size parity tests).
+backward, and q30b and q235b at full size (bit equality only: the oracle
+at those sizes is covered by the full-size parity tests).
 """
 import numpy as np
 import pytest
@@ -108,10 +108,13 @@ def test_persistent_recompute_equals_saved():
                names=("out", "dx", "dW_gate_up", "dW_down", "d_topk_w", "dlogits"))
 
 
-def test_persistent_q30b_full_size_bit_equal():
-    wl = S.WORKLOADS["q30b"]
+@pytest.mark.parametrize("name", ["q30b", "q235b"])
+def test_persistent_full_size_bit_equal(name):
+    """Full sizes, where every tile runs 32 (q30b) or 64 (q235b) K steps and
+    the expert loads are uneven (q235b's routing bias)."""
+    wl = S.WORKLOADS[name]
     inp = S.make_inputs(wl, seed=35)
-    print("persistent case q30b", flush=True)
+    print(f"persistent case {name}", flush=True)
     a = _run(wl, inp, True)
     b = _run(wl, inp, False)
     _bit_equal(a, b)

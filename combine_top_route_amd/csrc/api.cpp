@@ -4,6 +4,7 @@
 // Every check runs before the first HIP call of an entry point, so a bad
 // argument enqueues nothing.  The library owns no device memory: all buffers
 // come from the caller, and the workspace is carved into fixed regions.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -203,7 +204,10 @@ Layout layout(const moe_shape* s, int op) {
   if (bwd) {
     L.tok = take(sizeof(int32_t) * R);
     L.dH = take(es * R * 2 * s->I);
-    L.dXp = take(es * R * s->d);
+    // the bf16 backward first writes the down GEMM's data gradient G [R, I]
+    // into this buffer, which holds the permuted dx [R, d] only later
+    const bool g_in_dxp = s->dtype == MOE_BF16 && !bwd_fp8(s);
+    L.dXp = take(es * R * (g_in_dxp ? std::max(s->d, s->I) : s->d));
     L.dwp = take(sizeof(float) * R * dw_blocks(s));
     if (s->dtype == MOE_F32) L.G = take(sizeof(float) * R * s->I);
   }

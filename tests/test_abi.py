@@ -105,6 +105,15 @@ def test_bad_enums_rejected():
     assert _status(_shape(persistent=True))[0] == 0
 
 
+def test_bf16_backward_workspace_holds_the_down_dgrad():
+    # the bf16 backward keeps dH [R, 2I] and the down GEMM's data gradient
+    # G [R, I] side by side, also when I is far above d
+    for d, I in ((64, 2048), (2048, 64), (8, 16384)):
+        st, w = _status(_shape(dtype=torch.bfloat16, d=d, I=I), op=B.OP_BACKWARD)
+        R = 64 * 2
+        assert st == 0 and w >= 2 * R * (2 * I + max(I, d)), (d, I, w)
+
+
 def test_fp8_requirements():
     s = _shape(precision="fp8_block")                     # f32 storage
     assert _status(s)[0] == 2                            # MOE_ERR_UNSUPPORTED

@@ -91,6 +91,9 @@ SMALL = {
     "fp8_single_expert": BASE.scaled(T=300, d=256, E=1, k=1, I=128),
     # the skewed router (Zipf bias, empty experts) at a small hidden size
     "fp8_skew_small": S.WORKLOADS["fp8_skew"].scaled(T=1024, d=256, I=256),
+    # the largest hidden and intermediate sizes the boundary accepts
+    "fp8_max_d": BASE.scaled(T=40, d=16384, E=4, k=2, I=128),
+    "fp8_max_i": BASE.scaled(T=40, d=128, E=3, k=2, I=16384),
 }
 
 
@@ -150,6 +153,7 @@ FP8_BWD = {
     "fp8bwd_tiles": SMALL["fp8_tiles"].scaled(precision="fp8_bwd"),
     "fp8bwd_one_token": SMALL["fp8_one_token"].scaled(precision="fp8_bwd"),
     "fp8bwd_skew_small": S.WORKLOADS["fp8_bwd_skew"].scaled(T=1024, d=256, I=256),
+    "fp8bwd_max_d": SMALL["fp8_max_d"].scaled(precision="fp8_bwd"),
 }
 
 

@@ -36,6 +36,16 @@ SMALL_CASES = {
     "bf16_e12": TINY.scaled(T=300, d=128, E=12, k=3, I=64, **BF),
     "bf16_d4096": TINY.scaled(T=64, d=4096, E=8, k=2, I=256, **BF),
     "bf16_f32_logits": TINY.scaled(T=300, d=256, E=16, k=4, I=128, dtype="bf16", logits_dtype="f32"),
+    # the smallest and largest extents the boundary accepts (d, I multiples
+    # of 8 in [8, 16384]): one-step K loops with an 8-wide tail, 8-column N
+    # tiles, and 256-step K loops
+    "bf16_min_dims": TINY.scaled(T=333, d=8, E=6, k=2, I=8, **BF),
+    "f32_min_dims": TINY.scaled(T=333, d=8, E=6, k=2, I=8),
+    "bf16_max_d": TINY.scaled(T=40, d=16384, E=4, k=2, I=64, **BF),
+    "bf16_max_i": TINY.scaled(T=40, d=64, E=3, k=2, I=16384, **BF),
+    # intermediate size above the hidden size (the backward's I-wide
+    # intermediates must not fit a d-wide buffer by accident)
+    "bf16_wide_i": TINY.scaled(T=500, d=136, E=8, k=2, I=648, **BF),
 }
 
 

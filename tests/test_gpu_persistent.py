@@ -31,6 +31,9 @@ CASES = {
     "one_k_step": TINY.scaled(T=500, d=64, E=12, k=3, I=40, **BF),
     "one_token": TINY.scaled(T=1, d=128, E=8, k=2, I=128, **BF),
     "fp8_bwd": TINY.scaled(T=600, d=256, E=8, k=2, I=256, precision="fp8_bwd", **BF),
+    "min_dims": TINY.scaled(T=333, d=8, E=6, k=2, I=8, **BF),
+    "max_d": TINY.scaled(T=40, d=16384, E=4, k=2, I=64, **BF),
+    "wide_i": TINY.scaled(T=500, d=136, E=8, k=2, I=648, **BF),
 }
 NAMES = ("out", "saved", "dx", "dW_gate_up", "dW_down", "d_topk_w", "dlogits")
 

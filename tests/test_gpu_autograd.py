@@ -30,6 +30,11 @@ CASES = {
                                         logits_dtype="bf16", precision="mxfp8"),
     "fp8_bwd": S.WORKLOADS["tiny"].scaled(T=300, d=256, E=16, k=4, I=128, dtype="bf16",
                                           logits_dtype="bf16", precision="fp8_bwd"),
+    # intermediate size five times the hidden size
+    "bf16_wide_i": S.WORKLOADS["tiny"].scaled(T=300, d=128, E=8, k=2, I=640, dtype="bf16",
+                                              logits_dtype="bf16"),
+    "fp8_block_wide_i": S.WORKLOADS["tiny"].scaled(T=300, d=128, E=8, k=2, I=640, dtype="bf16",
+                                                   logits_dtype="bf16", precision="fp8_block"),
 }
 GRADS = ("dx", "dlogits", "dW_gate_up", "dW_down")
 

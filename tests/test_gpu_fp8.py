@@ -154,6 +154,7 @@ FP8_BWD = {
     "fp8bwd_one_token": SMALL["fp8_one_token"].scaled(precision="fp8_bwd"),
     "fp8bwd_skew_small": S.WORKLOADS["fp8_bwd_skew"].scaled(T=1024, d=256, I=256),
     "fp8bwd_max_d": SMALL["fp8_max_d"].scaled(precision="fp8_bwd"),
+    "fp8bwd_max_i": SMALL["fp8_max_i"].scaled(precision="fp8_bwd"),
 }
 
 

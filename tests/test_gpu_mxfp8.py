@@ -99,6 +99,9 @@ SMALL = {
     "mx_single_expert": BASE.scaled(T=300, d=256, E=1, k=1, I=128),
     # the skewed router (Zipf bias, empty experts) at a small hidden size
     "mx_skew_small": S.WORKLOADS["mxfp8_skew"].scaled(T=1024, d=256, I=256),
+    # the largest hidden and intermediate sizes the boundary accepts
+    "mx_max_d": BASE.scaled(T=40, d=16384, E=4, k=2, I=128),
+    "mx_max_i": BASE.scaled(T=40, d=128, E=3, k=2, I=16384),
 }
 
 

@@ -46,6 +46,9 @@ SMALL_CASES = {
     # intermediate size above the hidden size (the backward's I-wide
     # intermediates must not fit a d-wide buffer by accident)
     "bf16_wide_i": TINY.scaled(T=500, d=136, E=8, k=2, I=648, **BF),
+    # the most experts the boundary accepts: about a dozen rows each, many
+    # experts empty, every row tile a quarter-height tail
+    "bf16_e1024": TINY.scaled(T=1500, d=64, E=1024, k=8, I=64, **BF),
 }
 
 
@@ -159,7 +162,8 @@ def test_permute_combine_identity(dtype):
 
 
 @pytest.mark.parametrize("ldt", ["f32", "bf16"])
-@pytest.mark.parametrize("E,k", [(16, 2), (128, 8), (12, 5), (40, 12), (64, 20), (128, 80)])
+@pytest.mark.parametrize("E,k", [(16, 2), (128, 8), (12, 5), (40, 12), (64, 20), (128, 80),
+                                 (1024, 8), (1000, 16), (1024, 100), (1024, 1024), (2, 1), (2, 2)])
 def test_routing_signed_zeros_and_minus_inf(ldt, E, k):
     """Logits with +0.0 / -0.0 ties at the selection boundary and -inf
     entries, including rows with fewer than k finite logits (their -inf

@@ -427,49 +427,26 @@ __global__ __launch_bounds__(256) void quant_weight_mx_kernel(const bf16_t* __re
 // Token blocks, transposed.  Block b (of blk_off[E] in all) is the
 // (b - blk_off[e])-th run of 128 rows of expert e's segment; row i of the run
 // is src row srow(offsets[e] + 128 * (b - blk_off[e]) + i), with srow(r) =
-// src_of[r] / kdiv (token rows of x or dout) or r.  A work-group handles 64
-// columns: q[c][128 b + i] = code (0 past the segment) and the scale word
-// of (column c, run b) at s[c * s_row + b * s_blk]: the run's fp32 scale or,
-// MX, the E8M0 codes of its four 32-row blocks.  Run-major words (s_row = 1,
-// s_blk = columns) put the words of one run for consecutive columns side by
-// side, as one K step of the weight-gradient GEMMs reads them.
+// src_of[r] / kdiv (token rows of x or dout) or r.  A work-group handles
+// cpw chunks of 64 columns, one after the other: q[c][128 b + i] = code (0
+// past the segment) and the scale word of (column c, run b) at
+// s[c * s_row + b * s_blk]: the run's fp32 scale or, MX, the E8M0 codes of
+// its four 32-row blocks.  Run-major words (s_row = 1, s_blk = columns) put
+// the words of one run for consecutive columns side by side, as one K step
+// of the weight-gradient GEMMs reads them.
+//
+// The run's expert, first row and source rows take a chain of dependent
+// loads (the search over blk_off, offsets, src_of); walking several column
+// chunks per work-group pays that chain once for all of them, and each
+// chunk's loads leave while the previous chunk is encoded.
 // ---------------------------------------------------------------------------
 constexpr int kTokCols = 64;
 
+// One 128-row x 64-column chunk of quant_tok_kernel, staged in tile.
 template <bool MX>
-__global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict__ src, int64_t ld,
-                                                       const int32_t* __restrict__ src_of, int kdiv,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ blk_off, int E,
-                                                       uint8_t* __restrict__ q, int64_t ldq,
-                                                       uint32_t* __restrict__ s, int64_t s_row, int64_t s_blk) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 136];  // [row][64 bf16], 136-byte rows
-  const int b = blockIdx.x;
-  if (b >= blk_off[E]) return;
-  int lo = 0, hi = E;  // largest e with blk_off[e] <= b
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (blk_off[mid] <= b) lo = mid;
-    else hi = mid - 1;
-  }
-  const int e = lo;
-  const int r0 = offsets[e] + (b - blk_off[e]) * 128;
-  const int n = min(128, offsets[e + 1] - r0);
-  const int c0 = blockIdx.y * kTokCols;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = (t >> 3) + 32 * p, ch = t & 7;
-    u32x4_t v = {0, 0, 0, 0};
-    if (i < n) {
-      const int64_t sr = src_of ? (int64_t)(src_of[r0 + i] / kdiv) : (int64_t)(r0 + i);
-      v = *(const u32x4_t*)(src + sr * ld + c0 + ch * 8);
-    }
-    u32x2_t* dst = (u32x2_t*)(tile + i * 136 + ch * 16);
-    dst[0] = u32x2_t{v[0], v[1]};
-    dst[1] = u32x2_t{v[2], v[3]};
-  }
-  __syncthreads();
+__device__ __forceinline__ void quant_tok_chunk(const uint8_t* tile, int t, int c0, int b,
+                                                uint8_t* __restrict__ q, int64_t ldq,
+                                                uint32_t* __restrict__ s, int64_t s_row, int64_t s_blk) {
   // thread: column pair cp (columns c0 + 2cp, +1), rows 16 rg .. 16 rg + 15
   const int cp = t >> 3, rg = t & 7;
   float f0[16], f1[16];
@@ -520,6 +497,59 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
   if (rg == 0) {
     s[(int64_t)c * s_row + (int64_t)b * s_blk] = w0;
     s[(int64_t)(c + 1) * s_row + (int64_t)b * s_blk] = w1;
+  }
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict__ src, int64_t ld,
+                                                       const int32_t* __restrict__ src_of, int kdiv,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ blk_off, int E,
+                                                       uint8_t* __restrict__ q, int64_t ldq,
+                                                       uint32_t* __restrict__ s, int64_t s_row, int64_t s_blk,
+                                                       int cpw) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 136];  // [row][64 bf16], 136-byte rows
+  const int b = blockIdx.x;
+  if (b >= blk_off[E]) return;
+  int lo = 0, hi = E;  // largest e with blk_off[e] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (blk_off[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (b - blk_off[e]) * 128;
+  const int n = min(128, offsets[e + 1] - r0);
+  const int t = threadIdx.x;
+  // this thread's four source rows (i = t/8 + 32 p), 16 bytes of each per chunk
+  const bf16_t* rp[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = (t >> 3) + 32 * p;
+    rp[p] = nullptr;
+    if (i < n) {
+      const int64_t sr = src_of ? (int64_t)(src_of[r0 + i] / kdiv) : (int64_t)(r0 + i);
+      rp[p] = src + sr * ld + (t & 7) * 8;
+    }
+  }
+  u32x4_t v[4];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v[p] = rp[p] ? *(const u32x4_t*)(rp[p] + c0) : u32x4_t{0, 0, 0, 0};
+  };
+  int c0 = blockIdx.y * cpw * kTokCols;
+  load(c0);
+  for (int j = 0; j < cpw; ++j, c0 += kTokCols) {
+    if (j) __syncthreads();  // the previous chunk's tile reads are done
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      u32x2_t* dst = (u32x2_t*)(tile + ((t >> 3) + 32 * p) * 136 + (t & 7) * 16);
+      dst[0] = u32x2_t{v[p][0], v[p][1]};
+      dst[1] = u32x2_t{v[p][2], v[p][3]};
+    }
+    if (j + 1 < cpw) load(c0 + kTokCols);
+    __syncthreads();
+    quant_tok_chunk<MX>(tile, t, c0, b, q, ldq, s, s_row, s_blk);
   }
 }
 
@@ -676,14 +706,19 @@ hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* sr
                             const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
                             bool mx, bool run_major) {
   const int64_t s_row = run_major ? 1 : nblk_max, s_blk = run_major ? C : 1;
+  // column chunks per work-group: up to 8, dividing C / 64, while the grid
+  // keeps at least 2048 work-groups
+  const int chunks = C / kTokCols;
+  int cpw = 8;
+  while (cpw > 1 && (chunks % cpw || (int64_t)nblk_max * (chunks / cpw) < 2048)) cpw >>= 1;
   if (mx)
-    MOE_LAUNCH(c, name, quant_tok_kernel<true>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
+    MOE_LAUNCH(c, name, quant_tok_kernel<true>, dim3(nblk_max, C / kTokCols / cpw), dim3(256), 0,
                (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
-               (uint32_t*)s, s_row, s_blk);
+               (uint32_t*)s, s_row, s_blk, cpw);
   else
-    MOE_LAUNCH(c, name, quant_tok_kernel<false>, dim3(nblk_max, C / kTokCols), dim3(256), 0,
+    MOE_LAUNCH(c, name, quant_tok_kernel<false>, dim3(nblk_max, C / kTokCols / cpw), dim3(256), 0,
                (const bf16_t*)src, ld, src_of, kdiv, offsets, blk_off, E, q, (int64_t)nblk_max * 128,
-               (uint32_t*)s, s_row, s_blk);
+               (uint32_t*)s, s_row, s_blk, cpw);
   return hipSuccess;
 }
 

@@ -83,6 +83,43 @@ def test_quantize_tokens_bit_exact(gather):
         blk += nb
 
 
+def _wide_token_case(gather, seed):
+    """65,536 expert-sorted rows over 8 experts and 1024 columns: the token
+    quantisers then walk several 64-column chunks per work-group.  Returns
+    the routing, the source matrix, the oracle's routing and a sample of 48
+    columns, three in every chunk."""
+    T, E, k, C = 16384, 8, 4, 1024
+    g = np.random.default_rng(seed)
+    ids = torch.from_numpy(np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32))
+    w = torch.from_numpy(g.uniform(0.1, 1.0, (T, k)).astype(np.float32))
+    r = B.route_ids(ids.to(DEV), w.to(DEV), E)
+    src = bf16_test_matrix((T if gather else T * k, C), seed + 1)
+    rt = O.route(None, k, E, ids=ids.numpy(), w=w.double().numpy())
+    cols = [64 * j + c for j in range(C // 64) for c in (0, 37, 63)]
+    return r, src, rt, cols, (T, E, k)
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_quantize_tokens_bit_exact_many_column_chunks(gather):
+    """Every 128-row run of a sample of columns spread over all chunks, at a
+    size where each work-group encodes several column chunks in turn."""
+    r, src, rt, cols, (T, E, k) = _wide_token_case(gather, 11)
+    q, s = B.quantize_tokens_fp8(src.to(DEV), r, T, k, gather)
+    q, s = q.cpu()[cols], s.cpu().numpy().astype(np.float64)[cols]
+    rows = src.float().numpy()[rt["src_of"] // k] if gather else src.float().numpy()
+    rows = rows[:, cols]
+    counts, off = rt["counts"], rt["offsets"]
+    blk = 0
+    for e in range(E):
+        n = counts[e]
+        nb = -(-n // 128)
+        ref = O.quant_tokens_128(rows[off[e]:off[e + 1]])
+        got = _decode(q[:, 128 * blk:128 * (blk + nb)], np.repeat(s[:, blk:blk + nb], 128, axis=1))
+        assert np.array_equal(got[:, :n], ref.T), e
+        assert np.all(q[:, 128 * blk + n:128 * (blk + nb)].numpy() == 0), e
+        blk += nb
+
+
 SMALL = {
     # several tiles, ragged rows, a 128-wide feature tail (d = I = 384)
     "fp8_tiles": BASE.scaled(T=777, d=384, E=16, k=4, I=384),

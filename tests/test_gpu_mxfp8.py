@@ -91,6 +91,34 @@ def test_mx_quantize_tokens_bit_exact(gather):
         blk += nb
 
 
+@pytest.mark.parametrize("gather", [True, False])
+def test_mx_quantize_tokens_bit_exact_many_column_chunks(gather):
+    """Every 32-row block of a sample of columns spread over all 64-column
+    chunks, at a size where each work-group encodes several chunks in turn
+    (65,536 expert-sorted rows, 1024 columns)."""
+    T, E, k, C = 16384, 8, 4, 1024
+    g = np.random.default_rng(13)
+    ids = torch.from_numpy(np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32))
+    w = torch.from_numpy(g.uniform(0.1, 1.0, (T, k)).astype(np.float32))
+    r = B.route_ids(ids.to(DEV), w.to(DEV), E)
+    src = bf16_test_matrix((T if gather else T * k, C), 14)
+    q, s = B.quantize_tokens_mxfp8(src.to(DEV), r, T, k, gather)
+    cols = [64 * j + c for j in range(C // 64) for c in (0, 37, 63)]
+    q, s = q.cpu()[cols], s.cpu()[cols]
+    rt = O.route(None, k, E, ids=ids.numpy(), w=w.double().numpy())
+    rows = src.float().numpy()[rt["src_of"] // k] if gather else src.float().numpy()
+    rows = rows[:, cols]
+    counts, off = rt["counts"], rt["offsets"]
+    blk = 0
+    for e in range(E):
+        n = counts[e]
+        nb = -(-n // 128)
+        pad = np.zeros((128 * nb, len(cols)), np.float32)
+        pad[:n] = rows[off[e]:off[e + 1]]
+        _check_encoding(q[:, 128 * blk:128 * (blk + nb)], s[:, 4 * blk:4 * (blk + nb)], pad.T.copy())
+        blk += nb
+
+
 SMALL = {
     # several tiles, ragged rows, a 128-wide feature tail (d = I = 384)
     "mx_tiles": BASE.scaled(T=777, d=384, E=16, k=4, I=384),

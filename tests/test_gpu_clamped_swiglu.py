@@ -96,3 +96,31 @@ def test_clamped_recompute_and_operators_equal_saved_direct_calls(name):
     plain = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=x.dtype, logits_dtype=lg.dtype,
                        precision=wl.precision, device=dev)
     assert not torch.equal(plain.forward(x, wgu, wd, logits=lg), res[0][0])
+
+
+@pytest.mark.parametrize("name", ["bf16_tiles", "bf16_ktail", "fp8_bwd"])
+def test_clamped_persistent_equals_default_and_oracle(name):
+    """The persistent row GEMMs (MOE_FLAG_PERSISTENT) apply the clamp in
+    their own gate/up epilogue: results bit-equal to the default engine's
+    and within the layer tolerance of the oracle."""
+    from combine_top_route_amd import binding as B
+    wl = CASES[name]
+    print(f"case clamped persistent {name}: {wl} limit={LIMIT}", flush=True)
+    inp = grid_inputs(wl, seed=5)
+    dev = torch.device("cuda", 0)
+    x, wgu, wd, lg, dout = (inp[n].to(dev) for n in ("x", "w_gate_up", "w_down", "logits", "dout"))
+    res = []
+    for persistent in (True, False):
+        layer = B.MoeLayer(wl.T, wl.d, wl.E, wl.k, wl.I, dtype=S.torch_dtype(wl.dtype),
+                           logits_dtype=S.torch_dtype(wl.logits_dtype), precision=wl.precision, device=dev,
+                           swiglu_limit=LIMIT, persistent=persistent)
+        out = layer.forward(x, wgu, wd, logits=lg).clone()
+        g = {n: v.clone() for n, v in layer.backward(dout, x, wgu, wd).items()}
+        torch.cuda.synchronize()
+        res.append({"out": out, "saved": layer.saved.clone(), **g})
+    for n in res[1]:
+        assert torch.equal(res[0][n], res[1][n]), n
+    ref = run_oracle(wl, inp, limit=LIMIT)
+    got = {n: v.cpu().double().numpy() for n, v in res[0].items() if n != "saved"}
+    tol = TOL["fp8"] if wl.precision != "native" else TOL[wl.dtype]
+    check_floats(got, ref, tol)

@@ -152,20 +152,27 @@ __device__ __forceinline__ void issue_stage(const OT& ot, const OF& of, const ui
 // acc[i][j][r]: token wave_m*16*TMX + 16 i + lane % 16, feature
 // wave_n*64 + 16 j + 4 (lane / 16) + r.
 // ---------------------------------------------------------------------------
-// acc += P s_token s_feature for one sub-tile row's TN partials.
+// acc += P s_token s_feature for one sub-tile row's TN partials.  With
+// weight scales (SC_WEIGHT) a wave's 64 features lie in one 128-row weight
+// block, or, in the gate/up GEMM, in one 32-row block of gate rows (tiles 0,
+// 1) and one of up rows (tiles 2, 3): tiles 0 and 1 share a scale, as do 2
+// and 3, so two products serve all four (the same floats, so the same
+// results as one product per tile, with a quarter of the multiplies).
+static_assert(TN == 4, "feature tiles per wave");
 template <int SC>
 __device__ __forceinline__ void promote(f32x4_t (&acc)[TN], const f32x4_t (&P)[TN], float sa,
                                         const f32x4_t (&sb)[TN]) {
+  if constexpr (SC == SC_ROW) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    if constexpr (SC == SC_ROW) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[j][r] * sb[j][r], sa, acc[j][r]);
-    } else {
-      const float s = sa * sb[j][0];
+  } else {
+    const float s01 = sa * sb[0][0], s23 = sa * sb[2][0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[j][r], s, acc[j][r]);
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[j][r], j < 2 ? s01 : s23, acc[j][r]);
   }
 }
 
@@ -257,7 +264,7 @@ __device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, int s
     for (int j = 0; j < TN; ++j) {
       const int fr = wn * 64 + j * 16 + 4 * (lane >> 4);
       if constexpr (SC == SC_ROW) sb[j] = *(const __attribute__((address_space(3))) f32x4_t*)(SB + fr);
-      else sb[j][0] = SB[fr];
+      else if (j % 2 == 0) sb[j][0] = SB[fr];  // tiles 0, 2 (see promote)
     }
   }
   const lds_t* tb = cur + trow * KB;           // this wave's token rows

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -103,7 +104,7 @@ moe_status check_shape(const moe_shape* s) {
   if (s->precision < MOE_PREC_NATIVE || s->precision > MOE_PREC_FP8_BWD)
     return fail(MOE_ERR_INVALID_ARGUMENT, "precision=%d unknown", s->precision);
   if (s->flags & ~MOE_FLAG_PERSISTENT) return fail(MOE_ERR_INVALID_ARGUMENT, "flags=%d has unknown bits", (int)s->flags);
-  if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f))
+  if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= std::numeric_limits<float>::max()))
     return fail(MOE_ERR_INVALID_ARGUMENT, "swiglu_limit=%g must be 0 (plain SwiGLU) or a positive finite clamp",
                 (double)s->swiglu_limit);
   if (s->precision != MOE_PREC_NATIVE) {

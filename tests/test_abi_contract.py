@@ -44,21 +44,26 @@ def _sizes(shape):
     return out
 
 
-extent = st.one_of(st.integers(-3, 40), st.sampled_from([64, 128, 136, 256, 384, 1000, 1024, 2048, 4096,
-                                                         16376, 16384, 16392, 1 << 20]))
+# each field mostly valid (so that whole shapes often are), sometimes not
+extent = st.one_of(st.integers(1, 64).map(lambda x: 8 * x),
+                   st.sampled_from([1000, 1536, 2048, 4096, 16376, 16384]),
+                   st.sampled_from([-8, 0, 4, 12, 130, 16392, 1 << 20]))
 shapes = st.tuples(
-    st.one_of(st.integers(-2, 5000), st.sampled_from([1 << 24, (1 << 24) + 1, 1 << 25])),  # T
+    st.one_of(st.integers(1, 5000), st.sampled_from([1 << 24]),
+              st.sampled_from([-2, 0, (1 << 24) + 1, 1 << 25])),                        # T
     extent,                                                                               # d
-    st.one_of(st.integers(-1, 20), st.sampled_from([128, 1023, 1024, 1025])),             # E
-    st.one_of(st.integers(-1, 12), st.sampled_from([64, 100, 1024])),                     # k
+    st.one_of(st.integers(1, 40), st.sampled_from([128, 1023, 1024]), st.sampled_from([-1, 0, 1025])),  # E
+    st.one_of(st.integers(1, 12), st.sampled_from([64, 100, 1024]), st.sampled_from([-1, 0])),         # k
     extent,                                                                               # I
-    st.integers(-1, 2), st.integers(-1, 2), st.integers(-1, 4),                           # dtypes, precision
-    st.one_of(st.just(0.0), st.floats(allow_nan=True, allow_infinity=True, width=32)),    # swiglu_limit
-    st.sampled_from([0, 1, 2, 3, -1]),                                                    # flags
+    st.sampled_from([0, 1, 1, -1, 2]), st.sampled_from([0, 1, 1, 2]),                     # dtypes
+    st.sampled_from([0, 0, 1, 2, 3, -1, 4]),                                              # precision
+    st.one_of(st.just(0.0), st.floats(min_value=2.0 ** -100, max_value=2.0 ** 127, width=32),
+              st.floats(allow_nan=True, allow_infinity=True, width=32)),                  # swiglu_limit
+    st.sampled_from([0, 0, 1, 2, -1]),                                                    # flags
 )
 
 
-@settings(max_examples=600, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=1500, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(shapes)
 def test_shape_validation_matches_the_header(args):
     T, d, E, k, I, dtype, ldt, prec, lim, flags = args
@@ -91,3 +96,24 @@ def test_shape_validation_matches_the_header(args):
 def test_every_positive_finite_limit_is_accepted(lim):
     s = B.make_shape(64, 64, 8, 2, 128, torch.bfloat16, swiglu_limit=lim)
     assert B.lib().moe_workspace_bytes(ctypes.byref(s), B.OP_FORWARD) > 0
+
+
+# boundary shapes the random draw reaches rarely: the fp8 size limit at
+# T*k = 2^27 (whose operand widest in K is 2I here), the largest extents
+BOUNDARY = [
+    (1 << 24, 1024, 128, 8, 1536, 1, 1, 1, 0.0, 0),   # fp8: 2^27 rows x 2I = 3072 -> unsupported
+    (1 << 24, 1024, 128, 8, 896, 1, 1, 1, 0.0, 0),    # 2I = 1792 -> 14 * 2^27 < 2^31: accepted
+    (1 << 24, 2048, 128, 8, 768, 1, 1, 2, 0.0, 0),    # d = 2048 -> 16 * 2^27 = 2^31: unsupported
+    (1 << 24, 1024, 128, 8, 1536, 1, 1, 0, 0.0, 1),   # the same shape in bf16 is accepted
+    (1, 16384, 1024, 1024, 16384, 0, 1, 0, 7.0, 0),   # largest extents, k = E
+    ((1 << 27) // 1024, 8, 1024, 1024, 8, 1, 0, 0, 0.0, 0),  # T*k = 2^27 exactly
+    ((1 << 27) // 1024 + 1, 8, 1024, 1024, 8, 1, 0, 0, 0.0, 0),  # one row too many
+]
+
+
+@pytest.mark.parametrize("args", BOUNDARY)
+def test_boundary_shapes(args):
+    s = B.MoeShape(*args)
+    want = expected_status(*args)
+    for key, (status, _, _) in _sizes(s).items():
+        assert status == want, (key, args)

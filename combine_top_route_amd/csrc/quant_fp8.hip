@@ -268,7 +268,8 @@ __device__ __forceinline__ void load_block_staged(const bf16_t* Wb, int K, tile:
     const int q = w * 8 + i;  // 1 KB of LDS: rows 4q .. 4q+3
     const int row = 4 * q + (l >> 4);
     const int c = (l & 15) ^ ((row >> 2) & 15);
-    tile::dma16(Wb + (int64_t)row * K + c * 8, stage + q * 1024);
+    // non-temporal (cache policy nt): the weight is read once
+    __builtin_amdgcn_global_load_lds(Wb + (int64_t)row * K + c * 8, (tile::lds_void_t*)(stage + q * 1024), 16, 0, 2);
   }
   tile::wait_vmcnt<0>();
   __syncthreads();

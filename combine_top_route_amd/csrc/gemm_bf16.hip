@@ -13,15 +13,18 @@
 //
 // Tile engine (all six GEMMs): C[m,n] = sum_k A(m,k) B(n,k) on a 256x256
 // output tile, K in steps of 64, eight waves (two per SIMD) of 128x64, each
-// 4x2 MFMA 32x32x16 bf16 tiles.  The tile size is set by the memory side:
-// a CU sustains roughly 30 bytes/clock of global->LDS traffic with eight
-// waves, and a 256x256x64 step moves 64 KB per 2048 MFMA cycles (32 B/clk).
-// Operands move global -> LDS with direct loads (global_load_lds_dwordx4, no
-// register staging) into a two-stage ring: all loads of step k+1 leave at
-// the start of step k and are in flight while the MFMAs consume step k - for
-// the gate/up GEMM those are the gathered token rows of the next K slice, the
-// one-GPU analogue of computing on one token group while the next one moves.
-// One barrier per K step.
+// 4x2 MFMA 32x32x16 bf16 tiles: the largest tile whose accumulators (128
+// per lane) fit the registers at two waves per SIMD.  A 256x256x64 step
+// moves 64 KB per 2048 MFMA cycles; that stream (its L2 misses, and the LDS
+// that the direct loads share with the fragment reads) is what bounds the
+// main loop.  Operands move global -> LDS with direct loads
+// (global_load_lds_dwordx4, no register staging) into a ring: two 64 KB
+// stages for the gradients, whose loads of step k+1 all leave at the start
+// of step k, and five 32 KB half stages for the forward GEMMs (weights two
+// steps ahead, token rows one).  For the gate/up GEMM the loads in flight are
+// the gathered token rows of the next K slice, the one-GPU analogue of
+// computing on one token group while the next one moves.  One barrier per K
+// step.
 //
 // LDS layouts: an operand whose rows are K-contiguous in memory is stored
 // [row][64 k] and read with ds_read_b128; an operand whose rows are contiguous

@@ -121,11 +121,18 @@ def kernel_work(wl):
 
 
 def source_digest(wl) -> str:
+    """Digest of the GEMM sources' code, comments removed (a comment edit
+    leaves the counters of the committed summaries valid; any code edit
+    voids them)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[wl.precision]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

@@ -390,8 +390,8 @@ def main():
                         flags=" --persistent" if args.persistent else "")
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU's share of the layer: this build runs on exactly one GPU "
-              "(expert-parallel exchange across GPUs is not built); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer on exactly one GPU (the library has no "
+              "expert-parallel exchange across GPUs); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     wl = S.WORKLOADS[args.workload]

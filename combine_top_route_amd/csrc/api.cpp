@@ -138,10 +138,11 @@ int dw_blocks(const moe_shape* s) {
 int64_t nblk_max(const moe_shape* s) { return cdiv(s->T * s->k, kTokBlock) + s->E; }
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// `saved`: H [R,2I] then Aw [R,I] (dtype); for fp8 also the transposed weight
-// codes and scales the backward's dgrads read.
+// `saved`: H [R,2I] then Aw [R,I] (dtype); for fp8 also the weight codes and
+// scales the backward's data gradients read: blockwise the forward encodings
+// ([E,2I,d], [E,d,I]), MX the transposed ones ([E,d,2I], [E,I,d]).
 struct SavedLayout {
-  size_t H = 0, A = 0, wgutq = 0, wdtq = 0, wguts = 0, wdts = 0, total = 0;
+  size_t H = 0, A = 0, wgu_dgq = 0, wd_dgq = 0, wgu_dgs = 0, wd_dgs = 0, total = 0;
 };
 
 SavedLayout saved_layout(const moe_shape* s) {
@@ -158,10 +159,10 @@ SavedLayout saved_layout(const moe_shape* s) {
       off += bytes;
       return o;
     };
-    L.wgutq = take(E * d * 2 * I);
-    L.wdtq = take(E * I * d);
-    L.wguts = take(wscale_bytes(s, d, 2 * I));
-    L.wdts = take(wscale_bytes(s, I, d));
+    L.wgu_dgq = take(E * d * 2 * I);
+    L.wd_dgq = take(E * I * d);
+    L.wgu_dgs = take(wscale_bytes(s, d, 2 * I));
+    L.wd_dgs = take(wscale_bytes(s, I, d));
   }
   L.total = off;
   return L;
@@ -175,7 +176,7 @@ struct Layout {
   size_t xq = 0, xs = 0, wguq = 0, wgus = 0, wdq = 0, wds = 0, awq = 0, aws = 0;
   size_t doutq = 0, douts = 0, dhq = 0, dhs = 0;
   size_t tqa = 0, tsa = 0, tqb = 0, tsb = 0, Gf = 0;
-  size_t wgutq = 0, wguts = 0, wdtq = 0, wdts = 0;  // fp8_bwd: transposed weights
+  size_t wgu_dgq = 0, wgu_dgs = 0, wd_dgq = 0, wd_dgs = 0;  // fp8_bwd: the data gradients' weight codes
   size_t rsaved = 0;                                // recompute: the saved buffer
   size_t total = 0;
 };
@@ -243,10 +244,10 @@ Layout layout(const moe_shape* s, int op) {
       L.tsb = take(w * rb * nb);
       L.Gf = take(sizeof(float) * R * I);
       if (!fwd_fp8(s)) {
-        L.wgutq = take(E * d * 2 * I);
-        L.wdtq = take(E * I * d);
-        L.wguts = take(wscale_bytes(s, d, 2 * I));
-        L.wdts = take(wscale_bytes(s, I, d));
+        L.wgu_dgq = take(E * d * 2 * I);
+        L.wd_dgq = take(E * I * d);
+        L.wgu_dgs = take(wscale_bytes(s, d, 2 * I));
+        L.wd_dgs = take(wscale_bytes(s, I, d));
       }
     }
   }
@@ -260,10 +261,10 @@ Fp8Saved fp8_saved(const moe_shape* s, const void* saved) {
   if (!saved) return v;
   const SavedLayout L = saved_layout(s);
   char* b = (char*)saved;
-  v.wgutq = (uint8_t*)(b + L.wgutq);
-  v.wdtq = (uint8_t*)(b + L.wdtq);
-  v.wguts = b + L.wguts;
-  v.wdts = b + L.wdts;
+  v.wgu_dgq = (uint8_t*)(b + L.wgu_dgq);
+  v.wd_dgq = (uint8_t*)(b + L.wd_dgq);
+  v.wgu_dgs = b + L.wgu_dgs;
+  v.wd_dgs = b + L.wd_dgs;
   return v;
 }
 
@@ -540,8 +541,8 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
     q.quant_weights = !fwd_fp8(shape);
     q.doutq = (uint8_t*)at(workspace, L.doutq); q.douts = at(workspace, L.douts);
     if (q.quant_weights) {
-      q.sv.wgutq = (uint8_t*)at(workspace, L.wgutq); q.sv.wguts = at(workspace, L.wguts);
-      q.sv.wdtq = (uint8_t*)at(workspace, L.wdtq); q.sv.wdts = at(workspace, L.wdts);
+      q.sv.wgu_dgq = (uint8_t*)at(workspace, L.wgu_dgq); q.sv.wgu_dgs = at(workspace, L.wgu_dgs);
+      q.sv.wd_dgq = (uint8_t*)at(workspace, L.wd_dgq); q.sv.wd_dgs = at(workspace, L.wd_dgs);
     } else {
       q.sv = fp8_saved(shape, saved);
     }

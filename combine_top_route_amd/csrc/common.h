@@ -224,10 +224,13 @@ hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void*
                                  const float* topk_w, const int32_t* src_of, int R, int I, float lim,
                                  void* dH, float* dw, uint8_t* dhq, void* dhs, bool mx);
 
-// Transposed weight codes the fp8 forward leaves in `saved` for the backward.
+// Weight codes the backward's data gradients read, left in `saved` by the
+// fp8 forward: blockwise the forward encodings (one scale per 128 x 128
+// block either way), MX the transposed encodings (blocks along the other
+// axis).
 struct Fp8Saved {
-  uint8_t* wdtq; void* wdts;    // [E,I,d] codes and scales
-  uint8_t* wgutq; void* wguts;  // [E,d,2I]
+  uint8_t* wd_dgq; void* wd_dgs;    // codes and scales: blockwise [E,d,I], MX [E,I,d]
+  uint8_t* wgu_dgq; void* wgu_dgs;  // blockwise [E,2I,d], MX [E,d,2I]
 };
 // Workspace of the fp8 forward: quantised x, weights and Aw with their scales.
 struct Fp8Fwd {
@@ -243,7 +246,7 @@ struct Fp8Fwd {
 // ([max(d,2I)] and [max(I,d)] rows of 128 nblk_max bytes).
 struct Fp8Bwd {
   bool mx;
-  bool quant_weights;           // encode the transposed weights into sv first
+  bool quant_weights;           // encode the weights into sv first
                                 // (no fp8 forward ran)
   uint8_t* doutq; void* douts;  // codes [T,d]; scale words [d/128, R] per expert-sorted row
   Fp8Saved sv;                  // from the forward's saved buffer

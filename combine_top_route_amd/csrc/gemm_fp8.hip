@@ -27,6 +27,8 @@
 // B operand the token side, so a lane's four results share one token row:
 // the blockwise promotion costs one multiply-add per result, and it runs a
 // sub-step behind the MFMAs that produced the partial.
+#include <type_traits>
+
 #include "common.h"
 #include "tile.h"
 
@@ -67,6 +69,8 @@ __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 // One operand: 64 NI rows x 128 bytes per stage (NI = 4: 256 rows).
 // Instruction q covers rows 8q..8q+7 (1 KB); wave w issues q = w + 8i, i < NI.
 // ---------------------------------------------------------------------------
+struct FragOff;
+
 template <int NI = 4>
 struct Op8 {
   static constexpr int N = NI;
@@ -94,6 +98,7 @@ struct Op8 {
 #pragma unroll
     for (int i = 0; i < NI; ++i) ptr[i] += KB;
   }
+  __device__ static i32x8_t frag(const lds_t* fb, int n0, const FragOff& fo);  // after frag8
 };
 
 // MFMA operand of 16 rows in the instruction's K order: lane l holds row
@@ -116,6 +121,78 @@ __device__ __forceinline__ i32x8_t frag8(const lds_t* s, const FragOff& o) {
                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   return r;
 }
+
+// Feature fragment (16 features from n0, one K step) of a stage whose
+// feature operand is stored [row][128 K bytes].
+template <int NI>
+__device__ __forceinline__ i32x8_t Op8<NI>::frag(const lds_t* fb, int n0, const FragOff& fo) {
+  return frag8(fb + n0 * KB, fo);
+}
+
+// ---------------------------------------------------------------------------
+// Feature operand whose memory rows run along the features: element (n, k)
+// at base[k * ld + n] (a blockwise weight read in its forward layout by a
+// data gradient, where the contraction runs over the weight's rows).  A stage
+// is 128 k-rows of the tile's 256 features, 256 bytes each; row k's 16-byte
+// chunk c sits at chunk c ^ kn_swz(k).  Instruction q covers k-rows 4q ..
+// 4q+3 (1 KB); wave w issues q = w + 8i, i < 4.  Features at or past N read
+// the row's first chunk (computed, never stored).
+//
+// Fragments come from ds_read_b64_tr_b8.  Within each 16-lane group, lane i
+// < 8 receives byte i of the 8 bytes that lanes 0, 2, .., 14 address, lane
+// 8 + i byte i of those of lanes 1, 3, .., 15 (probed).  So with lane s
+// addressing k-row k0 + s / 2 at feature n0 + 8 (s % 2), lane i gets K bytes
+// k0 .. k0 + 7 of feature n0 + i: the MFMA's own layout (lane l: feature l %
+// 16, K bytes 16 g .. 16 g + 15 and 64 + 16 g .. + 15, g = l / 16) takes
+// four such reads.  The swizzle folds row bit 4 into bit 3 so that the 32
+// k-rows one read covers spread over all chunk positions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kn_swz(int k) { return (k & 15) ^ (((k >> 4) & 1) << 3); }
+
+struct Op8KN {
+  static constexpr int N = 4;
+  const uint8_t* ptr[N];  // this lane's 16-byte chunk at the current stage
+  int64_t step;           // bytes per K step (128 rows)
+
+  // base: element (feature of the tile's first column, k = 0); nvalid:
+  // features of the tile inside N
+  __device__ void init(const uint8_t* base, int64_t ld, int nvalid) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    step = (int64_t)KB * ld;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int row = 4 * (w + NWAVE * i) + (lane >> 4);
+      int c = (lane & 15) ^ kn_swz(row);
+      if (c * 16 >= nvalid) c = 0;
+      ptr[i] = base + (int64_t)row * ld + c * 16;
+    }
+  }
+  template <int I0, int I1>
+  __device__ void issue(lds_t* s) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int i = I0; i < (I1 < N ? I1 : N); ++i) dma16(ptr[i], s + (w + NWAVE * i) * 1024);
+  }
+  __device__ void advance() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) ptr[i] += step;
+  }
+  __device__ static i32x8_t frag(const lds_t* fb, int n0, const FragOff&) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const int lane = threadIdx.x & 63, sl = lane & 15, g = lane >> 4;
+    const int cb = n0 >> 4, byte = 8 * (sl & 1);
+    v2i r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 16 * g + 8 * (q & 1) + 64 * (q >> 1) + (sl >> 1);
+      r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(fb + k * (TBN) + ((cb ^ kn_swz(k)) << 4) + byte));
+    }
+    const i32x8_t f = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    return f;
+  }
+};
+static_assert(TBN == 256 && KB * TBN == OPB, "Op8KN stage: 128 k-rows of 256 features");
 
 __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / WN; }
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % WN; }
@@ -278,11 +355,10 @@ __device__ __forceinline__ void kstep(OT& ot, OF& of, const uint32_t*& sp, int s
       else if (j % 2 == 0) sb[j][0] = SB[fr];  // tiles 0, 2 (see promote)
     }
   }
-  const lds_t* tb = cur + trow * KB;           // this wave's token rows
-  const lds_t* fb = cur + OPB + wn * 64 * KB;  // this wave's feature rows
+  const lds_t* tb = cur + trow * KB;  // this wave's token rows
   i32x8_t f[TN];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) f[j] = frag8(fb + j * 16 * KB, fo);
+  for (int j = 0; j < TN; ++j) f[j] = OF::frag(cur + OPB, wn * 64 + j * 16, fo);
   i32x8_t t[2];
   t[0] = frag8(tb, fo);
   if constexpr (TMX > 1) t[1] = frag8(tb + 16 * KB, fo);
@@ -396,6 +472,10 @@ struct Rows8Args {
   int64_t bs_estride, b_srow, b_skb;
   int b_rshift;
   int gateup;
+  // b_kn: the feature side is stored along the features instead, element
+  // (n, k) at B + e * b_estride + k * ldb + n (blockwise weights in their
+  // forward layout, read by a data gradient); b_srow and b_skb step the
+  // scale words per 128 features and per K step as above
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
   const int32_t* offsets;
   const int32_t* tile_off;
@@ -418,7 +498,7 @@ struct Rows8Args {
 // One row tile of ROWS token rows: 256, or 128 / 64 for a segment's last
 // tile holding at most that many rows (the waves then take 64 / 32 rows:
 // a half / a quarter of the MFMA work and of the token operand).
-template <int EPI, int SC, int ROWS>
+template <int EPI, int SC, int ROWS, bool KN>
 __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int nt, int e, int m0, int seg1) {
   constexpr int TMX = ROWS / WM / 16;
   const int seg0 = m0;  // rows past the segment repeat the tile's first row
@@ -446,9 +526,10 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
   const uint8_t* Be = p.B + (int64_t)e * p.b_estride;
   const uint32_t* Bse = p.Bs + (int64_t)e * p.bs_estride;
   Op8<ROWS / 64> ot;
-  Op8<> of;
   ot.init([&](int row) { return p.A + arow(row) * p.lda; });
-  of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
+  std::conditional_t<KN, Op8KN, Op8<>> of;
+  if constexpr (KN) of.init(Be + nt * TBN, p.ldb, p.N - nt * TBN);
+  else of.init([&](int n) { return Be + (int64_t)wrow(n) * p.ldb; });
   const int srow = 64 * (wave_id() & 3) + lane;
   const uint32_t* sp = wave_id() < 4 ? p.As + (p.a_s_sorted ? srt(srow) : arow(srow)) * p.a_srow
                                      : Bse + (int64_t)(wrow(srow) >> p.b_rshift) * p.b_srow;
@@ -524,7 +605,7 @@ __device__ __forceinline__ void rows8_tile(const Rows8Args& p, char* smem, int n
 
 // TAG only tells launch sites with the same epilogue apart in profiles.
 // SC: SC_WEIGHT (blockwise) or SC_MX.
-template <int EPI, int TAG, int SC>
+template <int EPI, int TAG, int SC, bool KN>
 __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int L = xcd_tile(blockIdx.x, p.tile_off[p.E] * p.n_tiles);
@@ -542,9 +623,9 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   const int nt = j / nrt;
   const int m0 = seg0 + (j - nt * nrt) * TBM;
   const int rows = seg1 - m0;
-  if (rows <= TBM / 4) rows8_tile<EPI, SC, TBM / 4>(p, smem, nt, e, m0, seg1);
-  else if (rows <= TBM / 2) rows8_tile<EPI, SC, TBM / 2>(p, smem, nt, e, m0, seg1);
-  else rows8_tile<EPI, SC, TBM>(p, smem, nt, e, m0, seg1);
+  if (rows <= TBM / 4) rows8_tile<EPI, SC, TBM / 4, KN>(p, smem, nt, e, m0, seg1);
+  else if (rows <= TBM / 2) rows8_tile<EPI, SC, TBM / 2, KN>(p, smem, nt, e, m0, seg1);
+  else rows8_tile<EPI, SC, TBM, KN>(p, smem, nt, e, m0, seg1);
 }
 
 // ===========================================================================
@@ -608,22 +689,24 @@ constexpr size_t kStoreF32Epi = (size_t)TBM * (128 * 4 + 16);
 constexpr size_t kSmem = cmax(cmax(kRingBytes, kStoreF32Epi), cmax(kStoreEpi, kGateupEpi));
 static_assert(kSmem <= 160 * 1024, "LDS");
 
-template <int EPI, int TAG, int SC>
+template <int EPI, int TAG, int SC, bool KN = false>
 hipError_t launch_rows8_sc(const LaunchCtx& c, const char* name, const Rows8Args& p, int R) {
   {
-    hipError_t e = allow_smem_once<rows8_kernel<EPI, TAG, SC>>(kSmem);
+    hipError_t e = allow_smem_once<rows8_kernel<EPI, TAG, SC, KN>>(kSmem);
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = (int64_t)(R / TBM + p.E) * p.n_tiles;
   const unsigned nblocks = (unsigned)((tiles + 7) / 8 * 8);
-  MOE_LAUNCH(c, name, (rows8_kernel<EPI, TAG, SC>), dim3(nblocks), dim3(NTHR), kSmem, p);
+  MOE_LAUNCH(c, name, (rows8_kernel<EPI, TAG, SC, KN>), dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
 
+// kn: the feature side in its forward layout (blockwise weights only)
 template <int EPI, int TAG>
-hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R, bool mx) {
+hipError_t launch_rows8(const LaunchCtx& c, const char* name, Rows8Args p, int R, bool mx, bool kn = false) {
   p.b_rshift = mx ? 0 : 7;
-  return mx ? launch_rows8_sc<EPI, TAG, SC_MX>(c, name, p, R)
+  if (mx) return launch_rows8_sc<EPI, TAG, SC_MX>(c, name, p, R);
+  return kn ? launch_rows8_sc<EPI, TAG, SC_WEIGHT, true>(c, name, p, R)
             : launch_rows8_sc<EPI, TAG, SC_WEIGHT>(c, name, p, R);
 }
 
@@ -668,18 +751,27 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
   // x's scale words per expert-sorted row (run-major), so that the gathering
   // gate/up GEMM reads one K step's words contiguously
   HIP_RET(launch_quant_rows(c, "quant_x", a.x, d, a.T, a.d, q.xq, q.xs, mx, true, a.row_of, a.k));
-  // both layouts in one pass: the transposed codes serve the backward's dgrads
-  HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, q.wguq, q.wgus,
-                        q.sv.wgutq, q.sv.wguts));
-  HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, q.wdq, q.wds, q.sv.wdtq,
-                        q.sv.wdts));
+  // The backward's data gradients contract over the weights' other axis.
+  // Blockwise, a 128 x 128 block has one scale either way, so they read the
+  // forward codes along the weight rows: those go straight into `saved` when
+  // it is kept.  MX blocks run along one axis: a second, transposed encoding
+  // (from the same read) goes into `saved`.
+  uint8_t* wguq = q.wguq; void* wgus = q.wgus;
+  uint8_t* wdq = q.wdq; void* wds = q.wds;
+  if (!mx && q.sv.wgu_dgq) { wguq = q.sv.wgu_dgq; wgus = q.sv.wgu_dgs; }
+  if (!mx && q.sv.wd_dgq) { wdq = q.sv.wd_dgq; wds = q.sv.wd_dgs; }
+  HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, wguq, wgus,
+                        mx ? q.sv.wgu_dgq : nullptr, mx ? q.sv.wgu_dgs : nullptr));
+  if (wdq || (mx && q.sv.wd_dgq))
+    HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, wdq, wds,
+                          mx ? q.sv.wd_dgq : nullptr, mx ? q.sv.wd_dgs : nullptr));
   {  // gate/up GEMM on token rows gathered from xq; SwiGLU and top-k weight in the epilogue
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.xq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.As = (const uint32_t*)q.xs; p.a_srow = 1; p.a_skb = a.R; p.a_s_sorted = 1;
-    p.B = q.wguq; p.b_estride = 2 * I * d; p.ldb = d;
-    p.Bs = (const uint32_t*)q.wgus; p.bs_estride = wscale_words(2 * I, d, mx);
+    p.B = wguq; p.b_estride = 2 * I * d; p.ldb = d;
+    p.Bs = (const uint32_t*)wgus; p.bs_estride = wscale_words(2 * I, d, mx);
     p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? 2 * I : 1;
     p.gateup = 1;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
@@ -693,8 +785,8 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
   p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
   p.A = q.awq; p.lda = I; p.a_src = nullptr; p.a_div = 1;
   p.As = (const uint32_t*)q.aws; p.a_srow = 1; p.a_skb = a.R;
-  p.B = q.wdq; p.b_estride = d * I; p.ldb = I;
-  p.Bs = (const uint32_t*)q.wds; p.bs_estride = wscale_words(d, I, mx);
+  p.B = wdq; p.b_estride = d * I; p.ldb = I;
+  p.Bs = (const uint32_t*)wds; p.bs_estride = wscale_words(d, I, mx);
   p.b_srow = mx ? 1 : I / 128; p.b_skb = mx ? d : 1;
   p.gateup = 0;
   p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
@@ -707,11 +799,11 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
                          void* dW_d) {
   const int64_t I = a.I, d = a.d;
   const bool mx = q.mx;
-  if (q.quant_weights) {  // the data-gradient (transposed) encodings only
-    HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, nullptr, nullptr,
-                          q.sv.wgutq, q.sv.wguts));
-    HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, nullptr, nullptr, q.sv.wdtq,
-                          q.sv.wdts));
+  if (q.quant_weights) {  // the data gradients' encodings only (see fp8_fwd_gemms)
+    HIP_RET(quant_weights(c, "quant_w_gate_up", a.w_gate_up, a.E, 2 * a.I, a.d, mx, mx ? nullptr : q.sv.wgu_dgq,
+                          mx ? nullptr : q.sv.wgu_dgs, mx ? q.sv.wgu_dgq : nullptr, mx ? q.sv.wgu_dgs : nullptr));
+    HIP_RET(quant_weights(c, "quant_w_down", a.w_down, a.E, a.d, a.I, mx, mx ? nullptr : q.sv.wd_dgq,
+                          mx ? nullptr : q.sv.wd_dgs, mx ? q.sv.wd_dgq : nullptr, mx ? q.sv.wd_dgs : nullptr));
   }
   HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx, true, a.row_of, a.k));
   {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
@@ -720,13 +812,17 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.As = (const uint32_t*)q.douts; p.a_srow = 1; p.a_skb = a.R; p.a_s_sorted = 1;
-    p.B = q.sv.wdtq; p.b_estride = I * d; p.ldb = d;
-    p.Bs = (const uint32_t*)q.sv.wdts; p.bs_estride = wscale_words(I, d, mx);
-    p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? I : 1;
+    p.B = q.sv.wd_dgq; p.b_estride = I * d;
+    p.Bs = (const uint32_t*)q.sv.wd_dgs; p.bs_estride = wscale_words(I, d, mx);
+    if (mx) {  // transposed codes [E,I,d], rows along I
+      p.ldb = d; p.b_srow = 1; p.b_skb = I;
+    } else {   // forward codes [E,d,I] read along I; scales [d/128][I/128]
+      p.ldb = I; p.b_srow = 1; p.b_skb = I / 128;
+    }
     p.gateup = 0;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Cf = q.G; p.ldc = I;
-    HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx));
+    HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx, !mx));
     HIP_RET(launch_swiglu_bwd_fp8(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, dH, dwp, q.dhq,
                                   q.dhs, mx));
   }
@@ -735,13 +831,17 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
     p.As = (const uint32_t*)q.dhs; p.a_srow = 1; p.a_skb = a.R;  // run-major (swiglu_bwd_fp8)
-    p.B = q.sv.wgutq; p.b_estride = d * 2 * I; p.ldb = 2 * I;
-    p.Bs = (const uint32_t*)q.sv.wguts; p.bs_estride = wscale_words(d, 2 * I, mx);
-    p.b_srow = mx ? 1 : 2 * I / 128; p.b_skb = mx ? d : 1;
+    p.B = q.sv.wgu_dgq; p.b_estride = d * 2 * I;
+    p.Bs = (const uint32_t*)q.sv.wgu_dgs; p.bs_estride = wscale_words(d, 2 * I, mx);
+    if (mx) {  // transposed codes [E,d,2I], rows along d
+      p.ldb = 2 * I; p.b_srow = 1; p.b_skb = d;
+    } else {   // forward codes [E,2I,d] read along d; scales [2I/128][d/128]
+      p.ldb = d; p.b_srow = 1; p.b_skb = d / 128;
+    }
     p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
     p.C = (bf16_t*)dXp; p.ldc = d;
-    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx));
+    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx, !mx));
   }
   const int nb = q.nblk_max;
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]

@@ -162,8 +162,11 @@ size_t moe_workspace_bytes(const moe_shape* shape, int op);
  * pre-activations) followed by Aw [T*k, I] (SwiGLU output times the row's
  * top-k weight), both in dtype, in expert-sorted row order.  With an fp8
  * forward (MOE_PREC_FP8_BLOCK, MOE_PREC_MXFP8) the buffer also holds the
- * transposed e4m3 weight codes and scales that the backward's data
- * gradients use (both weights are quantised once, in the forward).  The
+ * e4m3 weight codes and scales that the backward's data gradients use (both
+ * weights are quantised once, in the forward): for MOE_PREC_FP8_BLOCK the
+ * forward's own encodings (a 128 x 128 block has one scale whichever axis
+ * the contraction runs over), for MOE_PREC_MXFP8 a second, transposed
+ * encoding (its 32-value blocks run along one axis).  The
  * forward keeps these so that the backward, which repeats the layer's
  * exchange for gradients ("Prime Mega MoE Trains Giant AI Models 55%
  * Faster", section "Where MoE training loses time"), need not recompute

@@ -1,8 +1,8 @@
 """The layer's calls allocate nothing and never synchronise, so a caller
 can capture forward + backward into one HIP graph (torch.cuda.CUDAGraph)
 and replay it.  Every replay, with eager work on the same buffers in
-between, must give the eager results bit for bit, in bf16 and in blockwise
-fp8, with the routing computed inside the graph."""
+between, must give the eager results bit for bit, in bf16 and in every fp8
+precision, with the routing computed inside the graph."""
 import pytest
 import torch
 
@@ -15,6 +15,8 @@ BF = dict(dtype="bf16", logits_dtype="bf16")
 CASES = {
     "bf16": S.WORKLOADS["tiny"].scaled(T=1500, d=384, E=16, k=4, I=320, **BF),
     "fp8_block": S.WORKLOADS["tiny"].scaled(T=900, d=256, E=8, k=2, I=256, precision="fp8_block", **BF),
+    "mxfp8": S.WORKLOADS["tiny"].scaled(T=900, d=384, E=8, k=2, I=256, precision="mxfp8", **BF),
+    "fp8_bwd": S.WORKLOADS["tiny"].scaled(T=700, d=256, E=12, k=3, I=384, precision="fp8_bwd", **BF),
 }
 
 

@@ -52,7 +52,7 @@ KERNEL_SITES = [
     ("permute_kernel", "permute"), ("permute_scatter_kernel", "permute"),  # before route's scatter_kernel
     ("scan_kernel", "route_scan"), ("scatter_kernel", "route_scatter"), ("schedule_kernel", "route_schedule"),
     ("tok_of_kernel", "route_tok"),
-    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("quant_rows_kernel", "quant_x/dout/aw/dh"),
+    ("topk_grad_kernel", "topk_grad"), ("swiglu_bwd", "swiglu_bwd"), ("quant_rows_kernel", "quant_x/dout/aw"),
     ("quant_weight_kernel", "quant_w_*"), ("quant_weight_mx_kernel", "quant_w_*"),
     ("quant_tok_kernel", "quant_*_tok"),
 ]

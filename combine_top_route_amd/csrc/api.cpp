@@ -205,7 +205,7 @@ Layout layout(const moe_shape* s, int op) {
   const bool bwd = op == MOE_OP_BACKWARD || op == MOE_OP_BACKWARD_RECOMPUTE;
   if (bwd) {
     L.tok = take(sizeof(int32_t) * R);
-    L.dH = take(es * R * 2 * s->I);
+    if (!bwd_fp8(s)) L.dH = take(es * R * 2 * s->I);  // the fp8 backward encodes dH in-kernel
     // the bf16 backward first writes the down GEMM's data gradient G [R, I]
     // into this buffer, which holds the permuted dx [R, d] only later
     const bool g_in_dxp = s->dtype == MOE_BF16 && !bwd_fp8(s);
@@ -552,7 +552,7 @@ moe_status moe_backward(const moe_shape* shape, const void* dout, const void* x,
     q.G = (float*)at(workspace, L.Gf);
     q.blk_off = (const int32_t*)at(workspace, L.blk_off);
     q.nblk_max = (int)nblk_max(shape);
-    HIP_TRY(fp8_bwd_gemms(c, a, q, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
+    HIP_TRY(fp8_bwd_gemms(c, a, q, dout, H, A, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
   } else
     HIP_TRY(bf16_bwd_gemms(c, a, dout, H, A, dH, dXp, dwp, dw_gate_up, dw_down), "backward GEMMs");
   HIP_TRY(launch_topk_grad(c, dwp, dw_blocks(shape), routing->row_of, routing->topk_ids,

@@ -217,12 +217,15 @@ hipError_t launch_quant_tok(const LaunchCtx& c, const char* name, const void* sr
                             const int32_t* blk_off, int E, int nblk_max, uint8_t* q, void* s,
                             bool mx, bool run_major);
 
-// fp8 path's SwiGLU backward row pass: as launch_swiglu_bwd from an fp32 G
-// [R,I], plus dH's e4m3 row codes dhq [R,2I] and scale words dhs, run-major
-// [2I/128, R] (I % 128 == 0).
-hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
-                                 const float* topk_w, const int32_t* src_of, int R, int I, float lim,
-                                 void* dH, float* dw, uint8_t* dhq, void* dhs, bool mx);
+// fp8 path's SwiGLU backward: from an fp32 G [R,I] and H, dH (bf16-rounded,
+// never stored) in two e4m3 encodings: row codes dhq [R,2I] with scale words
+// run-major dhs [2I/128, R], and the transposed token blocks of
+// launch_quant_tok (run_major) in q / s; per-row partials of <G, a> into dw
+// [R, I/128] (I % 128 == 0).
+hipError_t launch_swiglu_bwd_tok(const LaunchCtx& c, const float* G, const void* H, const float* topk_w,
+                                 const int32_t* src_of, int R, int I, float lim, const int32_t* offsets,
+                                 const int32_t* blk_off, int E, int nblk_max, float* dw, uint8_t* dhq,
+                                 void* dhs, uint8_t* q, void* s, bool mx);
 
 // Weight codes the backward's data gradients read, left in `saved` by the
 // fp8 forward: blockwise the forward encodings (one scale per 128 x 128
@@ -262,7 +265,6 @@ int fp8_dw_blocks(int I);
 hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q, void* H, void* Aw,
                          void* Yw);
 hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
-                         const void* H, const void* Aw, void* dH, void* dXp, float* dwp, void* dW_gu,
-                         void* dW_d);
+                         const void* H, const void* Aw, void* dXp, float* dwp, void* dW_gu, void* dW_d);
 
 }  // namespace moe

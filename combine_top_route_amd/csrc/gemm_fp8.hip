@@ -728,7 +728,7 @@ hipError_t launch_wgrad8(const LaunchCtx& c, const char* name, const Wgrad8Args&
 
 }  // namespace
 
-int fp8_dw_blocks(int) { return 1; }
+int fp8_dw_blocks(int I) { return I / 128; }  // one partial per 128 columns of I
 
 namespace {
 // Scale words per expert of a weight [N, K] encoded for a GEMM with K along
@@ -795,8 +795,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
 }
 
 hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q, const void* dout,
-                         const void* H, const void* Aw, void* dH, void* dXp, float* dwp, void* dW_gu,
-                         void* dW_d) {
+                         const void* H, const void* Aw, void* dXp, float* dwp, void* dW_gu, void* dW_d) {
   const int64_t I = a.I, d = a.d;
   const bool mx = q.mx;
   if (q.quant_weights) {  // the data gradients' encodings only (see fp8_fwd_gemms)
@@ -806,8 +805,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
                           mx ? nullptr : q.sv.wd_dgs, mx ? q.sv.wd_dgq : nullptr, mx ? q.sv.wd_dgs : nullptr));
   }
   HIP_RET(launch_quant_rows(c, "quant_dout", dout, d, a.T, a.d, q.doutq, q.douts, mx, true, a.row_of, a.k));
-  {  // down dgrad: G = dout_t W_down[e] (fp32); one row pass then forms dH,
-     // <G, a> and dH's row codes
+  {  // down dgrad: G = dout_t W_down[e] (fp32)
     Rows8Args p = {};
     p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
     p.A = q.doutq; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
@@ -823,25 +821,6 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
     p.Cf = q.G; p.ldc = I;
     HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx, !mx));
-    HIP_RET(launch_swiglu_bwd_fp8(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, dH, dwp, q.dhq,
-                                  q.dhs, mx));
-  }
-  {  // gate/up dgrad: dXp = dH W_gate_up[e]
-    Rows8Args p = {};
-    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
-    p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
-    p.As = (const uint32_t*)q.dhs; p.a_srow = 1; p.a_skb = a.R;  // run-major (swiglu_bwd_fp8)
-    p.B = q.sv.wgu_dgq; p.b_estride = d * 2 * I;
-    p.Bs = (const uint32_t*)q.sv.wgu_dgs; p.bs_estride = wscale_words(d, 2 * I, mx);
-    if (mx) {  // transposed codes [E,d,2I], rows along d
-      p.ldb = 2 * I; p.b_srow = 1; p.b_skb = d;
-    } else {   // forward codes [E,2I,d] read along d; scales [2I/128][d/128]
-      p.ldb = d; p.b_srow = 1; p.b_skb = d / 128;
-    }
-    p.gateup = 0;
-    p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
-    p.C = (bf16_t*)dXp; p.ldc = d;
-    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx, !mx));
   }
   const int nb = q.nblk_max;
   {  // down wgrad: dW_d[e][c, i] = sum_r dout[t_r, c] Aw[r, i]
@@ -857,9 +836,29 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
     HIP_RET(launch_wgrad8<0>(c, "gemm_down_wgrad", p, mx));
   }
+  // SwiGLU backward from G: dH never leaves the kernel; its row codes feed
+  // the gate/up dgrad and its token-block codes (into tqa, free once the
+  // down wgrad has run) the gate/up wgrad
+  HIP_RET(launch_swiglu_bwd_tok(c, q.G, H, a.topk_w, a.src_of, a.R, a.I, a.swiglu_lim, a.offsets, q.blk_off,
+                                a.E, nb, dwp, q.dhq, q.dhs, q.tqa, q.tsa, mx));
+  {  // gate/up dgrad: dXp = dH W_gate_up[e]
+    Rows8Args p = {};
+    p.offsets = a.offsets; p.tile_off = a.tile_off; p.tiles = a.tiles; p.E = a.E;
+    p.A = q.dhq; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
+    p.As = (const uint32_t*)q.dhs; p.a_srow = 1; p.a_skb = a.R;  // run-major
+    p.B = q.sv.wgu_dgq; p.b_estride = d * 2 * I;
+    p.Bs = (const uint32_t*)q.sv.wgu_dgs; p.bs_estride = wscale_words(d, 2 * I, mx);
+    if (mx) {  // transposed codes [E,d,2I], rows along d
+      p.ldb = 2 * I; p.b_srow = 1; p.b_skb = d;
+    } else {   // forward codes [E,2I,d] read along d; scales [2I/128][d/128]
+      p.ldb = d; p.b_srow = 1; p.b_skb = d / 128;
+    }
+    p.gateup = 0;
+    p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+    p.C = (bf16_t*)dXp; p.ldc = d;
+    HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx, !mx));
+  }
   {  // gate/up wgrad: dW_gu[e][j, c] = sum_r dH[r, j] x[t_r, c]
-    HIP_RET(launch_quant_tok(c, "quant_dh_tok", dH, 2 * I, nullptr, 1, 2 * a.I, a.offsets, q.blk_off,
-                             a.E, nb, q.tqa, q.tsa, mx, true));
     HIP_RET(launch_quant_tok(c, "quant_x_tok", a.x, d, a.src_of, a.k, a.d, a.offsets, q.blk_off, a.E,
                              nb, q.tqb, q.tsb, mx, true));
     Wgrad8Args p = {};

@@ -162,6 +162,25 @@ __device__ __forceinline__ uint32_t gather4_codes(uint32_t code, int base, int s
          ((uint32_t)__shfl((int)code, base + 3 * stride, kWave) << 24);
 }
 
+// Lane exchanges within a row of 16 lanes by DPP (no LDS trip): quad
+// permutations 0xB1 (the lane xor 1) and 0x4E (xor 2), and the half-row
+// mirror (lane i of each 8 takes lane 7 - i).
+constexpr int kHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Reduction over the four lanes 4m .. 4m + 3 of a quad: combine with the
+// lane xor 1, then with the lane xor 2.
+template <class Op>
+__device__ __forceinline__ float quad_reduce(float v, Op op) {
+  v = op(v, dpp_f32<0xB1>(v));
+  return op(v, dpp_f32<0x4E>(v));
+}
+__device__ __forceinline__ float quad_max(float v) {
+  return quad_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
 // Eight values divided by s, as eight e4m3 codes.
 __device__ __forceinline__ u32x2_t quant8(const float (&f)[8], float s) {
   float g[8];
@@ -467,8 +486,8 @@ __device__ __forceinline__ void quant_tok_chunk(const uint8_t* tile, int t, int 
   u32x4_t q0, q1;
   uint32_t w0, w1;
   if constexpr (MX) {  // a 32-row block spans lanes rg = 2m, 2m + 1
-    a0 = fmaxf(a0, __shfl_xor(a0, 1, kWave));
-    a1 = fmaxf(a1, __shfl_xor(a1, 1, kWave));
+    a0 = fmaxf(a0, dpp_f32<0xB1>(a0));
+    a1 = fmaxf(a1, dpp_f32<0xB1>(a1));
     const MxScale s0 = mx_scale(a0), s1 = mx_scale(a1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -479,11 +498,10 @@ __device__ __forceinline__ void quant_tok_chunk(const uint8_t* tile, int t, int 
     w0 = gather4_codes(s0.code, base, 2);
     w1 = gather4_codes(s1.code, base, 2);
   } else {
-#pragma unroll
-    for (int off = 4; off >= 1; off >>= 1) {
-      a0 = fmaxf(a0, __shfl_xor(a0, off, kWave));
-      a1 = fmaxf(a1, __shfl_xor(a1, off, kWave));
-    }
+    a0 = quad_max(a0);  // then the other quad of the eight lanes rg
+    a1 = quad_max(a1);
+    a0 = fmaxf(a0, dpp_f32<kHalfMirror>(a0));
+    a1 = fmaxf(a1, dpp_f32<kHalfMirror>(a1));
     const float s0 = block_scale(a0), s1 = block_scale(a1);
     const float r0 = __fdiv_rn(1.0f, s0), r1 = __fdiv_rn(1.0f, s1);
     quot_run2<16>(f0, s0, r0, f1, s1, r1, [&] {
@@ -557,121 +575,161 @@ __global__ __launch_bounds__(256) void quant_tok_kernel(const bf16_t* __restrict
   }
 }
 
-// SwiGLU backward of one row per wave from G = dout_t W_down[e] (fp32), as
-// in the bf16 path (clamp lim included), that also encodes the bf16-rounded dH in 1 x 128 blocks
-// (fp32 scales) or, MX, 1 x 32 blocks (a word of four E8M0 codes per 128
-// columns), the words stored run-major ([I/64][R]): the A operand of the
-// gate/up dgrad.  Lane l handles the 8-column
-// chunks l, l + 64, ... of the gate and of the up half; a 16-lane group
-// covers 128 columns.  Requires I % 128 == 0.
+// SwiGLU backward with both fp8 encodings of dH, for the blockwise and MX
+// backwards: one work-group per (128-row run of an expert's segment, 128
+// columns of I), as quant_tok_kernel's runs.  From G = dout_t W_down[e]
+// (fp32) and the stored H it forms dH (bf16-rounded, as the bf16 path
+// stores it; clamp lim as there), then encodes it twice without writing it:
+// rows in 1 x 128 blocks (blockwise fp32 scales) or 1 x 32 (MX), the gate/up
+// dgrad's operand (codes dhq [R, 2I], words run-major dhs [2I/128][R]); and
+// columns in the run's 128-row blocks (or 32-row, MX), transposed, the
+// gate/up wgrad's operand (q [2I][128 nblk], words as quant_tok_kernel's).
+// It also writes <G_r, a_r> over its 128 columns to dw[r * (I/128) + chunk].
+// Thread t: row t / 4 of the run, the four 8-column pieces 8 (t % 4) + 32 j
+// of the chunk (gate and up).  The bf16 dH goes through LDS as four
+// 128 x 64 tiles (gate 0-63, gate 64-127, up 0-63, up 64-127) for the
+// column encoding.
 template <bool MX>
-__global__ __launch_bounds__(256) void swiglu_bwd_fp8_kernel(
-    const f32x4_t* __restrict__ G, const u32x4_t* __restrict__ H, const float* __restrict__ topk_w,
-    const int32_t* __restrict__ src_of, int R, int chunks, float lim, u32x4_t* __restrict__ dH,
-    float* __restrict__ dw, uint8_t* __restrict__ dhq, uint32_t* __restrict__ dhs) {
-  // dH scale words run-major: word (row r, 128-column block j) at dhs[j * R + r]
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const int lane = threadIdx.x & 63;
-  const float wr = topk_w[src_of[r]];
-  const f32x4_t* Gr = G + (int64_t)r * 2 * chunks;  // 8 columns = two float4
-  const u32x4_t* Hg = H + (int64_t)r * 2 * chunks;
-  u32x4_t* Dr = dH + (int64_t)r * 2 * chunks;
-  uint8_t* Qr = dhq + (int64_t)r * 2 * chunks * 8;
-  uint32_t* Sr = dhs + r;
+__global__ __launch_bounds__(512) void swiglu_bwd_tok_kernel(
+    const float* __restrict__ G, const bf16_t* __restrict__ H, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ src_of, int R, int I, float lim, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ blk_off, int E, float* __restrict__ dw, uint8_t* __restrict__ dhq,
+    uint32_t* __restrict__ dhs, uint8_t* __restrict__ q, int64_t ldq, uint32_t* __restrict__ s,
+    int64_t s_row, int64_t s_blk) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][128 * 136];
+  const int b = blockIdx.x;
+  if (b >= blk_off[E]) return;
+  int lo = 0, hi = E;  // largest e with blk_off[e] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (blk_off[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (b - blk_off[e]) * 128;
+  const int n = min(128, offsets[e + 1] - r0);
+  const int chunk = blockIdx.y, c0 = chunk * 128;
+  const int t = threadIdx.x, i = t >> 2, qd = t & 3;
+  const bool ok = i < n;
+  const int64_t r = r0 + (ok ? i : 0);
+  const float wr = ok ? topk_w[src_of[r]] : 0.0f;
+  // chunk j (0..3) of this thread: columns c0 + 8 qd + 32 j .. +7, so the
+  // four threads of a row read 32 (gate/up: 16) contiguous bytes each
+  const float* Gr = G + r * I + c0 + 8 * qd;
+  const bf16_t* Hg = H + r * 2 * I + c0 + 8 * qd;
+  const bf16_t* Hu = Hg + I;
+  f32x4_t gr[8];
+  u32x4_t hg[4], hu[4];
+  const f32x4_t fz = {0.0f, 0.0f, 0.0f, 0.0f};
+  const u32x4_t uz = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    gr[2 * j] = ok ? *(const f32x4_t*)(Gr + 32 * j) : fz;
+    gr[2 * j + 1] = ok ? *(const f32x4_t*)(Gr + 32 * j + 4) : fz;
+    hg[j] = ok ? *(const u32x4_t*)(Hg + 32 * j) : uz;
+    hu[j] = ok ? *(const u32x4_t*)(Hu + 32 * j) : uz;
+  }
+  u32x4_t pg[4], pu[4];  // bf16 dH of chunk j, packed pairs
   float part = 0.0f;
-  for (int c0 = 0; c0 < chunks; c0 += kWave) {  // uniform trip count
-    const int c = c0 + lane;
-    const bool ok = c < chunks;  // whole 16-lane groups share ok (chunks % 16 == 0)
-    float gv[8], g[8], u[8], dg[8], du[8];
-    u32x4_t zero = {0, 0, 0, 0};
-    const f32x4_t fz = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4_t g0 = ok ? Gr[2 * c] : fz, g1 = ok ? Gr[2 * c + 1] : fz;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gv[i] = g0[i];
-      gv[4 + i] = g1[i];
-    }
-    unpack8(ok ? Hg[c] : zero, g);
-    unpack8(ok ? Hg[chunks + c] : zero, u);
+  for (int j = 0; j < 4; ++j) {
+    float g[8], u[8];
+    unpack8(hg[j], g);
+    unpack8(hu[j], u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float gc = clamp_gate(g[i], lim), uc = clamp_up(u[i], lim);
-      const float sg = sigmoidf_(gc);
-      part += gv[i] * (gc * sg * uc);
-      const float dA = wr * gv[i];
-      dg[i] = g[i] <= lim ? dA * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
-      du[i] = fabsf(u[i]) <= lim ? dA * gc * sg : 0.0f;
-    }
-    // bf16 rounding first: the codes encode the stored dH
-    u32x4_t pg, pu;
+    for (int m = 0; m < 8; m += 2) {
+      float dg[2], du[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pg[i] = pack_bf16x2(dg[2 * i], dg[2 * i + 1]);
-      pu[i] = pack_bf16x2(du[2 * i], du[2 * i + 1]);
-    }
-    unpack8(pg, dg);
-    unpack8(pu, du);
-    float ag = 0.0f, au = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ag = fmaxf(ag, fabsf(dg[i]));
-      au = fmaxf(au, fabsf(du[i]));
-    }
-    u32x2_t qg, qu;
-    uint32_t wg, wu;
-    if constexpr (MX) {  // four lanes per 32-column block
-#pragma unroll
-      for (int off = 2; off >= 1; off >>= 1) {
-        ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
-        au = fmaxf(au, __shfl_xor(au, off, kWave));
+      for (int x = 0; x < 2; ++x) {
+        const float gv = gr[2 * j + ((m + x) >> 2)][(m + x) & 3];
+        const float gc = clamp_gate(g[m + x], lim), uc = clamp_up(u[m + x], lim);
+        const float sg = sigmoidf_(gc);
+        part += gv * (gc * sg * uc);
+        const float dA = wr * gv;
+        dg[x] = g[m + x] <= lim ? dA * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+        du[x] = fabsf(u[m + x]) <= lim ? dA * gc * sg : 0.0f;
       }
-      const MxScale sgate = mx_scale(ag), sup = mx_scale(au);
-      qg = quant8_mx(dg, sgate.inv);
-      qu = quant8_mx(du, sup.inv);
-      wg = gather4_codes(sgate.code, lane & ~15, 4);
-      wu = gather4_codes(sup.code, lane & ~15, 4);
-    } else {
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        ag = fmaxf(ag, __shfl_xor(ag, off, kWave));
-        au = fmaxf(au, __shfl_xor(au, off, kWave));
-      }
-      const float sgate = block_scale(ag), sup = block_scale(au);
-      qg = quant8(dg, sgate);
-      qu = quant8(du, sup);
-      wg = __float_as_uint(sgate);
-      wu = __float_as_uint(sup);
-    }
-    if (ok) {
-      Dr[c] = pg;
-      Dr[chunks + c] = pu;
-      *(u32x2_t*)(Qr + c * 8) = qg;
-      *(u32x2_t*)(Qr + (chunks + c) * 8) = qu;
-      if ((lane & 15) == 0) {
-        Sr[(int64_t)(c / 16) * R] = wg;
-        Sr[(int64_t)((chunks + c) / 16) * R] = wu;
-      }
+      pg[j][m >> 1] = pack_bf16x2(dg[0], dg[1]);
+      pu[j][m >> 1] = pack_bf16x2(du[0], du[1]);
     }
   }
+  // the bf16 dH into the column-encoding tiles (column c of the chunk: tile
+  // c / 64, byte 2 (c % 64) of a 136-byte row)
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
-  if (lane == 0) dw[r] = part;
+  for (int j = 0; j < 4; ++j) {
+    const int off = i * 136 + 16 * qd + 64 * (j & 1);
+    *(u32x4_t*)(tiles[j >> 1] + off) = pg[j];
+    *(u32x4_t*)(tiles[2 + (j >> 1)] + off) = pu[j];
+  }
+  // dw partial over the chunk's 128 columns (four threads of the row)
+  part = quad_reduce(part, [](float a, float b) { return a + b; });
+  if (ok && qd == 0) dw[r * (I / 128) + chunk] = part;
+  // row encodings of the gate (half 0) and up (half 1) columns: a 1 x 128
+  // block spans the four threads of the row; MX block j is their chunks j
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    float f[4][8], am[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unpack8(half ? pu[j] : pg[j], f[j]);
+      am[j] = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) am[j] = fmaxf(am[j], fabsf(f[j][x]));
+    }
+    u32x2_t code[4];
+    uint32_t word;
+    if constexpr (MX) {
+      word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const MxScale sc = mx_scale(quad_max(am[j]));
+        code[j] = quant8_mx(f[j], sc.inv);
+        word |= sc.code << (8 * j);
+      }
+    } else {
+      const float sc = block_scale(quad_max(fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]))));
+      quot_run<32>(&f[0][0], sc, __fdiv_rn(1.0f, sc), [&] {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          code[j][0] = e4m3x4(f[j][0], f[j][1], f[j][2], f[j][3]);
+          code[j][1] = e4m3x4(f[j][4], f[j][5], f[j][6], f[j][7]);
+        }
+      });
+      word = __float_as_uint(sc);
+    }
+    if (ok) {
+      const int col = half * I + c0;
+      uint8_t* dq = dhq + r * 2 * I + col + 8 * qd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(u32x2_t*)(dq + 32 * j) = code[j];
+      if (qd == 0) dhs[(int64_t)(col >> 7) * R + r] = word;
+    }
+  }
+  __syncthreads();
+  // column encodings: threads 0-255 the gate tiles, 256-511 the up tiles
+  const int grp = t >> 8, tt = t & 255;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    quant_tok_chunk<MX>(tiles[2 * grp + k], tt, grp * I + c0 + 64 * k, b, q, ldq, s, s_row, s_blk);
 }
 
 }  // namespace
 
-hipError_t launch_swiglu_bwd_fp8(const LaunchCtx& c, const float* G, const void* H,
-                                 const float* topk_w, const int32_t* src_of, int R, int I, float lim,
-                                 void* dH, float* dw, uint8_t* dhq, void* dhs, bool mx) {
+hipError_t launch_swiglu_bwd_tok(const LaunchCtx& c, const float* G, const void* H, const float* topk_w,
+                                 const int32_t* src_of, int R, int I, float lim, const int32_t* offsets,
+                                 const int32_t* blk_off, int E, int nblk_max, float* dw, uint8_t* dhq,
+                                 void* dhs, uint8_t* q, void* s, bool mx) {
+  // token-block words run-major (s_row = 1, s_blk = 2I), as quant_tok's
+  const int64_t s_row = 1, s_blk = 2 * (int64_t)I, ldq = (int64_t)nblk_max * 128;
+  const dim3 grid(nblk_max, I / 128);
   if (mx)
-    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<true>, dim3((R + 3) / 4), dim3(256), 0,
-               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, lim, (u32x4_t*)dH, dw,
-               dhq, (uint32_t*)dhs);
+    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_tok_kernel<true>, grid, dim3(512), 0, G, (const bf16_t*)H, topk_w,
+               src_of, R, I, lim, offsets, blk_off, E, dw, dhq, (uint32_t*)dhs, q, ldq, (uint32_t*)s, s_row,
+               s_blk);
   else
-    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_fp8_kernel<false>, dim3((R + 3) / 4), dim3(256), 0,
-               (const f32x4_t*)G, (const u32x4_t*)H, topk_w, src_of, R, I / 8, lim, (u32x4_t*)dH, dw,
-               dhq, (uint32_t*)dhs);
+    MOE_LAUNCH(c, "swiglu_bwd", swiglu_bwd_tok_kernel<false>, grid, dim3(512), 0, G, (const bf16_t*)H, topk_w,
+               src_of, R, I, lim, offsets, blk_off, E, dw, dhq, (uint32_t*)dhs, q, ldq, (uint32_t*)s, s_row,
+               s_blk);
   return hipSuccess;
 }
 

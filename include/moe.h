@@ -79,8 +79,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * fp8_bwd option): FP8 in the backward only -- the forward of the bf16 layer,
  * then the backward of MOE_PREC_FP8_BLOCK on the saved bf16 H and Aw (the
  * backward quantises the weights itself).  The fp8 precisions require dtype
- * MOE_BF16, d and I multiples of 128 and T*k*max(d, 2I)/128 < 2^31; H, Aw
- * and dH stay bf16. */
+ * MOE_BF16, d and I multiples of 128 and T*k*max(d, 2I)/128 < 2^31; H and
+ * Aw are stored in bf16, and dH is rounded to bf16 before it is encoded. */
 typedef enum {
   MOE_PREC_NATIVE = 0,
   MOE_PREC_FP8_BLOCK = 1,

@@ -134,6 +134,38 @@ SMALL = {
 }
 
 
+# rows per expert: a whole 128-row run, one row past it, a single row, none,
+# one short of two runs, two runs, one short of a run, three runs
+RUN_COUNTS = [128, 129, 1, 0, 255, 256, 127, 384]
+
+
+@pytest.mark.parametrize("precision", ["fp8_block", "mxfp8"])
+def test_fp8_layer_run_boundaries(precision):
+    """Expert segments that end exactly at, one past and one short of a
+    128-row run boundary, hold one row, or none.  The token-run encodings
+    (of x, dout and Aw, and of dH, which the SwiGLU backward writes itself)
+    and the weight gradients over them meet the oracle at the layer
+    tolerance, and the empty expert's gradients are zero."""
+    counts = np.array(RUN_COUNTS)
+    E, k = len(counts), 2
+    T = int(counts.sum()) // k
+    slots = np.repeat(np.arange(E, dtype=np.int32), counts)   # expert order
+    ids = np.ascontiguousarray(np.stack([slots[:T], slots[T:]], axis=1))
+    assert np.all(ids[:, 0] != ids[:, 1])                     # no expert holds T rows
+    w = np.random.default_rng(8).uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    wl = BASE.scaled(T=T, d=256, E=E, k=k, I=256, precision=precision)
+    print(f"case {precision}: {wl} counts {RUN_COUNTS}", flush=True)
+    inp = S.make_inputs(wl, seed=9)
+    ids_t, w_t = torch.from_numpy(ids), torch.from_numpy(w)
+    gpu = run_gpu(wl, inp, ids=ids_t, w=w_t)
+    ref = run_oracle(wl, inp, ids=ids_t, w=w_t)
+    assert np.array_equal(ref["rt"]["counts"], counts)
+    check_routing(gpu, ref)
+    errs = check_floats(gpu, ref, TOL["fp8"])
+    assert np.all(gpu["dW_gate_up"][3] == 0) and np.all(gpu["dW_down"][3] == 0)
+    print(precision, errs)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_fp8_layer_parity_small(name):
     wl = SMALL[name]

@@ -212,7 +212,7 @@ def cpu_baseline(wl, inp: dict, tokens: int):
 
 COPY_BYTES = 1 << 30
 # oracle sample per workload: about 10-30 s of float64 numpy on 16 host cores
-CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q235b": 8192, "fp8_skew": 2048,
+CPU_SAMPLE_TOKENS = {"q30b": 16384, "q30b_t4096": 4096, "q30b_ep8": 131072, "q235b": 8192, "fp8_skew": 2048,
                      "mxfp8_skew": 2048, "fp8_bwd_skew": 2048}
 
 

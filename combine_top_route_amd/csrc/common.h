@@ -62,6 +62,15 @@ __device__ __forceinline__ float clamp_up(float u, float lim) { return __builtin
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Order of a row GEMM's tiles within an expert.  Either order re-reads one
+// operand once per group of tiles that runs together: taken N-tile-major,
+// the token rows (once per N tile); taken row-tile-major, the weight (once
+// per group of row tiles).  The re-read operand should be the one that
+// stays in the caches, the smaller: row-tile-major when the token operand's
+// distinct bytes exceed the weight's (as for a GPU's expert-parallel share,
+// few experts with many rows), else N-tile-major.
+inline int rows_tile_order(int64_t token_bytes, int64_t weight_bytes) { return token_bytes > weight_bytes; }
+
 // ----------------------------------------------------------------------------
 // Host side: every launcher enqueues through MOE_LAUNCH, which checks the
 // launch status and, while the API layer is timing kernels, hands the

@@ -623,6 +623,7 @@ struct RowsArgs {
   const bf16_t* B;
   int64_t b_estride, ldb;
   int N, K, n_tiles;  // N: output columns (gate/up: gate columns I)
+  int row_major;      // tile order within an expert (rows_tile_order)
   const int32_t* offsets;
   const int32_t* tile_off;
   const int4* tiles;  // row-tile descriptors {expert, first row, segment end, expert's first tile}
@@ -779,8 +780,9 @@ struct RowTile {
 
 // Logical tile L: an expert's (row tile, N tile) pairs are a contiguous
 // range of L, taken N-tile-major (work-groups that run close together share
-// a weight tile through L2); the descriptor of L's row-tile-major row tile
-// lies in the same expert and gives the range.
+// a weight tile through L2) or, with row_major, row-tile-major (they share
+// token rows); the descriptor of L's row-tile-major row tile lies in the
+// same expert and gives the range.
 __device__ __forceinline__ RowTile decode_tile(const RowsArgs& p, int L) {
   const int T = L / p.n_tiles;
   const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
@@ -791,8 +793,9 @@ __device__ __forceinline__ RowTile decode_tile(const RowsArgs& p, int L) {
   RowTile t;
   t.e = d0.x;
   t.seg1 = d0.z;
-  t.nt = j / nrt;
-  t.m0 = seg0 + (j - t.nt * nrt) * TBM;
+  const int rt = p.row_major ? j / p.n_tiles : j % nrt;
+  t.nt = p.row_major ? j - rt * p.n_tiles : j / nrt;
+  t.m0 = seg0 + rt * TBM;
   return t;
 }
 
@@ -1121,6 +1124,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
     p.A = (const bf16_t*)a.x; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
+    p.row_major = rows_tile_order(a.T * d, a.E * 2 * I * d);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I; p.lim = a.swiglu_lim;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     hipError_t err = launch_rows<EPI_GATEUP, B_MK_GATEUP>(c, "gemm_gateup_fwd", p, a.R, a.persistent);
@@ -1133,6 +1137,7 @@ hipError_t bf16_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, void* H, void*
   q.A = (const bf16_t*)Aw; q.lda = I; q.a_src = nullptr; q.a_div = 1;
   q.B = (const bf16_t*)a.w_down; q.b_estride = d * I; q.ldb = I;
   q.N = a.d; q.K = a.I; q.n_tiles = (int)cdiv(a.d, TBN);
+  q.row_major = rows_tile_order(a.R * I, a.E * d * I);
   q.C = (bf16_t*)Yw; q.ldc = d;
   return launch_rows<EPI_STORE, B_MK>(c, "gemm_down_fwd", q, a.R, a.persistent);
 }
@@ -1150,6 +1155,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.A = (const bf16_t*)dout; p.lda = d; p.a_src = a.src_of; p.a_div = a.k;
     p.B = (const bf16_t*)a.w_down; p.b_estride = d * I; p.ldb = I;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
+    p.row_major = rows_tile_order(a.T * d, a.E * d * I);
     p.C = G; p.ldc = I;
     err = launch_rows<EPI_STORE, B_KM, 1>(c, "gemm_down_dgrad", p, a.R, a.persistent);
     if (err != hipSuccess) return err;
@@ -1172,6 +1178,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.A = (const bf16_t*)dH; p.lda = 2 * I; p.a_src = nullptr; p.a_div = 1;
     p.B = (const bf16_t*)a.w_gate_up; p.b_estride = 2 * I * d; p.ldb = d;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+    p.row_major = rows_tile_order(a.R * 2 * I, a.E * 2 * I * d);
     p.C = (bf16_t*)dXp; p.ldc = d;
     err = launch_rows<EPI_STORE, B_KM>(c, "gemm_gateup_dgrad", p, a.R, a.persistent);
     if (err != hipSuccess) return err;

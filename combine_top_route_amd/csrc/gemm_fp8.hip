@@ -477,6 +477,7 @@ struct Rows8Args {
   // forward layout, read by a data gradient); b_srow and b_skb step the
   // scale words per 128 features and per K step as above
   int N, K, n_tiles;  // N: output features (gate/up: gate columns I)
+  int row_major;      // tile order within an expert (rows_tile_order)
   const int32_t* offsets;
   const int32_t* tile_off;
   const int4* tiles;  // row-tile descriptors {expert, first row, segment end, expert's first tile}
@@ -612,16 +613,18 @@ __global__ __launch_bounds__(NTHR, 1) void rows8_kernel(Rows8Args p) {
   if (L < 0) return;
   // An expert's (row tile, N tile) pairs are a contiguous range of L, taken
   // N-tile-major (work-groups that start close together share a weight tile
-  // through L2); the descriptor of L's row-tile-major row tile lies in the
-  // same expert and gives the range.
+  // through L2) or, with row_major, row-tile-major (they share token rows);
+  // the descriptor of L's row-tile-major row tile lies in the same expert
+  // and gives the range.
   const int T = L / p.n_tiles;
   const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
   const int e = d0.x, seg1 = d0.z, first = d0.w;
   const int seg0 = d0.y - (T - first) * TBM;
   const int nrt = (seg1 - seg0 + TBM - 1) / TBM;
   const int j = L - first * p.n_tiles;
-  const int nt = j / nrt;
-  const int m0 = seg0 + (j - nt * nrt) * TBM;
+  const int rt = p.row_major ? j / p.n_tiles : j % nrt;
+  const int nt = p.row_major ? j - rt * p.n_tiles : j / nrt;
+  const int m0 = seg0 + rt * TBM;
   const int rows = seg1 - m0;
   if (rows <= TBM / 4) rows8_tile<EPI, SC, TBM / 4, KN>(p, smem, nt, e, m0, seg1);
   else if (rows <= TBM / 2) rows8_tile<EPI, SC, TBM / 2, KN>(p, smem, nt, e, m0, seg1);
@@ -775,6 +778,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
     p.b_srow = mx ? 1 : d / 128; p.b_skb = mx ? 2 * I : 1;
     p.gateup = 1;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN / 2);
+    p.row_major = rows_tile_order(a.T * d, a.E * 2 * I * d);
     p.H = (bf16_t*)H; p.Aout = (bf16_t*)Aw; p.I = a.I; p.lim = a.swiglu_lim;
     p.topk_w = a.topk_w; p.src_of = a.src_of;
     HIP_RET(launch_rows8<EPI_GATEUP, 0>(c, "gemm_gateup_fwd", p, a.R, mx));
@@ -790,6 +794,7 @@ hipError_t fp8_fwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Fwd& q
   p.b_srow = mx ? 1 : I / 128; p.b_skb = mx ? d : 1;
   p.gateup = 0;
   p.N = a.d; p.K = a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+  p.row_major = rows_tile_order(a.R * I, a.E * d * I);
   p.C = (bf16_t*)Yw; p.ldc = d;
   return launch_rows8<EPI_STORE, 0>(c, "gemm_down_fwd", p, a.R, mx);
 }
@@ -819,6 +824,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     }
     p.gateup = 0;
     p.N = a.I; p.K = a.d; p.n_tiles = (int)cdiv(a.I, TBN);
+    p.row_major = rows_tile_order(a.T * d, a.E * d * I);
     p.Cf = q.G; p.ldc = I;
     HIP_RET(launch_rows8<EPI_STORE_F32, 2>(c, "gemm_down_dgrad", p, a.R, mx, !mx));
   }
@@ -855,6 +861,7 @@ hipError_t fp8_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const Fp8Bwd& q
     }
     p.gateup = 0;
     p.N = a.d; p.K = 2 * a.I; p.n_tiles = (int)cdiv(a.d, TBN);
+    p.row_major = rows_tile_order(a.R * 2 * I, a.E * 2 * I * d);
     p.C = (bf16_t*)dXp; p.ldc = d;
     HIP_RET(launch_rows8<EPI_STORE, 1>(c, "gemm_gateup_dgrad", p, a.R, mx, !mx));
   }

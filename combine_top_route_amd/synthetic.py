@@ -71,6 +71,10 @@ WORKLOADS = {
     "tiny": Workload("tiny", 128, 64, 8, 2, 128, "f32", "f32", "native", "none"),
     "q30b_t4096": Workload("q30b_t4096", 4096, 2048, 128, 8, 768, "bf16", "bf16", "native", "none"),
     "q30b": Workload("q30b", 16384, 2048, 128, 8, 768, "bf16", "bf16", "native", "none"),
+    # one GPU's share of the q30b layer under 8-way expert parallelism: the
+    # 16 experts it holds and the 131,072 rows the dispatch exchange brings
+    # it, each row its own token (k = 1), about 8192 rows per expert
+    "q30b_ep8": Workload("q30b_ep8", 131072, 2048, 16, 1, 768, "bf16", "bf16", "native", "none"),
     "q235b": Workload("q235b", 16384, 4096, 128, 8, 1536, "bf16", "bf16", "native", "normal", 0.5),
     "fp8_skew": Workload("fp8_skew", 16384, 4096, 128, 8, 1536, "bf16", "bf16", "fp8_block", "zipf"),
     # the same skewed layer in MXFP8 (32-value blocks, power-of-two scales)

@@ -131,6 +131,9 @@ SMALL = {
     # the largest hidden and intermediate sizes the boundary accepts
     "fp8_max_d": BASE.scaled(T=40, d=16384, E=4, k=2, I=128),
     "fp8_max_i": BASE.scaled(T=40, d=128, E=3, k=2, I=16384),
+    # few experts with many rows: every row GEMM takes its tiles
+    # row-tile-major (token operands larger than the weights)
+    "fp8_ep_share": BASE.scaled(T=3000, d=512, E=2, k=1, I=512),
 }
 
 

@@ -49,6 +49,10 @@ SMALL_CASES = {
     # the most experts the boundary accepts: about a dozen rows each, many
     # experts empty, every row tile a quarter-height tail
     "bf16_e1024": TINY.scaled(T=1500, d=64, E=1024, k=8, I=64, **BF),
+    # few experts with many rows (token operands larger than the weights):
+    # every row GEMM takes its tiles row-tile-major, ragged row tiles and
+    # two to four N tiles per expert
+    "bf16_ep_share": TINY.scaled(T=3000, d=512, E=2, k=1, I=512, **BF),
 }
 
 
@@ -93,13 +97,15 @@ def test_layer_parity_q30b_t4096():
     print(errs)
 
 
-@pytest.mark.parametrize("name", ["q30b", "q235b"])
+@pytest.mark.parametrize("name", ["q30b", "q235b", "q30b_ep8"])
 def test_layer_parity_full_size_sampled(name):
-    """Qwen3-30B-A3B and Qwen3-235B-A22B layer shapes at 16,384 tokens in the
-    benchmark's launch configuration: all routing artefacts bit-exact; out,
-    dx, top-k-weight and logit gradients on sampled tokens; weight gradients
-    of expert 0, of the busiest expert (q235b's router bias gives it about
-    five times the mean load) and, for q235b, of a median one."""
+    """Qwen3-30B-A3B and Qwen3-235B-A22B layer shapes at 16,384 tokens, and
+    one GPU's share of the former under 8-way expert parallelism (16
+    experts, 131,072 single-row tokens), in the benchmark's launch
+    configuration: all routing artefacts bit-exact; out, dx, top-k-weight and
+    logit gradients on sampled tokens; weight gradients of expert 0, of the
+    busiest expert (q235b's router bias gives it about five times the mean
+    load) and, for q235b, of a median one."""
     wl = S.WORKLOADS[name]
     print(f"case {name}: {wl}", flush=True)
     inp = S.make_inputs(wl, seed=0)

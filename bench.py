@@ -360,6 +360,43 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
         fh.write("\n".join(lines) + "\n")
 
 
+def library_gemms(wl, layer, x, wgu, wd, steps):
+    """The forward GEMM shapes of the layer through torch's own GEMMs, for
+    context: torch._grouped_mm over the expert-sorted rows (no gather, no
+    SwiGLU, no weighting: plain grouped products at the same offsets), and one
+    dense torch.mm with the same FLOPs (all rows against one expert's weight).
+    Times are per call from CUDA events over `steps` calls after one warm-up."""
+    dt = x.dtype
+    R, d, I = wl.R, wl.d, wl.I
+    xp = torch.empty((R, d), dtype=dt, device=x.device)
+    B.permute(x, layer.routing, wl.k, out=xp)
+    offs = layer.routing.offsets[1:].to(torch.int32).contiguous()
+    aw = torch.randn((R, I), device=x.device).to(dt)
+    cases = {
+        "grouped_gateup_fwd": (lambda: torch._grouped_mm(xp, wgu.transpose(1, 2), offs=offs), 4.0 * R * d * I),
+        "grouped_down_fwd": (lambda: torch._grouped_mm(aw, wd.transpose(1, 2), offs=offs), 2.0 * R * d * I),
+        "dense_gateup_fwd": (lambda: torch.mm(xp, wgu[0].t()), 4.0 * R * d * I),
+        "dense_down_fwd": (lambda: torch.mm(aw, wd[0].t()), 2.0 * R * d * I),
+    }
+    out = {}
+    for name, (fn, flop) in cases.items():
+        try:
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            b.synchronize()
+            ms = a.elapsed_time(b) / steps
+            out[name] = {"avg_ms": ms, "tflops": flop / (ms * 1e-3) / 1e12}
+        except Exception as e:  # an op this torch build does not run on the device
+            out[name] = {"error": f"{type(e).__name__}: {str(e).splitlines()[0][:200]}"}
+    del xp, aw
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +407,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the oracle's CPU sample (default: sized for roughly 10-30 s)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="also time the forward GEMM shapes through torch._grouped_mm and torch.mm (context)")
     ap.add_argument("--persistent", action="store_true",
                     help="bf16 row GEMMs as persistent kernels (MOE_FLAG_PERSISTENT)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -448,6 +487,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    lib = library_gemms(wl, layer, x, wgu, wd, args.steps) if args.library_gemms and wl.dtype == "bf16" else None
 
     # forward alone and backward alone (events around each call)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -549,6 +590,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if lib is not None:
+        res["library_gemms"] = lib
     if not args.no_cpu:
         n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(wl.name, wl.T)
         print(f"bench: GPU timing done ({ms_per_step:.3f} ms/step); CPU oracle baseline on {min(n, wl.T)} "

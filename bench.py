@@ -44,6 +44,7 @@ KERNEL_SITES = [
     ("rows_persist_kernel<1, 1, 0>(", "gemm_gateup_fwd"), ("rows_persist_kernel<0, 0, 0>(", "gemm_down_fwd"),
     ("rows_persist_kernel<0, 2, 1>(", "gemm_down_dgrad"), ("rows_persist_kernel<0, 2, 0>(", "gemm_gateup_dgrad"),
     ("wgrad_kernel<0>(", "gemm_down_wgrad"), ("wgrad_kernel<1>(", "gemm_gateup_wgrad"),
+    ("wgrad_persist_kernel<0>(", "gemm_down_wgrad"), ("wgrad_persist_kernel<1>(", "gemm_gateup_wgrad"),
     ("rows8_kernel<1, 0, ", "gemm_gateup_fwd"), ("rows8_kernel<0, 0, ", "gemm_down_fwd"),
     ("rows8_kernel<2, 2, ", "gemm_down_dgrad"), ("rows8_kernel<0, 1, ", "gemm_gateup_dgrad"),
     ("wgrad8_kernel<0, ", "gemm_down_wgrad"), ("wgrad8_kernel<1, ", "gemm_gateup_wgrad"),
@@ -410,7 +411,7 @@ def main():
     ap.add_argument("--library-gemms", action="store_true",
                     help="also time the forward GEMM shapes through torch._grouped_mm and torch.mm (context)")
     ap.add_argument("--persistent", action="store_true",
-                    help="bf16 row GEMMs as persistent kernels (MOE_FLAG_PERSISTENT)")
+                    help="bf16 GEMMs as persistent kernels (MOE_FLAG_PERSISTENT)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 1 GiB once (a plain copy kernel of known size "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")

@@ -112,7 +112,7 @@ FLAG_PERSISTENT = 1
 def make_shape(T, d, E, k, I, dtype=torch.bfloat16, logits_dtype=None, precision="native",
                swiglu_limit=0.0, persistent=False) -> MoeShape:
     """swiglu_limit > 0: the clamped SwiGLU with that limit; persistent: the
-    bf16 row GEMMs as persistent kernels (MOE_FLAG_PERSISTENT; see moe.h)."""
+    bf16 GEMMs as persistent kernels (MOE_FLAG_PERSISTENT; see moe.h)."""
     logits_dtype = dtype if logits_dtype is None else logits_dtype
     return MoeShape(T, d, E, k, I, _DT[dtype], _DT[logits_dtype], _PREC[precision], float(swiglu_limit),
                     FLAG_PERSISTENT if persistent else 0)

@@ -875,6 +875,29 @@ __device__ __forceinline__ int fresh_tid() {
   return t;
 }
 
+// Plain store of a full 256 x 256 tile to C0 (leading dimension ldc; rows
+// >= row_lim and columns >= col_lim skipped), staged inside the 96 KB area
+// beside slot `last ^ 1` (which holds the next tile's first stage) in two
+// rounds of 128 rows: round h holds the waves' MFMA row tiles 2h and 2h + 1,
+// so staged row s is tile row (s / 64) * 128 + 64 h + s % 64.
+__device__ __forceinline__ void persist_store(lds_t* base, int last, f32x16_t (&acc)[TM][TN], bf16_t* C0,
+                                              int64_t ldc, int row_lim, int col_lim) {
+  const int tid = fresh_tid();
+  const int wm = (tid >> 6) / WN, wn = (tid >> 6) % WN;
+  constexpr int S = ep_stride<TBN>();
+  static_assert(128 * S <= kPSlot && 64 * 1024 + 128 * S <= (int)kPSmem, "staging area beside either slot");
+  lds_t* const stg = base + (last ? 64 * 1024 : 0);
+  barrier_lds();  // every wave is done with the last step's slot
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h) barrier_lds();
+    stage_quads<2, TN, S>(stg, wm * 64, wn * (TBN / WN), [&](int i, int j, int r) { return acc[2 * h + i][j][r]; }, tid);
+    barrier_lds();
+    lds_to_global<128, TBN, S>(stg, C0, ldc, row_lim, col_lim,
+                               [h](int s) { return (s >> 6) * 128 + h * 64 + (s & 63); }, tid);
+  }
+}
+
 // Epilogue of a full-height tile, staged inside the 96 KB area beside slot
 // `last ^ 1` (which holds the next tile's first stage).
 template <int EPI>
@@ -884,21 +907,7 @@ __device__ __forceinline__ void persist_epilogue(const RowsArgs& p, const RowTil
   const int wm = (tid >> 6) / WN, wn = (tid >> 6) % WN;
   const int rows_valid = t.seg1 - t.m0;
   if constexpr (EPI == EPI_STORE) {
-    // two rounds of 128 rows: round h holds the waves' MFMA row tiles 2h and
-    // 2h + 1, so staged row s is tile row (s / 64) * 128 + 64 h + s % 64
-    constexpr int S = ep_stride<TBN>();
-    static_assert(128 * S <= kPSlot && 64 * 1024 + 128 * S <= (int)kPSmem, "staging area beside either slot");
-    lds_t* const stg = base + (last ? 64 * 1024 : 0);
-    bf16_t* const C0 = p.C + (int64_t)t.m0 * p.ldc + t.nt * TBN;
-    barrier_lds();  // every wave is done with the last step's slot
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h) barrier_lds();
-      stage_quads<2, TN, S>(stg, wm * 64, wn * (TBN / WN), [&](int i, int j, int r) { return acc[2 * h + i][j][r]; }, tid);
-      barrier_lds();
-      lds_to_global<128, TBN, S>(stg, C0, p.ldc, rows_valid, p.N - t.nt * TBN,
-                                 [h](int s) { return (s >> 6) * 128 + h * 64 + (s & 63); }, tid);
-    }
+    persist_store(base, last, acc, p.C + (int64_t)t.m0 * p.ldc + t.nt * TBN, p.ldc, rows_valid, p.N - t.nt * TBN);
   } else {
     // three rounds of 256 x 128: Aw, then H's gate and up columns; the row
     // weights sit in the 32 KB gap, clear of both the staged tile and the
@@ -1046,6 +1055,137 @@ __global__ __launch_bounds__(NTHR, 1) void wgrad_kernel(WgradArgs p) {
                              p.N, p.M - mt * TBM, p.N - nt * TBN);
 }
 
+// ===========================================================================
+// Persistent weight gradients: one work-group per CU walks its XCD's tiles
+// (the tiles wgrad_kernel deals to that XCD, in the same order) with stride
+// the XCD's work-group count, and issues the next tile's first stage in the
+// current tile's last K step, so that it loads during that step's MFMAs and
+// the epilogue (the LDS plan of the persistent row GEMMs: slots at 0 and
+// 96 KB, the epilogue staged beside the slot being filled).  Tiles of
+// experts with no rows are written as zeros directly, outside the pipeline.
+// ===========================================================================
+struct WTile {
+  int e, mt, nt, seg0, len;
+};
+
+struct WgradWalk {
+  const WgradArgs& p;
+  int xcd, per, total, stride;
+
+  // The schedule is read through the constant address space, so these
+  // uniform loads are scalar: waiting for them (lgkmcnt) does not wait for
+  // the direct loads in flight, as a vector load's vmcnt would.
+  __device__ WTile at(int j) const {
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    WTile t;
+    const int s = j / per, rem = j - s * per;
+    t.e = ((cptr)p.xorder)[s * 8 + xcd];
+    t.mt = rem / p.n_tiles;
+    t.nt = rem - t.mt * p.n_tiles;
+    t.seg0 = t.e >= 0 ? ((cptr)p.offsets)[t.e] : 0;
+    t.len = t.e >= 0 ? ((cptr)p.offsets)[t.e + 1] - t.seg0 : 0;
+    return t;
+  }
+  // zeros for the tile of an expert with no rows
+  __device__ void zero_tile(const WTile& t) const {
+    constexpr int CPR = TBN / 8;
+    bf16_t* const C0 = p.C + (int64_t)t.e * p.c_estride + (int64_t)t.mt * TBM * p.N + t.nt * TBN;
+    const int row_lim = p.M - t.mt * TBM, col_lim = p.N - t.nt * TBN;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int q = (int)threadIdx.x; q < TBM * CPR; q += NTHR) {
+      const int row = q / CPR, c8 = q % CPR;
+      if (row < row_lim && c8 * 8 < col_lim)
+        __builtin_nontemporal_store(z, (u32x4_t*)(C0 + (int64_t)row * p.N + c8 * 8));
+    }
+  }
+  // the first of this work-group's tiles at or after j whose expert has
+  // rows (total if none), zeroing the empty experts' tiles passed on the way
+  __device__ int next(int j, WTile& t) const {
+    for (; j < total; j += stride) {
+      t = at(j);
+      if (t.e < 0) continue;
+      if (t.len > 0) return j;
+      zero_tile(t);
+    }
+    return total;
+  }
+};
+
+// Issues the next tile's first stage in the current tile's last K step: its
+// row indices load right after the step's barrier, its direct loads leave in
+// the last sub-step (bounds-checked); oa / ob become the next tile's
+// operands, advanced past that stage.
+template <int TAG>
+struct WNextIssue {
+  const WgradArgs& p;
+  const WTile& t;
+  bool more;
+  OpKMg<TBM, TAG == 0>& oa;
+  OpKMg<TBN, TAG == 1>& ob;
+  __device__ void early() {
+    if (!more) return;
+    oa.init(p.A, p.lda, p.tok, t.seg0, t.mt * TBM, p.M, t.len);
+    ob.init(p.B, p.ldb, p.tok, t.seg0, t.nt * TBN, p.N, t.len);
+  }
+  __device__ void issue(lds_t* dst) {
+    if (!more) return;
+    issue_stage<false>(oa, ob, 0, dst);
+    oa.advance();
+    ob.advance();
+  }
+};
+
+template <int TAG>
+__global__ __launch_bounds__(NTHR, 1) void wgrad_persist_kernel(WgradArgs p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  using OA = OpKMg<TBM, TAG == 0>;
+  using OB = OpKMg<TBN, TAG == 1>;
+  const int per = p.m_tiles * p.n_tiles;
+  const WgradWalk w{p, (int)(blockIdx.x & 7), per, (p.E + 7) / 8 * per, (int)(gridDim.x >> 3)};
+  WTile t;
+  int j = w.next((int)(blockIdx.x >> 3), t);
+  if (j >= w.total) return;
+  lds_t* const base = (lds_t*)smem;
+  OA oa;
+  OB ob;
+  oa.init(p.A, p.lda, p.tok, t.seg0, t.mt * TBM, p.M, t.len);
+  ob.init(p.B, p.ldb, p.tok, t.seg0, t.nt * TBN, p.N, t.len);
+  wait_vmcnt<0>();  // the first stage's row indices
+  issue_stage<false>(oa, ob, 0, base);
+  oa.advance();
+  ob.advance();
+  int slot = 0;
+  for (;;) {
+    WTile tn;
+    const int jn = w.next(j + w.stride, tn);
+    const bool more = jn < w.total;
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    const int nk = (int)cdiv(t.len, BK);  // >= 1: empty experts never get here
+    const int nfa = oa.nfull(nk), nfb = ob.nfull(nk);
+    const int nf = nfa < nfb ? nfa : nfb;
+    int kt = 0;
+    for (; kt + 1 < nf; ++kt) kstep<TM, true, true, kPSlot>(oa, ob, kt, base, slot, acc);
+    for (; kt + 1 < nk; ++kt) kstep<TM, true, false, kPSlot>(oa, ob, kt, base, slot, acc);
+    const int last = slot;
+    {
+      WNextIssue<TAG> is{p, tn, more, oa, ob};
+      kstep_core<TM, true, kPSlot, BK / 16 - 1, OA, OB>(is, base, slot, acc);
+    }
+    persist_store(base, last, acc,
+                  p.C + (int64_t)t.e * p.c_estride + (int64_t)t.mt * TBM * p.N + t.nt * TBN, p.N,
+                  p.M - t.mt * TBM, p.N - t.nt * TBN);
+    if (!more) break;
+    j = jn;
+    t = tn;
+  }
+}
+
 // Dynamic LDS: the operand ring, or the largest epilogue staging area.
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t kRingBytes = (size_t)NSTAGE * (TBM + TBN) * BK * 2;
@@ -1095,12 +1235,20 @@ hipError_t launch_rows_persist(const LaunchCtx& c, const char* name, RowsArgs p,
 }
 
 template <int TAG>
-hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p, int E) {
+hipError_t launch_wgrad(const LaunchCtx& c, const char* name, const WgradArgs& p, int E, bool persistent) {
+  const int64_t per_xcd_tiles = cdiv(E, 8) * p.m_tiles * p.n_tiles;
+  if (persistent) {
+    hipError_t e = allow_smem_once<wgrad_persist_kernel<TAG>>(kPSmem);
+    if (e != hipSuccess) return e;
+    const int64_t per_xcd = std::min<int64_t>(std::max(cu_count() / 8, 1), per_xcd_tiles);
+    MOE_LAUNCH(c, name, wgrad_persist_kernel<TAG>, dim3((unsigned)(8 * per_xcd)), dim3(NTHR), kPSmem, p);
+    return hipSuccess;
+  }
   {
     hipError_t e = allow_smem_once<wgrad_kernel<TAG>>(kSmem);
     if (e != hipSuccess) return e;
   }
-  const unsigned nblocks = (unsigned)(cdiv(E, 8) * 8 * p.m_tiles * p.n_tiles);
+  const unsigned nblocks = (unsigned)(8 * per_xcd_tiles);
   MOE_LAUNCH(c, name, wgrad_kernel<TAG>, dim3(nblocks), dim3(NTHR), kSmem, p);
   return hipSuccess;
 }
@@ -1169,7 +1317,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.M = a.d; p.N = a.I; p.m_tiles = (int)cdiv(a.d, TBM); p.n_tiles = (int)cdiv(a.I, TBN);
     p.offsets = a.offsets; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_d; p.c_estride = d * I;
-    err = launch_wgrad<0>(c, "gemm_down_wgrad", p, a.E);
+    err = launch_wgrad<0>(c, "gemm_down_wgrad", p, a.E, a.persistent);
     if (err != hipSuccess) return err;
   }
   {  // gate/up dgrad: dXp = dH W_gate_up[e]
@@ -1190,7 +1338,7 @@ hipError_t bf16_bwd_gemms(const LaunchCtx& c, const LayerArgs& a, const void* do
     p.M = 2 * a.I; p.N = a.d; p.m_tiles = (int)cdiv(2 * a.I, TBM); p.n_tiles = (int)cdiv(a.d, TBN);
     p.offsets = a.offsets; p.xorder = a.xorder;
     p.C = (bf16_t*)dW_gu; p.c_estride = 2 * I * d;
-    err = launch_wgrad<1>(c, "gemm_gateup_wgrad", p, a.E);
+    err = launch_wgrad<1>(c, "gemm_gateup_wgrad", p, a.E, a.persistent);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -106,16 +106,18 @@ typedef struct {
   int32_t flags;        /* moe_flags; unknown bits are rejected            */
 } moe_shape;
 
-/* MOE_FLAG_PERSISTENT: the bf16 row GEMMs (gate/up and down forward, down
- * and gate/up data gradients; also the forward of MOE_PREC_FP8_BWD) run as
- * persistent kernels, one work-group per CU walking its XCD's tiles, that
- * issue the next tile's first stage (its gathered token rows and weight
- * slice) during the current tile's last K step, so that it loads while that
- * step's MFMAs run and while the epilogue stores: the one-GPU form of the
- * overlapped pipeline in "Prime Intellect's Prime Mega MoE Trains Giant AI
- * Models 55% Faster", section "One kernel overlaps the pipeline".  Results
- * are bit-identical to the default engine's (every tile runs at full height,
- * with the same MFMA order).  Other precisions and MOE_F32 ignore the flag. */
+/* MOE_FLAG_PERSISTENT: the bf16 GEMMs (gate/up and down forward, down and
+ * gate/up data gradients, and, in MOE_PREC_NATIVE, both weight gradients;
+ * also the forward of MOE_PREC_FP8_BWD) run as persistent kernels, one
+ * work-group per CU walking its XCD's tiles, that issue the next tile's
+ * first stage (its gathered token rows and weight slice, or for a weight
+ * gradient its first 64 rows of both operands) during the current tile's
+ * last K step, so that it loads while that step's MFMAs run and while the
+ * epilogue stores: the one-GPU form of the overlapped pipeline in "Prime
+ * Intellect's Prime Mega MoE Trains Giant AI Models 55% Faster", section
+ * "One kernel overlaps the pipeline".  Results are bit-identical to the
+ * default engine's (every tile runs at full height, with the same MFMA
+ * order).  Other precisions and MOE_F32 ignore the flag. */
 typedef enum { MOE_FLAG_PERSISTENT = 1 } moe_flags;
 
 /* swiglu_limit > 0 selects the clamped SwiGLU that "Mario/overlap moe kernel

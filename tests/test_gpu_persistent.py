@@ -1,9 +1,10 @@
-"""Persistent row GEMMs (MOE_FLAG_PERSISTENT) against the oracle and
-against the default engine.
+"""Persistent GEMMs (MOE_FLAG_PERSISTENT: the bf16 row GEMMs and weight
+gradients) against the oracle and against the default engine.
 
-With the flag, one work-group per CU walks its XCD's row tiles and issues
-the next tile's first stage (gathered token rows and weight slice) during
-the current tile's last K step ("Prime Intellect's Prime Mega MoE Trains
+With the flag, one work-group per CU walks its XCD's tiles and issues the
+next tile's first stage (gathered token rows and weight slice; for a weight
+gradient, its first rows of both operands) during the current tile's last K
+step ("Prime Intellect's Prime Mega MoE Trains
 Giant AI Models 55% Faster", section "One kernel overlaps the pipeline").
 Every output row still takes the same MFMAs in the same K order, so all
 results must equal the default engine's bit for bit, and the oracle's

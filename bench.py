@@ -361,6 +361,49 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
         fh.write("\n".join(lines) + "\n")
 
 
+def attainable_peaks(wl, dev, reps: int = 10):
+    """Measured attainable peaks on this GPU, for the roofline fractions
+    beside the published ones: a large square GEMM through torch (hipBLASLt)
+    in bf16, and in fp8 (torch._scaled_mm, unit scales) for the fp8
+    workloads, and torch's streaming copy of 1 GiB (bytes read + written;
+    the row passes of this library run faster than it, so it is reported,
+    not used as a ceiling)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    out = {}
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    bt = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    out["gemm_bf16_tflops"] = 2.0 * n ** 3 / timed(lambda: torch.mm(a, bt.t())) / 1e12
+    out["gemm_bf16_shape"] = f"{n}x{n}x{n}, torch.mm (hipBLASLt), B transposed"
+    if wl.precision in FP8:
+        try:
+            a8, b8 = a.to(torch.float8_e4m3fn), bt.to(torch.float8_e4m3fn)
+            one = torch.ones((), device=dev)
+            out["gemm_fp8_tflops"] = 2.0 * n ** 3 / timed(
+                lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)) / 1e12
+        except Exception as e:  # an op this torch build does not run on the device
+            out["gemm_fp8_error"] = f"{type(e).__name__}: {str(e).splitlines()[0][:200]}"
+    del a, bt
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    out["copy_gbs"] = 2.0 * COPY_BYTES / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def library_gemms(wl, layer, x, wgu, wd, steps):
     """The forward GEMM shapes of the layer through torch's own GEMMs, for
     context: torch._grouped_mm over the expert-sorted rows (no gather, no
@@ -490,6 +533,7 @@ def main():
         del src, dst
 
     lib = library_gemms(wl, layer, x, wgu, wd, args.steps) if args.library_gemms and wl.dtype == "bf16" else None
+    attain = attainable_peaks(wl, dev)
 
     # forward alone and backward alone (events around each call)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -536,9 +580,15 @@ def main():
             if kind == "flop":
                 entry["tflops"] = amt / (avg * 1e-3) / 1e12
                 entry["mfma_frac"] = entry["tflops"] / mfma_peak(wl, name)
+                att = attain.get("gemm_fp8_tflops" if mfma_peak(wl, name) == PEAK_FP8_TFLOPS
+                                 else "gemm_bf16_tflops") if wl.dtype == "bf16" else None
+                if att:
+                    entry["frac_attainable"] = entry["tflops"] / att
             else:
                 entry["gbs"] = amt / (avg * 1e-3) / 1e9
                 entry["hbm_frac"] = entry["gbs"] / PEAK_HBM_GBS
+                # torch's copy kernel is no ceiling: the row passes here run faster
+                entry["frac_of_torch_copy"] = entry["gbs"] / attain["copy_gbs"]
         kernels[name] = entry
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
     kind, amt = work[dom]
@@ -551,6 +601,13 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": amt / (avg * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same against the measured attainable peak (a square GEMM of the
+    # kernel's dtype through the vendor library)
+    att = attain.get("gemm_fp8_tflops" if roof["peak"] == PEAK_FP8_TFLOPS else "gemm_bf16_tflops") \
+        if kind == "flop" and wl.dtype == "bf16" else None
+    if att:
+        roof["attainable"] = att
+        roof["frac_attainable"] = roof["achieved"] / att
     tr = measured_traffic(wl, dom)
     roof["traffic"] = None if tr is None else tr["bytes"]
     if tr is not None:
@@ -590,6 +647,7 @@ def main():
         "gemm_mfma_util": (wl.flops_fwd() + wl.flops_bwd()) / (gemm_ms * 1e-3) / 1e12 / mfma_peak(wl),
         "roofline": roof,
         "kernels": kernels,
+        "attainable": attain,
     }
     if lib is not None:
         res["library_gemms"] = lib

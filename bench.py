@@ -104,15 +104,18 @@ def kernel_work(wl):
         # bf16 in, one code byte out per element, plus scales: an fp32 scale
         # per 128 values of a row (blockwise) or an E8M0 byte per 32 (MX) --
         # the same 1/32 byte per value; weights: an fp32 scale per 128 x 128
-        # block (blockwise) or a byte per 32 values (MX), in both layouts
+        # block (blockwise) or a byte per 32 values (MX)
         q = lambda n: float(n * 2 + n + n // 32)
         ws = (lambda n: n // 32) if wl.precision == "mxfp8" else (lambda n: 4 * n // 16384)
-        nl = 1 if wl.precision == "fp8_bwd" else 2   # fp8_bwd encodes the transposed layout only
+        # layouts a weight encoder writes: blockwise one (a 128 x 128 block
+        # has one scale whichever axis a GEMM contracts, so the data
+        # gradients read the forward codes); MX two (its 1 x 32 blocks run
+        # along one axis, so the data gradients get a transposed encoding)
+        nl = 2 if wl.precision == "mxfp8" else 1
         qw = lambda n: float(n * 2 + nl * (n + ws(n)))
         work.update({
             "quant_x": ("byte", q(T * d)), "quant_dout": ("byte", q(T * d)),
             "quant_aw": ("byte", q(R * I)),
-            # both layouts (the transposed one is kept for the backward)
             "quant_w_gate_up": ("byte", qw(E * 2 * I * d)),
             "quant_w_down": ("byte", qw(E * d * I)),
             "quant_dout_tok": ("byte", q(R * d) + 4 * R), "quant_x_tok": ("byte", q(R * d) + 4 * R),

@@ -314,11 +314,16 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
     stats = _csv_rows(stats_dir, "kernel_stats.csv")
     lines += ["Kernel durations (rocprofv3 --kernel-trace --stats):", "",
               "| launch | kernel | calls | avg us | % GPU time |", "|---|---|---|---|---|"]
+    other = 0.0
     for r in sorted(stats, key=lambda r: -float(r["Percentage"])):
         name = r["Name"]
+        if site_of(name) is None:  # torch's and the runtime's own kernels
+            other += float(r["Percentage"])
+            continue
         short = name.replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
-        lines.append(f"| {site_of(name) or '-'} | `{short}` | {r['Calls']} | "
+        lines.append(f"| {site_of(name)} | `{short}` | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"Left out above: torch's and the runtime's own kernels ({other:.2f}% of GPU time)."]
     if fetch_dir and write_dir:
         per = {}
         for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -326,7 +331,7 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
                 if r["Counter_Name"] != key:
                     continue
                 site = site_of(r["Kernel_Name"])
-                if site is None and "moe::" not in r["Kernel_Name"]:
+                if site is None and "copyBuffer" in r["Kernel_Name"]:  # the runtime's device copy
                     site = "calibration copy"
                 if site is None:
                     continue
@@ -334,8 +339,9 @@ def rocprof_summary(wl, out: str, stats_dir: str, fetch_dir: str | None = None, 
         cal = per.get("calibration copy")
         if not cal or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
             raise SystemExit("no calibration copy kernel in the counter runs (bench.py --copy-calibration)")
-        # the 1 GiB copy is by far the largest dispatch outside the layer (the
-        # others are torch's small fills), so it is the maximum, not the mean
+        # the 1 GiB copies (the calibration copy and the attainable-peak
+        # copy, the same size) are the runtime's largest copies; smaller ones
+        # move inputs, so the maximum, not the mean
         cal = {key: [max(v)] for key, v in cal.items()}
         f_fetch = COPY_BYTES / float(np.mean(cal["FETCH_SIZE"]))
         f_write = COPY_BYTES / float(np.mean(cal["WRITE_SIZE"]))

@@ -785,7 +785,11 @@ struct RowTile {
 // same expert and gives the range.
 __device__ __forceinline__ RowTile decode_tile(const RowsArgs& p, int L) {
   const int T = L / p.n_tiles;
-  const int4 d0 = p.tiles[T];  // {expert, first row, segment end, expert's first tile}
+  // {expert, first row, segment end, expert's first tile}, read through the
+  // constant address space: a scalar load, so that in the persistent loop
+  // waiting for it does not wait for the direct loads in flight
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  const i32x4_t d0 = ((const __attribute__((address_space(4))) i32x4_t*)p.tiles)[T];
   const int first = d0.w;
   const int seg0 = d0.y - (T - first) * TBM;
   const int nrt = (d0.z - seg0 + TBM - 1) / TBM;
